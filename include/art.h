@@ -1,0 +1,160 @@
+/*
+ * libart -- ART (Attention Run-time Termination) decode attention for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What the library computes
+ * -------------------------
+ * For every unit (batch b, kv head h) with G = num_q_heads / num_kv_heads
+ * query heads (query head h*G + g uses kv head h):
+ *
+ *   * the KV cache of sequence b is split into blocks of `block_size` tokens
+ *     (the last block may be partial) and walked in a traversal order pi
+ *     (ART paper, section 3.1: blockwise FlashAttention-style execution over
+ *     tiles {(K_t, V_t)}; gist.science explainer of the paper, section 2.4:
+ *     recency-first / other orders, block 0 always evaluated first);
+ *   * after t blocks the partial output O^(t) = softmax(q K_S^T / sqrt(d)) V_S
+ *     over the tokens S of the first t blocks (ART paper, section 3.1,
+ *     Eq. (1) restricted to the processed blocks);
+ *   * a probe x^(t) = head dims 0, 4, 8, ..., d-4 of O^(t) for each of the G
+ *     query heads, concatenated (ART paper, section 3.2: a fixed scattered
+ *     subsample of the head dims);
+ *   * for t >= 2 two metrics (gist.science explainer, section 2.2):
+ *       d_scale = | |x^(t)| - |x^(t-1)| | / |x^(t-1)|
+ *       d_dir   = 1 - cos(x^(t), x^(t-1))
+ *     a check is stable when d_scale < eps_scale and d_dir < eps_dir (strict;
+ *     a zero-norm probe is never stable);
+ *   * with patience p (gist.science explainer, section 2.3) the unit stops
+ *     after block t once the last p checks were all stable; no further KV
+ *     block of that unit is loaded or computed.
+ *
+ * Outputs: out[b][h*G+g][:] = O^(stop_idx) in fp32, stop_idx[b][h] = number
+ * of traversal blocks processed (1..T'), optional blocks_issued[b][h] =
+ * number of blocks whose K/V loads were issued (processed + discarded
+ * prefetch + speculative split work + recomputation).  In ART_MODE_FULL no
+ * criterion is evaluated and stop_idx = T' (plain blockwise attention).
+ * A unit with no tokens (context length 0, or kept_count 0) gets out = 0
+ * and stop_idx = 0.
+ *
+ * Conventions (all entry points)
+ * ------------------------------
+ *   * Every data pointer is a DEVICE pointer owned by the caller; the
+ *     library never allocates, frees or retains memory.  Shape and parameter
+ *     structs are HOST pointers, read during the call only.
+ *   * art_decode is asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL = the default stream).  Argument errors are detected on the host
+ *     and returned before anything is enqueued.  Errors only visible on the
+ *     device (a malformed kept list, a look-back timeout) are recorded in the
+ *     workspace; read them with art_last_error after synchronizing `stream`.
+ *   * Nothing prints, throws or exits.  Calls that share one workspace must
+ *     not overlap in time.
+ *
+ * Supported set (anything else returns ART_ERR_UNSUPPORTED):
+ *   dtype ART_DT_BF16 with head_dim 128, or ART_DT_F32 with head_dim 64;
+ *   G = num_q_heads / num_kv_heads in {1, 2, 4}; block_size 64;
+ *   page_size 0 (contiguous) or a multiple of 16 that divides 64 or is
+ *   divided by it.
+ */
+#ifndef LIBART_ART_H
+#define LIBART_ART_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ART_OK = 0,
+  ART_ERR_INVALID_ARG = 1,   /* null pointer, bad size, bad parameter       */
+  ART_ERR_UNSUPPORTED = 2,   /* valid but outside the supported set         */
+  ART_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required  */
+  ART_ERR_HIP = 4,           /* a HIP runtime call or launch failed         */
+  ART_ERR_TIMEOUT = 5,       /* device: a split look-back wait timed out    */
+  ART_ERR_DEVICE_INPUT = 6   /* device: a kept list was out of range or not
+                                strictly ascending where required           */
+} art_status;
+
+typedef enum { ART_DT_F32 = 0, ART_DT_BF16 = 1 } art_dtype;
+
+/* Traversal order pi over the candidate blocks (all blocks, or the kept
+ * list).  Block 0, when it is a candidate, is always first (gist.science
+ * explainer, section 2.4).  NATURAL: ascending block index.  RECENT_FIRST:
+ * descending (most recent first).  GIVEN: the kept list's own order; needs a
+ * kept list. */
+typedef enum { ART_ORDER_NATURAL = 0, ART_ORDER_RECENT_FIRST = 1, ART_ORDER_GIVEN = 2 } art_order;
+
+typedef enum { ART_MODE_FULL = 0, ART_MODE_ART = 1 } art_mode;
+
+typedef struct {
+  int32_t block_size;    /* tokens per ART block (64)                        */
+  float eps_scale;       /* tau: threshold on d_scale, >= 0, finite          */
+  float eps_dir;         /* phi: threshold on d_dir (1 - cos), >= 0, finite  */
+  int32_t patience;      /* p >= 1 consecutive stable checks                 */
+  int32_t order;         /* art_order                                        */
+  int32_t mode;          /* art_mode                                         */
+  int32_t split_blocks;  /* blocks per split-KV chunk; 0 = library's choice,
+                            a value >= T' means one chunk per unit           */
+} art_params;
+
+typedef struct {
+  int32_t batch;          /* B                                               */
+  int32_t num_q_heads;    /* Hq                                              */
+  int32_t num_kv_heads;   /* Hkv (Hq % Hkv == 0)                             */
+  int32_t head_dim;       /* d                                               */
+  int32_t dtype;          /* art_dtype of q, K and V                         */
+  int32_t page_size;      /* 0: contiguous K/V [B][Hkv][max_ctx][d];
+                             else paged K/V [num_pages][Hkv][page_size][d]   */
+  int32_t max_ctx;        /* contiguous: row stride in tokens; every
+                             context_lens[b] <= max_ctx                      */
+  int32_t max_pages;      /* paged: row stride of block_table; every
+                             context_lens[b] <= max_pages * page_size        */
+  int32_t num_pages;      /* paged: pages in the pool (bounds check only)    */
+  int32_t max_kept;       /* row stride of kept_blocks; 0 = no kept list     */
+} art_shape;
+
+/* Bytes of device workspace art_decode needs for this shape and params
+ * (never 0).  Returns 0 if the shape or params are invalid. */
+size_t art_workspace_size(const art_shape* shape, const art_params* params);
+
+/* Blockwise ART decode attention (see the top of this file).
+ *
+ *   q             [B][Hq][d] in `dtype`
+ *   k, v          contiguous [B][Hkv][max_ctx][d] or paged
+ *                 [num_pages][Hkv][page_size][d], in `dtype`
+ *   context_lens  int32 [B], 0 <= len (bounded as described in art_shape)
+ *   block_table   int32 [B][max_pages] page ids (paged only, else NULL);
+ *                 entries past ceil(len/page_size) are never read
+ *   kept_blocks   int32 [B][Hkv][max_kept] candidate block indices, or NULL;
+ *                 strictly ascending for NATURAL/RECENT_FIRST, distinct and
+ *                 in [0, ceil(len/block_size)) for all orders
+ *   kept_count    int32 [B][Hkv] entries used per unit (NULL iff kept_blocks)
+ *   out           fp32 [B][Hq][d]                  (written)
+ *   stop_idx      int32 [B][Hkv]                   (written)
+ *   blocks_issued int32 [B][Hkv] or NULL           (written)
+ *   workspace     device buffer of >= art_workspace_size() bytes, 256-byte
+ *                 aligned; its contents on entry do not matter
+ */
+art_status art_decode(const art_shape* shape, const art_params* params,
+                      const void* q, const void* k, const void* v,
+                      const int32_t* context_lens, const int32_t* block_table,
+                      const int32_t* kept_blocks, const int32_t* kept_count,
+                      float* out, int32_t* stop_idx, int32_t* blocks_issued,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Device-side error recorded by the last art_decode that used `workspace`
+ * (ART_OK, ART_ERR_TIMEOUT or ART_ERR_DEVICE_INPUT).  Synchronous: reads
+ * 4 bytes from the workspace; call after synchronizing the decode's stream. */
+art_status art_last_error(const void* workspace);
+
+/* Static English description of a status code. */
+const char* art_status_string(art_status status);
+
+/* Probe-stride constant used for x^(t) (4), for callers that report it. */
+int32_t art_probe_stride(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBART_ART_H */

@@ -1,0 +1,184 @@
+"""Thin ctypes binding over libart's C ABI (include/art.h).
+
+Argument marshalling only: every step of the decode runs in the HIP
+kernels of libart.so.  torch is used for device memory and streams.  The
+library must have been built (``python -m kv_cache_early_amd.build``); there
+is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libart.so")
+
+ART_OK = 0
+ART_ERR_INVALID_ARG = 1
+ART_ERR_UNSUPPORTED = 2
+ART_ERR_WORKSPACE = 3
+ART_ERR_HIP = 4
+ART_ERR_TIMEOUT = 5
+ART_ERR_DEVICE_INPUT = 6
+
+ART_DT_F32 = 0
+ART_DT_BF16 = 1
+ART_ORDER_NATURAL = 0
+ART_ORDER_RECENT_FIRST = 1
+ART_ORDER_GIVEN = 2
+ART_MODE_FULL = 0
+ART_MODE_ART = 1
+
+EXPORTS = ("art_workspace_size", "art_decode", "art_last_error", "art_status_string", "art_probe_stride")
+
+
+class art_params(ctypes.Structure):
+    _fields_ = [("block_size", ctypes.c_int32), ("eps_scale", ctypes.c_float), ("eps_dir", ctypes.c_float),
+                ("patience", ctypes.c_int32), ("order", ctypes.c_int32), ("mode", ctypes.c_int32),
+                ("split_blocks", ctypes.c_int32)]
+
+
+class art_shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("max_ctx", ctypes.c_int32), ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("max_kept", ctypes.c_int32)]
+
+
+class ArtError(RuntimeError):
+    def __init__(self, status: int, what: str = "art_decode"):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libart.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libart.so not built at {path}; run `python -m kv_cache_early_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
+    lib.art_workspace_size.argtypes = [ctypes.POINTER(art_shape), ctypes.POINTER(art_params)]
+    lib.art_workspace_size.restype = ctypes.c_size_t
+    lib.art_decode.argtypes = [ctypes.POINTER(art_shape), ctypes.POINTER(art_params), vp, vp, vp, vp, vp, vp, vp,
+                               vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.art_decode.restype = ctypes.c_int
+    lib.art_last_error.argtypes = [vp]
+    lib.art_last_error.restype = ctypes.c_int
+    lib.art_status_string.argtypes = [ctypes.c_int]
+    lib.art_status_string.restype = ctypes.c_char_p
+    lib.art_probe_stride.argtypes = []
+    lib.art_probe_stride.restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().art_status_string(int(status)).decode()
+
+
+def make_shape(batch, num_q_heads, num_kv_heads, head_dim, dtype, page_size=0, max_ctx=0, max_pages=0,
+               num_pages=0, max_kept=0) -> art_shape:
+    return art_shape(batch, num_q_heads, num_kv_heads, head_dim, dtype, page_size, max_ctx, max_pages,
+                     num_pages, max_kept)
+
+
+def make_params(eps_scale=1e-3, eps_dir=1e-4, patience=2, order=ART_ORDER_RECENT_FIRST, mode=ART_MODE_ART,
+                block_size=64, split_blocks=0) -> art_params:
+    return art_params(block_size, eps_scale, eps_dir, patience, order, mode, split_blocks)
+
+
+def workspace_size(shape: art_shape, params: art_params) -> int:
+    return int(load().art_workspace_size(ctypes.byref(shape), ctypes.byref(params)))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def decode_raw(shape: art_shape, params: art_params, q, k, v, context_lens, block_table, kept_blocks, kept_count,
+               out, stop_idx, blocks_issued, workspace, workspace_bytes: int, stream: Optional[int]) -> int:
+    """Call art_decode with raw device pointers taken from tensors; returns the status."""
+    return int(load().art_decode(ctypes.byref(shape), ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v),
+                                 _ptr(context_lens), _ptr(block_table), _ptr(kept_blocks), _ptr(kept_count),
+                                 _ptr(out), _ptr(stop_idx), _ptr(blocks_issued), _ptr(workspace),
+                                 workspace_bytes, stream))
+
+
+def last_error(workspace) -> int:
+    return int(load().art_last_error(_ptr(workspace)))
+
+
+@dataclass
+class DecodeResult:
+    out: object            # fp32 [B, Hq, d]
+    stop_idx: object       # int32 [B, Hkv]
+    blocks_issued: object  # int32 [B, Hkv]
+
+
+class ArtDecoder:
+    """Owns a workspace and calls art_decode on torch device tensors.
+
+    Tensors: q [B, Hq, d]; k, v contiguous [B, Hkv, max_ctx, d] or paged
+    [num_pages, Hkv, page, d]; bf16 data may be passed as torch.bfloat16 or
+    as int16/uint16 bit patterns.  All tensors must be contiguous and on the
+    same device.
+    """
+
+    def __init__(self, device=None):
+        import torch
+        self.torch = torch
+        self.device = torch.device(device or "cuda")
+        self._ws = None
+        load()
+
+    def workspace(self, nbytes: int):
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = self.torch.empty(max(nbytes, 256), dtype=self.torch.uint8, device=self.device)
+        return self._ws
+
+    def decode(self, q, k, v, context_lens, *, dtype: int, page_size: int = 0, block_table=None,
+               kept_blocks=None, kept_count=None, eps_scale=1e-3, eps_dir=1e-4, patience=2,
+               order=ART_ORDER_RECENT_FIRST, mode=ART_MODE_ART, block_size=64, split_blocks=0,
+               out=None, stop_idx=None, blocks_issued=None, stream=None) -> DecodeResult:
+        torch = self.torch
+        B, Hq, d = q.shape
+        Hkv = k.shape[1]
+        for t in (q, k, v, context_lens, block_table, kept_blocks, kept_count):
+            if t is not None and not t.is_contiguous():
+                raise ValueError("art_decode needs contiguous tensors")
+        shape = make_shape(B, Hq, Hkv, d, dtype, page_size,
+                           max_ctx=k.shape[2] if page_size == 0 else 0,
+                           max_pages=block_table.shape[1] if block_table is not None else 0,
+                           num_pages=k.shape[0] if page_size else 0,
+                           max_kept=kept_blocks.shape[2] if kept_blocks is not None else 0)
+        params = make_params(eps_scale, eps_dir, patience, order, mode, block_size, split_blocks)
+        nbytes = workspace_size(shape, params)
+        if nbytes == 0:
+            raise ArtError(ART_ERR_INVALID_ARG, "art_workspace_size")
+        ws = self.workspace(nbytes)
+        if out is None:
+            out = torch.empty((B, Hq, d), dtype=torch.float32, device=self.device)
+        if stop_idx is None:
+            stop_idx = torch.empty((B, Hkv), dtype=torch.int32, device=self.device)
+        if blocks_issued is None:
+            blocks_issued = torch.empty((B, Hkv), dtype=torch.int32, device=self.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device).cuda_stream
+        st = decode_raw(shape, params, q, k, v, context_lens, block_table, kept_blocks, kept_count, out, stop_idx,
+                        blocks_issued, ws, ws.numel(), stream)
+        if st != ART_OK:
+            raise ArtError(st)
+        return DecodeResult(out, stop_idx, blocks_issued)
+
+    def device_error(self) -> int:
+        """Device-side status of the last decode (synchronizes the device first)."""
+        self.torch.cuda.synchronize(self.device)
+        return last_error(self._ws) if self._ws is not None else ART_OK

@@ -1,0 +1,185 @@
+// libart C-ABI front end: argument validation, work decomposition,
+// workspace layout and kernel launches.  The operations themselves are
+// described in include/art.h; the kernels live in art_kernels.hip.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+
+#include "art.h"
+#include "art_internal.h"
+
+namespace {
+
+constexpr int kBlockTokens = 64;
+constexpr int kProbeStride = 4;
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool finite_nonneg(float x) { return std::isfinite(x) && x >= 0.f; }
+
+// Upper bound on T' (traversal blocks per unit) implied by the shape.
+int64_t max_traversal(const art_shape& s) {
+  if (s.max_kept > 0) return s.max_kept;
+  int64_t tokens = s.page_size == 0 ? (int64_t)s.max_ctx : (int64_t)s.max_pages * s.page_size;
+  return (tokens + kBlockTokens - 1) / kBlockTokens;
+}
+
+art_status validate(const art_shape* sp, const art_params* pp) {
+  if (!sp || !pp) return ART_ERR_INVALID_ARG;
+  const art_shape& s = *sp;
+  const art_params& p = *pp;
+  if (s.batch < 0 || s.num_q_heads <= 0 || s.num_kv_heads <= 0 || s.head_dim <= 0) return ART_ERR_INVALID_ARG;
+  if (s.num_q_heads % s.num_kv_heads != 0) return ART_ERR_INVALID_ARG;
+  if (s.dtype != ART_DT_F32 && s.dtype != ART_DT_BF16) return ART_ERR_INVALID_ARG;
+  if (s.page_size < 0 || s.max_ctx < 0 || s.max_pages < 0 || s.num_pages < 0 || s.max_kept < 0)
+    return ART_ERR_INVALID_ARG;
+  if (p.block_size <= 0 || p.patience < 1 || p.split_blocks < 0) return ART_ERR_INVALID_ARG;
+  if (!finite_nonneg(p.eps_scale) || !finite_nonneg(p.eps_dir)) return ART_ERR_INVALID_ARG;
+  if (p.order < ART_ORDER_NATURAL || p.order > ART_ORDER_GIVEN) return ART_ERR_INVALID_ARG;
+  if (p.mode != ART_MODE_FULL && p.mode != ART_MODE_ART) return ART_ERR_INVALID_ARG;
+  if (p.order == ART_ORDER_GIVEN && s.max_kept == 0) return ART_ERR_INVALID_ARG;
+  if (s.page_size > 0 && s.page_size % 16 != 0) return ART_ERR_INVALID_ARG;
+  // supported set
+  const int G = s.num_q_heads / s.num_kv_heads;
+  if (!((s.dtype == ART_DT_BF16 && s.head_dim == 128) || (s.dtype == ART_DT_F32 && s.head_dim == 64)))
+    return ART_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4) return ART_ERR_UNSUPPORTED;
+  if (p.block_size != kBlockTokens) return ART_ERR_UNSUPPORTED;
+  if (s.page_size > 0 && !(kBlockTokens % s.page_size == 0 || s.page_size % kBlockTokens == 0))
+    return ART_ERR_UNSUPPORTED;
+  // index ranges the kernels compute in 32-bit
+  const int64_t units = (int64_t)s.batch * s.num_kv_heads;
+  if (units > (1 << 26) || max_traversal(s) > (1 << 24)) return ART_ERR_UNSUPPORTED;
+  return ART_OK;
+}
+
+// Traversal blocks per work item.  ART mode currently walks each unit in
+// one work item (exact sequential stopping); full mode splits long units so
+// that the grid holds enough waves to cover all compute units.
+int chunk_blocks(const art_shape& s, const art_params& p) {
+  const int64_t tmax = std::max<int64_t>(1, max_traversal(s));
+  if (p.mode == ART_MODE_ART) return (int)tmax;
+  if (p.split_blocks > 0) return (int)std::min<int64_t>(p.split_blocks, tmax);
+  const int64_t units = std::max<int64_t>(1, (int64_t)s.batch * s.num_kv_heads);
+  const int64_t target_items = 4096;
+  if (units >= target_items) return (int)tmax;
+  int64_t c = (tmax * units + target_items - 1) / target_items;
+  c = std::max<int64_t>(c, 16);
+  return (int)std::min<int64_t>(c, tmax);
+}
+
+art::WsLayout layout(const art_shape& s, const art_params& p, int chunk, int max_chunks) {
+  art::WsLayout L{};
+  const int64_t units = (int64_t)s.batch * s.num_kv_heads;
+  const int G = s.num_q_heads / s.num_kv_heads;
+  const int d = s.head_dim;
+  L.header = round256(sizeof(art::WsHeader));
+  L.unit_state = round256(sizeof(art::UnitState) * (size_t)std::max<int64_t>(units, 1));
+  L.partials = max_chunks > 1 ? round256((size_t)units * max_chunks * G * (d + 2) * sizeof(float)) : 0;
+  const size_t carry_bytes = 16 + (size_t)G * 4 + (size_t)G * 8 + (size_t)G * (d / kProbeStride) * 8;
+  L.carries = (max_chunks > 1 && p.mode == ART_MODE_ART) ? round256((size_t)units * max_chunks * round256(carry_bytes)) : 0;
+  (void)chunk;
+  L.total = L.header + L.unit_state + L.partials + L.carries;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t art_workspace_size(const art_shape* shape, const art_params* params) {
+  if (validate(shape, params) != ART_OK) return 0;
+  const int chunk = chunk_blocks(*shape, *params);
+  const int64_t tmax = std::max<int64_t>(1, max_traversal(*shape));
+  const int max_chunks = (int)((tmax + chunk - 1) / chunk);
+  return layout(*shape, *params, chunk, max_chunks).total;
+}
+
+art_status art_decode(const art_shape* shape, const art_params* params, const void* q, const void* k,
+                      const void* v, const int32_t* context_lens, const int32_t* block_table,
+                      const int32_t* kept_blocks, const int32_t* kept_count, float* out, int32_t* stop_idx,
+                      int32_t* blocks_issued, void* workspace, size_t workspace_bytes, void* stream) {
+  art_status st = validate(shape, params);
+  if (st != ART_OK) return st;
+  const art_shape& s = *shape;
+  const art_params& p = *params;
+  if ((kept_blocks == nullptr) != (kept_count == nullptr)) return ART_ERR_INVALID_ARG;
+  if ((kept_blocks != nullptr) != (s.max_kept > 0)) return ART_ERR_INVALID_ARG;
+  if (s.batch == 0) return ART_OK;
+  if (!q || !k || !v || !context_lens || !out || !stop_idx) return ART_ERR_INVALID_ARG;
+  if (s.page_size > 0 && (!block_table || s.max_pages <= 0 || s.num_pages <= 0)) return ART_ERR_INVALID_ARG;
+  if (s.page_size == 0 && block_table) return ART_ERR_INVALID_ARG;
+
+  const int chunk = chunk_blocks(s, p);
+  const int64_t tmax = std::max<int64_t>(1, max_traversal(s));
+  const int max_chunks = (int)((tmax + chunk - 1) / chunk);
+  const int64_t units = (int64_t)s.batch * s.num_kv_heads;
+  if (units * max_chunks > INT32_MAX) return ART_ERR_UNSUPPORTED;
+  const art::WsLayout L = layout(s, p, chunk, max_chunks);
+  if (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return ART_ERR_WORKSPACE;
+
+  art::KernelArgs a{};
+  a.batch = s.batch;
+  a.hq = s.num_q_heads;
+  a.hkv = s.num_kv_heads;
+  a.dtype = s.dtype;
+  a.page_size = s.page_size;
+  a.max_ctx = s.max_ctx;
+  a.max_pages = s.max_pages;
+  a.num_pages = s.num_pages;
+  a.max_kept = s.max_kept;
+  a.eps_scale = p.eps_scale;
+  a.eps_dir = p.eps_dir;
+  a.patience = p.patience;
+  a.order = p.order;
+  a.mode = p.mode;
+  a.chunk_blocks = chunk;
+  a.max_chunks = max_chunks;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.context_lens = context_lens;
+  a.block_table = block_table;
+  a.kept_blocks = kept_blocks;
+  a.kept_count = kept_count;
+  a.out = out;
+  a.stop_idx = stop_idx;
+  a.blocks_issued = blocks_issued;
+  char* w = static_cast<char*>(workspace);
+  a.ws = reinterpret_cast<art::WsHeader*>(w);
+  a.unit_state = reinterpret_cast<art::UnitState*>(w + L.header);
+  a.partials = L.partials ? reinterpret_cast<float*>(w + L.header + L.unit_state) : nullptr;
+  a.carries = L.carries ? static_cast<void*>(w + L.header + L.unit_state + L.partials) : nullptr;
+  a.spin_limit = 1u << 22;
+
+  hipError_t e = art::launch(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ART_OK : ART_ERR_HIP;
+}
+
+art_status art_last_error(const void* workspace) {
+  if (!workspace) return ART_ERR_INVALID_ARG;
+  int32_t err = 0;
+  if (hipMemcpy(&err, workspace, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess) return ART_ERR_HIP;
+  return static_cast<art_status>(err);
+}
+
+const char* art_status_string(art_status status) {
+  switch (status) {
+    case ART_OK: return "ok";
+    case ART_ERR_INVALID_ARG: return "invalid argument";
+    case ART_ERR_UNSUPPORTED: return "unsupported shape or parameter";
+    case ART_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case ART_ERR_HIP: return "HIP runtime or launch failure";
+    case ART_ERR_TIMEOUT: return "split look-back wait timed out on the device";
+    case ART_ERR_DEVICE_INPUT: return "kept list out of range or not strictly ascending";
+  }
+  return "unknown status";
+}
+
+int32_t art_probe_stride(void) { return kProbeStride; }
+
+}  // extern "C"

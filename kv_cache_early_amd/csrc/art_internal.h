@@ -1,0 +1,73 @@
+// Internal structures shared by the C-ABI front end (art_api.cpp) and the
+// gfx950 kernels (art_kernels.hip).  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace art {
+
+// Workspace header: device-side error word and the split ticket counter.
+struct alignas(256) WsHeader {
+  int32_t error;       // art_status recorded on the device (max wins)
+  uint32_t ticket;     // ordered work-item dispenser (split ART mode)
+  int32_t pad[62];
+};
+
+// Per-unit state, one per (batch, kv head).
+struct UnitState {
+  int32_t status;      // 0 running, 1 stopped
+  int32_t stop_chunk;  // chunk that holds the stop, -1 if none yet
+  int32_t stop_idx;    // traversal blocks processed at the stop
+  int32_t issued;      // blocks whose loads were issued (all chunks)
+};
+
+// Look-back carry published by a chunk for its successor (split ART mode):
+// the prefix state of the probe dims after the chunk's last block.
+template <int G, int NP>
+struct alignas(16) Carry {
+  int32_t flag;        // 0 not ready, 1 ready (running), 2 ready (stopped)
+  int32_t counter;     // consecutive stable checks at the end of the chunk
+  int32_t stop_idx;    // when stopped
+  int32_t pad;
+  float m[G];          // running max (log2 domain) per head
+  double l[G];         // running denominator per head
+  double pacc[G][NP];  // running numerators on the probe dims
+};
+
+struct KernelArgs {
+  // shape
+  int32_t batch, hq, hkv, dtype, page_size, max_ctx, max_pages, num_pages, max_kept;
+  // params
+  float eps_scale, eps_dir;
+  int32_t patience, order, mode;
+  int32_t chunk_blocks;  // traversal blocks per work item
+  int32_t max_chunks;    // work items per unit
+  // inputs
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* context_lens;
+  const int32_t* block_table;
+  const int32_t* kept_blocks;
+  const int32_t* kept_count;
+  // outputs
+  float* out;
+  int32_t* stop_idx;
+  int32_t* blocks_issued;
+  // workspace
+  WsHeader* ws;
+  UnitState* unit_state;
+  float* partials;     // [units][max_chunks][G][d + 2]  (m, l, acc[d])
+  void* carries;       // [units][max_chunks] Carry<G, d/4>
+  uint32_t spin_limit; // look-back polls before ART_ERR_TIMEOUT
+};
+
+// Workspace layout for a given shape (bytes, 256-aligned pieces).
+struct WsLayout {
+  size_t header, unit_state, partials, carries, total;
+};
+
+hipError_t launch(const KernelArgs& a, hipStream_t stream);
+
+}  // namespace art

@@ -1,0 +1,118 @@
+"""Parity helpers: run libart on a workload and compare with the fp64 oracle.
+
+The acceptance rule (per unit = (batch, kv head)):
+  * stop_idx equal to the oracle's, unless the unit is margin-excused: some
+    check t <= max(stop_gpu, stop_oracle) has a metric within a relative
+    margin of 1e-4 of its threshold (|d / eps - 1| <= 1e-4);
+  * the GPU output is compared with the oracle's O^(stop_gpu) (the exact
+    truncated attention at the GPU's own stop): relative L2 <= 1e-3 and
+    max-abs <= 4e-3 per unit.
+"""
+from __future__ import annotations
+
+import sys
+from dataclasses import dataclass, field
+
+import numpy as np
+
+import oracle as orc
+from workloads.device import to_device
+
+REL_L2 = 1e-3
+MAX_ABS = 4e-3
+MARGIN = 1e-4
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(w, mode=1, patience=None, eps_scale=None, eps_dir=None, order=None, split_blocks=0, dev=None,
+            decoder=None):
+    """Upload (unless ``dev`` is given) and run art_decode; returns numpy arrays."""
+    import torch
+    from kv_cache_early_amd import ArtDecoder
+    s = w.spec
+    dev = dev or to_device(w)
+    dec = decoder or ArtDecoder()
+    r = dec.decode(dev.q, dev.k, dev.v, dev.context_lens, dtype=dev.dtype_code, page_size=dev.page_size,
+                   block_table=dev.block_table, kept_blocks=dev.kept_blocks, kept_count=dev.kept_count,
+                   eps_scale=s.eps_scale if eps_scale is None else eps_scale,
+                   eps_dir=s.eps_dir if eps_dir is None else eps_dir,
+                   patience=s.patience if patience is None else patience,
+                   order=s.order if order is None else order, mode=mode, split_blocks=split_blocks)
+    torch.cuda.synchronize()
+    err = dec.device_error()
+    return (r.out.cpu().numpy().astype(np.float64), r.stop_idx.cpu().numpy().astype(np.int64),
+            r.blocks_issued.cpu().numpy().astype(np.int64), err)
+
+
+@dataclass
+class Report:
+    units: int = 0
+    stop_equal: int = 0
+    excused: int = 0
+    unexcused: list = field(default_factory=list)
+    worst_rel_l2: float = 0.0
+    worst_abs: float = 0.0
+    bad_outputs: list = field(default_factory=list)
+
+    def ok(self):
+        return not self.unexcused and not self.bad_outputs
+
+    def __str__(self):
+        return (f"units={self.units} stop_equal={self.stop_equal} excused={self.excused} "
+                f"unexcused={len(self.unexcused)} worst_rel_l2={self.worst_rel_l2:.2e} "
+                f"worst_abs={self.worst_abs:.2e} bad_outputs={len(self.bad_outputs)}")
+
+
+def compare(w, out_gpu, stop_gpu, units=None, mode=1, patience=None, eps_scale=None, eps_dir=None, order=None):
+    """Compare GPU results with the oracle on ``units`` (default: all)."""
+    s = w.spec
+    es = s.eps_scale if eps_scale is None else eps_scale
+    ed = s.eps_dir if eps_dir is None else eps_dir
+    _, _, res = orc.art_decode_workload(w, mode=mode, patience=patience, units=units, keep_results=True,
+                                        eps_scale=es, eps_dir=ed, order=order)
+    G = s.group
+    rep = Report()
+    for (b, h), r in res.items():
+        rep.units += 1
+        sg, so = int(stop_gpu[b, h]), int(r.stop)
+        if sg == so:
+            rep.stop_equal += 1
+        else:
+            hi = max(sg, so)
+            rs = orc.relative_margin(r.d_scale[1:hi], es)
+            rd = orc.relative_margin(r.d_dir[1:hi], ed)
+            m = np.nanmin(np.minimum(rs, rd)) if hi > 1 else np.inf
+            if m <= MARGIN:
+                rep.excused += 1
+            else:
+                rep.unexcused.append(((b, h), sg, so, float(m)))
+        if not (0 <= sg <= r.num_traversal):
+            rep.bad_outputs.append(((b, h), "stop out of range", sg))
+            continue
+        ref = r.O[sg - 1] if sg > 0 else np.zeros_like(r.out)
+        got = out_gpu[b, h * G:(h + 1) * G]
+        diff = got - ref
+        nrm = np.linalg.norm(ref)
+        rel = np.linalg.norm(diff) / nrm if nrm > 0 else np.linalg.norm(diff)
+        mab = float(np.abs(diff).max()) if diff.size else 0.0
+        if not np.isfinite(rel):
+            rel = np.inf
+        rep.worst_rel_l2 = max(rep.worst_rel_l2, rel)
+        rep.worst_abs = max(rep.worst_abs, mab)
+        if not (rel <= REL_L2 and mab <= MAX_ABS):
+            rep.bad_outputs.append(((b, h), rel, mab))
+    return rep, res
+
+
+def sample_units(w, n, seed=0):
+    B, H = w.spec.batch, w.spec.num_kv_heads
+    rng = np.random.default_rng(seed)
+    allu = [(b, h) for b in range(B) for h in range(H)]
+    if n >= len(allu):
+        return allu
+    idx = rng.choice(len(allu), size=n, replace=False)
+    return sorted(allu[i] for i in idx)

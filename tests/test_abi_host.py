@@ -1,0 +1,116 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+declared in include/art.h, and rejects bad arguments on the host before
+anything is enqueued."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from kv_cache_early_amd import art
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "art.h")
+
+FAKE = 0x10000  # a non-null address; validation fails before any use
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(art_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = art.load()
+    names = declared_functions()
+    assert set(names) == set(art.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_probe_stride():
+    for s in range(7):
+        assert art.status_string(s) and art.status_string(s) != "unknown status"
+    assert art.status_string(99) == "unknown status"
+    assert art.load().art_probe_stride() == 4
+
+
+def good_shape(**kw):
+    d = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, dtype=art.ART_DT_BF16, page_size=16,
+             max_ctx=0, max_pages=64, num_pages=200, max_kept=0)
+    d.update(kw)
+    return art.make_shape(**d)
+
+
+def good_params(**kw):
+    d = dict(eps_scale=1e-3, eps_dir=1e-4, patience=2, order=art.ART_ORDER_RECENT_FIRST, mode=art.ART_MODE_ART,
+             block_size=64, split_blocks=0)
+    d.update(kw)
+    return art.make_params(**d)
+
+
+def call(shape, params, q=FAKE, k=FAKE, v=FAKE, lens=FAKE, bt=FAKE, kept=None, kc=None, out=FAKE, stop=FAKE,
+         issued=None, ws=FAKE * 16, ws_bytes=1 << 30, stream=None, shape_ptr=True, params_ptr=True):
+    lib = art.load()
+    return lib.art_decode(ctypes.byref(shape) if shape_ptr else None, ctypes.byref(params) if params_ptr else None,
+                          q, k, v, lens, bt, kept, kc, out, stop, issued, ws, ws_bytes, stream)
+
+
+CASES = [
+    ("null shape", dict(shape_ptr=False), art.ART_ERR_INVALID_ARG),
+    ("null params", dict(params_ptr=False), art.ART_ERR_INVALID_ARG),
+    ("Hq % Hkv", dict(shape=good_shape(num_q_heads=6, num_kv_heads=4)), art.ART_ERR_INVALID_ARG),
+    ("negative batch", dict(shape=good_shape(batch=-1)), art.ART_ERR_INVALID_ARG),
+    ("bad dtype", dict(shape=good_shape(dtype=7)), art.ART_ERR_INVALID_ARG),
+    ("head_dim 96", dict(shape=good_shape(head_dim=96)), art.ART_ERR_UNSUPPORTED),
+    ("bf16 d64", dict(shape=good_shape(head_dim=64)), art.ART_ERR_UNSUPPORTED),
+    ("group 8", dict(shape=good_shape(num_q_heads=16)), art.ART_ERR_UNSUPPORTED),
+    ("block_size 32", dict(params=good_params(block_size=32)), art.ART_ERR_UNSUPPORTED),
+    ("block_size 0", dict(params=good_params(block_size=0)), art.ART_ERR_INVALID_ARG),
+    ("page 24", dict(shape=good_shape(page_size=24)), art.ART_ERR_INVALID_ARG),
+    ("page 48", dict(shape=good_shape(page_size=48)), art.ART_ERR_UNSUPPORTED),
+    ("patience 0", dict(params=good_params(patience=0)), art.ART_ERR_INVALID_ARG),
+    ("eps negative", dict(params=good_params(eps_scale=-1e-3)), art.ART_ERR_INVALID_ARG),
+    ("eps nan", dict(params=good_params(eps_dir=math.nan)), art.ART_ERR_INVALID_ARG),
+    ("eps inf", dict(params=good_params(eps_scale=math.inf)), art.ART_ERR_INVALID_ARG),
+    ("bad order", dict(params=good_params(order=3)), art.ART_ERR_INVALID_ARG),
+    ("bad mode", dict(params=good_params(mode=2)), art.ART_ERR_INVALID_ARG),
+    ("given without kept list", dict(params=good_params(order=art.ART_ORDER_GIVEN)), art.ART_ERR_INVALID_ARG),
+    ("negative split", dict(params=good_params(split_blocks=-1)), art.ART_ERR_INVALID_ARG),
+    ("kept without count", dict(shape=good_shape(max_kept=8), kept=FAKE), art.ART_ERR_INVALID_ARG),
+    ("count without kept", dict(kc=FAKE), art.ART_ERR_INVALID_ARG),
+    ("kept list but max_kept 0", dict(kept=FAKE, kc=FAKE), art.ART_ERR_INVALID_ARG),
+    ("null q", dict(q=None), art.ART_ERR_INVALID_ARG),
+    ("null out", dict(out=None), art.ART_ERR_INVALID_ARG),
+    ("null stop", dict(stop=None), art.ART_ERR_INVALID_ARG),
+    ("null lens", dict(lens=None), art.ART_ERR_INVALID_ARG),
+    ("paged without table", dict(bt=None), art.ART_ERR_INVALID_ARG),
+    ("contiguous with table", dict(shape=good_shape(page_size=0, max_ctx=4096)), art.ART_ERR_INVALID_ARG),
+    ("null workspace", dict(ws=None), art.ART_ERR_WORKSPACE),
+    ("small workspace", dict(ws_bytes=64), art.ART_ERR_WORKSPACE),
+    ("misaligned workspace", dict(ws=FAKE * 16 + 8), art.ART_ERR_WORKSPACE),
+]
+
+
+@pytest.mark.parametrize("name,kw,expect", CASES, ids=[c[0] for c in CASES])
+def test_host_rejects(name, kw, expect):
+    kw = dict(kw)
+    shape = kw.pop("shape", good_shape())
+    params = kw.pop("params", good_params())
+    assert call(shape, params, **kw) == expect
+
+
+def test_empty_batch_is_a_no_op():
+    assert call(good_shape(batch=0), good_params(), q=None, k=None, v=None, lens=None, bt=None, out=None,
+                stop=None) == art.ART_OK
+
+
+def test_workspace_size():
+    s, p = good_shape(), good_params()
+    n = art.workspace_size(s, p)
+    assert n > 0 and n % 256 == 0
+    assert art.workspace_size(good_shape(head_dim=96), p) == 0
+    full_split = art.workspace_size(s, good_params(mode=art.ART_MODE_FULL, split_blocks=4))
+    assert full_split > n  # room for the split partials

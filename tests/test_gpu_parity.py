@@ -1,0 +1,173 @@
+"""GPU parity: libart (through the C ABI) against the fp64 oracle.
+
+Every test prints the case it is about to run before touching the GPU.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import oracle as orc
+from tests.parity import compare, log, run_gpu, sample_units
+from workloads import config, make_workload, scaled
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def check(w, mode=1, tag="", **kw):
+    log(f"[case] {tag or w.spec.name} reading={w.spec.reading} mode={mode} {kw}")
+    out, stop, issued, err = run_gpu(w, mode=mode, **kw)
+    assert err == 0, f"device error {err}"
+    ckw = {k: v for k, v in kw.items() if k in ("patience", "eps_scale", "eps_dir", "order")}
+    rep, res = compare(w, out, stop, mode=mode, **ckw)
+    log(f"   {rep}")
+    assert rep.ok(), (rep.unexcused[:5], rep.bad_outputs[:5])
+    Tp = w.traversal_lengths()
+    assert np.all(issued >= stop) and np.all(issued <= Tp), "blocks_issued out of range"
+    return out, stop, issued, rep
+
+
+@pytest.mark.parametrize("reading", ["A", "B"])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_scaled_configs(torch_cuda, n, reading, mode):
+    w = make_workload(scaled(n, reading))
+    _, stop, _, _ = check(w, mode=mode, tag=f"scaled cfg{n}")
+    if mode == 0:
+        np.testing.assert_array_equal(stop, w.traversal_lengths())
+
+
+@pytest.mark.parametrize("p", [1, 2, 3])
+def test_forced_stop_after_p_plus_one(torch_cuda, p):
+    """eps huge: every check is stable, so the stop is at min(T', p+1)."""
+    w = make_workload(scaled(3, "B"))
+    _, stop, issued, _ = check(w, tag="huge eps", eps_scale=1e30, eps_dir=1e30, patience=p)
+    Tp = w.traversal_lengths()
+    np.testing.assert_array_equal(stop, np.minimum(Tp, p + 1))
+    # loads stop: at most one prefetched block beyond the stop
+    assert np.all(issued <= np.minimum(Tp, stop + 1))
+
+
+def test_eps_zero_runs_to_the_end(torch_cuda):
+    w = make_workload(scaled(3, "B"))
+    _, stop, _, _ = check(w, tag="eps 0", eps_scale=0.0, eps_dir=0.0)
+    np.testing.assert_array_equal(stop, w.traversal_lengths())
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 5])
+def test_criterion_fires_at_real_lengths(torch_cuda, n):
+    """Reading B at the configs' own context lengths, few units: ART fires."""
+    s = config(n, "B", batch=2, num_q_heads=8, num_kv_heads=2)
+    w = make_workload(s)
+    _, stop, _, _ = check(w, tag=f"firing cfg{n}")
+    assert np.all(stop < w.traversal_lengths()), "expected the criterion to fire on every unit"
+
+
+@pytest.mark.parametrize("order", [orc.ORDER_NATURAL, orc.ORDER_RECENT_FIRST])
+def test_orders(torch_cuda, order):
+    w = make_workload(config(2, "B", batch=1, num_q_heads=8, num_kv_heads=2, ctx=(20000, 20000)))
+    check(w, tag=f"order {order}", order=order)
+
+
+def test_given_order_with_block0_moved_first(torch_cuda):
+    import torch
+    s = scaled(3, "B")
+    w = make_workload(s)
+    rng = np.random.default_rng(3)
+    T = w.num_blocks
+    kmax = int(T.max())
+    kb = np.full((s.batch, s.num_kv_heads, kmax), -1, dtype=np.int32)
+    kc = np.zeros((s.batch, s.num_kv_heads), dtype=np.int32)
+    for b in range(s.batch):
+        for h in range(s.num_kv_heads):
+            n = int(rng.integers(1, T[b] + 1))
+            lst = rng.choice(T[b], size=n, replace=False).astype(np.int32)
+            kb[b, h, :n] = lst
+            kc[b, h] = n
+    w.kept_blocks, w.kept_count = kb, kc
+    check(w, tag="given order", order=orc.ORDER_GIVEN, eps_scale=5e-2, eps_dir=5e-3)
+
+
+def test_layout_equivalence_bitwise(torch_cuda):
+    """Same logical KV, paged (shuffled pages) vs contiguous: identical bits."""
+    base = scaled(3, "B")
+    lens = np.array([700, 1333, 64, 2049], dtype=np.int32)
+    wp = make_workload(base, context_lens=lens)
+    wc = make_workload(replace(base, page_size=0), context_lens=lens)
+    log("[case] layout equivalence")
+    op, sp, _, e1 = run_gpu(wp)
+    oc, sc, _, e2 = run_gpu(wc)
+    assert e1 == e2 == 0
+    np.testing.assert_array_equal(sp, sc)
+    np.testing.assert_array_equal(op, oc)
+
+
+@pytest.mark.parametrize("page", [16, 32, 64, 128])
+def test_page_sizes(torch_cuda, page):
+    w = make_workload(replace(scaled(3, "B"), page_size=page))
+    check(w, tag=f"page {page}", eps_scale=2e-2, eps_dir=2e-3)
+
+
+def test_edge_lengths(torch_cuda):
+    """Empty, one-token, exact-block and ragged sequences in one batch."""
+    s = replace(scaled(3, "B"), batch=8)
+    lens = np.array([0, 1, 63, 64, 65, 127, 129, 1000], dtype=np.int32)
+    w = make_workload(s, context_lens=lens)
+    out, stop, issued, _ = check(w, tag="edge lengths", eps_scale=5e-2, eps_dir=5e-3, patience=1)
+    assert np.all(stop[0] == 0) and np.all(out[0] == 0) and np.all(issued[0] == 0)
+    assert np.all(stop[1] == 1)
+
+
+@pytest.mark.parametrize("split", [1, 3, 7])
+def test_full_mode_split_kv(torch_cuda, split):
+    w = make_workload(scaled(3, "A"))
+    _, stop, issued, _ = check(w, mode=0, tag=f"full split {split}", split_blocks=split)
+    np.testing.assert_array_equal(stop, w.traversal_lengths())
+    np.testing.assert_array_equal(issued, w.traversal_lengths())
+
+
+def test_kept_list_out_of_range_is_reported(torch_cuda):
+    from kv_cache_early_amd import art
+    w = make_workload(scaled(5, "B"))
+    w.kept_blocks = w.kept_blocks.copy()
+    w.kept_blocks[0, 1, 3] = 10 ** 6
+    log("[case] bad kept list")
+    out, stop, issued, err = run_gpu(w)
+    assert err == art.ART_ERR_DEVICE_INPUT
+    assert stop[0, 1] == -1
+    good = [(b, h) for b in range(w.spec.batch) for h in range(w.spec.num_kv_heads) if (b, h) != (0, 1)]
+    rep, _ = compare(w, out, stop, units=good)
+    assert rep.ok(), str(rep)
+
+
+# ---------------------------------------------------------------------------
+# full-size configurations: every unit on the GPU, sampled units in the oracle
+# ---------------------------------------------------------------------------
+FULL = [(2, "B"), (3, "A"), (3, "B"), (4, "A"), (4, "B"), (5, "A"), (5, "B")]
+
+
+@pytest.mark.parametrize("n,reading", FULL)
+def test_full_size_sampled(torch_cuda, n, reading):
+    log(f"[case] full-size cfg{n} reading={reading}: generating")
+    w = make_workload(config(n, reading))
+    units = sample_units(w, 12, seed=n)
+    log(f"[case] full-size cfg{n} reading={reading}: GPU")
+    patiences = (1, 2, 4) if n == 4 else (w.spec.patience,)
+    from workloads.device import to_device
+    dev = to_device(w)
+    for p in patiences:
+        out, stop, issued, err = run_gpu(w, patience=p, dev=dev)
+        assert err == 0
+        rep, _ = compare(w, out, stop, units=units, patience=p)
+        log(f"   p={p} {rep} skipped={1 - stop.sum() / w.traversal_lengths().sum():.3f}")
+        assert rep.ok(), (rep.unexcused[:5], rep.bad_outputs[:5])
+        assert np.all((stop >= 1) & (stop <= w.traversal_lengths()))
+    del dev
