@@ -48,8 +48,7 @@ art_status validate(const art_shape* sp, const art_params* pp) {
     return ART_ERR_UNSUPPORTED;
   if (G != 1 && G != 2 && G != 4) return ART_ERR_UNSUPPORTED;
   if (p.block_size != kBlockTokens) return ART_ERR_UNSUPPORTED;
-  if (s.page_size > 0 && !(kBlockTokens % s.page_size == 0 || s.page_size % kBlockTokens == 0))
-    return ART_ERR_UNSUPPORTED;
+  if (s.page_size > 0 && (s.page_size & (s.page_size - 1)) != 0) return ART_ERR_UNSUPPORTED;  // powers of two
   // index ranges the kernels compute in 32-bit
   const int64_t units = (int64_t)s.batch * s.num_kv_heads;
   if (units > (1 << 26) || max_traversal(s) > (1 << 24)) return ART_ERR_UNSUPPORTED;
@@ -64,7 +63,7 @@ int chunk_blocks(const art_shape& s, const art_params& p) {
   if (p.mode == ART_MODE_ART) return (int)tmax;
   if (p.split_blocks > 0) return (int)std::min<int64_t>(p.split_blocks, tmax);
   const int64_t units = std::max<int64_t>(1, (int64_t)s.batch * s.num_kv_heads);
-  const int64_t target_items = 4096;
+  const int64_t target_items = 1024;  // workgroups of 4 waves
   if (units >= target_items) return (int)tmax;
   int64_t c = (tmax * units + target_items - 1) / target_items;
   c = std::max<int64_t>(c, 16);
@@ -139,6 +138,7 @@ art_status art_decode(const art_shape* shape, const art_params* params, const vo
   a.mode = p.mode;
   a.chunk_blocks = chunk;
   a.max_chunks = max_chunks;
+  a.waves = 4;
   a.q = q;
   a.k = k;
   a.v = v;

@@ -43,6 +43,7 @@ struct KernelArgs {
   int32_t patience, order, mode;
   int32_t chunk_blocks;  // traversal blocks per work item
   int32_t max_chunks;    // work items per unit
+  int32_t waves;         // waves per workgroup (one work item per workgroup)
   // inputs
   const void* q;
   const void* k;

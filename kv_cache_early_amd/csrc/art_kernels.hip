@@ -1,23 +1,34 @@
 // ART decode attention kernels for gfx950 (MI355X).
 //
-// One 64-lane wave owns one work item = (unit, chunk): unit = (batch b, kv
-// head h) with its G query heads, chunk = a contiguous range of positions of
-// the unit's traversal order.  Per 64-token ART block the wave
-//   1. loads K straight into MFMA B-operand registers and V in row order,
-//      16-byte loads, one block ahead (software pipeline);
+// Work decomposition.  One workgroup of W waves (W = blockDim.x / 64) owns
+// one work item = (unit, chunk): unit = (batch b, kv head h) with its G
+// query heads, chunk = a range of positions of the unit's traversal order
+// (the whole traversal in ART mode).  The work item is walked in rounds of W
+// consecutive traversal positions; wave w takes position t0 + w of round t0.
+//
+// Per 64-token ART block a wave
+//   1. has K in MFMA B-operand registers and V in row order (16-byte loads,
+//      issued one round ahead);
 //   2. computes the G x 64 scores with v_mfma_f32_16x16x32_bf16
 //      (v_mfma_f32_16x16x4_f32 for fp32 inputs); the A operand holds the
 //      G query rows replicated over the 16 MFMA rows, so every lane receives
 //      the scores of "its" token for all G heads;
-//   3. runs the online softmax (running max in the log2 domain);
+//   3. runs the online softmax (running max in the log2 domain) against the
+//      wave's running maximum;
 //   4. accumulates P V on the VALU in fp32 (P stays fp32);
-//   5. builds the probe (dims 0,4,8,... of every head) from fp64 running sums
-//      of the per-block contributions and evaluates the two stability
-//      metrics and the patience counter; the decision is wave-uniform, and a
-//      stopped unit issues no further loads.
+//   5. (ART mode) publishes a block summary: per head its reference max,
+//      its softmax mass and its sums on the probe dims.
+// (ART mode) After a barrier every wave merges the summaries of positions up
+// to its own onto the carried prefix state (fp64 on the probe dims), so wave
+// w holds the probe x^(t) at its position t and x^(t-1); it evaluates the two
+// stability metrics there.  After a second barrier every wave runs the
+// patience counter over the round's checks in order: the first position
+// where `patience` consecutive checks were stable is the stop, blocks after
+// it are discarded and no further loads are issued.  The decision is the
+// one a strictly sequential walk makes.
 //
-// Method sources: ART paper section 3.1 Eq. (1) (blockwise attention and
-// the partial outputs O^(t)), section 3.2 (probe of scattered head dims);
+// Method sources: ART paper section 3.1 Eq. (1) (blockwise attention and the
+// partial outputs O^(t)), section 3.2 (probe of scattered head dims);
 // gist.science explainer sections 2.2 (scale and direction metrics, dual
 // threshold), 2.3 (patience), 2.4 (traversal order, block 0 first).
 //
@@ -25,8 +36,9 @@
 // 16 chunks of 16 bytes): lane l = 16*lg + c with lg = l / 16, c = l % 16.
 //   K (MFMA B operand): load i of tile nt -> token 16*nt + c, chunk 4*i + lg.
 //   V (row order)     : load i            -> token 4*i + lg,   chunk c.
-// PV accumulators are therefore partial over the four token groups lg and
-// are summed through LDS for the probe and for the output.
+// PV accumulators are partial over the four token groups lg and are summed
+// through LDS for the probe and for the output.  For the probe, lane
+// (lg, c) owns head lg (when lg < G) and the probe dims inside chunk c.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -41,20 +53,18 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+constexpr int kMaxWaves = 4;      // waves per workgroup (launch bound)
 constexpr int kBlk = 64;          // tokens per ART block
 constexpr int kTiles = kBlk / 16; // 16-token MFMA tiles per block
 constexpr int kRowChunks = 16;    // 16-byte chunks per K/V row
 constexpr int kVLoads = kBlk * kRowChunks / kWave;  // 16 row-order loads per block
 constexpr int kKLoads = kRowChunks / 4;             // 4 loads per tile per lane
 
-// ---------------------------------------------------------------------------
-// element-type geometry
-// ---------------------------------------------------------------------------
 template <int DT>
 struct Geo;
 template <>
 struct Geo<ART_DT_BF16> {
-  static constexpr int D = 128, ES = 2, EPC = 8, PPC = 2;  // elements / probes per chunk
+  static constexpr int D = 128, ES = 2, EPC = 8, PPC = 2;  // elements / probe dims per chunk
 };
 template <>
 struct Geo<ART_DT_F32> {
@@ -62,53 +72,58 @@ struct Geo<ART_DT_F32> {
 };
 
 // ---------------------------------------------------------------------------
-// cross-lane helpers (gfx9 DPP; all 64 lanes active)
+// small helpers
 // ---------------------------------------------------------------------------
-#define ART_DPP(x, ctrl) \
-  __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (x)), (ctrl), 0xF, 0xF, false))
-#define ART_DPP_I(x, ctrl) __builtin_amdgcn_update_dpp(0, (x), (ctrl), 0xF, 0xF, false)
+#define ART_DPP_I(x, ctrl, rmask) __builtin_amdgcn_update_dpp(0, (x), (ctrl), (rmask), 0xF, false)
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror, row_bcast:15, row_bcast:31
+constexpr int kQx1 = 0xB1, kQx2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140, kBcast15 = 0x142, kBcast31 = 0x143;
 
-// DPP controls: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.
-constexpr int kQx1 = 0xB1, kQx2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140;
+template <int CTRL, int RMASK = 0xF>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, ART_DPP_I(__builtin_bit_cast(int, x), CTRL, RMASK));
+}
+template <int CTRL, int RMASK = 0xF>
+__device__ __forceinline__ double dpp(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const int lo = ART_DPP_I((int)(uint32_t)u, CTRL, RMASK);
+  const int hi = ART_DPP_I((int)(uint32_t)(u >> 32), CTRL, RMASK);
+  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
+}
 
+// All-reduce over the 16 lanes of each row (every lane gets its row's result).
 __device__ __forceinline__ float row_max(float x) {
-  x = fmaxf(x, ART_DPP(x, kQx1));
-  x = fmaxf(x, ART_DPP(x, kQx2));
-  x = fmaxf(x, ART_DPP(x, kHalfMirror));
-  x = fmaxf(x, ART_DPP(x, kMirror));
-  return x;
+  x = fmaxf(x, dpp<kQx1>(x));
+  x = fmaxf(x, dpp<kQx2>(x));
+  x = fmaxf(x, dpp<kHalfMirror>(x));
+  return fmaxf(x, dpp<kMirror>(x));
 }
 __device__ __forceinline__ float row_sum(float x) {
-  x += ART_DPP(x, kQx1);
-  x += ART_DPP(x, kQx2);
-  x += ART_DPP(x, kHalfMirror);
-  x += ART_DPP(x, kMirror);
-  return x;
+  x += dpp<kQx1>(x);
+  x += dpp<kQx2>(x);
+  x += dpp<kHalfMirror>(x);
+  return x + dpp<kMirror>(x);
 }
-#define ART_DPP_D(x, ctrl)                                                              \
-  ({                                                                                    \
-    uint64_t _u = __builtin_bit_cast(uint64_t, (x));                                    \
-    int _lo = ART_DPP_I((int)(uint32_t)_u, ctrl);                                       \
-    int _hi = ART_DPP_I((int)(uint32_t)(_u >> 32), ctrl);                               \
-    __builtin_bit_cast(double, ((uint64_t)(uint32_t)_hi << 32) | (uint64_t)(uint32_t)_lo); \
-  })
-__device__ __forceinline__ double row_sum_d(double x) {
-  x += ART_DPP_D(x, kQx1);
-  x += ART_DPP_D(x, kQx2);
-  x += ART_DPP_D(x, kHalfMirror);
-  x += ART_DPP_D(x, kMirror);
-  return x;
-}
-
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 __device__ __forceinline__ float uni_f(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
 }
-__device__ __forceinline__ double uni_d(double x) {
-  uint64_t u = __builtin_bit_cast(uint64_t, x);
-  uint32_t lo = __builtin_amdgcn_readfirstlane((int)(uint32_t)u);
-  uint32_t hi = __builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+__device__ __forceinline__ double lane_d(double x, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+// Sum over all 64 lanes in fp64, returned uniform.  Rows are reduced with
+// mirrors, then row totals are chained with row broadcasts; lane 63 ends
+// with the total.
+__device__ __forceinline__ double wave_sum_d(double x) {
+  x += dpp<kQx1>(x);
+  x += dpp<kQx2>(x);
+  x += dpp<kHalfMirror>(x);
+  x += dpp<kMirror>(x);
+  x += dpp<kBcast15, 0xA>(x);
+  x += dpp<kBcast31, 0xC>(x);
+  return lane_d(x, 63);
 }
 
 // Reinterpret a 32-bit word as fp32.  Takes the word by value: bit-casting a
@@ -117,144 +132,185 @@ __device__ __forceinline__ float as_f32(uint32_t w) { return __builtin_bit_cast(
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
+// Uniform load through the scalar data cache (read-only metadata: context
+// lengths, block tables, kept lists).  Keeps metadata off the vector-load
+// counter, so waiting for it never waits for in-flight K/V loads.
+template <typename T>
+__device__ __forceinline__ T sload(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)(p);
+}
+
+// Order LDS traffic between the lanes of one wave.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ---------------------------------------------------------------------------
-// per-unit view of the inputs
+// per-unit view of the inputs (all fields uniform)
 // ---------------------------------------------------------------------------
 struct UnitView {
   const char* k;         // contiguous: row 0 of (b, h); paged: pool base
   const char* v;
-  const int32_t* bt;     // block-table row of b (paged) or null
+  const int32_t* bt;     // block-table row of b (paged)
   const int32_t* kept;   // kept list of (b, h) or null
   int n_ctx;             // tokens in the sequence
   int n_blocks;          // ceil(n_ctx / 64)
   int n_pages;           // ceil(n_ctx / page) (paged)
   int n_trav;            // T'
   int zero_pos;          // GIVEN order: position of block 0 in the list, or -1
-  int page;              // page size (0 = contiguous)
-  int hkv;               // kv heads
-  int h;                 // kv head of this unit
-  int num_pages;         // pages in the pool (page ids are checked against it)
-  WsHeader* ws;
+  int log2_page;         // paged: log2(page size)
+  int hkv, h;
+  int num_pages;
 };
 
-// Context length of sequence b, clamped to what the shape can hold; an
-// out-of-range value is recorded as a device input error.
-__device__ __forceinline__ int clamped_len(const KernelArgs& a, int b, bool report) {
-  const int len = a.context_lens[b];
-  const long long cap = a.page_size ? (long long)a.max_pages * a.page_size : (long long)a.max_ctx;
-  if (len < 0 || (long long)len > cap) {
-    if (report && threadIdx.x == 0) atomicMax(&a.ws->error, (int)ART_ERR_DEVICE_INPUT);
-    return len < 0 ? 0 : (int)cap;
-  }
-  return len;
-}
-
-// Block index at traversal position t (uniform).  Block 0, when a candidate,
-// comes first; NATURAL ascending, RECENT_FIRST descending, GIVEN list order.
+// Block index at traversal position t.  Block 0, when a candidate, comes
+// first; NATURAL ascending, RECENT_FIRST descending, GIVEN list order.
 __device__ __forceinline__ int block_at(const UnitView& u, int order, int t) {
   if (!u.kept) {
     if (order == ART_ORDER_NATURAL) return t;
     return t == 0 ? 0 : u.n_blocks - t;  // RECENT_FIRST: [0, T-1, ..., 1]
   }
   const int n = u.n_trav;
-  if (order == ART_ORDER_NATURAL) return u.kept[t];
+  if (order == ART_ORDER_NATURAL) return sload(u.kept + t);
   if (order == ART_ORDER_RECENT_FIRST) {
-    const bool has0 = u.kept[0] == 0;
-    if (has0) return t == 0 ? 0 : u.kept[n - t];
-    return u.kept[n - 1 - t];
+    if (sload(u.kept) == 0) return t == 0 ? 0 : sload(u.kept + (n - t));
+    return sload(u.kept + (n - 1 - t));
   }
-  // GIVEN
-  if (u.zero_pos < 0) return u.kept[t];
+  if (u.zero_pos < 0) return sload(u.kept + t);
   if (t == 0) return 0;
-  return t <= u.zero_pos ? u.kept[t - 1] : u.kept[t];
+  return sload(u.kept + (t <= u.zero_pos ? t - 1 : t));
 }
 
-// Page ids covering one 64-token block (uniform).  Page sizes are multiples
-// of 16, so a 16-token MFMA tile and a 4-token row-order load never straddle
-// a page.  Indices past the sequence's last page are clamped to it: those
-// rows are read (in bounds) and then masked.
-struct BlockPages {
-  int pg[4];
+// Uniform addressing of one 64-token block.
+//   contiguous: rows past the context are clamped per lane to the last token
+//               at load time (read in bounds, then masked);
+//   paged:      one base per 16-token group (page sizes are powers of two
+//               >= 16), page ids read through the scalar cache; page indices
+//               past the sequence are clamped to its last page, page ids
+//               outside the pool are replaced by page 0 and recorded.
+struct BlockAddr {
+  const char* kb[4];   // paged: row of token 16*g of the block
+  const char* vb[4];
+  int j;               // block index
+  int nvalid;          // valid tokens in the block
 };
-__device__ __forceinline__ BlockPages block_pages(const UnitView& u, int j) {
-  BlockPages bp;
-  if (u.page == 0) return bp;
-  const int first = (j * kBlk) / u.page;
-  const int npb = u.page >= kBlk ? 1 : kBlk / u.page;
+
+template <int ROW, bool PAGED>
+__device__ __forceinline__ BlockAddr block_addr(const UnitView& u, int j, int& bad) {
+  BlockAddr ba;
+  ba.j = j;
+  ba.nvalid = min(kBlk, u.n_ctx - j * kBlk);
+  if constexpr (PAGED) {
+    const int pmask = (1 << u.log2_page) - 1;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int pg = i < npb ? uni(u.bt[min(first + i, u.n_pages - 1)]) : 0;
-    if (pg < 0 || pg >= u.num_pages) {  // never address outside the pool
-      if (threadIdx.x == 0) atomicMax(&u.ws->error, (int)ART_ERR_DEVICE_INPUT);
-      pg = 0;
+    for (int g = 0; g < 4; ++g) {
+      const int tok = j * kBlk + 16 * g;
+      const int pi = min(tok >> u.log2_page, u.n_pages - 1);
+      int pg = sload(u.bt + pi);
+      const bool oob = (unsigned)pg >= (unsigned)u.num_pages;
+      bad |= oob;
+      pg = oob ? 0 : pg;
+      const size_t row = ((size_t)pg * u.hkv + u.h) * ((size_t)pmask + 1) + (size_t)(tok & pmask);
+      ba.kb[g] = u.k + row * ROW;
+      ba.vb[g] = u.v + row * ROW;
     }
-    bp.pg[i] = pg;
-  }
-  return bp;
-}
-// Uniform base pointer of the row of token j*64 + tb (tb a multiple of 4
-// within one page); lanes add their own row / chunk offsets.
-template <int ROW>
-__device__ __forceinline__ const char* row_base(const UnitView& u, const char* base, const BlockPages& bp,
-                                                int j, int tb) {
-  if (u.page == 0) return base + (size_t)(j * kBlk + tb) * ROW;
-  const int idx = u.page >= kBlk ? 0 : tb / u.page;
-  int pg = bp.pg[0];
+  } else {
 #pragma unroll
-  for (int i = 1; i < 4; ++i) pg = idx == i ? bp.pg[i] : pg;
-  return base + (((size_t)pg * u.hkv + u.h) * u.page + (j * kBlk + tb) % u.page) * ROW;
+    for (int g = 0; g < 4; ++g) ba.kb[g] = ba.vb[g] = nullptr;
+  }
+  return ba;
 }
 
 // ---------------------------------------------------------------------------
-// LDS scratch of one wave
+// LDS layout (one workgroup)
 // ---------------------------------------------------------------------------
-template <int G, int EPC>
-struct alignas(16) Lds {
+template <int G, int D>
+struct Summary {             // one block, published for the round
+  float m[4];                // reference max per head (log2 domain)
+  float l[4];                // softmax mass per head relative to m
+  float ps[G][D / 4];        // sums on the probe dims relative to m
+};
+template <int G, int D>
+struct CarryLds {            // prefix state on the probe dims
+  float m[4];
+  int counter;
+  int pad[3];
+  double l[4];
+  double pacc[G][D / 4];
+};
+template <int G>
+struct alignas(16) WaveLds {
+  float p[kBlk][4];               // softmax weights of the block, by token
+  float probe[4][16][G][2];       // per-token-group sums on probe dims
+};
+template <int G, int D, int EPC>
+struct alignas(16) GroupLds {
   union {
-    float p[kBlk][4];                 // softmax weights of the block, by token
-    float acc[4][16][G][EPC];         // epilogue: per-token-group partial outputs
+    struct {
+      WaveLds<G> wave[kMaxWaves];
+      Summary<G, D> sum[kMaxWaves];
+      CarryLds<G, D> carry[2];
+      int stable[kMaxWaves];
+      int bad;
+      int zero_pos;
+    } r;
+    struct {                       // epilogue: per-wave state
+      float m[kMaxWaves][4];
+      float l[kMaxWaves][4];
+      int issued[kMaxWaves];
+      float acc[kMaxWaves][4][16][G][EPC];
+    } e;
   };
-  float probe[4][16][G][2];           // per-token-group block sums on probe dims
-  double red[4][2];                   // per-row partial (|x|^2, x.x_prev)
 };
 
 // ---------------------------------------------------------------------------
 // the decode kernel
 // ---------------------------------------------------------------------------
-template <int DT, int G>
-__global__ __launch_bounds__(kWave) void art_decode_kernel(KernelArgs a) {
+template <int DT, int G, bool PAGED>
+__global__ __launch_bounds__(kWave * kMaxWaves) void art_decode_kernel(KernelArgs a) {
   using GE = Geo<DT>;
   constexpr int D = GE::D, ES = GE::ES, EPC = GE::EPC, PPC = GE::PPC;
   constexpr int ROW = D * ES;
   static_assert(ROW == kRowChunks * 16, "rows must be 16 chunks of 16 bytes");
-  __shared__ Lds<G, EPC> lds;
+  __shared__ GroupLds<G, D, EPC> S_;
+  auto& R = S_.r;
 
-  const int lane = threadIdx.x;
-  const int lg = lane >> 4;   // token group / MFMA k-slot group
-  const int c = lane & 15;    // chunk / MFMA row-column index
+  const int W = blockDim.x >> 6;
+  const int wid = uni(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int lg = lane >> 4;
+  const int c = lane & 15;
+  WaveLds<G>& wl = R.wave[wid];
 
-  // ---- work item -------------------------------------------------------
+  // ---- work item --------------------------------------------------------
   const int n_units = a.batch * a.hkv;
-  const int item = blockIdx.x;
-  const int unit = item % n_units;
-  const int chunk = item / n_units;
+  const int unit = blockIdx.x % n_units;
+  const int chunk = blockIdx.x / n_units;
   const int b = unit / a.hkv;
   const int h = unit % a.hkv;
 
   UnitView u;
-  u.ws = a.ws;
-  u.num_pages = a.num_pages;
-  u.n_ctx = clamped_len(a, b, chunk == 0);
-  u.n_blocks = (u.n_ctx + kBlk - 1) / kBlk;
-  u.page = a.page_size;
   u.hkv = a.hkv;
   u.h = h;
-  if (a.page_size) {
-    u.n_pages = (u.n_ctx + a.page_size - 1) / a.page_size;
+  u.num_pages = a.num_pages;
+  int bad_input = 0;
+  {
+    const int len = sload(a.context_lens + b);
+    const long long cap = PAGED ? (long long)a.max_pages * a.page_size : (long long)a.max_ctx;
+    bad_input = (len < 0) || ((long long)len > cap);
+    u.n_ctx = len < 0 ? 0 : ((long long)len > cap ? (int)cap : len);
+  }
+  u.n_blocks = (u.n_ctx + kBlk - 1) / kBlk;
+  if constexpr (PAGED) {
+    u.log2_page = 31 - __builtin_clz(a.page_size);
+    u.n_pages = (u.n_ctx + a.page_size - 1) >> u.log2_page;
     u.bt = a.block_table + (size_t)b * a.max_pages;
     u.k = (const char*)a.k;
     u.v = (const char*)a.v;
   } else {
+    u.log2_page = 0;
     u.n_pages = 0;
     u.bt = nullptr;
     const size_t base = ((size_t)b * a.hkv + h) * (size_t)a.max_ctx * ROW;
@@ -266,351 +322,404 @@ __global__ __launch_bounds__(kWave) void art_decode_kernel(KernelArgs a) {
   u.n_trav = u.n_blocks;
   if (a.kept_blocks) {
     u.kept = a.kept_blocks + ((size_t)b * a.hkv + h) * a.max_kept;
-    u.n_trav = a.kept_count[(size_t)b * a.hkv + h];
+    u.n_trav = sload(a.kept_count + unit);
   }
-
   const int t_begin = chunk * a.chunk_blocks;
   const int t_end = min(u.n_trav, t_begin + a.chunk_blocks);
-  if (t_begin >= u.n_trav && !(chunk == 0)) return;
+  const bool single = a.chunk_blocks >= u.n_trav;  // whole traversal in this work item
+  float* out_rows = a.out + ((size_t)b * a.hq + h * G) * D;
 
-  // ---- validate the kept list (device-side input) ----------------------
+  // ---- kept list: validate (device input) and find block 0 --------------
   if (u.kept) {
-    bool bad = u.n_trav < 0 || u.n_trav > a.max_kept;
-    int zp = -1;
-    if (!bad) {
-      for (int base = 0; base < u.n_trav; base += kWave) {
-        const int i = base + lane;
-        bool lane_bad = false;
-        bool is0 = false;
-        if (i < u.n_trav) {
-          const int e = u.kept[i];
-          lane_bad = e < 0 || e >= u.n_blocks;
-          if (a.order != ART_ORDER_GIVEN && i > 0) lane_bad |= e <= u.kept[i - 1];
-          is0 = e == 0;
-        }
-        if (__builtin_amdgcn_ballot_w64(lane_bad)) bad = true;
-        const uint64_t z = __builtin_amdgcn_ballot_w64(is0);
-        if (z && zp < 0) zp = base + __builtin_ctzll(z);
+    if (threadIdx.x == 0) {
+      R.bad = (u.n_trav < 0 || u.n_trav > a.max_kept) ? 1 : 0;
+      R.zero_pos = 0x7fffffff;
+    }
+    __syncthreads();
+    if (u.n_trav >= 0 && u.n_trav <= a.max_kept) {
+      for (int i = threadIdx.x; i < u.n_trav; i += blockDim.x) {
+        const int e = u.kept[i];
+        bool lb = e < 0 || e >= u.n_blocks;
+        if (a.order != ART_ORDER_GIVEN && i > 0) lb |= e <= u.kept[i - 1];
+        if (lb) atomicOr(&R.bad, 1);
+        if (e == 0) atomicMin(&R.zero_pos, i);
       }
     }
+    __syncthreads();
+    const int bad = uni(R.bad);
+    const int zp = uni(R.zero_pos);
+    __syncthreads();
     if (bad) {
-      if (lane == 0) atomicMax(&a.ws->error, (int)ART_ERR_DEVICE_INPUT);
+      if (threadIdx.x == 0) atomicMax(&a.ws->error, (int)ART_ERR_DEVICE_INPUT);
       if (chunk == 0) {
-        for (int i = lane; i < G * D; i += kWave) a.out[((size_t)b * a.hq + h * G) * D + i] = 0.f;
-        if (lane == 0) {
+        for (int i = threadIdx.x; i < G * D; i += blockDim.x) out_rows[i] = 0.f;
+        if (threadIdx.x == 0) {
           a.stop_idx[unit] = -1;
           if (a.blocks_issued) a.blocks_issued[unit] = 0;
         }
       }
       return;
     }
-    u.zero_pos = zp;
+    u.zero_pos = zp == 0x7fffffff ? -1 : zp;
   }
+  if (bad_input && chunk == 0 && threadIdx.x == 0) atomicMax(&a.ws->error, (int)ART_ERR_DEVICE_INPUT);
 
-  if (u.n_trav == 0) {  // nothing to attend to: out = 0, stop = 0
+  if (u.n_trav <= 0) {  // nothing to attend to: out = 0, stop = 0
     if (chunk == 0) {
-      for (int i = lane; i < G * D; i += kWave) a.out[((size_t)b * a.hq + h * G) * D + i] = 0.f;
-      if (lane == 0) {
+      for (int i = threadIdx.x; i < G * D; i += blockDim.x) out_rows[i] = 0.f;
+      if (threadIdx.x == 0) {
         a.stop_idx[unit] = 0;
         if (a.blocks_issued) a.blocks_issued[unit] = 0;
       }
     }
     return;
   }
+  if (t_begin >= t_end) return;  // chunk past this unit's traversal
 
-  // ---- query operand (rows replicated: MFMA row r -> head r % G) --------
-  const int qhead = c % G;
-  const char* qrow = (const char*)a.q + (((size_t)b * a.hq + h * G + qhead) * D) * ES;
+  // ---- query operand (rows replicated: MFMA row r -> head r % G) ---------
+  const char* qrow = (const char*)a.q + (((size_t)b * a.hq + h * G + (c % G)) * D) * ES;
   u32x4 qa[kKLoads];
 #pragma unroll
   for (int i = 0; i < kKLoads; ++i) qa[i] = *(const u32x4*)(qrow + (4 * i + lg) * 16);
-
   const float c2 = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(d)
 
-  // ---- state -------------------------------------------------------------
-  float m_run[G], l_run[G];
-  float acc[G][EPC];
+  // ---- per-wave running softmax state -------------------------------------
+  float m_w[G], l_w[G], acc[G][EPC];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    m_run[g] = -INFINITY;
-    l_run[g] = 0.f;
+    m_w[g] = -INFINITY;
+    l_w[g] = 0.f;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[g][e] = 0.f;
   }
-  // fp64 probe state of this lane: head lg (if lg < G), probe dims of chunk c
-  double pacc[PPC], xprev[PPC];
-#pragma unroll
-  for (int k = 0; k < PPC; ++k) pacc[k] = 0.0, xprev[k] = 0.0;
-  double l64 = 0.0;        // running denominator of head lg (uniform per row)
-  double spp = 0.0;        // |x^(t-1)|^2
-  int counter = 0;
-  int processed = 0;       // traversal blocks folded into the state
-  int issued = 0;
   const bool art_mode = a.mode == ART_MODE_ART;
   const double tau = (double)a.eps_scale, phi = (double)a.eps_dir;
+  if (art_mode) {
+    if (threadIdx.x < 4) {
+      R.carry[0].m[threadIdx.x] = -INFINITY;
+      R.carry[0].l[threadIdx.x] = 0.0;
+    }
+    if (threadIdx.x == 0) R.carry[0].counter = 0;
+    for (int i = threadIdx.x; i < G * (D / 4); i += blockDim.x) (&R.carry[0].pacc[0][0])[i] = 0.0;
+  }
 
-  // ---- loads -------------------------------------------------------------
+  // ---- loads ---------------------------------------------------------------
   u32x4 kr[kTiles][kKLoads];
   u32x4 vr[kVLoads];
-
-  // K of tile nt -> token 16*nt + c, chunk 4*i + lg.  Contiguous rows past
-  // the context are clamped to the last token (masked later); paged rows stay
-  // inside the (clamped) page.
-  auto load_k = [&](int jb, const BlockPages& bp) {
+  auto load_k = [&](const BlockAddr& ba) {
 #pragma unroll
     for (int nt = 0; nt < kTiles; ++nt) {
       const char* row;
-      if (u.page == 0) {
-        row = u.k + (size_t)min(jb * kBlk + nt * 16 + c, u.n_ctx - 1) * ROW;
-      } else {
-        row = row_base<ROW>(u, u.k, bp, jb, nt * 16) + c * ROW;
-      }
+      if constexpr (PAGED) row = ba.kb[nt] + c * ROW;
+      else row = u.k + (size_t)min(ba.j * kBlk + nt * 16 + c, u.n_ctx - 1) * ROW;
 #pragma unroll
       for (int i = 0; i < kKLoads; ++i) kr[nt][i] = *(const u32x4*)(row + (4 * i + lg) * 16);
     }
   };
-  // V load i -> token 4*i + lg, chunk c.
-  auto load_v = [&](int jb, const BlockPages& bp) {
+  auto load_v = [&](const BlockAddr& ba) {
 #pragma unroll
     for (int i = 0; i < kVLoads; ++i) {
       const char* row;
-      if (u.page == 0) {
-        row = u.v + (size_t)min(jb * kBlk + 4 * i + lg, u.n_ctx - 1) * ROW;
-      } else {
-        row = row_base<ROW>(u, u.v, bp, jb, 4 * i) + lg * ROW;
-      }
+      if constexpr (PAGED) row = ba.vb[i >> 2] + (((4 * i) & 15) + lg) * ROW;
+      else row = u.v + (size_t)min(ba.j * kBlk + 4 * i + lg, u.n_ctx - 1) * ROW;
       vr[i] = *(const u32x4*)(row + c * 16);
     }
   };
 
-  int t = t_begin;
-  int j = uni(block_at(u, a.order, t));
-  {
-    const BlockPages bp0 = block_pages(u, j);
-    load_k(j, bp0);
-    load_v(j, bp0);
+  int bad_page = 0;
+  int issued = 0;
+  int stop = -1;  // traversal blocks processed at the stop (ART mode)
+  BlockAddr cur;
+  if (t_begin + wid < t_end) {
+    cur = block_addr<ROW, PAGED>(u, uni(block_at(u, a.order, t_begin + wid)), bad_page);
+    load_k(cur);
+    load_v(cur);
+    ++issued;
   }
-  issued = 1;
-  int jn = (t + 1 < t_end) ? uni(block_at(u, a.order, t + 1)) : j;
-  BlockPages bpn = block_pages(u, jn);
-  int stop = -1;
+  int parity = 0;
 
-  for (; t < t_end; ++t) {
-    const int nvalid = min(kBlk, u.n_ctx - j * kBlk);
+  for (int t0 = t_begin; t0 < t_end; t0 += W) {
+    const int t = t0 + wid;
+    const bool active = t < t_end;
+    const int n_act = min(W, t_end - t0);
+    const int tn = t + W;
+    const bool has_next = tn < t_end;
+    BlockAddr nxt = cur;
+    if (has_next) nxt = block_addr<ROW, PAGED>(u, uni(block_at(u, a.order, tn)), bad_page);
 
-    // ---- scores: S[nt][r] = q_{r%G} . k_{16 nt + c} ------------------------
-    f32x4 S[kTiles];
-#pragma unroll
-    for (int nt = 0; nt < kTiles; ++nt) {
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (DT == ART_DT_BF16) {
-#pragma unroll
-        for (int i = 0; i < kKLoads; ++i)
-          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[i]),
-                                                      __builtin_bit_cast(bf16x8, kr[nt][i]), s, 0, 0, 0);
-      } else {
-#pragma unroll
-        for (int i = 0; i < kKLoads; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            s = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(qa[i][e]), as_f32(kr[nt][i][e]), s, 0, 0, 0);
-      }
-      S[nt] = s;
-    }
-    if (t + 1 < t_end) {
-      load_k(jn, bpn);
-      ++issued;
-    }
-
-    // ---- online softmax (log2 domain) -------------------------------------
-    float alpha[G], lblk[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int nt = 0; nt < kTiles; ++nt) {
-        const bool ok = nt * 16 + c < nvalid;
-        const float sv = ok ? S[nt][g] * c2 : -INFINITY;
-        S[nt][g] = sv;
-        mx = fmaxf(mx, sv);
-      }
-      mx = uni_f(row_max(mx));
-      const float mnew = fmaxf(m_run[g], mx);
-      alpha[g] = __builtin_amdgcn_exp2f(m_run[g] - mnew);
-      m_run[g] = mnew;
-      float ls = 0.f;
-#pragma unroll
-      for (int nt = 0; nt < kTiles; ++nt) {
-        const float pv = __builtin_amdgcn_exp2f(S[nt][g] - mnew);
-        S[nt][g] = pv;
-        ls += pv;
-      }
-      lblk[g] = uni_f(row_sum(ls));
-      l_run[g] = l_run[g] * alpha[g] + lblk[g];
-    }
-    // publish this lane's token (16*lg + c) weights; tile lg selected by lane
-    {
-      f32x4 mine = S[0];
-#pragma unroll
-      for (int nt = 1; nt < kTiles; ++nt) mine = (lg == nt) ? S[nt] : mine;
-      float4 w;
-      w.x = mine[0];
-      w.y = G > 1 ? mine[1] : 0.f;
-      w.z = G > 2 ? mine[2] : 0.f;
-      w.w = G > 3 ? mine[3] : 0.f;
-      *(float4*)&lds.p[16 * lg + c][0] = w;
-    }
-    __syncthreads();
-
-    // ---- P V --------------------------------------------------------------
+    float alpha[G], m_new[G], lblk[G];
     float bacc[G][EPC];
+    if (active) {
+      const int nvalid = cur.nvalid;
+      // ---- scores: S[nt][r] = q_{r%G} . k_{16 nt + c} ----------------------
+      f32x4 S[kTiles];
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+      for (int nt = 0; nt < kTiles; ++nt) {
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (DT == ART_DT_BF16) {
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) bacc[g][e] = 0.f;
+          for (int i = 0; i < kKLoads; ++i)
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[i]),
+                                                        __builtin_bit_cast(bf16x8, kr[nt][i]), s, 0, 0, 0);
+        } else {
 #pragma unroll
-    for (int i = 0; i < kVLoads; ++i) {
-      const int tok = 4 * i + lg;
-      const float4 pw = *(const float4*)&lds.p[tok][0];
-      const float pg[4] = {pw.x, pw.y, pw.z, pw.w};
-      u32x4 w = vr[i];
-      if (tok >= nvalid) w = u32x4{0u, 0u, 0u, 0u};
-      float ve[EPC];
-      if constexpr (DT == ART_DT_BF16) {
+          for (int i = 0; i < kKLoads; ++i)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          ve[2 * k] = bf16_lo(w[k]);
-          ve[2 * k + 1] = bf16_hi(w[k]);
+            for (int e = 0; e < 4; ++e)
+              s = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(qa[i][e]), as_f32(kr[nt][i][e]), s, 0, 0, 0);
         }
-      } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) ve[k] = as_f32(w[k]);
+        S[nt] = s;
       }
+      if (has_next) {
+        load_k(nxt);
+        ++issued;
+      }
+      // ---- online softmax against the wave's running max --------------------
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int nt = 0; nt < kTiles; ++nt) {
+          const float sv = (nt * 16 + c < nvalid) ? S[nt][g] * c2 : -INFINITY;
+          S[nt][g] = sv;
+          mx = fmaxf(mx, sv);
+        }
+        mx = uni_f(row_max(mx));
+        m_new[g] = fmaxf(m_w[g], mx);
+        alpha[g] = __builtin_amdgcn_exp2f(m_w[g] - m_new[g]);
+        float ls = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < kTiles; ++nt) {
+          const float pv = __builtin_amdgcn_exp2f(S[nt][g] - m_new[g]);
+          S[nt][g] = pv;
+          ls += pv;
+        }
+        lblk[g] = uni_f(row_sum(ls));
+      }
+      {  // this lane's token (16*lg + c) lives in tile lg
+        f32x4 mine = S[0];
+#pragma unroll
+        for (int nt = 1; nt < kTiles; ++nt) mine = (lg == nt) ? S[nt] : mine;
+        float4 w4;
+        w4.x = mine[0];
+        w4.y = G > 1 ? mine[1] : 0.f;
+        w4.z = G > 2 ? mine[2] : 0.f;
+        w4.w = G > 3 ? mine[3] : 0.f;
+        *(float4*)&wl.p[16 * lg + c][0] = w4;
+      }
+      wave_lds_sync();
+      // ---- P V ---------------------------------------------------------------
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) bacc[g][e] = fmaf(pg[g], ve[e], bacc[g][e]);
-    }
-    if (t + 1 < t_end) load_v(jn, bpn);
-    // next-next block: index and pages, consumed by the next iteration's loads
-    const int jnn = (t + 2 < t_end) ? uni(block_at(u, a.order, t + 2)) : jn;
-    const BlockPages bpnn = (t + 2 < t_end) ? block_pages(u, jnn) : bpn;
-
+        for (int e = 0; e < EPC; ++e) bacc[g][e] = 0.f;
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+      for (int i = 0; i < kVLoads; ++i) {
+        const int tok = 4 * i + lg;
+        const float4 pw = *(const float4*)&wl.p[tok][0];
+        const float pg[4] = {pw.x, pw.y, pw.z, pw.w};
+        u32x4 w = vr[i];
+        if (tok >= nvalid) w = u32x4{0u, 0u, 0u, 0u};
+        float ve[EPC];
+        if constexpr (DT == ART_DT_BF16) {
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) acc[g][e] = fmaf(acc[g][e], alpha[g], bacc[g][e]);
-    ++processed;
-
-    // ---- probe + criterion -------------------------------------------------
-    if (art_mode) {
-      // block sums on probe dims (elements 0 and 4 of the chunk), per token group
+          for (int k = 0; k < 4; ++k) {
+            ve[2 * k] = bf16_lo(w[k]);
+            ve[2 * k + 1] = bf16_hi(w[k]);
+          }
+        } else {
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        lds.probe[lg][c][g][0] = bacc[g][0];
-        if (PPC > 1) lds.probe[lg][c][g][1] = bacc[g][PPC > 1 ? 4 : 0];
-      }
-      __syncthreads();
-      double sxx = 0.0, sxp = 0.0;
-      if (lg < G) {
-        double alpha_g = 0.0, lb = 0.0;
+          for (int k = 0; k < 4; ++k) ve[k] = as_f32(w[k]);
+        }
 #pragma unroll
         for (int g = 0; g < G; ++g)
-          if (g == lg) alpha_g = (double)alpha[g], lb = (double)lblk[g];
-        l64 = l64 * alpha_g + lb;
-        const double inv_l = 1.0 / l64;
 #pragma unroll
-        for (int k = 0; k < PPC; ++k) {
-          const float s = (lds.probe[0][c][lg][k] + lds.probe[1][c][lg][k]) +
-                          (lds.probe[2][c][lg][k] + lds.probe[3][c][lg][k]);
-          pacc[k] = pacc[k] * alpha_g + (double)s;
-          const double x = pacc[k] * inv_l;
-          sxx = fma(x, x, sxx);
-          sxp = fma(x, xprev[k], sxp);
-          xprev[k] = x;
-        }
+          for (int e = 0; e < EPC; ++e) bacc[g][e] = fmaf(pg[g], ve[e], bacc[g][e]);
       }
-      sxx = row_sum_d(sxx);
-      sxp = row_sum_d(sxp);
-      if (c == 0) {
-        lds.red[lg][0] = sxx;
-        lds.red[lg][1] = sxp;
+      if (has_next) load_v(nxt);
+    }
+
+    int stop_round = -1;  // this round's stop, as a traversal count
+    if (art_mode) {
+      // ---- publish the block summary ------------------------------------------
+      if (active) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          wl.probe[lg][c][g][0] = bacc[g][0];
+          if (PPC > 1) wl.probe[lg][c][g][1] = bacc[g][PPC > 1 ? 4 : 0];
+        }
+        wave_lds_sync();
+        if (lg < G) {
+#pragma unroll
+          for (int k = 0; k < PPC; ++k)
+            R.sum[wid].ps[lg][c * PPC + k] = (wl.probe[0][c][lg][k] + wl.probe[1][c][lg][k]) +
+                                             (wl.probe[2][c][lg][k] + wl.probe[3][c][lg][k]);
+        }
+        if (lane < G) {
+          float mv = m_new[0], lv = lblk[0];
+#pragma unroll
+          for (int g = 1; g < G; ++g)
+            if (lane == g) mv = m_new[g], lv = lblk[g];
+          R.sum[wid].m[lane] = mv;
+          R.sum[wid].l[lane] = lv;
+        }
       }
       __syncthreads();
-      const double stt = uni_d((lds.red[0][0] + lds.red[1][0]) + (lds.red[2][0] + lds.red[3][0]));
-      const double stp = uni_d((lds.red[0][1] + lds.red[1][1]) + (lds.red[2][1] + lds.red[3][1]));
-      const int count = t + 1;  // traversal blocks processed so far
-      if (count >= 2) {
+      // ---- prefix on the probe dims through this wave's position -------------
+      // lane (lg, c): head lg (if lg < G), probe dims c*PPC .. c*PPC+PPC-1
+      const CarryLds<G, D>& cin = R.carry[parity];
+      const int hg = lg < G ? lg : 0;
+      float mP = cin.m[hg];
+      double lP = cin.l[hg];
+      double pP[PPC], xprev[PPC], xcur[PPC];
+#pragma unroll
+      for (int k = 0; k < PPC; ++k) {
+        pP[k] = cin.pacc[hg][c * PPC + k];
+        xprev[k] = xcur[k] = 0.0;
+      }
+      const bool carry_out = wid == W - 1;  // the last wave forwards the round's prefix
+      const int upto = carry_out ? n_act - 1 : (active ? wid : -1);
+      for (int w2 = 0; w2 <= upto; ++w2) {
+        if (w2 == wid) {  // x^(t-1): the prefix before this position
+          const double inv = lP > 0.0 ? 1.0 / lP : 0.0;
+#pragma unroll
+          for (int k = 0; k < PPC; ++k) xprev[k] = pP[k] * inv;
+        }
+        const float mb = R.sum[w2].m[hg];
+        const float M = fmaxf(mP, mb);
+        const double sP = (double)__builtin_amdgcn_exp2f(mP - M);
+        const double sB = (double)__builtin_amdgcn_exp2f(mb - M);
+        lP = lP * sP + (double)R.sum[w2].l[hg] * sB;
+#pragma unroll
+        for (int k = 0; k < PPC; ++k) pP[k] = pP[k] * sP + (double)R.sum[w2].ps[hg][c * PPC + k] * sB;
+        mP = M;
+        if (w2 == wid) {  // x^(t)
+          const double inv = 1.0 / lP;
+#pragma unroll
+          for (int k = 0; k < PPC; ++k) xcur[k] = pP[k] * inv;
+        }
+      }
+      int stable = 0;
+      if (active && t + 1 >= 2) {  // a check exists from the second block on
+        double spp = 0.0, stt = 0.0, stp = 0.0;
+        if (lg < G) {
+#pragma unroll
+          for (int k = 0; k < PPC; ++k) {
+            spp = fma(xprev[k], xprev[k], spp);
+            stt = fma(xcur[k], xcur[k], stt);
+            stp = fma(xcur[k], xprev[k], stp);
+          }
+        }
+        spp = wave_sum_d(spp);
+        stt = wave_sum_d(stt);
+        stp = wave_sum_d(stp);
         const double pa = sqrt(spp), pb = sqrt(stt);
-        bool stable = false;
         if (pa > 0.0 && pb > 0.0) {
-          const double ds = fabs(pb - pa) / pa;
-          const double dd = 1.0 - stp / (pa * pb);
+          const double ds = fabs(pb - pa) / pa;        // relative norm change
+          const double dd = 1.0 - stp / (pa * pb);     // 1 - cos
           stable = (ds < tau) && (dd < phi);
         }
-        counter = stable ? counter + 1 : 0;
+      }
+      if (lane == 0) R.stable[wid] = stable;
+      if (carry_out && lg < G) {
+        CarryLds<G, D>& co = R.carry[parity ^ 1];
+        if (c == 0) {
+          co.m[lg] = mP;
+          co.l[lg] = lP;
+        }
+#pragma unroll
+        for (int k = 0; k < PPC; ++k) co.pacc[lg][c * PPC + k] = pP[k];
+      }
+      __syncthreads();
+      // ---- patience counter over the round, in order --------------------------
+      int counter = R.carry[parity].counter;
+      for (int w2 = 0; w2 < n_act; ++w2) {
+        const int cnt = t0 + w2 + 1;
+        if (cnt < 2) continue;
+        counter = R.stable[w2] ? counter + 1 : 0;
         if (counter >= a.patience) {
-          stop = count;
+          stop_round = cnt;
           break;
         }
       }
-      spp = stt;
+      counter = uni(counter);
+      stop_round = uni(stop_round);
+      if (threadIdx.x == 0) R.carry[parity ^ 1].counter = counter;
+      parity ^= 1;
     }
-    __syncthreads();
-    j = jn;
-    jn = jnn;
-    bpn = bpnn;
-  }
-  if (stop < 0) stop = t_end;  // single-chunk: ran to the end
 
-  // ---- epilogue: reduce token groups, normalize, write ----------------------
+    // ---- commit this wave's block (unless it lies after the stop) -------------
+    if (active && (stop_round < 0 || t + 1 <= stop_round)) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        m_w[g] = m_new[g];
+        l_w[g] = l_w[g] * alpha[g] + lblk[g];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[g][e] = fmaf(acc[g][e], alpha[g], bacc[g][e]);
+      }
+    }
+    if (stop_round >= 0) {
+      stop = stop_round;
+      break;
+    }
+    cur = nxt;
+  }
+  if (stop < 0) stop = t_end;
+
+  // ---- epilogue: merge waves, reduce token groups, normalize ---------------
+  __syncthreads();
+  auto& E = S_.e;
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) lds.acc[lg][c][g][e] = acc[g][e];
+    for (int e = 0; e < EPC; ++e) E.acc[wid][lg][c][g][e] = acc[g][e];
+  if (lane < G) {
+    float mv = m_w[0], lv = l_w[0];
+#pragma unroll
+    for (int g = 1; g < G; ++g)
+      if (lane == g) mv = m_w[g], lv = l_w[g];
+    E.m[wid][lane] = mv;
+    E.l[wid][lane] = lv;
+  }
+  if (lane == 0) E.issued[wid] = issued;
   __syncthreads();
-  if (a.chunk_blocks >= u.n_trav) {
-    // whole traversal in this work item: write the output directly
-    if (lg < G) {
-      float l_g = 0.f;
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-        if (g == lg) l_g = l_run[g];
-      const float inv = 1.0f / l_g;
-      float o[EPC];
-#pragma unroll
-      for (int e = 0; e < EPC; ++e)
-        o[e] = ((lds.acc[0][c][lg][e] + lds.acc[1][c][lg][e]) + (lds.acc[2][c][lg][e] + lds.acc[3][c][lg][e])) * inv;
-      float* dst = a.out + ((size_t)b * a.hq + h * G + lg) * D + c * EPC;
-#pragma unroll
-      for (int e = 0; e < EPC; e += 4) *(float4*)(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
+  for (int o = threadIdx.x; o < G * D; o += blockDim.x) {
+    const int g = o / D, dim = o % D;
+    const int cc = dim / EPC, e = dim % EPC;
+    float M = -INFINITY;
+    for (int w2 = 0; w2 < W; ++w2)
+      if (E.l[w2][g] > 0.f) M = fmaxf(M, E.m[w2][g]);
+    float L = 0.f, num = 0.f;
+    for (int w2 = 0; w2 < W; ++w2) {
+      if (!(E.l[w2][g] > 0.f)) continue;  // a wave with no committed block
+      const float s = __builtin_amdgcn_exp2f(E.m[w2][g] - M);
+      L = fmaf(E.l[w2][g], s, L);
+      const float v = (E.acc[w2][0][cc][g][e] + E.acc[w2][1][cc][g][e]) +
+                      (E.acc[w2][2][cc][g][e] + E.acc[w2][3][cc][g][e]);
+      num = fmaf(v, s, num);
     }
-    if (lane == 0) {
-      a.stop_idx[unit] = stop;
-      if (a.blocks_issued) a.blocks_issued[unit] = issued;
-    }
-  } else {
-    // split (full mode): write this chunk's partial (m, l, unnormalized acc)
-    float* part = a.partials + ((size_t)unit * a.max_chunks + chunk) * G * (D + 2);
-    if (lg < G) {
-      float o[EPC];
-#pragma unroll
-      for (int e = 0; e < EPC; ++e)
-        o[e] = (lds.acc[0][c][lg][e] + lds.acc[1][c][lg][e]) + (lds.acc[2][c][lg][e] + lds.acc[3][c][lg][e]);
-      float* dst = part + lg * (D + 2) + 2 + c * EPC;
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) dst[e] = o[e];
-      if (c == 0) {
-        float m_g = 0.f, l_g = 0.f;
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-          if (g == lg) m_g = m_run[g], l_g = l_run[g];
-        part[lg * (D + 2) + 0] = m_g;
-        part[lg * (D + 2) + 1] = l_g;
+    if (single) {
+      out_rows[o] = num / L;
+    } else {
+      float* part = a.partials + ((size_t)unit * a.max_chunks + chunk) * G * (D + 2) + g * (D + 2);
+      part[2 + dim] = num;
+      if (dim == 0) {
+        part[0] = M;
+        part[1] = L;
       }
     }
-    if (lane == 0) atomicAdd(&a.unit_state[unit].issued, issued);
   }
+  if (threadIdx.x == 0) {
+    int tot = 0;
+    for (int w2 = 0; w2 < W; ++w2) tot += E.issued[w2];
+    if (single) {
+      a.stop_idx[unit] = stop;
+      if (a.blocks_issued) a.blocks_issued[unit] = tot;
+    } else {
+      atomicAdd(&a.unit_state[unit].issued, tot);
+    }
+  }
+  if (bad_page && lane == 0) atomicMax(&a.ws->error, (int)ART_ERR_DEVICE_INPUT);
 }
 
 // ---------------------------------------------------------------------------
@@ -620,22 +729,27 @@ template <int D, int G>
 __global__ __launch_bounds__(kWave) void art_combine_kernel(KernelArgs a) {
   const int unit = blockIdx.x;
   const int b = unit / a.hkv, h = unit % a.hkv;
-  const int n_ctx = clamped_len(a, b, false);
-  const int n_trav = a.kept_blocks ? a.kept_count[unit] : (n_ctx + kBlk - 1) / kBlk;
-  if (n_trav <= 0 || n_trav > (a.kept_blocks ? a.max_kept : (1 << 30))) return;  // handled by the decode kernel
-  const int n_chunks = (n_trav + a.chunk_blocks - 1) / a.chunk_blocks;
-  if (n_chunks <= 1) return;
-  if (__builtin_amdgcn_readfirstlane(a.ws->error) != 0) {
-    // a kept-list error was recorded; the decode kernel already wrote this unit if bad
+  int n_ctx = sload(a.context_lens + b);
+  const long long cap = a.page_size ? (long long)a.max_pages * a.page_size : (long long)a.max_ctx;
+  n_ctx = n_ctx < 0 ? 0 : ((long long)n_ctx > cap ? (int)cap : n_ctx);
+  int n_trav = (n_ctx + kBlk - 1) / kBlk;
+  if (a.kept_blocks) {
+    n_trav = sload(a.kept_count + unit);
+    if (n_trav > a.max_kept) return;  // rejected by the decode kernel
   }
+  if (n_trav <= 0) return;
+  const int n_chunks = (n_trav + a.chunk_blocks - 1) / a.chunk_blocks;
+  if (n_chunks <= 1) return;  // written directly by the decode kernel
+  if (a.kept_blocks && a.stop_idx[unit] == -1) return;  // bad kept list: already reported
   const float* part = a.partials + (size_t)unit * a.max_chunks * G * (D + 2);
   for (int g = 0; g < G; ++g) {
     float M = -INFINITY;
-    for (int k = 0; k < n_chunks; ++k) M = fmaxf(M, part[(k * G + g) * (D + 2)]);
-    float L = 0.f;
-    float o0 = 0.f, o1 = 0.f;
+    for (int k = 0; k < n_chunks; ++k)
+      if (part[(k * G + g) * (D + 2) + 1] > 0.f) M = fmaxf(M, part[(k * G + g) * (D + 2)]);
+    float L = 0.f, o0 = 0.f, o1 = 0.f;
     for (int k = 0; k < n_chunks; ++k) {
       const float* pk = part + (k * G + g) * (D + 2);
+      if (!(pk[1] > 0.f)) continue;
       const float w = __builtin_amdgcn_exp2f(pk[0] - M);
       L = fmaf(pk[1], w, L);
       o0 = fmaf(pk[2 + threadIdx.x], w, o0);
@@ -672,9 +786,9 @@ __global__ void art_init_kernel(WsHeader* ws, UnitState* st, int n_units) {
 // ---------------------------------------------------------------------------
 // launch
 // ---------------------------------------------------------------------------
-template <int DT, int G>
-static hipError_t launch_t(const KernelArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((art_decode_kernel<DT, G>), dim3(grid), dim3(kWave), 0, s, a);
+template <int DT, int G, bool PAGED>
+static hipError_t launch_t(const KernelArgs& a, int grid, int waves, hipStream_t s) {
+  hipLaunchKernelGGL((art_decode_kernel<DT, G, PAGED>), dim3(grid), dim3(kWave * waves), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.max_chunks > 1) {
@@ -684,21 +798,27 @@ static hipError_t launch_t(const KernelArgs& a, int grid, hipStream_t s) {
   return e;
 }
 
+template <int DT, int G>
+static hipError_t launch_g(const KernelArgs& a, int grid, int waves, hipStream_t s) {
+  return a.page_size ? launch_t<DT, G, true>(a, grid, waves, s) : launch_t<DT, G, false>(a, grid, waves, s);
+}
+
 hipError_t launch(const KernelArgs& a, hipStream_t s) {
   const int n_units = a.batch * a.hkv;
   hipLaunchKernelGGL(art_init_kernel, dim3((n_units + 255) / 256), dim3(256), 0, s, a.ws, a.unit_state, n_units);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int grid = n_units * a.max_chunks;
+  const int waves = a.waves < 1 ? 1 : (a.waves > kMaxWaves ? kMaxWaves : a.waves);
   const int G = a.hq / a.hkv;
   if (a.dtype == ART_DT_BF16) {
-    if (G == 1) return launch_t<ART_DT_BF16, 1>(a, grid, s);
-    if (G == 2) return launch_t<ART_DT_BF16, 2>(a, grid, s);
-    return launch_t<ART_DT_BF16, 4>(a, grid, s);
+    if (G == 1) return launch_g<ART_DT_BF16, 1>(a, grid, waves, s);
+    if (G == 2) return launch_g<ART_DT_BF16, 2>(a, grid, waves, s);
+    return launch_g<ART_DT_BF16, 4>(a, grid, waves, s);
   }
-  if (G == 1) return launch_t<ART_DT_F32, 1>(a, grid, s);
-  if (G == 2) return launch_t<ART_DT_F32, 2>(a, grid, s);
-  return launch_t<ART_DT_F32, 4>(a, grid, s);
+  if (G == 1) return launch_g<ART_DT_F32, 1>(a, grid, waves, s);
+  if (G == 2) return launch_g<ART_DT_F32, 2>(a, grid, waves, s);
+  return launch_g<ART_DT_F32, 4>(a, grid, waves, s);
 }
 
 }  // namespace art
