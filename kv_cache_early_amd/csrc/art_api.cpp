@@ -52,6 +52,9 @@ art_status validate(const art_shape* sp, const art_params* pp) {
   // index ranges the kernels compute in 32-bit
   const int64_t units = (int64_t)s.batch * s.num_kv_heads;
   if (units > (1 << 26) || max_traversal(s) > (1 << 24)) return ART_ERR_UNSUPPORTED;
+  // paged pool rows (page * Hkv + h) * page_size + slot are 32-bit in the kernels
+  if (s.page_size > 0 && (int64_t)s.num_pages * s.num_kv_heads * s.page_size > (int64_t)UINT32_MAX)
+    return ART_ERR_UNSUPPORTED;
   return ART_OK;
 }
 

@@ -35,13 +35,17 @@
 // Lane geometry (both supported element types have 256-byte rows cut into
 // 16 chunks of 16 bytes): lane l = 16*lg + c with lg = l / 16, c = l % 16.
 //   K (MFMA B operand): load i of tile nt -> token 16*nt + c, chunk 4*i + lg.
-//   V (row order)     : load i            -> token 4*i + lg,   chunk c.
-// PV accumulators are partial over the four token groups lg and are summed
+//   V (row order)     : load i            -> token 16*lg + i,  chunk c.
+// The score of token 16*lg + i sits in lane i of row lg (MFMA tile lg), so
+// PV fetches it with a row broadcast instead of an LDS exchange.  PV
+// accumulators are partial over the four token groups lg and are summed
 // through LDS for the probe and for the output.  For the probe, lane
 // (lg, c) owns head lg (when lg < G) and the probe dims inside chunk c.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "art.h"
 #include "art_internal.h"
@@ -126,6 +130,31 @@ __device__ __forceinline__ double wave_sum_d(double x) {
   return lane_d(x, 63);
 }
 
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+// acc += bcast_N(p) * v where bcast_N = row_newbcast:N (gfx90a and later):
+// every lane of a 16-lane row reads p from lane N of that row.  One fused
+// instruction, so the broadcast value never occupies a register.  The
+// caller guarantees two wait states between the last VALU write of p and
+// the first use (see pv_sources_ready).
+template <int N>
+__device__ __forceinline__ float fma_bcast(float acc, float p, float v) {
+  asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+               : "+v"(acc)
+               : "v"(p), "v"(v), "n"(N));
+  return acc;
+}
+// Two wait states after the VALU writes of the broadcast sources.
+__device__ __forceinline__ void pv_sources_ready(float a, float b, float c, float d) {
+  asm volatile("s_nop 1" ::"v"(a), "v"(b), "v"(c), "v"(d));
+}
+
 // Reinterpret a 32-bit word as fp32.  Takes the word by value: bit-casting a
 // vector-element expression directly reads element 0 with this compiler.
 __device__ __forceinline__ float as_f32(uint32_t w) { return __builtin_bit_cast(float, w); }
@@ -139,6 +168,26 @@ template <typename T>
 __device__ __forceinline__ T sload(const T* p) {
   return *(const __attribute__((address_space(4))) T*)(p);
 }
+
+// Direct global -> LDS load of 16 bytes per lane: lane l writes
+// lds_base + 16*l (lds_base uniform).  The compiler does not order these
+// writes against later LDS reads, so users wait explicitly (wait_vm) and
+// fence the compiler (compiler_fence).
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+// Wait until at most N vector-memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS traffic
+// and meets the other waves, without waiting for in-flight global loads (a
+// full __syncthreads() would drain the K/V prefetch).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Order LDS traffic between the lanes of one wave.
 __device__ __forceinline__ void wave_lds_sync() {
@@ -191,8 +240,7 @@ __device__ __forceinline__ int block_at(const UnitView& u, int order, int t) {
 //               past the sequence are clamped to its last page, page ids
 //               outside the pool are replaced by page 0 and recorded.
 struct BlockAddr {
-  const char* kb[4];   // paged: row of token 16*g of the block
-  const char* vb[4];
+  uint32_t row[4];     // paged: pool row (page * Hkv + h) * page + slot of token 16*g
   int j;               // block index
   int nvalid;          // valid tokens in the block
 };
@@ -212,13 +260,11 @@ __device__ __forceinline__ BlockAddr block_addr(const UnitView& u, int j, int& b
       const bool oob = (unsigned)pg >= (unsigned)u.num_pages;
       bad |= oob;
       pg = oob ? 0 : pg;
-      const size_t row = ((size_t)pg * u.hkv + u.h) * ((size_t)pmask + 1) + (size_t)(tok & pmask);
-      ba.kb[g] = u.k + row * ROW;
-      ba.vb[g] = u.v + row * ROW;
+      ba.row[g] = (((uint32_t)pg * (uint32_t)u.hkv + (uint32_t)u.h) << u.log2_page) + (uint32_t)(tok & pmask);
     }
   } else {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) ba.kb[g] = ba.vb[g] = nullptr;
+    for (int g = 0; g < 4; ++g) ba.row[g] = 0;
   }
   return ba;
 }
@@ -242,7 +288,10 @@ struct CarryLds {            // prefix state on the probe dims
 };
 template <int G>
 struct alignas(16) WaveLds {
-  float p[kBlk][4];               // softmax weights of the block, by token
+  // K of the wave's current block, [token][16 chunks of 16 B]; chunk ch of
+  // token tk sits at position ch ^ (tk & 15) so that the MFMA operand reads
+  // (16 tokens, one chunk each) hit 16 different bank groups.
+  uint8_t k[kBlk][kRowChunks * 16];
   float probe[4][16][G][2];       // per-token-group sums on probe dims
 };
 template <int G, int D, int EPC>
@@ -269,7 +318,7 @@ struct alignas(16) GroupLds {
 // the decode kernel
 // ---------------------------------------------------------------------------
 template <int DT, int G, bool PAGED>
-__global__ __launch_bounds__(kWave * kMaxWaves) void art_decode_kernel(KernelArgs a) {
+__global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(KernelArgs a) {
   using GE = Geo<DT>;
   constexpr int D = GE::D, ES = GE::ES, EPC = GE::EPC, PPC = GE::PPC;
   constexpr int ROW = D * ES;
@@ -404,24 +453,33 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void art_decode_kernel(KernelArg
   }
 
   // ---- loads ---------------------------------------------------------------
-  u32x4 kr[kTiles][kKLoads];
   u32x4 vr[kVLoads];
+  // K: 16 DMA loads of 4 tokens x 256 B; lane l of load n carries token
+  // 4n + lg, stored chunk position c, i.e. global chunk c ^ (token & 15).
   auto load_k = [&](const BlockAddr& ba) {
+    wait_lgkm0();  // operand reads of the previous block have landed
 #pragma unroll
-    for (int nt = 0; nt < kTiles; ++nt) {
+    for (int n = 0; n < kVLoads; ++n) {
+      const int tk = 4 * n + lg;
       const char* row;
-      if constexpr (PAGED) row = ba.kb[nt] + c * ROW;
-      else row = u.k + (size_t)min(ba.j * kBlk + nt * 16 + c, u.n_ctx - 1) * ROW;
-#pragma unroll
-      for (int i = 0; i < kKLoads; ++i) kr[nt][i] = *(const u32x4*)(row + (4 * i + lg) * 16);
+      if constexpr (PAGED) row = u.k + ((size_t)ba.row[n >> 2] + (((4 * n) & 15) + lg)) * ROW;
+      else row = u.k + (size_t)min(ba.j * kBlk + tk, u.n_ctx - 1) * ROW;
+      lds_dma16(row + ((c ^ (tk & 15)) * 16), &wl.k[4 * n][0]);
     }
+    compiler_fence();
   };
+  // V load i -> token 16*lg + i, chunk c (four 256-byte rows, one per tile).
   auto load_v = [&](const BlockAddr& ba) {
+    // row of this lane's tile, picked with a select tree (an indexed pick is
+    // lowered to a private-memory array)
+    const uint32_t r01 = (lg & 1) ? ba.row[1] : ba.row[0];
+    const uint32_t r23 = (lg & 1) ? ba.row[3] : ba.row[2];
+    const uint32_t row_lg = (lg & 2) ? r23 : r01;
 #pragma unroll
     for (int i = 0; i < kVLoads; ++i) {
       const char* row;
-      if constexpr (PAGED) row = ba.vb[i >> 2] + (((4 * i) & 15) + lg) * ROW;
-      else row = u.v + (size_t)min(ba.j * kBlk + 4 * i + lg, u.n_ctx - 1) * ROW;
+      if constexpr (PAGED) row = u.v + ((size_t)row_lg + i) * ROW;
+      else row = u.v + (size_t)min(ba.j * kBlk + 16 * lg + i, u.n_ctx - 1) * ROW;
       vr[i] = *(const u32x4*)(row + c * 16);
     }
   };
@@ -452,21 +510,26 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void art_decode_kernel(KernelArg
     if (active) {
       const int nvalid = cur.nvalid;
       // ---- scores: S[nt][r] = q_{r%G} . k_{16 nt + c} ----------------------
+      wait_vm<kVLoads>();  // this block's K (its 16 V loads were issued after it)
       f32x4 S[kTiles];
 #pragma unroll
       for (int nt = 0; nt < kTiles; ++nt) {
+        const int tk = 16 * nt + c;
+        u32x4 kb[kKLoads];
+#pragma unroll
+        for (int i = 0; i < kKLoads; ++i) kb[i] = *(const u32x4*)&wl.k[tk][((4 * i + lg) ^ c) * 16];
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
         if constexpr (DT == ART_DT_BF16) {
 #pragma unroll
           for (int i = 0; i < kKLoads; ++i)
             s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[i]),
-                                                        __builtin_bit_cast(bf16x8, kr[nt][i]), s, 0, 0, 0);
+                                                        __builtin_bit_cast(bf16x8, kb[i]), s, 0, 0, 0);
         } else {
 #pragma unroll
           for (int i = 0; i < kKLoads; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              s = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(qa[i][e]), as_f32(kr[nt][i][e]), s, 0, 0, 0);
+              s = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(qa[i][e]), as_f32(kb[i][e]), s, 0, 0, 0);
         }
         S[nt] = s;
       }
@@ -496,28 +559,25 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void art_decode_kernel(KernelArg
         }
         lblk[g] = uni_f(row_sum(ls));
       }
-      {  // this lane's token (16*lg + c) lives in tile lg
-        f32x4 mine = S[0];
+      // weights of tile lg (tokens 16*lg + 0..15, one per lane of the row),
+      // picked with a select tree
+      f32x4 mine;
 #pragma unroll
-        for (int nt = 1; nt < kTiles; ++nt) mine = (lg == nt) ? S[nt] : mine;
-        float4 w4;
-        w4.x = mine[0];
-        w4.y = G > 1 ? mine[1] : 0.f;
-        w4.z = G > 2 ? mine[2] : 0.f;
-        w4.w = G > 3 ? mine[3] : 0.f;
-        *(float4*)&wl.p[16 * lg + c][0] = w4;
+      for (int g = 0; g < 4; ++g) {
+        const float s01 = (lg & 1) ? S[1][g] : S[0][g];
+        const float s23 = (lg & 1) ? S[3][g] : S[2][g];
+        mine[g] = (lg & 2) ? s23 : s01;
       }
-      wave_lds_sync();
       // ---- P V ---------------------------------------------------------------
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int e = 0; e < EPC; ++e) bacc[g][e] = 0.f;
-#pragma unroll
-      for (int i = 0; i < kVLoads; ++i) {
-        const int tok = 4 * i + lg;
-        const float4 pw = *(const float4*)&wl.p[tok][0];
-        const float pg[4] = {pw.x, pw.y, pw.z, pw.w};
+      const float mg[4] = {mine[0], G > 1 ? mine[1] : 0.f, G > 2 ? mine[2] : 0.f, G > 3 ? mine[3] : 0.f};
+      pv_sources_ready(mg[0], mg[1], mg[2], mg[3]);
+      static_for<0, kVLoads>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const int tok = 16 * lg + i;
         u32x4 w = vr[i];
         if (tok >= nvalid) w = u32x4{0u, 0u, 0u, 0u};
         float ve[EPC];
@@ -534,9 +594,12 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void art_decode_kernel(KernelArg
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
-          for (int e = 0; e < EPC; ++e) bacc[g][e] = fmaf(pg[g], ve[e], bacc[g][e]);
+          for (int e = 0; e < EPC; ++e) bacc[g][e] = fma_bcast<i>(bacc[g][e], mg[g], ve[e]);
+      });
+      if (has_next) {
+        compiler_fence();
+        load_v(nxt);
       }
-      if (has_next) load_v(nxt);
     }
 
     int stop_round = -1;  // this round's stop, as a traversal count
@@ -564,7 +627,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void art_decode_kernel(KernelArg
           R.sum[wid].l[lane] = lv;
         }
       }
-      __syncthreads();
+      lds_barrier();
       // ---- prefix on the probe dims through this wave's position -------------
       // lane (lg, c): head lg (if lg < G), probe dims c*PPC .. c*PPC+PPC-1
       const CarryLds<G, D>& cin = R.carry[parity];
@@ -630,7 +693,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void art_decode_kernel(KernelArg
 #pragma unroll
         for (int k = 0; k < PPC; ++k) co.pacc[lg][c * PPC + k] = pP[k];
       }
-      __syncthreads();
+      lds_barrier();
       // ---- patience counter over the round, in order --------------------------
       int counter = R.carry[parity].counter;
       for (int w2 = 0; w2 < n_act; ++w2) {
