@@ -58,18 +58,20 @@ art_status validate(const art_shape* sp, const art_params* pp) {
   return ART_OK;
 }
 
-// Traversal blocks per work item.  ART mode currently walks each unit in
-// one work item (exact sequential stopping); full mode splits long units so
-// that the grid holds enough waves to cover all compute units.
+// Traversal blocks per work item.  ART mode walks each unit in one work item
+// (exact sequential stopping); full mode splits units into chunks so that
+// about kTargetItems workgroups balance uneven context lengths across the
+// compute units (chunks of at least 32 blocks, multiples of the wave count).
+constexpr int64_t kTargetItems = 4096;
+constexpr int kWavesPerItem = 4;
 int chunk_blocks(const art_shape& s, const art_params& p) {
   const int64_t tmax = std::max<int64_t>(1, max_traversal(s));
   if (p.mode == ART_MODE_ART) return (int)tmax;
   if (p.split_blocks > 0) return (int)std::min<int64_t>(p.split_blocks, tmax);
   const int64_t units = std::max<int64_t>(1, (int64_t)s.batch * s.num_kv_heads);
-  const int64_t target_items = 1024;  // workgroups of 4 waves
-  if (units >= target_items) return (int)tmax;
-  int64_t c = (tmax * units + target_items - 1) / target_items;
-  c = std::max<int64_t>(c, 16);
+  int64_t c = (tmax * units + kTargetItems - 1) / kTargetItems;
+  c = std::max<int64_t>(c, 32);
+  c = (c + kWavesPerItem - 1) / kWavesPerItem * kWavesPerItem;
   return (int)std::min<int64_t>(c, tmax);
 }
 
@@ -137,11 +139,19 @@ art_status art_decode(const art_shape* shape, const art_params* params, const vo
   a.eps_scale = p.eps_scale;
   a.eps_dir = p.eps_dir;
   a.patience = p.patience;
+  {
+    const double tau = p.eps_scale, phi = p.eps_dir;
+    a.crit_hi = (1.0 + tau) * (1.0 + tau);
+    a.crit_lo = (1.0 - tau) * (1.0 - tau);
+    a.crit_c2 = (1.0 - phi) * (1.0 - phi);
+    a.crit_tau_lt1 = tau < 1.0;
+    a.crit_phi_le1 = phi <= 1.0;
+  }
   a.order = p.order;
   a.mode = p.mode;
   a.chunk_blocks = chunk;
   a.max_chunks = max_chunks;
-  a.waves = 4;
+  a.waves = kWavesPerItem;
   a.q = q;
   a.k = k;
   a.v = v;

@@ -41,6 +41,9 @@ struct KernelArgs {
   // params
   float eps_scale, eps_dir;
   int32_t patience, order, mode;
+  // squared forms of the thresholds (see the stability tests in the kernel)
+  double crit_hi, crit_lo, crit_c2;  // (1+eps_scale)^2, (1-eps_scale)^2, (1-eps_dir)^2
+  int32_t crit_tau_lt1, crit_phi_le1; // eps_scale < 1, eps_dir <= 1
   int32_t chunk_blocks;  // traversal blocks per work item
   int32_t max_chunks;    // work items per unit
   int32_t waves;         // waves per workgroup (one work item per workgroup)

@@ -117,6 +117,13 @@ __device__ __forceinline__ double lane_d(double x, int l) {
   const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
+// All-reduce of an fp64 value over the 16 lanes of each row.
+__device__ __forceinline__ double row_sum_d(double x) {
+  x += dpp<kQx1>(x);
+  x += dpp<kQx2>(x);
+  x += dpp<kHalfMirror>(x);
+  return x + dpp<kMirror>(x);
+}
 // Sum over all 64 lanes in fp64, returned uniform.  Rows are reduced with
 // mirrors, then row totals are chained with row broadcasts; lane 63 ends
 // with the total.
@@ -155,6 +162,59 @@ __device__ __forceinline__ void pv_sources_ready(float a, float b, float c, floa
   asm volatile("s_nop 1" ::"v"(a), "v"(b), "v"(c), "v"(d));
 }
 
+// Sums of 2 x 4 fp64 values at once (one DPP chain shared by all): first
+// over the 16 lanes of each row (every lane gets its row's sum), then over
+// the four rows (result uniform).
+#define ART_STEP8(CTRL, RM)                                \
+  _Pragma("unroll") for (int i = 0; i < 4; ++i) {          \
+    a[i] += dpp<CTRL, RM>(a[i]);                           \
+    b[i] += dpp<CTRL, RM>(b[i]);                           \
+  }
+__device__ __forceinline__ void row_sum_d8(double (&a)[4], double (&b)[4]) {
+  ART_STEP8(kQx1, 0xF)
+  ART_STEP8(kQx2, 0xF)
+  ART_STEP8(kHalfMirror, 0xF)
+  ART_STEP8(kMirror, 0xF)
+}
+__device__ __forceinline__ void cross_row_sum_d8(double (&a)[4], double (&b)[4]) {
+  ART_STEP8(kBcast15, 0xA)
+  ART_STEP8(kBcast31, 0xC)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = lane_d(a[i], 63);
+    b[i] = lane_d(b[i], 63);
+  }
+}
+#undef ART_STEP8
+
+// fp64 reciprocal: fp32 estimate plus one Newton step (relative error ~1e-14).
+__device__ __forceinline__ double recip_d(double x) {
+  const double r0 = (double)__builtin_amdgcn_rcpf((float)x);
+  return fma(r0, fma(-x, r0, 1.0), r0);
+}
+
+// The two stability tests on squared quantities, a = |x^(t-1)|, b = |x^(t)|,
+// p = x^(t).x^(t-1) (a, b > 0):
+//   |b - a| / a < tau   <=>  (1-tau)^2 a^2 < b^2 < (1+tau)^2 a^2   (tau < 1;
+//                            only the upper bound for tau >= 1)
+//   1 - p/(ab)  < phi   <=>  p > (1-phi) a b, i.e. for phi <= 1: p > 0 and
+//                            p^2 > (1-phi)^2 a^2 b^2; for phi > 1: p >= 0 or
+//                            p^2 < (phi-1)^2 a^2 b^2.
+// Squaring keeps the comparisons strict and avoids fp64 square roots and
+// divisions on the round's critical path.
+struct Criterion {
+  double hi, lo, c2;   // (1+tau)^2, (1-tau)^2, (1-phi)^2, computed on the host
+  bool tau_lt1, phi_le1;
+  __device__ bool scale_ok(double a2, double b2) const {
+    return b2 < hi * a2 && (!tau_lt1 || b2 > lo * a2);
+  }
+  __device__ bool dir_ok(double a2, double b2, double p) const {
+    const double r = c2 * a2 * b2;
+    if (phi_le1) return p > 0.0 && p * p > r;
+    return p >= 0.0 || p * p < r;
+  }
+};
+
 // Reinterpret a 32-bit word as fp32.  Takes the word by value: bit-casting a
 // vector-element expression directly reads element 0 with this compiler.
 __device__ __forceinline__ float as_f32(uint32_t w) { return __builtin_bit_cast(float, w); }
@@ -170,11 +230,18 @@ __device__ __forceinline__ T sload(const T* p) {
 }
 
 // Direct global -> LDS load of 16 bytes per lane: lane l writes
-// lds_base + 16*l (lds_base uniform).  The compiler does not order these
-// writes against later LDS reads, so users wait explicitly (wait_vm) and
-// fence the compiler (compiler_fence).
-__device__ __forceinline__ void lds_dma16(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+// lds + 16*l (lds uniform, passed in M0).  Issued as inline assembly so the
+// compiler, which cannot track LDS-DMA completion per LDS object, does not
+// put a full vmcnt(0) in front of every later LDS access; all waits for it
+// are explicit (wait_vm).  M0 has no other use in these kernels (LDS
+// instructions on this target do not read it, and no indirect register
+// indexing is generated), so setting it here cannot disturb compiler state.
+__device__ __forceinline__ void lds_dma16(const void* g, const void* lds) {
+  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(a) : "memory", "m0");
+#pragma clang diagnostic pop
 }
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 // Wait until at most N vector-memory operations are outstanding.
@@ -183,6 +250,47 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// 16-byte LDS read issued as inline assembly.  The compiler, which cannot
+// count LDS-DMA completions precisely, would otherwise put a full vmcnt(0)
+// in front of any read of a DMA-written buffer and so also wait for the
+// unrelated V loads in flight.  The caller orders the DMA with wait_vm and
+// the result with wait_lgkm_tied.
+__device__ __forceinline__ u32x4 lds_read16(const void* p) {
+  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(a));
+  return r;
+}
+// 16-byte global load issued as inline assembly, so the compiler does not
+// place its own (over-conservative) vmcnt waits for it; users wait with
+// wait_v_tied.
+template <int OFF = 0>
+__device__ __forceinline__ u32x4 gload16(const void* p) {
+  u32x4 r;
+  asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(r) : "v"(p), "n"(OFF) : "memory");
+  return r;
+}
+// Wait until at most N vector-memory operations are outstanding, tying the
+// 16 V registers to the wait so no use of them is scheduled ahead of it.
+template <int N>
+__device__ __forceinline__ void wait_v_tied(u32x4 (&v)[16]) {
+  asm volatile("s_waitcnt vmcnt(%16)"
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]),
+                 "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]),
+                 "+v"(v[15])
+               : "n"(N)
+               : "memory");
+}
+// Wait until at most N LDS/scalar operations are outstanding, tying four
+// operand registers to the wait so no use of them is scheduled ahead of it.
+// LDS operations complete in order, so after issuing reads A then B,
+// lgkmcnt(|B|) guarantees A (other outstanding scalar loads only make the
+// wait stricter).
+template <int N>
+__device__ __forceinline__ void wait_lgkm_tied(u32x4 (&k)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(k[0]), "+v"(k[1]), "+v"(k[2]), "+v"(k[3]) : "n"(N));
+}
 
 // Workgroup barrier that orders LDS only: waits for this wave's LDS traffic
 // and meets the other waves, without waiting for in-flight global loads (a
@@ -240,7 +348,8 @@ __device__ __forceinline__ int block_at(const UnitView& u, int order, int t) {
 //               past the sequence are clamped to its last page, page ids
 //               outside the pool are replaced by page 0 and recorded.
 struct BlockAddr {
-  uint32_t row[4];     // paged: pool row (page * Hkv + h) * page + slot of token 16*g
+  uint32_t row[4];     // row of token 16*g of the block: paged, in the pool
+                       // ((page * Hkv + h) * page + slot); contiguous, in the unit
   int j;               // block index
   int nvalid;          // valid tokens in the block
 };
@@ -264,7 +373,7 @@ __device__ __forceinline__ BlockAddr block_addr(const UnitView& u, int j, int& b
     }
   } else {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) ba.row[g] = 0;
+    for (int g = 0; g < 4; ++g) ba.row[g] = (uint32_t)(j * kBlk + 16 * g);
   }
   return ba;
 }
@@ -278,40 +387,33 @@ struct Summary {             // one block, published for the round
   float l[4];                // softmax mass per head relative to m
   float ps[G][D / 4];        // sums on the probe dims relative to m
 };
-template <int G, int D>
-struct CarryLds {            // prefix state on the probe dims
-  float m[4];
-  int counter;
-  int pad[3];
-  double l[4];
-  double pacc[G][D / 4];
-};
 template <int G>
 struct alignas(16) WaveLds {
-  // K of the wave's current block, [token][16 chunks of 16 B]; chunk ch of
-  // token tk sits at position ch ^ (tk & 15) so that the MFMA operand reads
-  // (16 tokens, one chunk each) hit 16 different bank groups.
-  uint8_t k[kBlk][kRowChunks * 16];
   float probe[4][16][G][2];       // per-token-group sums on probe dims
 };
-template <int G, int D, int EPC>
-struct alignas(16) GroupLds {
-  union {
-    struct {
-      WaveLds<G> wave[kMaxWaves];
-      Summary<G, D> sum[kMaxWaves];
-      CarryLds<G, D> carry[2];
-      int stable[kMaxWaves];
-      int bad;
-      int zero_pos;
-    } r;
-    struct {                       // epilogue: per-wave state
-      float m[kMaxWaves][4];
-      float l[kMaxWaves][4];
-      int issued[kMaxWaves];
-      float acc[kMaxWaves][4][16][G][EPC];
-    } e;
-  };
+// K of each wave's current block: 16 slabs, one per DMA load n, holding the
+// tokens 16*g + n (g = 0..3) as 4 rows of 256 B.  Slabs are 1040 B apart (256
+// B rows plus 16 B), so the 16 tokens one MFMA operand read touches (same g,
+// n = 0..15) fall into 16 different 16-byte bank groups.  A separate LDS
+// object from everything else, so the compiler can tell the DMA target apart
+// from the round's bookkeeping.
+constexpr int kKSlab = 4 * kRowChunks * 16 + 16;
+typedef uint8_t KBuf[kMaxWaves][kVLoads * kKSlab];
+template <int G, int D>
+struct alignas(16) RoundLds {
+  uint8_t q[G][kRowChunks * 16];    // the unit's G query rows (256 B each)
+  WaveLds<G> wave[kMaxWaves];
+  Summary<G, D> sum[2][kMaxWaves];  // by round parity
+  double crit[2][kMaxWaves][4][2];   // by round parity: per position, per head (a, c)
+  int bad;
+  int zero_pos;
+};
+template <int G, int EPC>
+struct alignas(16) EpilogueLds {   // per-wave final state (reuses the K buffers)
+  float m[kMaxWaves][4];
+  float l[kMaxWaves][4];
+  int issued[kMaxWaves];
+  float acc[kMaxWaves][4][16][G][EPC];
 };
 
 // ---------------------------------------------------------------------------
@@ -323,8 +425,9 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
   constexpr int D = GE::D, ES = GE::ES, EPC = GE::EPC, PPC = GE::PPC;
   constexpr int ROW = D * ES;
   static_assert(ROW == kRowChunks * 16, "rows must be 16 chunks of 16 bytes");
-  __shared__ GroupLds<G, D, EPC> S_;
-  auto& R = S_.r;
+  __shared__ RoundLds<G, D> R;
+  __shared__ alignas(16) KBuf kbuf;
+  static_assert(sizeof(EpilogueLds<G, EPC>) <= sizeof(KBuf), "epilogue state must fit the K buffers");
 
   const int W = blockDim.x >> 6;
   const int wid = uni(threadIdx.x >> 6);
@@ -425,11 +528,14 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
   }
   if (t_begin >= t_end) return;  // chunk past this unit's traversal
 
-  // ---- query operand (rows replicated: MFMA row r -> head r % G) ---------
-  const char* qrow = (const char*)a.q + (((size_t)b * a.hq + h * G + (c % G)) * D) * ES;
-  u32x4 qa[kKLoads];
-#pragma unroll
-  for (int i = 0; i < kKLoads; ++i) qa[i] = *(const u32x4*)(qrow + (4 * i + lg) * 16);
+  // ---- query rows in LDS; per block each lane reads its MFMA A operand
+  // (rows replicated: MFMA row r -> head r % G) instead of pinning 16 VGPRs
+  {
+    const char* qsrc = (const char*)a.q + (((size_t)b * a.hq + h * G) * D) * ES;
+    for (int i = threadIdx.x; i < G * kRowChunks; i += blockDim.x)
+      *(u32x4*)&R.q[i / kRowChunks][(i % kRowChunks) * 16] = *(const u32x4*)(qsrc + i * 16);
+  }
+  __syncthreads();
   const float c2 = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(d)
 
   // ---- per-wave running softmax state -------------------------------------
@@ -442,45 +548,61 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
     for (int e = 0; e < EPC; ++e) acc[g][e] = 0.f;
   }
   const bool art_mode = a.mode == ART_MODE_ART;
-  const double tau = (double)a.eps_scale, phi = (double)a.eps_dir;
-  if (art_mode) {
-    if (threadIdx.x < 4) {
-      R.carry[0].m[threadIdx.x] = -INFINITY;
-      R.carry[0].l[threadIdx.x] = 0.0;
-    }
-    if (threadIdx.x == 0) R.carry[0].counter = 0;
-    for (int i = threadIdx.x; i < G * (D / 4); i += blockDim.x) (&R.carry[0].pacc[0][0])[i] = 0.0;
-  }
+  // prefix state on the probe dims (same in every wave): running max, mass and
+  // numerators for head hg = lg (lanes with lg >= G carry head 0 unused),
+  // the previous probe, its squared norm, and the patience counter
+  const int hg = lg < G ? lg : 0;
+  float mP = -INFINITY;
+  double lP = 0.0, pP[PPC];
+#pragma unroll
+  for (int k = 0; k < PPC; ++k) pP[k] = 0.0;
+  double stt_last = 0.0;
+  int counter = 0;
+  const Criterion crit{a.crit_hi, a.crit_lo, a.crit_c2, a.crit_tau_lt1 != 0, a.crit_phi_le1 != 0};
 
   // ---- loads ---------------------------------------------------------------
   u32x4 vr[kVLoads];
-  // K: 16 DMA loads of 4 tokens x 256 B; lane l of load n carries token
-  // 4n + lg, stored chunk position c, i.e. global chunk c ^ (token & 15).
+  // Row of token 16*lg of a block (this lane's 16-token group), picked with a
+  // select tree (an indexed pick is lowered to a private-memory array).
+  auto lane_row = [&](const BlockAddr& ba) -> uint32_t {
+    const uint32_t r01 = (lg & 1) ? ba.row[1] : ba.row[0];
+    const uint32_t r23 = (lg & 1) ? ba.row[3] : ba.row[2];
+    return (lg & 2) ? r23 : r01;
+  };
+  // K: DMA load n carries token 16*lg + n, chunk c, into slab n.  Rows past a
+  // contiguous context are clamped to its last token (read in bounds, masked).
   auto load_k = [&](const BlockAddr& ba) {
     wait_lgkm0();  // operand reads of the previous block have landed
-#pragma unroll
-    for (int n = 0; n < kVLoads; ++n) {
-      const int tk = 4 * n + lg;
-      const char* row;
-      if constexpr (PAGED) row = u.k + ((size_t)ba.row[n >> 2] + (((4 * n) & 15) + lg)) * ROW;
-      else row = u.k + (size_t)min(ba.j * kBlk + tk, u.n_ctx - 1) * ROW;
-      lds_dma16(row + ((c ^ (tk & 15)) * 16), &wl.k[4 * n][0]);
+    uint8_t* dst = &kbuf[wid][0];
+    if (PAGED || ba.nvalid == kBlk) {
+      const char* base = u.k + (size_t)lane_row(ba) * ROW + c * 16;
+      static_for<0, kVLoads>([&](auto nc) {
+        constexpr int n = decltype(nc)::value;
+        lds_dma16(base + n * ROW, dst + n * kKSlab);
+      });
+    } else {
+      static_for<0, kVLoads>([&](auto nc) {
+        constexpr int n = decltype(nc)::value;
+        const int tok = min(ba.j * kBlk + 16 * lg + n, u.n_ctx - 1);
+        lds_dma16(u.k + (size_t)tok * ROW + c * 16, dst + n * kKSlab);
+      });
     }
     compiler_fence();
   };
   // V load i -> token 16*lg + i, chunk c (four 256-byte rows, one per tile).
   auto load_v = [&](const BlockAddr& ba) {
-    // row of this lane's tile, picked with a select tree (an indexed pick is
-    // lowered to a private-memory array)
-    const uint32_t r01 = (lg & 1) ? ba.row[1] : ba.row[0];
-    const uint32_t r23 = (lg & 1) ? ba.row[3] : ba.row[2];
-    const uint32_t row_lg = (lg & 2) ? r23 : r01;
-#pragma unroll
-    for (int i = 0; i < kVLoads; ++i) {
-      const char* row;
-      if constexpr (PAGED) row = u.v + ((size_t)row_lg + i) * ROW;
-      else row = u.v + (size_t)min(ba.j * kBlk + 16 * lg + i, u.n_ctx - 1) * ROW;
-      vr[i] = *(const u32x4*)(row + c * 16);
+    if (PAGED || ba.nvalid == kBlk) {
+      const char* base = u.v + (size_t)lane_row(ba) * ROW + c * 16;
+      static_for<0, kVLoads>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        vr[i] = gload16<i * ROW>(base);
+      });
+    } else {
+      static_for<0, kVLoads>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const int tok = min(ba.j * kBlk + 16 * lg + i, u.n_ctx - 1);
+        vr[i] = gload16(u.v + (size_t)tok * ROW + c * 16);
+      });
     }
   };
 
@@ -511,28 +633,46 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
       const int nvalid = cur.nvalid;
       // ---- scores: S[nt][r] = q_{r%G} . k_{16 nt + c} ----------------------
       wait_vm<kVLoads>();  // this block's K (its 16 V loads were issued after it)
+      // operand reads run two tiles ahead of the MFMAs
+      u32x4 qa[kKLoads];
+      u32x4 kb[kTiles][kKLoads];
+      auto read_tile = [&](int nt) {
+#pragma unroll
+        for (int i = 0; i < kKLoads; ++i)
+          kb[nt][i] = lds_read16(&kbuf[wid][c * kKSlab + nt * 256 + (4 * i + lg) * 16]);
+      };
       f32x4 S[kTiles];
-#pragma unroll
-      for (int nt = 0; nt < kTiles; ++nt) {
-        const int tk = 16 * nt + c;
-        u32x4 kb[kKLoads];
-#pragma unroll
-        for (int i = 0; i < kKLoads; ++i) kb[i] = *(const u32x4*)&wl.k[tk][((4 * i + lg) ^ c) * 16];
+      auto mfma_tile = [&](int nt) {
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
         if constexpr (DT == ART_DT_BF16) {
 #pragma unroll
           for (int i = 0; i < kKLoads; ++i)
             s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[i]),
-                                                        __builtin_bit_cast(bf16x8, kb[i]), s, 0, 0, 0);
+                                                        __builtin_bit_cast(bf16x8, kb[nt][i]), s, 0, 0, 0);
         } else {
 #pragma unroll
           for (int i = 0; i < kKLoads; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              s = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(qa[i][e]), as_f32(kb[i][e]), s, 0, 0, 0);
+              s = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(qa[i][e]), as_f32(kb[nt][i][e]), s, 0, 0, 0);
         }
         S[nt] = s;
-      }
+      };
+#pragma unroll
+      for (int i = 0; i < kKLoads; ++i) qa[i] = lds_read16(&R.q[c % G][(4 * i + lg) * 16]);
+      read_tile(0);
+      read_tile(1);
+      wait_lgkm_tied<8>(qa);
+      wait_lgkm_tied<4>(kb[0]);
+      mfma_tile(0);
+      read_tile(2);
+      wait_lgkm_tied<4>(kb[1]);
+      mfma_tile(1);
+      read_tile(3);
+      wait_lgkm_tied<4>(kb[2]);
+      mfma_tile(2);
+      wait_lgkm_tied<0>(kb[3]);
+      mfma_tile(3);
       if (has_next) {
         load_k(nxt);
         ++issued;
@@ -573,6 +713,9 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
       for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int e = 0; e < EPC; ++e) bacc[g][e] = 0.f;
+      // V of this block: the 16 K loads of the next block (if any) were issued after it
+      if (!has_next) wait_vm<0>();  // no K loads follow this block's V
+      wait_v_tied<kVLoads>(vr);
       const float mg[4] = {mine[0], G > 1 ? mine[1] : 0.f, G > 2 ? mine[2] : 0.f, G > 3 ? mine[3] : 0.f};
       pv_sources_ready(mg[0], mg[1], mg[2], mg[3]);
       static_for<0, kVLoads>([&](auto ic) {
@@ -605,6 +748,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
     int stop_round = -1;  // this round's stop, as a traversal count
     if (art_mode) {
       // ---- publish the block summary ------------------------------------------
+      Summary<G, D>& sw = R.sum[parity][wid];
       if (active) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -615,99 +759,90 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
         if (lg < G) {
 #pragma unroll
           for (int k = 0; k < PPC; ++k)
-            R.sum[wid].ps[lg][c * PPC + k] = (wl.probe[0][c][lg][k] + wl.probe[1][c][lg][k]) +
-                                             (wl.probe[2][c][lg][k] + wl.probe[3][c][lg][k]);
+            sw.ps[lg][c * PPC + k] = (wl.probe[0][c][lg][k] + wl.probe[1][c][lg][k]) +
+                                     (wl.probe[2][c][lg][k] + wl.probe[3][c][lg][k]);
         }
         if (lane < G) {
           float mv = m_new[0], lv = lblk[0];
 #pragma unroll
           for (int g = 1; g < G; ++g)
             if (lane == g) mv = m_new[g], lv = lblk[g];
-          R.sum[wid].m[lane] = mv;
-          R.sum[wid].l[lane] = lv;
+          sw.m[lane] = mv;
+          sw.l[lane] = lv;
         }
       }
       lds_barrier();
-      // ---- prefix on the probe dims through this wave's position -------------
-      // lane (lg, c): head lg (if lg < G), probe dims c*PPC .. c*PPC+PPC-1
-      const CarryLds<G, D>& cin = R.carry[parity];
-      const int hg = lg < G ? lg : 0;
-      float mP = cin.m[hg];
-      double lP = cin.l[hg];
-      double pP[PPC], xprev[PPC], xcur[PPC];
+      // ---- the round's positions, in order ------------------------------------
+      // Every wave merges all block summaries of the round onto the prefix
+      // state on the probe dims (lane (lg, c): head lg if lg < G, probe dims
+      // of chunk c), which keeps that state identical in all waves.  With
+      // P^(t) the prefix numerators and l^(t) the prefix mass of a head,
+      // x^(t) = P^(t) / l^(t).  At its own position a wave also forms, per
+      // head, A = P^(t).P^(t) and C = P^(t).P^(t-1) (row sums), scales them
+      // to a = A / l^(t)^2 and c = C / (l^(t) l^(t-1)) and publishes them; the
+      // ratio P/l is scale free, so P^(t-1), l^(t-1) keep their own running-
+      // max scale.  After a second barrier every wave sums the heads in a
+      // fixed order, so all reach the same |x^(t)|^2, x^(t).x^(t-1) and the
+      // same decision.
+      double own_a = 0.0, own_c = 0.0, l_before = 0.0, l_after = 1.0;
 #pragma unroll
-      for (int k = 0; k < PPC; ++k) {
-        pP[k] = cin.pacc[hg][c * PPC + k];
-        xprev[k] = xcur[k] = 0.0;
-      }
-      const bool carry_out = wid == W - 1;  // the last wave forwards the round's prefix
-      const int upto = carry_out ? n_act - 1 : (active ? wid : -1);
-      for (int w2 = 0; w2 <= upto; ++w2) {
-        if (w2 == wid) {  // x^(t-1): the prefix before this position
-          const double inv = lP > 0.0 ? 1.0 / lP : 0.0;
-#pragma unroll
-          for (int k = 0; k < PPC; ++k) xprev[k] = pP[k] * inv;
-        }
-        const float mb = R.sum[w2].m[hg];
-        const float M = fmaxf(mP, mb);
-        const double sP = (double)__builtin_amdgcn_exp2f(mP - M);
-        const double sB = (double)__builtin_amdgcn_exp2f(mb - M);
-        lP = lP * sP + (double)R.sum[w2].l[hg] * sB;
-#pragma unroll
-        for (int k = 0; k < PPC; ++k) pP[k] = pP[k] * sP + (double)R.sum[w2].ps[hg][c * PPC + k] * sB;
-        mP = M;
-        if (w2 == wid) {  // x^(t)
-          const double inv = 1.0 / lP;
-#pragma unroll
-          for (int k = 0; k < PPC; ++k) xcur[k] = pP[k] * inv;
-        }
-      }
-      int stable = 0;
-      if (active && t + 1 >= 2) {  // a check exists from the second block on
-        double spp = 0.0, stt = 0.0, stp = 0.0;
-        if (lg < G) {
+      for (int w2 = 0; w2 < kMaxWaves; ++w2) {
+        if (w2 < n_act) {
+          const Summary<G, D>& s2 = R.sum[parity][w2];
+          const float mb = s2.m[hg];
+          const float M = fmaxf(mP, mb);
+          const double sP = (double)__builtin_amdgcn_exp2f(mP - M);
+          const double sB = (double)__builtin_amdgcn_exp2f(mb - M);
+          const bool mine = w2 == wid;
+          if (mine) l_before = lP;
+          lP = fma(lP, sP, (double)s2.l[hg] * sB);
+          if (mine) l_after = lP;
+          mP = M;
 #pragma unroll
           for (int k = 0; k < PPC; ++k) {
-            spp = fma(xprev[k], xprev[k], spp);
-            stt = fma(xcur[k], xcur[k], stt);
-            stp = fma(xcur[k], xprev[k], stp);
+            const double p = fma(pP[k], sP, (double)s2.ps[hg][c * PPC + k] * sB);
+            if (mine && lg < G) {
+              own_a = fma(p, p, own_a);
+              own_c = fma(p, pP[k], own_c);
+            }
+            pP[k] = p;
           }
         }
-        spp = wave_sum_d(spp);
-        stt = wave_sum_d(stt);
-        stp = wave_sum_d(stp);
-        const double pa = sqrt(spp), pb = sqrt(stt);
-        if (pa > 0.0 && pb > 0.0) {
-          const double ds = fabs(pb - pa) / pa;        // relative norm change
-          const double dd = 1.0 - stp / (pa * pb);     // 1 - cos
-          stable = (ds < tau) && (dd < phi);
-        }
       }
-      if (lane == 0) R.stable[wid] = stable;
-      if (carry_out && lg < G) {
-        CarryLds<G, D>& co = R.carry[parity ^ 1];
-        if (c == 0) {
-          co.m[lg] = mP;
-          co.l[lg] = lP;
+      if (active) {
+        own_a = row_sum_d(own_a);
+        own_c = row_sum_d(own_c);
+        const double it = recip_d(l_after);
+        const double ip = l_before > 0.0 ? recip_d(l_before) : 0.0;
+        if (c == 0 && lg < G) {
+          R.crit[parity][wid][lg][0] = own_a * (it * it);
+          R.crit[parity][wid][lg][1] = own_c * (it * ip);
         }
-#pragma unroll
-        for (int k = 0; k < PPC; ++k) co.pacc[lg][c * PPC + k] = pP[k];
       }
       lds_barrier();
-      // ---- patience counter over the round, in order --------------------------
-      int counter = R.carry[parity].counter;
-      for (int w2 = 0; w2 < n_act; ++w2) {
-        const int cnt = t0 + w2 + 1;
-        if (cnt < 2) continue;
-        counter = R.stable[w2] ? counter + 1 : 0;
-        if (counter >= a.patience) {
-          stop_round = cnt;
-          break;
+      // ---- stability checks and patience counter, in traversal order -----------
+      double stt_prev = stt_last;
+#pragma unroll
+      for (int w2 = 0; w2 < kMaxWaves; ++w2) {
+        if (w2 < n_act) {
+          double stt = 0.0, stp = 0.0;
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            stt += R.crit[parity][w2][g][0];
+            stp += R.crit[parity][w2][g][1];
+          }
+          const int cnt = t0 + w2 + 1;
+          if (cnt >= 2 && stop_round < 0) {  // a check exists from the second block on
+            const bool stable =
+                stt_prev > 0.0 && stt > 0.0 && crit.scale_ok(stt_prev, stt) && crit.dir_ok(stt_prev, stt, stp);
+            counter = stable ? counter + 1 : 0;
+            if (counter >= a.patience) stop_round = cnt;
+          }
+          stt_prev = stt;
         }
       }
-      counter = uni(counter);
+      stt_last = stt_prev;
       stop_round = uni(stop_round);
-      if (threadIdx.x == 0) R.carry[parity ^ 1].counter = counter;
       parity ^= 1;
     }
 
@@ -730,8 +865,9 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
   if (stop < 0) stop = t_end;
 
   // ---- epilogue: merge waves, reduce token groups, normalize ---------------
+  wait_vm<0>();  // speculative K loads may still be landing in the K buffers
   __syncthreads();
-  auto& E = S_.e;
+  auto& E = *reinterpret_cast<EpilogueLds<G, EPC>*>(&kbuf[0][0]);
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
