@@ -7,25 +7,29 @@
 // consecutive traversal positions; wave w takes position t0 + w of round t0.
 //
 // Per 64-token ART block a wave
-//   1. has K in MFMA B-operand registers and V in row order (16-byte loads,
-//      issued one round ahead);
-//   2. computes the G x 64 scores with v_mfma_f32_16x16x32_bf16
-//      (v_mfma_f32_16x16x4_f32 for fp32 inputs); the A operand holds the
-//      G query rows replicated over the 16 MFMA rows, so every lane receives
-//      the scores of "its" token for all G heads;
-//   3. runs the online softmax (running max in the log2 domain) against the
-//      wave's running maximum;
-//   4. accumulates P V on the VALU in fp32 (P stays fp32);
+//   1. has K in MFMA A-operand registers (16-byte loads straight from HBM)
+//      and V in a private 16 KB LDS slab (direct global->LDS loads), both
+//      issued one round ahead;
+//   2. computes the transposed scores S^T = K q^T, 64 tokens x G heads, with
+//      v_mfma_f32_16x16x32_bf16 (v_mfma_f32_16x16x4_f32 for fp32 inputs); the
+//      B operand holds the G query rows replicated over the 16 MFMA columns;
+//   3. runs the online softmax (running max in the log2 domain) per head;
+//      a lane holds the weights of four consecutive tokens of one head,
+//      which is exactly the A-operand layout of the P V product;
+//   4. computes P V with MFMA: B operands come from the V slab through the
+//      transposing LDS read ds_read_b64_tr_b16 (fp32: plain LDS reads), and
+//      bf16 P is split into a high and a low bf16 part (two MFMAs), which
+//      keeps P to about 16 significant bits;
 //   5. (ART mode) publishes a block summary: per head its reference max,
 //      its softmax mass and its sums on the probe dims.
-// (ART mode) After a barrier every wave merges the summaries of positions up
-// to its own onto the carried prefix state (fp64 on the probe dims), so wave
-// w holds the probe x^(t) at its position t and x^(t-1); it evaluates the two
-// stability metrics there.  After a second barrier every wave runs the
-// patience counter over the round's checks in order: the first position
-// where `patience` consecutive checks were stable is the stop, blocks after
-// it are discarded and no further loads are issued.  The decision is the
-// one a strictly sequential walk makes.
+// (ART mode) After a barrier every wave merges the round's summaries in
+// order onto the carried prefix state (fp64 on the probe dims); at its own
+// position a wave forms the probe dot products and publishes them.  After a
+// second barrier every wave runs the two stability tests and the patience
+// counter over the round's positions in order: the first position where
+// `patience` consecutive checks were stable is the stop, blocks after it are
+// discarded and no further loads are issued.  The decision is the one a
+// strictly sequential walk makes.
 //
 // Method sources: ART paper section 3.1 Eq. (1) (blockwise attention and the
 // partial outputs O^(t)), section 3.2 (probe of scattered head dims);
@@ -34,13 +38,15 @@
 //
 // Lane geometry (both supported element types have 256-byte rows cut into
 // 16 chunks of 16 bytes): lane l = 16*lg + c with lg = l / 16, c = l % 16.
-//   K (MFMA B operand): load i of tile nt -> token 16*nt + c, chunk 4*i + lg.
-//   V (row order)     : load i            -> token 16*lg + i,  chunk c.
-// The score of token 16*lg + i sits in lane i of row lg (MFMA tile lg), so
-// PV fetches it with a row broadcast instead of an LDS exchange.  PV
-// accumulators are partial over the four token groups lg and are summed
-// through LDS for the probe and for the output.  For the probe, lane
-// (lg, c) owns head lg (when lg < G) and the probe dims inside chunk c.
+//   K (A operand)  : load j of tile nt -> token 16*nt + c, chunk 4*j + lg.
+//   q (B operand)  : k-step j           -> head c % G,     chunk 4*j + lg.
+//   S^T, O (D)     : lane l holds column c and rows 4*lg + r (r = 0..3); for
+//                    S^T the rows are tokens 16*nt + 4*lg + r of head c % G,
+//                    for O the rows are heads (4*lg + r) % G of dim 16*dt + c.
+//   V (LDS slab)   : DMA n (0..15) carries tokens 4n..4n+3 as four 256-byte
+//                    rows; chunk x of token row y (y = token % 4) is stored
+//                    at position x ^ 2y ^ 8(n & 1), which spreads the 16
+//                    lanes of a transposed read over distinct LDS banks.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -53,6 +59,9 @@
 namespace art {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -61,61 +70,33 @@ constexpr int kMaxWaves = 4;      // waves per workgroup (launch bound)
 constexpr int kBlk = 64;          // tokens per ART block
 constexpr int kTiles = kBlk / 16; // 16-token MFMA tiles per block
 constexpr int kRowChunks = 16;    // 16-byte chunks per K/V row
-constexpr int kVLoads = kBlk * kRowChunks / kWave;  // 16 row-order loads per block
-constexpr int kKLoads = kRowChunks / 4;             // 4 loads per tile per lane
+constexpr int kLoads = kBlk * kRowChunks / kWave;   // 16 loads per lane per block (K), 16 DMAs (V)
+constexpr int kVSlab = kBlk * kRowChunks * 16;      // 16 KB: V of one block
 
 template <int DT>
 struct Geo;
 template <>
 struct Geo<ART_DT_BF16> {
-  static constexpr int D = 128, ES = 2, EPC = 8, PPC = 2;  // elements / probe dims per chunk
+  static constexpr int D = 128, ES = 2, PPC = 2;  // PPC: probe dims per 16-byte chunk
 };
 template <>
 struct Geo<ART_DT_F32> {
-  static constexpr int D = 64, ES = 4, EPC = 4, PPC = 1;
+  static constexpr int D = 64, ES = 4, PPC = 1;
 };
 
 // ---------------------------------------------------------------------------
 // small helpers
 // ---------------------------------------------------------------------------
 #define ART_DPP_I(x, ctrl, rmask) __builtin_amdgcn_update_dpp(0, (x), (ctrl), (rmask), 0xF, false)
-// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror, row_bcast:15, row_bcast:31
-constexpr int kQx1 = 0xB1, kQx2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140, kBcast15 = 0x142, kBcast31 = 0x143;
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror
+constexpr int kQx1 = 0xB1, kQx2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140;
 
-template <int CTRL, int RMASK = 0xF>
-__device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, ART_DPP_I(__builtin_bit_cast(int, x), CTRL, RMASK));
-}
 template <int CTRL, int RMASK = 0xF>
 __device__ __forceinline__ double dpp(double x) {
   const uint64_t u = __builtin_bit_cast(uint64_t, x);
   const int lo = ART_DPP_I((int)(uint32_t)u, CTRL, RMASK);
   const int hi = ART_DPP_I((int)(uint32_t)(u >> 32), CTRL, RMASK);
   return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
-}
-
-// All-reduce over the 16 lanes of each row (every lane gets its row's result).
-__device__ __forceinline__ float row_max(float x) {
-  x = fmaxf(x, dpp<kQx1>(x));
-  x = fmaxf(x, dpp<kQx2>(x));
-  x = fmaxf(x, dpp<kHalfMirror>(x));
-  return fmaxf(x, dpp<kMirror>(x));
-}
-__device__ __forceinline__ float row_sum(float x) {
-  x += dpp<kQx1>(x);
-  x += dpp<kQx2>(x);
-  x += dpp<kHalfMirror>(x);
-  return x + dpp<kMirror>(x);
-}
-__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
-__device__ __forceinline__ float uni_f(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
-}
-__device__ __forceinline__ double lane_d(double x, int l) {
-  const uint64_t u = __builtin_bit_cast(uint64_t, x);
-  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, l);
-  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
-  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 // All-reduce of an fp64 value over the 16 lanes of each row.
 __device__ __forceinline__ double row_sum_d(double x) {
@@ -124,18 +105,27 @@ __device__ __forceinline__ double row_sum_d(double x) {
   x += dpp<kHalfMirror>(x);
   return x + dpp<kMirror>(x);
 }
-// Sum over all 64 lanes in fp64, returned uniform.  Rows are reduced with
-// mirrors, then row totals are chained with row broadcasts; lane 63 ends
-// with the total.
-__device__ __forceinline__ double wave_sum_d(double x) {
-  x += dpp<kQx1>(x);
-  x += dpp<kQx2>(x);
-  x += dpp<kHalfMirror>(x);
-  x += dpp<kMirror>(x);
-  x += dpp<kBcast15, 0xA>(x);
-  x += dpp<kBcast31, 0xC>(x);
-  return lane_d(x, 63);
+
+__device__ __forceinline__ uint32_t f2u(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float u2f(uint32_t x) { return __builtin_bit_cast(float, x); }
+// All-reduce over the four 16-lane rows: every lane gets the result over the
+// lanes with its own column (lanes l, l ^ 16, l ^ 32, l ^ 48).  The row swap
+// exchanges odd rows of its first operand with even rows of its second, the
+// half swap the upper half of the first with the lower half of the second.
+__device__ __forceinline__ float col_max(float x) {
+  const auto s = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+  x = fmaxf(u2f(s[0]), u2f(s[1]));
+  const auto t = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+  return fmaxf(u2f(t[0]), u2f(t[1]));
 }
+__device__ __forceinline__ float col_sum(float x) {
+  const auto s = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+  x = u2f(s[0]) + u2f(s[1]);
+  const auto t = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+  return u2f(t[0]) + u2f(t[1]);
+}
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ float lane_f(float x, int l) { return u2f(__builtin_amdgcn_readlane(f2u(x), l)); }
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
 template <int B, int E, typename F>
@@ -145,47 +135,6 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for<B + 1, E>(f);
   }
 }
-// acc += bcast_N(p) * v where bcast_N = row_newbcast:N (gfx90a and later):
-// every lane of a 16-lane row reads p from lane N of that row.  One fused
-// instruction, so the broadcast value never occupies a register.  The
-// caller guarantees two wait states between the last VALU write of p and
-// the first use (see pv_sources_ready).
-template <int N>
-__device__ __forceinline__ float fma_bcast(float acc, float p, float v) {
-  asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
-               : "+v"(acc)
-               : "v"(p), "v"(v), "n"(N));
-  return acc;
-}
-// Two wait states after the VALU writes of the broadcast sources.
-__device__ __forceinline__ void pv_sources_ready(float a, float b, float c, float d) {
-  asm volatile("s_nop 1" ::"v"(a), "v"(b), "v"(c), "v"(d));
-}
-
-// Sums of 2 x 4 fp64 values at once (one DPP chain shared by all): first
-// over the 16 lanes of each row (every lane gets its row's sum), then over
-// the four rows (result uniform).
-#define ART_STEP8(CTRL, RM)                                \
-  _Pragma("unroll") for (int i = 0; i < 4; ++i) {          \
-    a[i] += dpp<CTRL, RM>(a[i]);                           \
-    b[i] += dpp<CTRL, RM>(b[i]);                           \
-  }
-__device__ __forceinline__ void row_sum_d8(double (&a)[4], double (&b)[4]) {
-  ART_STEP8(kQx1, 0xF)
-  ART_STEP8(kQx2, 0xF)
-  ART_STEP8(kHalfMirror, 0xF)
-  ART_STEP8(kMirror, 0xF)
-}
-__device__ __forceinline__ void cross_row_sum_d8(double (&a)[4], double (&b)[4]) {
-  ART_STEP8(kBcast15, 0xA)
-  ART_STEP8(kBcast31, 0xC)
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    a[i] = lane_d(a[i], 63);
-    b[i] = lane_d(b[i], 63);
-  }
-}
-#undef ART_STEP8
 
 // fp64 reciprocal: fp32 estimate plus one Newton step (relative error ~1e-14).
 __device__ __forceinline__ double recip_d(double x) {
@@ -215,11 +164,14 @@ struct Criterion {
   }
 };
 
-// Reinterpret a 32-bit word as fp32.  Takes the word by value: bit-casting a
-// vector-element expression directly reads element 0 with this compiler.
-__device__ __forceinline__ float as_f32(uint32_t w) { return __builtin_bit_cast(float, w); }
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+// Two fp32 values rounded to nearest-even bf16, packed (first value in the
+// low half), and the two halves of a packed pair widened back to fp32.
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return u2f(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return u2f(w & 0xffff0000u); }
 
 // Uniform load through the scalar data cache (read-only metadata: context
 // lengths, block tables, kept lists).  Keeps metadata off the vector-load
@@ -236,11 +188,18 @@ __device__ __forceinline__ T sload(const T* p) {
 // are explicit (wait_vm).  M0 has no other use in these kernels (LDS
 // instructions on this target do not read it, and no indirect register
 // indexing is generated), so setting it here cannot disturb compiler state.
-__device__ __forceinline__ void lds_dma16(const void* g, const void* lds) {
-  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(a) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+#pragma clang diagnostic pop
+}
+// The same with a uniform 64-bit base in SGPRs plus a per-lane 32-bit offset.
+__device__ __forceinline__ void lds_dma16s(uint32_t voff, const void* sbase, uint32_t lds) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
 #pragma clang diagnostic pop
 }
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
@@ -251,28 +210,40 @@ __device__ __forceinline__ void wait_vm() {
 }
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// 16-byte LDS read issued as inline assembly.  The compiler, which cannot
-// count LDS-DMA completions precisely, would otherwise put a full vmcnt(0)
-// in front of any read of a DMA-written buffer and so also wait for the
-// unrelated V loads in flight.  The caller orders the DMA with wait_vm and
-// the result with wait_lgkm_tied.
-__device__ __forceinline__ u32x4 lds_read16(const void* p) {
-  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-  u32x4 r;
-  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(a));
-  return r;
-}
 // 16-byte global load issued as inline assembly, so the compiler does not
 // place its own (over-conservative) vmcnt waits for it; users wait with
-// wait_v_tied.
+// wait_v_tied.  The variant with `dep` takes a register operand it does not
+// use: the load is then issued only after the instruction that produced it.
 template <int OFF = 0>
 __device__ __forceinline__ u32x4 gload16(const void* p) {
   u32x4 r;
   asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(r) : "v"(p), "n"(OFF) : "memory");
   return r;
 }
+template <int OFF = 0>
+__device__ __forceinline__ u32x4 gload16_after(const void* p, float dep) {
+  u32x4 r;
+  asm volatile("global_load_dwordx4 %0, %1, off offset:%2 ; after %3" : "=v"(r) : "v"(p), "n"(OFF), "v"(dep) : "memory");
+  return r;
+}
+// Uniform 64-bit base in SGPRs plus a per-lane 32-bit offset.
+template <int OFF = 0>
+__device__ __forceinline__ u32x4 gload16s(uint32_t voff, const void* sbase) {
+  u32x4 r;
+  asm volatile("global_load_dwordx4 %0, %1, %2 offset:%3" : "=v"(r) : "v"(voff), "s"(sbase), "n"(OFF) : "memory");
+  return r;
+}
+template <int OFF = 0>
+__device__ __forceinline__ u32x4 gload16s_after(uint32_t voff, const void* sbase, float dep) {
+  u32x4 r;
+  asm volatile("global_load_dwordx4 %0, %1, %2 offset:%3 ; after %4"
+               : "=v"(r)
+               : "v"(voff), "s"(sbase), "n"(OFF), "v"(dep)
+               : "memory");
+  return r;
+}
 // Wait until at most N vector-memory operations are outstanding, tying the
-// 16 V registers to the wait so no use of them is scheduled ahead of it.
+// 16 K registers to the wait so no use of them is scheduled ahead of it.
 template <int N>
 __device__ __forceinline__ void wait_v_tied(u32x4 (&v)[16]) {
   asm volatile("s_waitcnt vmcnt(%16)"
@@ -282,27 +253,17 @@ __device__ __forceinline__ void wait_v_tied(u32x4 (&v)[16]) {
                : "n"(N)
                : "memory");
 }
-// Wait until at most N LDS/scalar operations are outstanding, tying four
-// operand registers to the wait so no use of them is scheduled ahead of it.
-// LDS operations complete in order, so after issuing reads A then B,
-// lgkmcnt(|B|) guarantees A (other outstanding scalar loads only make the
-// wait stricter).
-template <int N>
-__device__ __forceinline__ void wait_lgkm_tied(u32x4 (&k)[4]) {
-  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(k[0]), "+v"(k[1]), "+v"(k[2]), "+v"(k[3]) : "n"(N));
+
+// Transposing 8-byte LDS read (gfx950): within each 16-lane row, element e of
+// lane i is element i % 4 of what lane 4e + i / 4 of that row addresses.
+__device__ __forceinline__ s16x4 lds_read_tr(const __attribute__((address_space(3))) uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
 
 // Workgroup barrier that orders LDS only: waits for this wave's LDS traffic
 // and meets the other waves, without waiting for in-flight global loads (a
 // full __syncthreads() would drain the K/V prefetch).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Order LDS traffic between the lanes of one wave.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // ---------------------------------------------------------------------------
 // per-unit view of the inputs (all fields uniform)
@@ -381,39 +342,25 @@ __device__ __forceinline__ BlockAddr block_addr(const UnitView& u, int j, int& b
 // ---------------------------------------------------------------------------
 // LDS layout (one workgroup)
 // ---------------------------------------------------------------------------
-template <int G, int D>
-struct Summary {             // one block, published for the round
-  float m[4];                // reference max per head (log2 domain)
-  float l[4];                // softmax mass per head relative to m
-  float ps[G][D / 4];        // sums on the probe dims relative to m
+template <int D>
+struct alignas(16) Summary {   // one block, published for the round
+  float m[4];                  // reference max per head (log2 domain)
+  float l[4];                  // softmax mass per head relative to m
+  float ps[D / 4][4];          // sums on probe dim 4p, per head, relative to m
 };
-template <int G>
-struct alignas(16) WaveLds {
-  float probe[4][16][G][2];       // per-token-group sums on probe dims
-};
-// K of each wave's current block: 16 slabs, one per DMA load n, holding the
-// tokens 16*g + n (g = 0..3) as 4 rows of 256 B.  Slabs are 1040 B apart (256
-// B rows plus 16 B), so the 16 tokens one MFMA operand read touches (same g,
-// n = 0..15) fall into 16 different 16-byte bank groups.  A separate LDS
-// object from everything else, so the compiler can tell the DMA target apart
-// from the round's bookkeeping.
-constexpr int kKSlab = 4 * kRowChunks * 16 + 16;
-typedef uint8_t KBuf[kMaxWaves][kVLoads * kKSlab];
 template <int G, int D>
 struct alignas(16) RoundLds {
-  uint8_t q[G][kRowChunks * 16];    // the unit's G query rows (256 B each)
-  WaveLds<G> wave[kMaxWaves];
-  Summary<G, D> sum[2][kMaxWaves];  // by round parity
+  Summary<D> sum[2][kMaxWaves];      // by round parity
   double crit[2][kMaxWaves][4][2];   // by round parity: per position, per head (a, c)
   int bad;
   int zero_pos;
 };
-template <int G, int EPC>
-struct alignas(16) EpilogueLds {   // per-wave final state (reuses the K buffers)
+template <int G, int D>
+struct alignas(16) EpilogueLds {     // per-wave final state (reuses the V slabs)
   float m[kMaxWaves][4];
   float l[kMaxWaves][4];
   int issued[kMaxWaves];
-  float acc[kMaxWaves][4][16][G][EPC];
+  float acc[kMaxWaves][D][4];        // [wave][dim][head]
 };
 
 // ---------------------------------------------------------------------------
@@ -422,19 +369,19 @@ struct alignas(16) EpilogueLds {   // per-wave final state (reuses the K buffers
 template <int DT, int G, bool PAGED>
 __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(KernelArgs a) {
   using GE = Geo<DT>;
-  constexpr int D = GE::D, ES = GE::ES, EPC = GE::EPC, PPC = GE::PPC;
+  constexpr int D = GE::D, ES = GE::ES, PPC = GE::PPC;
+  constexpr int NDT = D / 16;  // 16-dim output tiles
   constexpr int ROW = D * ES;
   static_assert(ROW == kRowChunks * 16, "rows must be 16 chunks of 16 bytes");
   __shared__ RoundLds<G, D> R;
-  __shared__ alignas(16) KBuf kbuf;
-  static_assert(sizeof(EpilogueLds<G, EPC>) <= sizeof(KBuf), "epilogue state must fit the K buffers");
+  __shared__ alignas(16) uint8_t vbuf[kMaxWaves][kVSlab];
+  static_assert(sizeof(EpilogueLds<G, D>) <= sizeof(vbuf), "epilogue state must fit the V slabs");
 
   const int W = blockDim.x >> 6;
   const int wid = uni(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int lg = lane >> 4;
   const int c = lane & 15;
-  WaveLds<G>& wl = R.wave[wid];
 
   // ---- work item --------------------------------------------------------
   const int n_units = a.batch * a.hkv;
@@ -528,29 +475,27 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
   }
   if (t_begin >= t_end) return;  // chunk past this unit's traversal
 
-  // ---- query rows in LDS; per block each lane reads its MFMA A operand
-  // (rows replicated: MFMA row r -> head r % G) instead of pinning 16 VGPRs
+  // ---- query operand (B of S^T = K q^T): k-step j, lane (lg, c) holds the
+  // 16 bytes of chunk 4j + lg of head c % G (heads replicated over columns)
+  u32x4 qv[4];
   {
-    const char* qsrc = (const char*)a.q + (((size_t)b * a.hq + h * G) * D) * ES;
-    for (int i = threadIdx.x; i < G * kRowChunks; i += blockDim.x)
-      *(u32x4*)&R.q[i / kRowChunks][(i % kRowChunks) * 16] = *(const u32x4*)(qsrc + i * 16);
+    const char* qrow = (const char*)a.q + (((size_t)b * a.hq + h * G + c % G) * D) * ES;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qv[j] = *(const u32x4*)(qrow + (4 * j + lg) * 16);
   }
-  __syncthreads();
   const float c2 = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(d)
 
   // ---- per-wave running softmax state -------------------------------------
-  float m_w[G], l_w[G], acc[G][EPC];
+  // m_c, l_c: running max and mass of head c % G (this lane's S^T column);
+  // acc: running output in the O layout (rows = heads, columns = dims)
+  float m_c = -INFINITY, l_c = 0.f;
+  f32x4 acc[NDT];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m_w[g] = -INFINITY;
-    l_w[g] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[g][e] = 0.f;
-  }
+  for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const bool art_mode = a.mode == ART_MODE_ART;
   // prefix state on the probe dims (same in every wave): running max, mass and
   // numerators for head hg = lg (lanes with lg >= G carry head 0 unused),
-  // the previous probe, its squared norm, and the patience counter
+  // the previous probe's squared norm, and the patience counter
   const int hg = lg < G ? lg : 0;
   float mP = -INFINITY;
   double lP = 0.0, pP[PPC];
@@ -561,50 +506,79 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
   const Criterion crit{a.crit_hi, a.crit_lo, a.crit_c2, a.crit_tau_lt1 != 0, a.crit_phi_le1 != 0};
 
   // ---- loads ---------------------------------------------------------------
-  u32x4 vr[kVLoads];
-  // Row of token 16*lg of a block (this lane's 16-token group), picked with a
-  // select tree (an indexed pick is lowered to a private-memory array).
-  auto lane_row = [&](const BlockAddr& ba) -> uint32_t {
-    const uint32_t r01 = (lg & 1) ? ba.row[1] : ba.row[0];
-    const uint32_t r23 = (lg & 1) ? ba.row[3] : ba.row[2];
-    return (lg & 2) ? r23 : r01;
-  };
-  // K: DMA load n carries token 16*lg + n, chunk c, into slab n.  Rows past a
-  // contiguous context are clamped to its last token (read in bounds, masked).
-  auto load_k = [&](const BlockAddr& ba) {
-    wait_lgkm0();  // operand reads of the previous block have landed
-    uint8_t* dst = &kbuf[wid][0];
+  u32x4 kr[kLoads];  // K of the current block: [tile][k-step]
+  const __attribute__((address_space(3))) uint8_t* vb =
+      (const __attribute__((address_space(3))) uint8_t*)&vbuf[wid][0];
+  const uint32_t slab = (uint32_t)(uintptr_t)vb;
+  // V DMA n = 4g + q (tile g, quad q of its 16 tokens): lane (lg, c) carries
+  // token 4n + lg, global chunk c ^ 2lg ^ 8(q & 1) (byte offsets within the
+  // 16-token group of rows, one per q)
+  uint32_t voff[4];
+  {
+    const uint32_t e = (uint32_t)(lg * ROW + ((c ^ (2 * lg)) * 16));
+    voff[0] = e;
+    voff[1] = (e ^ 128u) + 4 * ROW;
+    voff[2] = e + 8 * ROW;
+    voff[3] = (e ^ 128u) + 12 * ROW;
+  }
+  const uint32_t koff = (uint32_t)(c * ROW + lg * 16);  // K: token c of the tile, chunk lg (+4j)
+  // K: load j of tile nt -> token 16 nt + c, chunk 4j + lg.  The first load
+  // of a block waits for `dep` (the score maximum), so it overwrites the K
+  // registers only after the MFMAs that read them have completed.
+  auto load_k = [&](const BlockAddr& ba, float dep) {
     if (PAGED || ba.nvalid == kBlk) {
-      const char* base = u.k + (size_t)lane_row(ba) * ROW + c * 16;
-      static_for<0, kVLoads>([&](auto nc) {
-        constexpr int n = decltype(nc)::value;
-        lds_dma16(base + n * ROW, dst + n * kKSlab);
+      static_for<0, kTiles>([&](auto ntc) {
+        constexpr int nt = decltype(ntc)::value;
+        const char* base = u.k + (size_t)ba.row[nt] * ROW;
+        if constexpr (nt == 0)
+          kr[0] = gload16s_after<0>(koff, base, dep);
+        else
+          kr[4 * nt] = gload16s<0>(koff, base);
+        kr[4 * nt + 1] = gload16s<64>(koff, base);
+        kr[4 * nt + 2] = gload16s<128>(koff, base);
+        kr[4 * nt + 3] = gload16s<192>(koff, base);
+      });
+    } else {  // last block of a contiguous sequence: rows clamped to the last token
+      static_for<0, kTiles>([&](auto ntc) {
+        constexpr int nt = decltype(ntc)::value;
+        const int tok = min(ba.j * kBlk + 16 * nt + c, u.n_ctx - 1);
+        const char* p = u.k + (size_t)tok * ROW + lg * 16;
+        if constexpr (nt == 0)
+          kr[0] = gload16_after<0>(p, dep);
+        else
+          kr[4 * nt] = gload16<0>(p);
+        kr[4 * nt + 1] = gload16<64>(p);
+        kr[4 * nt + 2] = gload16<128>(p);
+        kr[4 * nt + 3] = gload16<192>(p);
+      });
+    }
+  };
+  // V: the 16 DMAs of a block into this wave's slab (DMA n -> bytes 1024 n).
+  auto load_v = [&](const BlockAddr& ba) {
+    wait_lgkm0();  // LDS reads of the previous block have landed
+    if (PAGED || ba.nvalid == kBlk) {
+      static_for<0, kTiles>([&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        const char* base = u.v + (size_t)ba.row[g] * ROW;
+        static_for<0, 4>([&](auto qc) {
+          constexpr int q = decltype(qc)::value;
+          lds_dma16s(voff[q], base, slab + (4 * g + q) * 1024);
+        });
       });
     } else {
-      static_for<0, kVLoads>([&](auto nc) {
+      static_for<0, kLoads>([&](auto nc) {
         constexpr int n = decltype(nc)::value;
-        const int tok = min(ba.j * kBlk + 16 * lg + n, u.n_ctx - 1);
-        lds_dma16(u.k + (size_t)tok * ROW + c * 16, dst + n * kKSlab);
+        const int tok = min(ba.j * kBlk + 4 * n + lg, u.n_ctx - 1);
+        lds_dma16(u.v + (size_t)tok * ROW + ((c ^ (2 * lg) ^ (8 * (n & 1))) * 16), slab + n * 1024);
       });
     }
     compiler_fence();
   };
-  // V load i -> token 16*lg + i, chunk c (four 256-byte rows, one per tile).
-  auto load_v = [&](const BlockAddr& ba) {
-    if (PAGED || ba.nvalid == kBlk) {
-      const char* base = u.v + (size_t)lane_row(ba) * ROW + c * 16;
-      static_for<0, kVLoads>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        vr[i] = gload16<i * ROW>(base);
-      });
-    } else {
-      static_for<0, kVLoads>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        const int tok = min(ba.j * kBlk + 16 * lg + i, u.n_ctx - 1);
-        vr[i] = gload16(u.v + (size_t)tok * ROW + c * 16);
-      });
-    }
-  };
+  // Transposed V reads (bf16): lane (lg, c) addresses token 4lg + c/4 of a
+  // tile, dims 16dt + 4(c%4)..+3, i.e. chunk 2dt + (c%4)/2, half c%2, stored
+  // at position (2dt + (c%4)/2) ^ 2(c/4) ^ 8(lg&1) of row c/4 of DMA 4tt + lg.
+  const uint32_t tr_lane = (uint32_t)(lg * 1024 + (c >> 2) * 256 + 8 * (c & 1));
+  const uint32_t tr_x = (uint32_t)(16 * (((c & 3) >> 1) | (2 * (c >> 2)) | (8 * (lg & 1))));
 
   int bad_page = 0;
   int issued = 0;
@@ -612,7 +586,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
   BlockAddr cur;
   if (t_begin + wid < t_end) {
     cur = block_addr<ROW, PAGED>(u, uni(block_at(u, a.order, t_begin + wid)), bad_page);
-    load_k(cur);
+    load_k(cur, 0.f);
     load_v(cur);
     ++issued;
   }
@@ -627,148 +601,138 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
     BlockAddr nxt = cur;
     if (has_next) nxt = block_addr<ROW, PAGED>(u, uni(block_at(u, a.order, tn)), bad_page);
 
-    float alpha[G], m_new[G], lblk[G];
-    float bacc[G][EPC];
+    float m_new = m_c, alpha = 1.f, lblk = 0.f;
+    f32x4 bacc[NDT];
     if (active) {
       const int nvalid = cur.nvalid;
-      // ---- scores: S[nt][r] = q_{r%G} . k_{16 nt + c} ----------------------
-      wait_vm<kVLoads>();  // this block's K (its 16 V loads were issued after it)
-      // operand reads run two tiles ahead of the MFMAs
-      u32x4 qa[kKLoads];
-      u32x4 kb[kTiles][kKLoads];
-      auto read_tile = [&](int nt) {
-#pragma unroll
-        for (int i = 0; i < kKLoads; ++i)
-          kb[nt][i] = lds_read16(&kbuf[wid][c * kKSlab + nt * 256 + (4 * i + lg) * 16]);
-      };
+      // ---- scores S^T[token][head] = k_token . q_head --------------------------
+      wait_v_tied<kLoads>(kr);  // this block's K (its 16 V DMAs were issued after it)
       f32x4 S[kTiles];
-      auto mfma_tile = [&](int nt) {
+      static_for<0, kTiles>([&](auto ntc) {
+        constexpr int nt = decltype(ntc)::value;
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
         if constexpr (DT == ART_DT_BF16) {
 #pragma unroll
-          for (int i = 0; i < kKLoads; ++i)
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[i]),
-                                                        __builtin_bit_cast(bf16x8, kb[nt][i]), s, 0, 0, 0);
+          for (int j = 0; j < 4; ++j)
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[4 * nt + j]),
+                                                        __builtin_bit_cast(bf16x8, qv[j]), s, 0, 0, 0);
         } else {
 #pragma unroll
-          for (int i = 0; i < kKLoads; ++i)
+          for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              s = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32(qa[i][e]), as_f32(kb[nt][i][e]), s, 0, 0, 0);
+              s = __builtin_amdgcn_mfma_f32_16x16x4f32(u2f(kr[4 * nt + j][e]), u2f(qv[j][e]), s, 0, 0, 0);
         }
         S[nt] = s;
-      };
+      });
+      // ---- online softmax of head c % G against its running max ---------------
+      const int tb = 4 * lg;  // token of register 0 within each tile
+      float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < kKLoads; ++i) qa[i] = lds_read16(&R.q[c % G][(4 * i + lg) * 16]);
-      read_tile(0);
-      read_tile(1);
-      wait_lgkm_tied<8>(qa);
-      wait_lgkm_tied<4>(kb[0]);
-      mfma_tile(0);
-      read_tile(2);
-      wait_lgkm_tied<4>(kb[1]);
-      mfma_tile(1);
-      read_tile(3);
-      wait_lgkm_tied<4>(kb[2]);
-      mfma_tile(2);
-      wait_lgkm_tied<0>(kb[3]);
-      mfma_tile(3);
-      if (has_next) {
-        load_k(nxt);
-        ++issued;
-      }
-      // ---- online softmax against the wave's running max --------------------
+      for (int nt = 0; nt < kTiles; ++nt)
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int nt = 0; nt < kTiles; ++nt) {
-          const float sv = (nt * 16 + c < nvalid) ? S[nt][g] * c2 : -INFINITY;
-          S[nt][g] = sv;
+        for (int r = 0; r < 4; ++r) {
+          const float sv = (16 * nt + tb + r < nvalid) ? S[nt][r] * c2 : -INFINITY;
+          S[nt][r] = sv;
           mx = fmaxf(mx, sv);
         }
-        mx = uni_f(row_max(mx));
-        m_new[g] = fmaxf(m_w[g], mx);
-        alpha[g] = __builtin_amdgcn_exp2f(m_w[g] - m_new[g]);
-        float ls = 0.f;
-#pragma unroll
-        for (int nt = 0; nt < kTiles; ++nt) {
-          const float pv = __builtin_amdgcn_exp2f(S[nt][g] - m_new[g]);
-          S[nt][g] = pv;
-          ls += pv;
-        }
-        lblk[g] = uni_f(row_sum(ls));
-      }
-      // weights of tile lg (tokens 16*lg + 0..15, one per lane of the row),
-      // picked with a select tree
-      f32x4 mine;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float s01 = (lg & 1) ? S[1][g] : S[0][g];
-        const float s23 = (lg & 1) ? S[3][g] : S[2][g];
-        mine[g] = (lg & 2) ? s23 : s01;
-      }
-      // ---- P V ---------------------------------------------------------------
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) bacc[g][e] = 0.f;
-      // V of this block: the 16 K loads of the next block (if any) were issued after it
-      if (!has_next) wait_vm<0>();  // no K loads follow this block's V
-      wait_v_tied<kVLoads>(vr);
-      const float mg[4] = {mine[0], G > 1 ? mine[1] : 0.f, G > 2 ? mine[2] : 0.f, G > 3 ? mine[3] : 0.f};
-      pv_sources_ready(mg[0], mg[1], mg[2], mg[3]);
-      static_for<0, kVLoads>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        const int tok = 16 * lg + i;
-        u32x4 w = vr[i];
-        if (tok >= nvalid) w = u32x4{0u, 0u, 0u, 0u};
-        float ve[EPC];
-        if constexpr (DT == ART_DT_BF16) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            ve[2 * k] = bf16_lo(w[k]);
-            ve[2 * k + 1] = bf16_hi(w[k]);
-          }
-        } else {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) ve[k] = as_f32(w[k]);
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) bacc[g][e] = fma_bcast<i>(bacc[g][e], mg[g], ve[e]);
-      });
+      mx = col_max(mx);
       if (has_next) {
-        compiler_fence();
-        load_v(nxt);
+        load_k(nxt, mx);
+        ++issued;
       }
+      m_new = fmaxf(m_c, mx);
+      alpha = __builtin_amdgcn_exp2f(m_c - m_new);
+      float ls = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < kTiles; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(S[nt][r] - m_new);
+          S[nt][r] = p;
+          ls += p;
+        }
+      lblk = col_sum(ls);
+      // ---- P V on MFMA ---------------------------------------------------------
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) bacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // V of this block: the 16 K loads of the next block (if any) were issued after it
+      if (has_next)
+        wait_vm<kLoads>();
+      else
+        wait_vm<0>();
+      const bool partial = nvalid < kBlk;  // weights of the tail tokens are 0; their V may be garbage
+      if constexpr (DT == ART_DT_BF16) {
+        // A operand of tile pair jp: element e < 4 is token 16(2jp) + 4lg + e,
+        // element e >= 4 is token 16(2jp+1) + 4lg + e - 4, split as P = hi + lo
+        u32x4 ph[2], pl[2];
+#pragma unroll
+        for (int jp = 0; jp < 2; ++jp)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int nt = 2 * jp + hh;
+            const uint32_t w0 = pk_bf16(S[nt][0], S[nt][1]);
+            const uint32_t w1 = pk_bf16(S[nt][2], S[nt][3]);
+            ph[jp][2 * hh] = w0;
+            ph[jp][2 * hh + 1] = w1;
+            pl[jp][2 * hh] = pk_bf16(S[nt][0] - bf16_lo(w0), S[nt][1] - bf16_hi(w0));
+            pl[jp][2 * hh + 1] = pk_bf16(S[nt][2] - bf16_lo(w1), S[nt][3] - bf16_hi(w1));
+          }
+#pragma unroll
+        for (int jp = 0; jp < 2; ++jp) {
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            const auto* pv = vb + tr_lane + (((uint32_t)(32 * dt)) ^ tr_x);
+            s16x4 v0 = lds_read_tr(pv + (2 * jp) * 4096);
+            s16x4 v1 = lds_read_tr(pv + (2 * jp + 1) * 4096);
+            if (partial) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                if (32 * jp + tb + e >= nvalid) v0[e] = 0;
+                if (32 * jp + 16 + tb + e >= nvalid) v1[e] = 0;
+              }
+            }
+            const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+            bacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ph[jp]), bv, bacc[dt], 0, 0, 0);
+            bacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pl[jp]), bv, bacc[dt], 0, 0, 0);
+          }
+        }
+      } else {
+        // fp32: k = lg of step (nt, r) is token 16nt + 4lg + r; B element
+        // (token, dim 16dt + c) read directly from the slab
+        const auto* vf = (const __attribute__((address_space(3))) float*)vb;
+#pragma unroll
+        for (int nt = 0; nt < kTiles; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int tok = 16 * nt + tb + r;
+            const int zsw = (2 * r) ^ (8 * (lg & 1));
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+              const int pos = (4 * dt + (c >> 2)) ^ zsw;
+              float v = vf[((4 * nt + lg) * 1024 + r * 256 + pos * 16 + 4 * (c & 3)) >> 2];
+              if (tok >= nvalid) v = 0.f;
+              bacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(S[nt][r], v, bacc[dt], 0, 0, 0);
+            }
+          }
+      }
+      if (has_next) load_v(nxt);
     }
 
     int stop_round = -1;  // this round's stop, as a traversal count
     if (art_mode) {
       // ---- publish the block summary ------------------------------------------
-      Summary<G, D>& sw = R.sum[parity][wid];
+      // probe dims 4p: lanes c = 0, 4, 8, 12 of row 0 hold dims 16dt + c for
+      // heads r % G in register r
+      Summary<D>& sw = R.sum[parity][wid];
       if (active) {
+        if (lane < 16 && (c & 3) == 0) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          wl.probe[lg][c][g][0] = bacc[g][0];
-          if (PPC > 1) wl.probe[lg][c][g][1] = bacc[g][PPC > 1 ? 4 : 0];
-        }
-        wave_lds_sync();
-        if (lg < G) {
-#pragma unroll
-          for (int k = 0; k < PPC; ++k)
-            sw.ps[lg][c * PPC + k] = (wl.probe[0][c][lg][k] + wl.probe[1][c][lg][k]) +
-                                     (wl.probe[2][c][lg][k] + wl.probe[3][c][lg][k]);
+          for (int dt = 0; dt < NDT; ++dt) *(f32x4*)&sw.ps[4 * dt + (c >> 2)][0] = bacc[dt];
         }
         if (lane < G) {
-          float mv = m_new[0], lv = lblk[0];
-#pragma unroll
-          for (int g = 1; g < G; ++g)
-            if (lane == g) mv = m_new[g], lv = lblk[g];
-          sw.m[lane] = mv;
-          sw.l[lane] = lv;
+          sw.m[lane] = m_new;
+          sw.l[lane] = lblk;
         }
       }
       lds_barrier();
@@ -788,7 +752,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
 #pragma unroll
       for (int w2 = 0; w2 < kMaxWaves; ++w2) {
         if (w2 < n_act) {
-          const Summary<G, D>& s2 = R.sum[parity][w2];
+          const Summary<D>& s2 = R.sum[parity][w2];
           const float mb = s2.m[hg];
           const float M = fmaxf(mP, mb);
           const double sP = (double)__builtin_amdgcn_exp2f(mP - M);
@@ -800,7 +764,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
           mP = M;
 #pragma unroll
           for (int k = 0; k < PPC; ++k) {
-            const double p = fma(pP[k], sP, (double)s2.ps[hg][c * PPC + k] * sB);
+            const double p = fma(pP[k], sP, (double)s2.ps[c * PPC + k][hg] * sB);
             if (mine && lg < G) {
               own_a = fma(p, p, own_a);
               own_c = fma(p, pP[k], own_c);
@@ -848,13 +812,16 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
 
     // ---- commit this wave's block (unless it lies after the stop) -------------
     if (active && (stop_round < 0 || t + 1 <= stop_round)) {
+      // row r of the O layout holds head r % G, whose column values sit in lane r % G
+      float al[4];
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        m_w[g] = m_new[g];
-        l_w[g] = l_w[g] * alpha[g] + lblk[g];
+      for (int r = 0; r < 4; ++r) al[r] = lane_f(alpha, r % G);
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[g][e] = fmaf(acc[g][e], alpha[g], bacc[g][e]);
-      }
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[dt][r] = fmaf(acc[dt][r], al[r], bacc[dt][r]);
+      m_c = m_new;
+      l_c = fmaf(l_c, alpha, lblk);
     }
     if (stop_round >= 0) {
       stop = stop_round;
@@ -864,27 +831,22 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
   }
   if (stop < 0) stop = t_end;
 
-  // ---- epilogue: merge waves, reduce token groups, normalize ---------------
-  wait_vm<0>();  // speculative K loads may still be landing in the K buffers
+  // ---- epilogue: merge waves, normalize --------------------------------------
+  wait_vm<0>();  // speculative loads may still be landing in the V slabs
   __syncthreads();
-  auto& E = *reinterpret_cast<EpilogueLds<G, EPC>*>(&kbuf[0][0]);
+  auto& E = *reinterpret_cast<EpilogueLds<G, D>*>(&vbuf[0][0]);
+  if (lane < 16) {
 #pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) E.acc[wid][lg][c][g][e] = acc[g][e];
+    for (int dt = 0; dt < NDT; ++dt) *(f32x4*)&E.acc[wid][16 * dt + c][0] = acc[dt];
+  }
   if (lane < G) {
-    float mv = m_w[0], lv = l_w[0];
-#pragma unroll
-    for (int g = 1; g < G; ++g)
-      if (lane == g) mv = m_w[g], lv = l_w[g];
-    E.m[wid][lane] = mv;
-    E.l[wid][lane] = lv;
+    E.m[wid][lane] = m_c;
+    E.l[wid][lane] = l_c;
   }
   if (lane == 0) E.issued[wid] = issued;
   __syncthreads();
   for (int o = threadIdx.x; o < G * D; o += blockDim.x) {
     const int g = o / D, dim = o % D;
-    const int cc = dim / EPC, e = dim % EPC;
     float M = -INFINITY;
     for (int w2 = 0; w2 < W; ++w2)
       if (E.l[w2][g] > 0.f) M = fmaxf(M, E.m[w2][g]);
@@ -893,9 +855,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
       if (!(E.l[w2][g] > 0.f)) continue;  // a wave with no committed block
       const float s = __builtin_amdgcn_exp2f(E.m[w2][g] - M);
       L = fmaf(E.l[w2][g], s, L);
-      const float v = (E.acc[w2][0][cc][g][e] + E.acc[w2][1][cc][g][e]) +
-                      (E.acc[w2][2][cc][g][e] + E.acc[w2][3][cc][g][e]);
-      num = fmaf(v, s, num);
+      num = fmaf(E.acc[w2][dim][g], s, num);
     }
     if (single) {
       out_rows[o] = num / L;
