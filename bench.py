@@ -1,13 +1,14 @@
 #!/usr/bin/env python3
 """Benchmark: ART decode attention on one MI355X.
 
-A step is one art_decode call (all kernels of the hot path) over the whole
-batch of the large-batch paged decode workload: batch 64, 32 query / 8 KV
-heads, head_dim 128, bf16 KV in 16-token pages with a shuffled block table,
-context lengths uniform in [8192, 32768], 64-token ART blocks,
-eps_scale 2e-3, eps_dir 2e-4, patience 3, recency-first traversal.  Inputs
-are generated once (seeded, synthetic) and are resident in HBM before the
-timed region.
+A step is one art_decode call (the whole hot path: one kernel in ART mode)
+over the whole batch of the large-batch paged decode workload: batch 64,
+32 query / 8 KV heads, head_dim 128, bf16 KV in 16-token pages with a
+shuffled block table, context lengths uniform in [8192, 32768], 64-token ART
+blocks, eps_scale 2e-3, eps_dir 2e-4, patience 3, recency-first traversal.
+Inputs are generated once (seeded, synthetic) and are resident in HBM before
+the timed region.  Before every timed step an untimed 1 GiB scratch write
+evicts the last-level (MALL) and L2 caches.
 
 Reported (one JSON line on stdout):
   value          KV GB/s on the bytes actually loaded (blocks_issued x block
@@ -15,15 +16,29 @@ Reported (one JSON line on stdout):
                  ART mode, generator reading "B" (Llama-shaped keys, where
                  the criterion fires)
   roofline       algorithmic bytes (stop_idx x block bytes + per-unit terms)
-                 per launch / average launch time (HIP events on the
-                 decode stream) against the 8 TB/s HBM peak
-  cpu_baseline   the fp64 numpy oracle on a bounded sample of the same units
+                 per launch / average decode-kernel time (HIP events on the
+                 launch stream around the call, which enqueues only that
+                 kernel in ART mode) against the 8 TB/s HBM peak; `traffic`
+                 is the HBM bytes per launch measured with rocprofv3 counters
+                 (FETCH_SIZE + WRITE_SIZE, calibrated on a copy kernel),
+                 read from the committed counter summary and reported only
+                 while the kernel sources still match it
+  cpu_baseline   the fp64 numpy oracle over every unit of the same workload
   extra fields   full-attention mode and generator reading "A" on the same
                  shapes, % KV blocks skipped, effective tokens/s
+
+Other modes (no timing line):
+  --summarize-pmc FETCH_DIR WRITE_DIR   turn two rocprofv3 --pmc runs of
+        `bench.py --only art --copy-mib N ...` into the counter summary
+  --summarize-trace TRACE_DIR BENCH_LOG  turn a rocprofv3 --kernel-trace
+        --stats run into a markdown summary next to the events timing
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -36,6 +51,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BLOCK = 64
+KERNEL_SOURCES = ("kv_cache_early_amd/csrc/art_kernels.hip", "kv_cache_early_amd/csrc/art_internal.h",
+                  "kv_cache_early_amd/csrc/art_api.cpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "art_decode_kernel_cfg3B_art_pmc.json")
+WORKLOAD = ("cfg3 large-batch paged decode: B=64, Hq=32, Hkv=8, d=128, ctx U[8192,32768], page 16 shuffled, "
+            "block 64, eps (2e-3, 2e-4), patience 3, recent-first")
 
 
 def parse():
@@ -44,11 +64,28 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--reading", default="B", choices=["A", "B"])
+    ap.add_argument("--only", choices=["art", "full"], default=None,
+                    help="time only this mode (for profiling runs); the line then reports it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-units", type=int, default=0, help="oracle sample size (0 = sized to ~15 s)")
+    ap.add_argument("--cpu-units", type=int, default=0, help="oracle sample size (0 = every unit)")
     ap.add_argument("--skip-extra", action="store_true", help="only the headline measurement")
     ap.add_argument("--split-blocks", type=int, default=0)
+    ap.add_argument("--no-flush", action="store_true", help="skip the cache-evicting write between steps")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run an elementwise copy of this many MiB `steps` times (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_LOG"))
+    ap.add_argument("--command", default="", help="command line recorded in a summary")
+    ap.add_argument("--out", default="", help="summary output path")
     return ap.parse_args()
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def accounting(w, stop, issued):
@@ -77,10 +114,10 @@ def accounting(w, stop, issued):
     pages = 0
     if s.page_size:
         pages = int(np.sum(np.minimum(issued, 10 ** 9))) * (BLOCK // s.page_size) * 4
-    return kv_bytes(issued) + per_unit + pages, kv_bytes(stop) + per_unit + pages
+    return kv_bytes(issued) + per_unit + pages, kv_bytes(stop) + per_unit + pages, kv_bytes
 
 
-def time_steps(dec, dev, w, mode, steps, warmup, split_blocks):
+def time_steps(dec, dev, w, mode, steps, warmup, split_blocks, flush):
     import torch
     s = w.spec
     stream = torch.cuda.current_stream()
@@ -88,6 +125,7 @@ def time_steps(dec, dev, w, mode, steps, warmup, split_blocks):
               kept_blocks=dev.kept_blocks, kept_count=dev.kept_count, eps_scale=s.eps_scale, eps_dir=s.eps_dir,
               patience=s.patience, order=s.order, mode=mode, split_blocks=split_blocks,
               stream=stream.cuda_stream)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if flush else None
     r = dec.decode(dev.q, dev.k, dev.v, dev.context_lens, **kw)
     for _ in range(warmup):
         dec.decode(dev.q, dev.k, dev.v, dev.context_lens, out=r.out, stop_idx=r.stop_idx,
@@ -96,6 +134,8 @@ def time_steps(dec, dev, w, mode, steps, warmup, split_blocks):
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
     for a, b in evs:
+        if scratch is not None:
+            scratch.fill_(1)  # untimed: evicts the MALL and the L2s
         a.record(stream)
         dec.decode(dev.q, dev.k, dev.v, dev.context_lens, out=r.out, stop_idx=r.stop_idx,
                    blocks_issued=r.blocks_issued, **kw)
@@ -111,11 +151,11 @@ def time_steps(dec, dev, w, mode, steps, warmup, split_blocks):
                 issued=r.blocks_issued.cpu().numpy().astype(np.int64))
 
 
-def measure(dec, w, mode, steps, warmup, split_blocks, dev=None):
+def measure(dec, w, mode, args, dev=None):
     from workloads.device import to_device
     dev = dev or to_device(w)
-    t = time_steps(dec, dev, w, mode, steps, warmup, split_blocks)
-    loaded, algo = accounting(w, t["stop"], t["issued"])
+    t = time_steps(dec, dev, w, mode, args.steps, args.warmup, args.split_blocks, not args.no_flush)
+    loaded, algo, _ = accounting(w, t["stop"], t["issued"])
     sec = t["ms_mean"] * 1e-3
     Tp = w.traversal_lengths()
     res = dict(ms=t["ms_mean"], ms_min=t["ms_min"], ms_median=t["ms_median"], wall_ms=t["wall_ms"],
@@ -129,35 +169,170 @@ def measure(dec, w, mode, steps, warmup, split_blocks, dev=None):
     return res, t, dev
 
 
-def cpu_baseline(w, n_units, stop_gpu):
-    """The fp64 oracle as it stands on a bounded sample of the workload's units."""
+def copy_leg(mib, steps):
+    """Elementwise copy (y = x * 1) of `mib` MiB: reads and writes mib MiB per launch."""
+    import torch
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.mul(x, 1.0, out=y)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        torch.mul(x, 1.0, out=y)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    return dict(bytes_read=n * 4, bytes_written=n * 4, ms=ms, gbs=2 * n * 4 / (ms * 1e-3) / 1e9)
+
+
+def cpu_baseline(w, n_units, stop_gpu, kv_bytes):
+    """The fp64 oracle as it stands over the workload's units (all, or a bounded sample)."""
     import oracle as orc
     from threadpoolctl import threadpool_info
     s = w.spec
-    rng = np.random.default_rng(0)
     allu = [(b, h) for b in range(s.batch) for h in range(s.num_kv_heads)]
-    pick = sorted(allu[i] for i in rng.choice(len(allu), size=min(n_units, len(allu)), replace=False))
+    if n_units and n_units < len(allu):
+        rng = np.random.default_rng(0)
+        pick = sorted(allu[i] for i in rng.choice(len(allu), size=n_units, replace=False))
+    else:
+        pick = allu
     t0 = time.perf_counter()
     out, stop, res = orc.art_decode_workload(w, units=pick, keep_results=True)
     el = time.perf_counter() - t0
-    es = 2 if s.dtype == "bf16" else 4
-    kv = 0
+    count = np.zeros((s.batch, s.num_kv_heads), dtype=np.int64)
     rel = []
     agree = 0
     for (b, h), r in res.items():
-        kv += min(int(r.stop) * BLOCK, int(w.context_lens[b])) * s.head_dim * 2 * es
+        count[b, h] = int(r.stop)
         full = r.O[-1]
         rel.append(float(np.linalg.norm(r.out - full) / np.linalg.norm(full)))
         agree += int(r.stop == stop_gpu[b, h])
+    kv = kv_bytes(count)
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
-    return dict(value=kv / el / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
-                sample=f"{len(pick)} of {len(allu)} (batch, kv head) units of the same workload, fp64 numpy, "
-                       f"all prefix outputs and the stop rule; {el:.1f} s wall",
-                seconds=el, rel_l2_vs_full_median=float(np.median(rel)), stop_agree=f"{agree}/{len(pick)}")
+    what = "every" if len(pick) == len(allu) else f"{len(pick)} of {len(allu)}"
+    return dict(value=round(kv / el / 1e9, 4), unit="GB/s", cores=int(threads), kind="oracle",
+                sample=f"{what} (batch, kv head) units of the same workload ({len(allu)} units), fp64 numpy "
+                       f"oracle: all prefix outputs and the stop rule; {el:.1f} s wall, GB/s on the KV bytes of "
+                       f"the blocks it processed",
+                seconds=round(el, 2), rel_l2_vs_full_median=float(np.median(rel)),
+                stop_agree_with_gpu=f"{agree}/{len(pick)}")
+
+
+def traffic_from_summary():
+    """HBM bytes per launch from the committed counter summary, if it still matches the sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_hash():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# summaries of rocprofv3 runs
+# ---------------------------------------------------------------------------
+def _counter_rows(d):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = []
+    for p in files:
+        with open(p) as f:
+            rows += list(csv.DictReader(f))
+    return rows
+
+
+def _per_dispatch(rows, counter, name_pred):
+    """Mean over dispatches of the counter (summed over its instances per dispatch)."""
+    per = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter or not name_pred(r.get("Kernel_Name", "")):
+            continue
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} rows for the kernel")
+    return float(np.mean(list(per.values()))), len(per)
+
+
+def summarize_pmc(args):
+    fetch_rows = _counter_rows(args.summarize_pmc[0])
+    write_rows = _counter_rows(args.summarize_pmc[1])
+    is_art = lambda n: "art_decode_kernel" in n
+    is_copy = lambda n: "elementwise" in n.lower() and "mul" in n.lower() or "MulFunctor" in n
+    f_art, n1 = _per_dispatch(fetch_rows, "FETCH_SIZE", is_art)
+    w_art, n2 = _per_dispatch(write_rows, "WRITE_SIZE", is_art)
+    f_cp, n3 = _per_dispatch(fetch_rows, "FETCH_SIZE", is_copy)
+    w_cp, n4 = _per_dispatch(write_rows, "WRITE_SIZE", is_copy)
+    copy_bytes = args.copy_mib * (1 << 20)
+    fs = copy_bytes / (f_cp * 1024.0)
+    ws = copy_bytes / (w_cp * 1024.0)
+    traffic = f_art * 1024.0 * fs + w_art * 1024.0 * ws
+    out = dict(kernel="art::art_decode_kernel<bf16, G=4, paged>", workload=WORKLOAD + ", generator B, ART mode",
+               fetch_kib_per_dispatch=f_art, write_kib_per_dispatch=w_art, dispatches=[n1, n2],
+               copy_kernel="elementwise y = x * 1 (torch), fp32", copy_bytes_each_way=copy_bytes,
+               copy_fetch_kib=f_cp, copy_write_kib=w_cp, copy_dispatches=[n3, n4],
+               fetch_scale=fs, write_scale=ws, traffic_bytes_per_launch=traffic,
+               source_sha256=source_hash(), commands=args.command)
+    path = args.out or TRAFFIC_FILE
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def summarize_trace(args):
+    """Markdown summary of a kernel-trace run of `bench.py --only art --skip-extra ...`.
+
+    The average over the last `steps` decode dispatches (the timed, cache-cold
+    calls) is set beside the HIP-events time of the same run."""
+    trace_dir, log = args.summarize_trace
+    stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
+    trace = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)[0]
+    with open(stats) as f:
+        rows = list(csv.DictReader(f))
+    with open(trace) as f:
+        tr = [r for r in csv.DictReader(f) if "art_decode_kernel" in r["Kernel_Name"]]
+    tr.sort(key=lambda r: int(r["Start_Timestamp"]))
+    line = None
+    with open(log) as f:
+        for l in f:
+            l = l.strip()
+            if l.startswith("{") and '"metric"' in l:
+                line = json.loads(l)
+    steps = line["steps"] if line else len(tr)
+    timed = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in tr[-steps:]]
+    md = ["# rocprofv3 kernel trace: art_decode_kernel (bf16, G=4, paged), " + WORKLOAD + ", generator B, ART mode",
+          "", "Command (repository root):", "", "```", args.command, "```", "",
+          "## --stats summary (all dispatches of the run)", "",
+          "| kernel | calls | average us | min us | max us | total % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        md.append(f"| {r['Name'][:100]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                  f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
+    md += ["", f"## The {len(timed)} timed decode dispatches (cache-cold; the earlier ones are warmup)", "",
+           f"- kernel-trace average: {np.mean(timed):.1f} us (min {np.min(timed):.1f}, max {np.max(timed):.1f})"]
+    if line:
+        md += [f"- HIP events around the same calls (bench.py, launch stream): {line['ms_per_step'] * 1e3:.1f} us "
+               f"mean",
+               f"- value: {line['value']} {line['unit']} on loaded bytes; roofline achieved "
+               f"{line['roofline']['achieved']} GB/s on algorithmic bytes ({line['roofline']['frac']:.3f} of 8 TB/s)",
+               f"- blocks skipped: {line.get('pct_blocks_skipped')}"]
+    md += ["", "The fill kernel is the untimed 1 GiB cache-evicting write between timed calls; "
+           "__amd_rocclr_copyBuffer entries are host-device copies of inputs and results."]
+    with open(args.out, "w") as f:
+        f.write("\n".join(md) + "\n")
+    print("\n".join(md))
 
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        return summarize_pmc(args)
+    if args.summarize_trace:
+        return summarize_trace(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this build runs on one GPU; ART units are independent, so --gpus > 1 "
                                    "would shard (batch, kv head) units across devices with no exchange "
@@ -177,55 +352,67 @@ def main():
     print(f"[bench] generated {spec.name} reading {args.reading}: {w.kv_bytes_resident() / 1e9:.2f} GB KV "
           f"in {gen_s:.1f} s", file=sys.stderr, flush=True)
 
-    art_res, art_t, dev = measure(dec, w, 1, args.steps, args.warmup, args.split_blocks)
-    print(f"[bench] ART: {art_res['ms']:.3f} ms {art_res['gbs_loaded']:.0f} GB/s "
-          f"skip {art_res['pct_blocks_skipped']:.3f}", file=sys.stderr, flush=True)
+    head_mode = 0 if args.only == "full" else 1
+    head, head_t, dev = measure(dec, w, head_mode, args)
+    print(f"[bench] {'full' if head_mode == 0 else 'ART'}: {head['ms']:.3f} ms {head['gbs_loaded']:.0f} GB/s "
+          f"skip {head['pct_blocks_skipped']:.3f}", file=sys.stderr, flush=True)
     extra = {}
-    if not args.skip_extra:
-        full_res, _, _ = measure(dec, w, 0, args.steps, args.warmup, args.split_blocks, dev=dev)
-        extra["full_mode"] = {k: full_res[k] for k in ("ms", "gbs_loaded", "pct_of_peak", "effective_tokens_per_s")}
+    if not args.skip_extra and args.only is None:
+        full_res, _, _ = measure(dec, w, 0, args, dev=dev)
+        extra["full_mode"] = {k: round(full_res[k], 4) for k in ("ms", "gbs_loaded", "pct_of_peak",
+                                                                 "effective_tokens_per_s")}
         print(f"[bench] full: {full_res['ms']:.3f} ms {full_res['gbs_loaded']:.0f} GB/s", file=sys.stderr, flush=True)
-    roof = dict(bound="hbm", achieved=round(art_res["gbs_algorithmic"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=round(art_res["gbs_algorithmic"] / HBM_PEAK_GBS, 4), traffic=None)
+    traffic = traffic_from_summary() if head_mode == 1 else None
+    roof = dict(bound="hbm", achieved=round(head["gbs_algorithmic"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(head["gbs_algorithmic"] / HBM_PEAK_GBS, 4),
+                traffic=None if traffic is None else round(traffic),
+                traffic_unit="HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                algorithmic_bytes=int(head["bytes_algorithmic"]), kernel="art_decode_kernel",
+                kernel_ms=round(head["ms"], 4))
+
+    if args.copy_mib:
+        cp = copy_leg(args.copy_mib, args.steps)
+        extra["copy_kernel"] = cp
+        print(f"[bench] copy {args.copy_mib} MiB: {cp['ms']:.3f} ms {cp['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
-        n = args.cpu_units or 256
-        cpu = cpu_baseline(w, n, art_t["stop"])
-        print(f"[bench] cpu oracle: {cpu['value']:.2f} GB/s over {cpu['seconds']:.1f} s", file=sys.stderr, flush=True)
+        _, _, kv_bytes = accounting(w, head_t["stop"], head_t["issued"])
+        cpu = cpu_baseline(w, args.cpu_units, head_t["stop"], kv_bytes)
+        print(f"[bench] cpu oracle: {cpu['value']:.3f} GB/s over {cpu['seconds']:.1f} s", file=sys.stderr, flush=True)
 
-    if not args.skip_extra:
+    if not args.skip_extra and args.only is None:
         other = "A" if args.reading == "B" else "B"
         del dev
         w2 = make_workload(config(3, other))
-        r2, _, _ = measure(dec, w2, 1, args.steps, args.warmup, args.split_blocks)
-        extra[f"reading_{other}"] = {k: r2[k] for k in ("ms", "gbs_loaded", "pct_of_peak", "pct_blocks_skipped",
-                                                        "effective_tokens_per_s")}
+        r2, _, _ = measure(dec, w2, 1, args)
+        extra[f"reading_{other}"] = {k: round(r2[k], 4) for k in ("ms", "gbs_loaded", "pct_of_peak",
+                                                                  "pct_blocks_skipped", "effective_tokens_per_s")}
 
     line = {
         "metric": "decode-attn KV GB/s achieved (% of HBM peak) + effective tokens/s; % KV blocks skipped",
-        "value": round(art_res["gbs_loaded"], 1),
+        "value": round(head["gbs_loaded"], 1),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(art_res["ms"], 4),
+        "ms_per_step": round(head["ms"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; Llama-shaped keys with recency bias, sinks and low-score/high-value tokens)",
-        "config": {"workload": "cfg3 large-batch paged decode: B=64, Hq=32, Hkv=8, d=128, ctx U[8192,32768], "
-                               "page 16 shuffled, block 64, eps (2e-3, 2e-4), patience 3, recent-first",
-                   "generator": args.reading, "mode": "ART", "global_batch": spec.batch, "seq_len": "8192-32768",
-                   "parallelism": "single GPU"},
-        "pct_of_peak": round(art_res["pct_of_peak"], 4),
-        "effective_tokens_per_s": round(art_res["effective_tokens_per_s"], 1),
-        "context_tokens_per_s": round(art_res["context_tokens_per_s"], 1),
-        "pct_blocks_skipped": round(art_res["pct_blocks_skipped"], 4),
-        "wasted_block_frac": round(art_res["wasted_frac"], 4),
-        "ms_min": round(art_res["ms_min"], 4),
-        "wall_ms_per_step": round(art_res["wall_ms"], 4),
+        "config": {"workload": WORKLOAD, "generator": args.reading, "mode": "full" if head_mode == 0 else "ART",
+                   "global_batch": spec.batch, "seq_len": "8192-32768", "parallelism": "single GPU",
+                   "cache_flush_between_steps": not args.no_flush},
+        "pct_of_peak": round(head["pct_of_peak"], 4),
+        "effective_tokens_per_s": round(head["effective_tokens_per_s"], 1),
+        "context_tokens_per_s": round(head["context_tokens_per_s"], 1),
+        "pct_blocks_skipped": round(head["pct_blocks_skipped"], 4),
+        "wasted_block_frac": round(head["wasted_frac"], 4),
+        "ms_min": round(head["ms_min"], 4),
+        "ms_median": round(head["ms_median"], 4),
+        "wall_ms_per_step": round(head["wall_ms"], 4),
         "roofline": roof,
         "cpu_baseline": cpu,
         **extra,

@@ -51,8 +51,7 @@
  * Supported set (anything else returns ART_ERR_UNSUPPORTED):
  *   dtype ART_DT_BF16 with head_dim 128, or ART_DT_F32 with head_dim 64;
  *   G = num_q_heads / num_kv_heads in {1, 2, 4}; block_size 64;
- *   page_size 0 (contiguous) or a multiple of 16 that divides 64 or is
- *   divided by it.
+ *   page_size 0 (contiguous) or a power of two >= 16.
  */
 #ifndef LIBART_ART_H
 #define LIBART_ART_H
@@ -133,7 +132,12 @@ size_t art_workspace_size(const art_shape* shape, const art_params* params);
  *   stop_idx      int32 [B][Hkv]                   (written)
  *   blocks_issued int32 [B][Hkv] or NULL           (written)
  *   workspace     device buffer of >= art_workspace_size() bytes, 256-byte
- *                 aligned; its contents on entry do not matter
+ *                 aligned; its contents on entry do not matter (every call
+ *                 rewrites what it reads, so no initialisation or per-call
+ *                 clearing is needed and the call enqueues no memset)
+ *
+ * ART_MODE_ART enqueues one kernel; ART_MODE_FULL with more than one chunk
+ * per unit enqueues the decode kernel and an LSE-combine kernel.
  */
 art_status art_decode(const art_shape* shape, const art_params* params,
                       const void* q, const void* k, const void* v,
@@ -142,10 +146,13 @@ art_status art_decode(const art_shape* shape, const art_params* params,
                       float* out, int32_t* stop_idx, int32_t* blocks_issued,
                       void* workspace, size_t workspace_bytes, void* stream);
 
-/* Device-side error recorded by the last art_decode that used `workspace`
- * (ART_OK, ART_ERR_TIMEOUT or ART_ERR_DEVICE_INPUT).  Synchronous: reads
- * 4 bytes from the workspace; call after synchronizing the decode's stream. */
-art_status art_last_error(const void* workspace);
+/* Device-side error recorded by the last art_decode that enqueued work on
+ * `workspace` (ART_OK, ART_ERR_TIMEOUT or ART_ERR_DEVICE_INPUT; the most
+ * severe over its work items).  ART_OK if no launch has used the workspace.
+ * Synchronous (device-to-host copies of the workspace's status words); call
+ * after synchronizing the decode's stream.  `workspace_bytes` bounds what is
+ * read: ART_ERR_WORKSPACE if the recorded work does not fit in it. */
+art_status art_last_error(const void* workspace, size_t workspace_bytes);
 
 /* Static English description of a status code. */
 const char* art_status_string(art_status status);

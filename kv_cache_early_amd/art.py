@@ -70,7 +70,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.art_decode.argtypes = [ctypes.POINTER(art_shape), ctypes.POINTER(art_params), vp, vp, vp, vp, vp, vp, vp,
                                vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.art_decode.restype = ctypes.c_int
-    lib.art_last_error.argtypes = [vp]
+    lib.art_last_error.argtypes = [vp, ctypes.c_size_t]
     lib.art_last_error.restype = ctypes.c_int
     lib.art_status_string.argtypes = [ctypes.c_int]
     lib.art_status_string.restype = ctypes.c_char_p
@@ -112,8 +112,8 @@ def decode_raw(shape: art_shape, params: art_params, q, k, v, context_lens, bloc
                                  workspace_bytes, stream))
 
 
-def last_error(workspace) -> int:
-    return int(load().art_last_error(_ptr(workspace)))
+def last_error(workspace, workspace_bytes: int) -> int:
+    return int(load().art_last_error(_ptr(workspace), int(workspace_bytes)))
 
 
 @dataclass
@@ -181,4 +181,4 @@ class ArtDecoder:
     def device_error(self) -> int:
         """Device-side status of the last decode (synchronizes the device first)."""
         self.torch.cuda.synchronize(self.device)
-        return last_error(self._ws) if self._ws is not None else ART_OK
+        return last_error(self._ws, self._ws.numel()) if self._ws is not None else ART_OK

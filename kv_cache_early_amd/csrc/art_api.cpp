@@ -7,6 +7,8 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <vector>
+#include <algorithm>
 
 #include "art.h"
 #include "art_internal.h"
@@ -81,12 +83,12 @@ art::WsLayout layout(const art_shape& s, const art_params& p, int chunk, int max
   const int G = s.num_q_heads / s.num_kv_heads;
   const int d = s.head_dim;
   L.header = round256(sizeof(art::WsHeader));
-  L.unit_state = round256(sizeof(art::UnitState) * (size_t)std::max<int64_t>(units, 1));
+  L.items = round256(sizeof(art::ItemState) * (size_t)std::max<int64_t>(units * max_chunks, 1));
   L.partials = max_chunks > 1 ? round256((size_t)units * max_chunks * G * (d + 2) * sizeof(float)) : 0;
   const size_t carry_bytes = 16 + (size_t)G * 4 + (size_t)G * 8 + (size_t)G * (d / kProbeStride) * 8;
   L.carries = (max_chunks > 1 && p.mode == ART_MODE_ART) ? round256((size_t)units * max_chunks * round256(carry_bytes)) : 0;
   (void)chunk;
-  L.total = L.header + L.unit_state + L.partials + L.carries;
+  L.total = L.header + L.items + L.partials + L.carries;
   return L;
 }
 
@@ -164,20 +166,29 @@ art_status art_decode(const art_shape* shape, const art_params* params, const vo
   a.blocks_issued = blocks_issued;
   char* w = static_cast<char*>(workspace);
   a.ws = reinterpret_cast<art::WsHeader*>(w);
-  a.unit_state = reinterpret_cast<art::UnitState*>(w + L.header);
-  a.partials = L.partials ? reinterpret_cast<float*>(w + L.header + L.unit_state) : nullptr;
-  a.carries = L.carries ? static_cast<void*>(w + L.header + L.unit_state + L.partials) : nullptr;
+  a.items = reinterpret_cast<art::ItemState*>(w + L.header);
+  a.partials = L.partials ? reinterpret_cast<float*>(w + L.header + L.items) : nullptr;
+  a.carries = L.carries ? static_cast<void*>(w + L.header + L.items + L.partials) : nullptr;
   a.spin_limit = 1u << 22;
 
   hipError_t e = art::launch(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ART_OK : ART_ERR_HIP;
 }
 
-art_status art_last_error(const void* workspace) {
-  if (!workspace) return ART_ERR_INVALID_ARG;
-  int32_t err = 0;
-  if (hipMemcpy(&err, workspace, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess) return ART_ERR_HIP;
-  return static_cast<art_status>(err);
+art_status art_last_error(const void* workspace, size_t workspace_bytes) {
+  if (!workspace || workspace_bytes < sizeof(art::WsHeader)) return ART_ERR_INVALID_ARG;
+  art::WsHeader h;
+  if (hipMemcpy(&h, workspace, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess) return ART_ERR_HIP;
+  if (h.magic != art::kWsMagic) return ART_OK;  // no launch has used this workspace
+  const size_t off = round256(sizeof(art::WsHeader));
+  if (h.n_items < 0 || off + (size_t)h.n_items * sizeof(art::ItemState) > workspace_bytes) return ART_ERR_WORKSPACE;
+  std::vector<art::ItemState> items((size_t)h.n_items);
+  if (h.n_items > 0 && hipMemcpy(items.data(), static_cast<const char*>(workspace) + off,
+                                 items.size() * sizeof(art::ItemState), hipMemcpyDeviceToHost) != hipSuccess)
+    return ART_ERR_HIP;
+  int32_t worst = ART_OK;
+  for (const art::ItemState& it : items) worst = std::max(worst, it.status);
+  return static_cast<art_status>(worst);
 }
 
 const char* art_status_string(art_status status) {

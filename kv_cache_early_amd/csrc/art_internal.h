@@ -7,19 +7,20 @@
 
 namespace art {
 
-// Workspace header: device-side error word and the split ticket counter.
+// Workspace header, written by work item 0 of every decode launch.  Every
+// work item also writes its own ItemState on every launch, so a workspace
+// needs no initialisation and a call enqueues no memset.
+constexpr uint32_t kWsMagic = 0x31545241u;  // "ART1"
 struct alignas(256) WsHeader {
-  int32_t error;       // art_status recorded on the device (max wins)
-  uint32_t ticket;     // ordered work-item dispenser (split ART mode)
+  uint32_t magic;      // kWsMagic once a launch has written the header
+  int32_t n_items;     // work items of that launch (ItemState entries)
   int32_t pad[62];
 };
 
-// Per-unit state, one per (batch, kv head).
-struct UnitState {
-  int32_t status;      // 0 running, 1 stopped
-  int32_t stop_chunk;  // chunk that holds the stop, -1 if none yet
-  int32_t stop_idx;    // traversal blocks processed at the stop
-  int32_t issued;      // blocks whose loads were issued (all chunks)
+// Per work item (grid index), written unconditionally at its end.
+struct ItemState {
+  int32_t status;      // art_status seen by the item (ART_OK or a device error)
+  int32_t issued;      // blocks whose loads the item issued
 };
 
 // Look-back carry published by a chunk for its successor (split ART mode):
@@ -61,7 +62,7 @@ struct KernelArgs {
   int32_t* blocks_issued;
   // workspace
   WsHeader* ws;
-  UnitState* unit_state;
+  ItemState* items;    // [max_chunks][units], grid order
   float* partials;     // [units][max_chunks][G][d + 2]  (m, l, acc[d])
   void* carries;       // [units][max_chunks] Carry<G, d/4>
   uint32_t spin_limit; // look-back polls before ART_ERR_TIMEOUT
@@ -69,7 +70,7 @@ struct KernelArgs {
 
 // Workspace layout for a given shape (bytes, 256-aligned pieces).
 struct WsLayout {
-  size_t header, unit_state, partials, carries, total;
+  size_t header, items, partials, carries, total;
 };
 
 hipError_t launch(const KernelArgs& a, hipStream_t stream);

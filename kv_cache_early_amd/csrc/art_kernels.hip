@@ -360,6 +360,7 @@ struct alignas(16) EpilogueLds {     // per-wave final state (reuses the V slabs
   float m[kMaxWaves][4];
   float l[kMaxWaves][4];
   int issued[kMaxWaves];
+  int bad[kMaxWaves];
   float acc[kMaxWaves][D][4];        // [wave][dim][head]
 };
 
@@ -385,6 +386,10 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
 
   // ---- work item --------------------------------------------------------
   const int n_units = a.batch * a.hkv;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    a.ws->magic = kWsMagic;
+    a.ws->n_items = (int)gridDim.x;
+  }
   const int unit = blockIdx.x % n_units;
   const int chunk = blockIdx.x / n_units;
   const int b = unit / a.hkv;
@@ -449,7 +454,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
     const int zp = uni(R.zero_pos);
     __syncthreads();
     if (bad) {
-      if (threadIdx.x == 0) atomicMax(&a.ws->error, (int)ART_ERR_DEVICE_INPUT);
+      if (threadIdx.x == 0) a.items[blockIdx.x] = ItemState{ART_ERR_DEVICE_INPUT, 0};
       if (chunk == 0) {
         for (int i = threadIdx.x; i < G * D; i += blockDim.x) out_rows[i] = 0.f;
         if (threadIdx.x == 0) {
@@ -461,9 +466,11 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
     }
     u.zero_pos = zp == 0x7fffffff ? -1 : zp;
   }
-  if (bad_input && chunk == 0 && threadIdx.x == 0) atomicMax(&a.ws->error, (int)ART_ERR_DEVICE_INPUT);
-
-  if (u.n_trav <= 0) {  // nothing to attend to: out = 0, stop = 0
+  const int item_status = bad_input ? ART_ERR_DEVICE_INPUT : ART_OK;
+  if (u.n_trav <= 0 || t_begin >= u.n_trav) {  // nothing (left) to attend to
+    if (threadIdx.x == 0) a.items[blockIdx.x] = ItemState{item_status, 0};
+  }
+  if (u.n_trav <= 0) {  // out = 0, stop = 0
     if (chunk == 0) {
       for (int i = threadIdx.x; i < G * D; i += blockDim.x) out_rows[i] = 0.f;
       if (threadIdx.x == 0) {
@@ -843,7 +850,10 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
     E.m[wid][lane] = m_c;
     E.l[wid][lane] = l_c;
   }
-  if (lane == 0) E.issued[wid] = issued;
+  if (lane == 0) {
+    E.issued[wid] = issued;
+    E.bad[wid] = bad_page;
+  }
   __syncthreads();
   for (int o = threadIdx.x; o < G * D; o += blockDim.x) {
     const int g = o / D, dim = o % D;
@@ -869,16 +879,17 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
     }
   }
   if (threadIdx.x == 0) {
-    int tot = 0;
-    for (int w2 = 0; w2 < W; ++w2) tot += E.issued[w2];
+    int tot = 0, bad = 0;
+    for (int w2 = 0; w2 < W; ++w2) {
+      tot += E.issued[w2];
+      bad |= E.bad[w2];
+    }
+    a.items[blockIdx.x] = ItemState{bad ? (int)ART_ERR_DEVICE_INPUT : item_status, tot};
     if (single) {
       a.stop_idx[unit] = stop;
       if (a.blocks_issued) a.blocks_issued[unit] = tot;
-    } else {
-      atomicAdd(&a.unit_state[unit].issued, tot);
     }
   }
-  if (bad_page && lane == 0) atomicMax(&a.ws->error, (int)ART_ERR_DEVICE_INPUT);
 }
 
 // ---------------------------------------------------------------------------
@@ -920,25 +931,11 @@ __global__ __launch_bounds__(kWave) void art_combine_kernel(KernelArgs a) {
   }
   if (threadIdx.x == 0) {
     a.stop_idx[unit] = n_trav;
-    if (a.blocks_issued) a.blocks_issued[unit] = a.unit_state[unit].issued;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// workspace initialisation (a kernel, not a memset, so the call stays safe
-// to capture into a graph)
-// ---------------------------------------------------------------------------
-__global__ void art_init_kernel(WsHeader* ws, UnitState* st, int n_units) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i == 0) {
-    ws->error = 0;
-    ws->ticket = 0;
-  }
-  if (i < n_units) {
-    st[i].status = 0;
-    st[i].stop_chunk = -1;
-    st[i].stop_idx = 0;
-    st[i].issued = 0;
+    if (a.blocks_issued) {
+      int tot = 0;
+      for (int k = 0; k < n_chunks; ++k) tot += a.items[(size_t)k * a.batch * a.hkv + unit].issued;
+      a.blocks_issued[unit] = tot;
+    }
   }
 }
 
@@ -964,9 +961,6 @@ static hipError_t launch_g(const KernelArgs& a, int grid, int waves, hipStream_t
 
 hipError_t launch(const KernelArgs& a, hipStream_t s) {
   const int n_units = a.batch * a.hkv;
-  hipLaunchKernelGGL(art_init_kernel, dim3((n_units + 255) / 256), dim3(256), 0, s, a.ws, a.unit_state, n_units);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int grid = n_units * a.max_chunks;
   const int waves = a.waves < 1 ? 1 : (a.waves > kMaxWaves ? kMaxWaves : a.waves);
   const int G = a.hq / a.hkv;

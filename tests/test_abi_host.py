@@ -107,6 +107,12 @@ def test_empty_batch_is_a_no_op():
                 stop=None) == art.ART_OK
 
 
+def test_last_error_rejects_without_touching_the_device():
+    lib = art.load()
+    assert lib.art_last_error(None, 4096) == art.ART_ERR_INVALID_ARG
+    assert lib.art_last_error(FAKE * 16, 64) == art.ART_ERR_INVALID_ARG
+
+
 def test_workspace_size():
     s, p = good_shape(), good_params()
     n = art.workspace_size(s, p)

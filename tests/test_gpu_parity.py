@@ -150,6 +150,23 @@ def test_kept_list_out_of_range_is_reported(torch_cuda):
     assert rep.ok(), str(rep)
 
 
+def test_device_error_is_per_call(torch_cuda):
+    """A bad call's device error does not leak into the next call on the same workspace."""
+    from kv_cache_early_amd import ArtDecoder, art
+    dec = ArtDecoder()
+    w = make_workload(scaled(5, "B"))
+    bad = make_workload(scaled(5, "B"))
+    bad.kept_blocks = bad.kept_blocks.copy()
+    bad.kept_blocks[1, 0, 0] = -3
+    log("[case] bad kept list, then a good call on the same workspace")
+    _, _, _, e1 = run_gpu(bad, decoder=dec)
+    assert e1 == art.ART_ERR_DEVICE_INPUT
+    out, stop, _, e2 = run_gpu(w, decoder=dec)
+    assert e2 == art.ART_OK
+    rep, _ = compare(w, out, stop)
+    assert rep.ok(), str(rep)
+
+
 # ---------------------------------------------------------------------------
 # full-size configurations: every unit on the GPU, sampled units in the oracle
 # ---------------------------------------------------------------------------
