@@ -124,6 +124,19 @@ __device__ __forceinline__ float col_sum(float x) {
   const auto t = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
   return u2f(t[0]) + u2f(t[1]);
 }
+// The same all-reduce over the four rows for an fp64 value (both halves swapped).
+__device__ __forceinline__ double col_sum_d(double x) {
+  uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const auto sl = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+  const auto sh = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+  x = __builtin_bit_cast(double, ((uint64_t)sh[0] << 32) | sl[0]) +
+      __builtin_bit_cast(double, ((uint64_t)sh[1] << 32) | sl[1]);
+  u = __builtin_bit_cast(uint64_t, x);
+  const auto tl = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+  const auto th = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+  return __builtin_bit_cast(double, ((uint64_t)th[0] << 32) | tl[0]) +
+         __builtin_bit_cast(double, ((uint64_t)th[1] << 32) | tl[1]);
+}
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 __device__ __forceinline__ float lane_f(float x, int l) { return u2f(__builtin_amdgcn_readlane(f2u(x), l)); }
 
@@ -154,13 +167,15 @@ __device__ __forceinline__ double recip_d(double x) {
 struct Criterion {
   double hi, lo, c2;   // (1+tau)^2, (1-tau)^2, (1-phi)^2, computed on the host
   bool tau_lt1, phi_le1;
+  // Non-short-circuit forms (bitwise on the comparison results): no
+  // branches on the round's critical path.
   __device__ bool scale_ok(double a2, double b2) const {
-    return b2 < hi * a2 && (!tau_lt1 || b2 > lo * a2);
+    return (b2 < hi * a2) & ((!tau_lt1) | (b2 > lo * a2));
   }
   __device__ bool dir_ok(double a2, double b2, double p) const {
     const double r = c2 * a2 * b2;
-    if (phi_le1) return p > 0.0 && p * p > r;
-    return p >= 0.0 || p * p < r;
+    const double pp = p * p;
+    return (phi_le1 & (p > 0.0) & (pp > r)) | ((!phi_le1) & ((p >= 0.0) | (pp < r)));
   }
 };
 
@@ -348,10 +363,15 @@ struct alignas(16) Summary {   // one block, published for the round
   float l[4];                  // softmax mass per head relative to m
   float ps[D / 4][4];          // sums on probe dim 4p, per head, relative to m
 };
+struct alignas(16) Check {     // one position's stability test, published by its wave
+  double stt;                  // |x^(t)|^2
+  int stable;                  // the check at this position passed
+  int pad;
+};
 template <int G, int D>
 struct alignas(16) RoundLds {
   Summary<D> sum[2][kMaxWaves];      // by round parity
-  double crit[2][kMaxWaves][4][2];   // by round parity: per position, per head (a, c)
+  Check chk[2][kMaxWaves];            // by round parity: per position
   int bad;
   int zero_pos;
 };
@@ -378,20 +398,23 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
   __shared__ alignas(16) uint8_t vbuf[kMaxWaves][kVSlab];
   static_assert(sizeof(EpilogueLds<G, D>) <= sizeof(vbuf), "epilogue state must fit the V slabs");
 
-  const int W = blockDim.x >> 6;
-  const int wid = uni(threadIdx.x >> 6);
+  constexpr int W = kMaxWaves;  // waves per work item
+  const int tid = threadIdx.x;
+  const int wid = uni(tid >> 6);
   const int lane = threadIdx.x & 63;
   const int lg = lane >> 4;
   const int c = lane & 15;
 
   // ---- work item --------------------------------------------------------
   const int n_units = a.batch * a.hkv;
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
+  const int n_items = n_units * a.max_chunks;
+  const int item = blockIdx.x;
+  if (item == 0 && tid == 0) {
     a.ws->magic = kWsMagic;
-    a.ws->n_items = (int)gridDim.x;
+    a.ws->n_items = n_items;
   }
-  const int unit = blockIdx.x % n_units;
-  const int chunk = blockIdx.x / n_units;
+  const int unit = item % n_units;
+  const int chunk = item / n_units;
   const int b = unit / a.hkv;
   const int h = unit % a.hkv;
 
@@ -435,13 +458,13 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
 
   // ---- kept list: validate (device input) and find block 0 --------------
   if (u.kept) {
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
       R.bad = (u.n_trav < 0 || u.n_trav > a.max_kept) ? 1 : 0;
       R.zero_pos = 0x7fffffff;
     }
     __syncthreads();
     if (u.n_trav >= 0 && u.n_trav <= a.max_kept) {
-      for (int i = threadIdx.x; i < u.n_trav; i += blockDim.x) {
+      for (int i = tid; i < u.n_trav; i += kWave * kMaxWaves) {
         const int e = u.kept[i];
         bool lb = e < 0 || e >= u.n_blocks;
         if (a.order != ART_ORDER_GIVEN && i > 0) lb |= e <= u.kept[i - 1];
@@ -454,10 +477,10 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
     const int zp = uni(R.zero_pos);
     __syncthreads();
     if (bad) {
-      if (threadIdx.x == 0) a.items[blockIdx.x] = ItemState{ART_ERR_DEVICE_INPUT, 0};
+      if (tid == 0) a.items[item] = ItemState{ART_ERR_DEVICE_INPUT, 0};
       if (chunk == 0) {
-        for (int i = threadIdx.x; i < G * D; i += blockDim.x) out_rows[i] = 0.f;
-        if (threadIdx.x == 0) {
+        for (int i = tid; i < G * D; i += kWave * kMaxWaves) out_rows[i] = 0.f;
+        if (tid == 0) {
           a.stop_idx[unit] = -1;
           if (a.blocks_issued) a.blocks_issued[unit] = 0;
         }
@@ -468,12 +491,12 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
   }
   const int item_status = bad_input ? ART_ERR_DEVICE_INPUT : ART_OK;
   if (u.n_trav <= 0 || t_begin >= u.n_trav) {  // nothing (left) to attend to
-    if (threadIdx.x == 0) a.items[blockIdx.x] = ItemState{item_status, 0};
+    if (tid == 0) a.items[item] = ItemState{item_status, 0};
   }
   if (u.n_trav <= 0) {  // out = 0, stop = 0
     if (chunk == 0) {
-      for (int i = threadIdx.x; i < G * D; i += blockDim.x) out_rows[i] = 0.f;
-      if (threadIdx.x == 0) {
+      for (int i = tid; i < G * D; i += kWave * kMaxWaves) out_rows[i] = 0.f;
+      if (tid == 0) {
         a.stop_idx[unit] = 0;
         if (a.blocks_issued) a.blocks_issued[unit] = 0;
       }
@@ -685,24 +708,45 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
             pl[jp][2 * hh] = pk_bf16(S[nt][0] - bf16_lo(w0), S[nt][1] - bf16_hi(w0));
             pl[jp][2 * hh + 1] = pk_bf16(S[nt][2] - bf16_lo(w1), S[nt][3] - bf16_hi(w1));
           }
+        // B operand of (tile pair jp, dim tile dt): two transposed reads,
+        // tokens of tile 2jp then tile 2jp+1, dims 16dt + c
+        auto read_b = [&](int jp, int dt, bool mask) -> bf16x8 {
+          const auto* pv = vb + tr_lane + (((uint32_t)(32 * dt)) ^ tr_x);
+          s16x4 v0 = lds_read_tr(pv + (2 * jp) * 4096);
+          s16x4 v1 = lds_read_tr(pv + (2 * jp + 1) * 4096);
+          if (mask) {
 #pragma unroll
-        for (int jp = 0; jp < 2; ++jp) {
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            const auto* pv = vb + tr_lane + (((uint32_t)(32 * dt)) ^ tr_x);
-            s16x4 v0 = lds_read_tr(pv + (2 * jp) * 4096);
-            s16x4 v1 = lds_read_tr(pv + (2 * jp + 1) * 4096);
-            if (partial) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                if (32 * jp + tb + e >= nvalid) v0[e] = 0;
-                if (32 * jp + 16 + tb + e >= nvalid) v1[e] = 0;
-              }
+            for (int e = 0; e < 4; ++e) {
+              if (32 * jp + tb + e >= nvalid) v0[e] = 0;
+              if (32 * jp + 16 + tb + e >= nvalid) v1[e] = 0;
             }
-            const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-            bacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ph[jp]), bv, bacc[dt], 0, 0, 0);
-            bacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pl[jp]), bv, bacc[dt], 0, 0, 0);
           }
+          return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        // per tile pair and group of four dim tiles: the reads first, then the
+        // hi MFMAs, then the lo MFMAs (four independent accumulator chains)
+        auto pv_pass = [&](int jp, bool mask) {
+#pragma unroll
+          for (int d0 = 0; d0 < NDT; d0 += 4) {
+            bf16x8 bv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bv[i] = read_b(jp, d0 + i, mask);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              bacc[d0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ph[jp]), bv[i],
+                                                                     bacc[d0 + i], 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              bacc[d0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pl[jp]), bv[i],
+                                                                     bacc[d0 + i], 0, 0, 0);
+          }
+        };
+        if (!partial) {
+          pv_pass(0, false);
+          pv_pass(1, false);
+        } else {  // the last block of a sequence: zero the tail tokens' values
+          pv_pass(0, true);
+          pv_pass(1, true);
         }
       } else {
         // fp32: k = lg of step (nt, r) is token 16nt + 4lg + r; B element
@@ -744,75 +788,92 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
       }
       lds_barrier();
       // ---- the round's positions, in order ------------------------------------
-      // Every wave merges all block summaries of the round onto the prefix
-      // state on the probe dims (lane (lg, c): head lg if lg < G, probe dims
-      // of chunk c), which keeps that state identical in all waves.  With
-      // P^(t) the prefix numerators and l^(t) the prefix mass of a head,
-      // x^(t) = P^(t) / l^(t).  At its own position a wave also forms, per
-      // head, A = P^(t).P^(t) and C = P^(t).P^(t-1) (row sums), scales them
-      // to a = A / l^(t)^2 and c = C / (l^(t) l^(t-1)) and publishes them; the
-      // ratio P/l is scale free, so P^(t-1), l^(t-1) keep their own running-
-      // max scale.  After a second barrier every wave sums the heads in a
-      // fixed order, so all reach the same |x^(t)|^2, x^(t).x^(t-1) and the
-      // same decision.
-      double own_a = 0.0, own_c = 0.0, l_before = 0.0, l_after = 1.0;
+      // Every wave merges the round's block summaries, in traversal order,
+      // onto the carried prefix state on the probe dims (lane (lg, c): head
+      // lg if lg < G, probe dims of chunk c); all waves keep the same state.
+      // All terms are first put on the round's common maximum M, so the scale
+      // factors are independent of one another.  With P^(t) the prefix
+      // numerators and l^(t) the prefix mass of a head, x^(t) = P^(t) / l^(t)
+      // (the ratio is scale free).  A wave keeps the per-lane parts of
+      // |P|^2 at its own position and the one before, and of P^(t).P^(t-1)
+      // at its own, then forms |x^(t)|^2, |x^(t-1)|^2 and x^(t).x^(t-1)
+      // (per-head row sums, divided by that head's mass, summed over heads)
+      // and runs the two tests for its own position only.
+      float mk[kMaxWaves];
+      double lk[kMaxWaves], pk[kMaxWaves][PPC];
+      float M = mP;
 #pragma unroll
-      for (int w2 = 0; w2 < kMaxWaves; ++w2) {
-        if (w2 < n_act) {
-          const Summary<D>& s2 = R.sum[parity][w2];
-          const float mb = s2.m[hg];
-          const float M = fmaxf(mP, mb);
-          const double sP = (double)__builtin_amdgcn_exp2f(mP - M);
-          const double sB = (double)__builtin_amdgcn_exp2f(mb - M);
-          const bool mine = w2 == wid;
-          if (mine) l_before = lP;
-          lP = fma(lP, sP, (double)s2.l[hg] * sB);
-          if (mine) l_after = lP;
-          mP = M;
+      for (int k = 0; k < kMaxWaves; ++k) {
+        const Summary<D>& s2 = R.sum[parity][k];
+        const bool on = k < n_act;  // slots past the round's end hold stale data
+        mk[k] = on ? s2.m[hg] : -INFINITY;
+        lk[k] = on ? (double)s2.l[hg] : 0.0;
 #pragma unroll
-          for (int k = 0; k < PPC; ++k) {
-            const double p = fma(pP[k], sP, (double)s2.ps[c * PPC + k][hg] * sB);
-            if (mine && lg < G) {
-              own_a = fma(p, p, own_a);
-              own_c = fma(p, pP[k], own_c);
-            }
-            pP[k] = p;
-          }
-        }
+        for (int i = 0; i < PPC; ++i) pk[k][i] = on ? (double)s2.ps[c * PPC + i][hg] : 0.0;
+        M = fmaxf(M, mk[k]);
       }
+      const double sP = (double)__builtin_amdgcn_exp2f(mP - M);
+      double L = lP * sP, P[PPC];
+#pragma unroll
+      for (int i = 0; i < PPC; ++i) P[i] = pP[i] * sP;
+      double a_own = 0.0, c_own = 0.0, a_prev = 0.0, L_own = 1.0, L_prev = 0.0;
+#pragma unroll
+      for (int k = 0; k < kMaxWaves; ++k) {
+        const double sk = (double)__builtin_amdgcn_exp2f(mk[k] - M);  // 0 past the round's end
+        double pa = 0.0, pc = 0.0;
+#pragma unroll
+        for (int i = 0; i < PPC; ++i) {
+          const double pn = fma(pk[k][i], sk, P[i]);
+          pa = fma(pn, pn, pa);
+          pc = fma(pn, P[i], pc);
+          P[i] = pn;
+        }
+        const double Ln = fma(lk[k], sk, L);
+        const bool own = k == wid, before = k + 1 == wid;
+        a_own = own ? pa : a_own;
+        c_own = own ? pc : c_own;
+        L_prev = own ? L : L_prev;
+        L_own = own ? Ln : L_own;
+        a_prev = before ? pa : a_prev;
+        L = Ln;
+      }
+      mP = M;
+      lP = L;
+#pragma unroll
+      for (int i = 0; i < PPC; ++i) pP[i] = P[i];
       if (active) {
-        own_a = row_sum_d(own_a);
-        own_c = row_sum_d(own_c);
-        const double it = recip_d(l_after);
-        const double ip = l_before > 0.0 ? recip_d(l_before) : 0.0;
-        if (c == 0 && lg < G) {
-          R.crit[parity][wid][lg][0] = own_a * (it * it);
-          R.crit[parity][wid][lg][1] = own_c * (it * ip);
+        const double keep = lg < G ? 1.0 : 0.0;  // rows past G carry head 0 again
+        const double io = recip_d(L_own);
+        const double ip = L_prev > 0.0 ? recip_d(L_prev) : 0.0;
+        const double stt = col_sum_d(row_sum_d(a_own) * (io * io * keep));
+        const double stp = col_sum_d(row_sum_d(c_own) * (io * ip * keep));
+        const double spr = wid == 0 ? stt_last : col_sum_d(row_sum_d(a_prev) * (ip * ip * keep));
+        const bool stable =
+            (spr > 0.0) & (stt > 0.0) & crit.scale_ok(spr, stt) & crit.dir_ok(spr, stt, stp);
+        if (lane == 0) {
+          R.chk[parity][wid].stt = stt;
+          R.chk[parity][wid].stable = stable;
         }
       }
       lds_barrier();
-      // ---- stability checks and patience counter, in traversal order -----------
-      double stt_prev = stt_last;
+      // ---- patience counter over the round's checks, in traversal order ---------
+      int sbits = 0;  // bit w2: the check at position t0 + w2 passed
 #pragma unroll
       for (int w2 = 0; w2 < kMaxWaves; ++w2) {
-        if (w2 < n_act) {
-          double stt = 0.0, stp = 0.0;
+        const Check ck = R.chk[parity][w2];
+        sbits |= (ck.stable & 1) << w2;
+        if (w2 + 1 == n_act) stt_last = ck.stt;
+      }
+      sbits = uni(sbits);
+      // a check exists from the second traversal block on
 #pragma unroll
-          for (int g = 0; g < G; ++g) {
-            stt += R.crit[parity][w2][g][0];
-            stp += R.crit[parity][w2][g][1];
-          }
-          const int cnt = t0 + w2 + 1;
-          if (cnt >= 2 && stop_round < 0) {  // a check exists from the second block on
-            const bool stable =
-                stt_prev > 0.0 && stt > 0.0 && crit.scale_ok(stt_prev, stt) && crit.dir_ok(stt_prev, stt, stp);
-            counter = stable ? counter + 1 : 0;
-            if (counter >= a.patience) stop_round = cnt;
-          }
-          stt_prev = stt;
+      for (int w2 = 0; w2 < kMaxWaves; ++w2) {
+        const int cnt = t0 + w2 + 1;
+        if (w2 < n_act && cnt >= 2 && stop_round < 0) {
+          counter = ((sbits >> w2) & 1) ? counter + 1 : 0;
+          if (counter >= a.patience) stop_round = cnt;
         }
       }
-      stt_last = stt_prev;
       stop_round = uni(stop_round);
       parity ^= 1;
     }
@@ -855,7 +916,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
     E.bad[wid] = bad_page;
   }
   __syncthreads();
-  for (int o = threadIdx.x; o < G * D; o += blockDim.x) {
+  for (int o = tid; o < G * D; o += kWave * kMaxWaves) {
     const int g = o / D, dim = o % D;
     float M = -INFINITY;
     for (int w2 = 0; w2 < W; ++w2)
@@ -878,13 +939,13 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
       }
     }
   }
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     int tot = 0, bad = 0;
     for (int w2 = 0; w2 < W; ++w2) {
       tot += E.issued[w2];
       bad |= E.bad[w2];
     }
-    a.items[blockIdx.x] = ItemState{bad ? (int)ART_ERR_DEVICE_INPUT : item_status, tot};
+    a.items[item] = ItemState{bad ? (int)ART_ERR_DEVICE_INPUT : item_status, tot};
     if (single) {
       a.stop_idx[unit] = stop;
       if (a.blocks_issued) a.blocks_issued[unit] = tot;
@@ -944,7 +1005,8 @@ __global__ __launch_bounds__(kWave) void art_combine_kernel(KernelArgs a) {
 // ---------------------------------------------------------------------------
 template <int DT, int G, bool PAGED>
 static hipError_t launch_t(const KernelArgs& a, int grid, int waves, hipStream_t s) {
-  hipLaunchKernelGGL((art_decode_kernel<DT, G, PAGED>), dim3(grid), dim3(kWave * waves), 0, s, a);
+  (void)waves;
+  hipLaunchKernelGGL((art_decode_kernel<DT, G, PAGED>), dim3(grid), dim3(kWave * kMaxWaves), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.max_chunks > 1) {
