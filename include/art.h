@@ -93,7 +93,13 @@ typedef struct {
   int32_t order;         /* art_order                                        */
   int32_t mode;          /* art_mode                                         */
   int32_t split_blocks;  /* blocks per split-KV chunk; 0 = library's choice,
-                            a value >= T' means one chunk per unit           */
+                            a value >= T' means one chunk per unit.  In ART
+                            mode, a value below T' selects ordered split ART
+                            (chunks of min(round4(split_blocks), 32) blocks:
+                            a speculative pass per chunk, a look-back replay
+                            of the stop rule on the predecessor's carry, and
+                            a recompute of the chunk holding the stop);
+                            blocks_issued then counts the re-read blocks     */
 } art_params;
 
 typedef struct {

@@ -60,15 +60,33 @@ art_status validate(const art_shape* sp, const art_params* pp) {
   return ART_OK;
 }
 
-// Traversal blocks per work item.  ART mode walks each unit in one work item
-// (exact sequential stopping); full mode splits units into chunks so that
-// about kTargetItems workgroups balance uneven context lengths across the
-// compute units (chunks of at least 32 blocks, multiples of the wave count).
+// Traversal blocks per work item.
+//   full mode: chunks sized so that about kTargetItems workgroups balance
+//     uneven context lengths across the compute units (at least 32 blocks,
+//     multiples of the wave count);
+//   ART mode: one work item per unit (in-round sequential stopping) when
+//     there are enough units to fill the chip; otherwise chunks of
+//     kSplitArtBlocks with look-back (ordered split ART).  A caller's
+//     split_blocks is honoured, rounded up to the wave count and capped at
+//     kSplitArtBlocks (the look-back replay handles at most that many).
 constexpr int64_t kTargetItems = 4096;
 constexpr int kWavesPerItem = 4;
+// Fewer units than this: split ART by default.  Zero for now: the split path
+// is correct but its look-back chain is still slower than one work item per
+// unit on the measured configurations; callers can ask for it explicitly.
+constexpr int64_t kSplitArtUnits = 0;
+constexpr int kSplitArtBlocks = 32;
 int chunk_blocks(const art_shape& s, const art_params& p) {
   const int64_t tmax = std::max<int64_t>(1, max_traversal(s));
-  if (p.mode == ART_MODE_ART) return (int)tmax;
+  if (p.mode == ART_MODE_ART) {
+    const int64_t units = (int64_t)s.batch * s.num_kv_heads;
+    int64_t c;
+    if (p.split_blocks > 0)
+      c = p.split_blocks >= tmax ? tmax : std::min<int64_t>((p.split_blocks + 3) / 4 * 4, kSplitArtBlocks);
+    else
+      c = units >= kSplitArtUnits ? tmax : kSplitArtBlocks;
+    return (int)std::min<int64_t>(c, tmax);
+  }
   if (p.split_blocks > 0) return (int)std::min<int64_t>(p.split_blocks, tmax);
   const int64_t units = std::max<int64_t>(1, (int64_t)s.batch * s.num_kv_heads);
   int64_t c = (tmax * units + kTargetItems - 1) / kTargetItems;
@@ -85,10 +103,15 @@ art::WsLayout layout(const art_shape& s, const art_params& p, int chunk, int max
   L.header = round256(sizeof(art::WsHeader));
   L.items = round256(sizeof(art::ItemState) * (size_t)std::max<int64_t>(units * max_chunks, 1));
   L.partials = max_chunks > 1 ? round256((size_t)units * max_chunks * G * (d + 2) * sizeof(float)) : 0;
-  const size_t carry_bytes = 16 + (size_t)G * 4 + (size_t)G * 8 + (size_t)G * (d / kProbeStride) * 8;
-  L.carries = (max_chunks > 1 && p.mode == ART_MODE_ART) ? round256((size_t)units * max_chunks * round256(carry_bytes)) : 0;
+  const bool split_art = max_chunks > 1 && p.mode == ART_MODE_ART;
+  const size_t carry_bytes = d == 128 ? sizeof(art::CarryRec<128>) : sizeof(art::CarryRec<64>);
+  const size_t summary_bytes = d == 128 ? sizeof(art::Summary<128>) : sizeof(art::Summary<64>);
+  const int64_t tmax = std::max<int64_t>(1, max_traversal(s));
+  L.unit_stop = split_art ? round256((size_t)units * sizeof(int32_t)) : 0;
+  L.carries = split_art ? round256((size_t)units * max_chunks * carry_bytes) : 0;
+  L.summaries = split_art ? round256((size_t)units * tmax * summary_bytes) : 0;
   (void)chunk;
-  L.total = L.header + L.items + L.partials + L.carries;
+  L.total = L.header + L.items + L.partials + L.unit_stop + L.carries + L.summaries;
   return L;
 }
 
@@ -153,6 +176,8 @@ art_status art_decode(const art_shape* shape, const art_params* params, const vo
   a.mode = p.mode;
   a.chunk_blocks = chunk;
   a.max_chunks = max_chunks;
+  a.split_art = (p.mode == ART_MODE_ART && max_chunks > 1) ? 1 : 0;
+  a.max_trav = (int)tmax;
   a.waves = kWavesPerItem;
   a.q = q;
   a.k = k;
@@ -166,10 +191,17 @@ art_status art_decode(const art_shape* shape, const art_params* params, const vo
   a.blocks_issued = blocks_issued;
   char* w = static_cast<char*>(workspace);
   a.ws = reinterpret_cast<art::WsHeader*>(w);
-  a.items = reinterpret_cast<art::ItemState*>(w + L.header);
-  a.partials = L.partials ? reinterpret_cast<float*>(w + L.header + L.items) : nullptr;
-  a.carries = L.carries ? static_cast<void*>(w + L.header + L.items + L.partials) : nullptr;
-  a.spin_limit = 1u << 22;
+  size_t off = L.header;
+  a.items = reinterpret_cast<art::ItemState*>(w + off);
+  off += L.items;
+  a.partials = L.partials ? reinterpret_cast<float*>(w + off) : nullptr;
+  off += L.partials;
+  a.unit_stop = L.unit_stop ? reinterpret_cast<int32_t*>(w + off) : nullptr;
+  off += L.unit_stop;
+  a.carries = L.carries ? static_cast<void*>(w + off) : nullptr;
+  off += L.carries;
+  a.summaries = L.summaries ? static_cast<void*>(w + off) : nullptr;
+  a.spin_limit = 1u << 20;  // about a second of polling before ART_ERR_TIMEOUT
 
   hipError_t e = art::launch(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ART_OK : ART_ERR_HIP;

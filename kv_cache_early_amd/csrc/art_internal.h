@@ -14,27 +14,37 @@ constexpr uint32_t kWsMagic = 0x31545241u;  // "ART1"
 struct alignas(256) WsHeader {
   uint32_t magic;      // kWsMagic once a launch has written the header
   int32_t n_items;     // work items of that launch (ItemState entries)
-  int32_t pad[62];
+  uint32_t ticket;     // split ART: next work item to hand out (zeroed per call)
+  int32_t pad[61];
 };
 
 // Per work item (grid index), written unconditionally at its end.
 struct ItemState {
   int32_t status;      // art_status seen by the item (ART_OK or a device error)
-  int32_t issued;      // blocks whose loads the item issued
+  int32_t issued;      // blocks whose loads the item issued (-1: kept list rejected)
 };
 
-// Look-back carry published by a chunk for its successor (split ART mode):
-// the prefix state of the probe dims after the chunk's last block.
-template <int G, int NP>
-struct alignas(16) Carry {
-  int32_t flag;        // 0 not ready, 1 ready (running), 2 ready (stopped)
-  int32_t counter;     // consecutive stable checks at the end of the chunk
-  int32_t stop_idx;    // when stopped
-  int32_t pad;
-  float m[G];          // running max (log2 domain) per head
-  double l[G];         // running denominator per head
-  double pacc[G][NP];  // running numerators on the probe dims
+// Summary of one ART block on the probe dims (probe dim 4p of head g at
+// ps[p][g]), relative to the block's own score maximum m (log2 domain).
+template <int D>
+struct alignas(16) Summary {
+  float m[4];          // reference max per head
+  float l[4];          // softmax mass per head relative to m
+  float ps[D / 4][4];  // sums on the probe dims relative to m
 };
+
+// Split ART: prefix state of a unit after the last block of one chunk,
+// published for the next chunk (look-back).
+template <int D>
+struct alignas(16) CarryRec {
+  int32_t flag;        // 0 not yet; 1 ready (no stop so far); 2 stopped at or before this chunk's end
+  int32_t counter;     // consecutive stable checks at the chunk's end
+  double stt_last;     // |x|^2 at the chunk's last position
+  float m[4];          // reference max per head (log2 domain)
+  double l[4];         // prefix mass per head relative to m
+  double p[D / 4][4];  // prefix numerators on the probe dims relative to m
+};
+
 
 struct KernelArgs {
   // shape
@@ -45,6 +55,8 @@ struct KernelArgs {
   // squared forms of the thresholds (see the stability tests in the kernel)
   double crit_hi, crit_lo, crit_c2;  // (1+eps_scale)^2, (1-eps_scale)^2, (1-eps_dir)^2
   int32_t crit_tau_lt1, crit_phi_le1; // eps_scale < 1, eps_dir <= 1
+  int32_t split_art;     // ART mode with several chunks per unit (look-back)
+  int32_t max_trav;      // traversal blocks per unit bound (summary row stride)
   int32_t chunk_blocks;  // traversal blocks per work item
   int32_t max_chunks;    // work items per unit
   int32_t waves;         // waves per workgroup (one work item per workgroup)
@@ -63,14 +75,16 @@ struct KernelArgs {
   // workspace
   WsHeader* ws;
   ItemState* items;    // [max_chunks][units], grid order
+  int32_t* unit_stop;  // split ART: [units] traversal count at the stop, 0 while none
   float* partials;     // [units][max_chunks][G][d + 2]  (m, l, acc[d])
-  void* carries;       // [units][max_chunks] Carry<G, d/4>
+  void* carries;       // split ART: [units][max_chunks] CarryRec<d>
+  void* summaries;     // split ART: [units][max_trav] Summary<d>
   uint32_t spin_limit; // look-back polls before ART_ERR_TIMEOUT
 };
 
 // Workspace layout for a given shape (bytes, 256-aligned pieces).
 struct WsLayout {
-  size_t header, items, partials, carries, total;
+  size_t header, items, partials, unit_stop, carries, summaries, total;
 };
 
 hipError_t launch(const KernelArgs& a, hipStream_t stream);

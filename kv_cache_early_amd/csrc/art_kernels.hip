@@ -275,6 +275,19 @@ __device__ __forceinline__ s16x4 lds_read_tr(const __attribute__((address_space(
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
 
+// Coherent single accesses between workgroups on different XCDs (each XCD
+// has its own L2): relaxed system-scope atomics reach the point of coherence
+// one by one, so no cache-wide write-back or invalidation is needed.  A
+// writer waits for its stores to be acknowledged before it raises a flag.
+template <typename T>
+__device__ __forceinline__ T ld_sys(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+template <typename T>
+__device__ __forceinline__ void st_sys(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // Workgroup barrier that orders LDS only: waits for this wave's LDS traffic
 // and meets the other waves, without waiting for in-flight global loads (a
 // full __syncthreads() would drain the K/V prefetch).
@@ -357,12 +370,6 @@ __device__ __forceinline__ BlockAddr block_addr(const UnitView& u, int j, int& b
 // ---------------------------------------------------------------------------
 // LDS layout (one workgroup)
 // ---------------------------------------------------------------------------
-template <int D>
-struct alignas(16) Summary {   // one block, published for the round
-  float m[4];                  // reference max per head (log2 domain)
-  float l[4];                  // softmax mass per head relative to m
-  float ps[D / 4][4];          // sums on probe dim 4p, per head, relative to m
-};
 struct alignas(16) Check {     // one position's stability test, published by its wave
   double stt;                  // |x^(t)|^2
   int stable;                  // the check at this position passed
@@ -374,6 +381,22 @@ struct alignas(16) RoundLds {
   Check chk[2][kMaxWaves];            // by round parity: per position
   int bad;
   int zero_pos;
+  int ticket;                         // split ART: this workgroup's work item
+  int flag;                           // split ART: predecessor's carry flag / early stop
+};
+// Split ART look-back replay state (reuses the V slabs): the chunk's block
+// summaries transposed to [block][head][probe dim], |x|^2 per position and
+// the per-position stability bits.
+constexpr int kSplitMax = 32;  // chunk length the replay handles
+template <int D>
+struct alignas(16) ReplayLds {
+  float m[kSplitMax][4];
+  float l[kSplitMax][4];
+  float ps[kSplitMax][4][D / 4];
+  double stt[kSplitMax + 1];  // stt[j + 1] = |x|^2 at position j; stt[0] from the carry
+  int bits[kSplitMax];
+  int stop_local;             // blocks of the chunk up to and including the stop, -1 if none
+  int counter;
 };
 template <int G, int D>
 struct alignas(16) EpilogueLds {     // per-wave final state (reuses the V slabs)
@@ -387,7 +410,9 @@ struct alignas(16) EpilogueLds {     // per-wave final state (reuses the V slabs
 // ---------------------------------------------------------------------------
 // the decode kernel
 // ---------------------------------------------------------------------------
-template <int DT, int G, bool PAGED>
+// SPLIT: the ordered split-ART instantiation (ticket order, look-back replay,
+// recompute); the other instantiation serves full mode and single-chunk ART.
+template <int DT, int G, bool PAGED, bool SPLIT>
 __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(KernelArgs a) {
   using GE = Geo<DT>;
   constexpr int D = GE::D, ES = GE::ES, PPC = GE::PPC;
@@ -396,7 +421,11 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
   static_assert(ROW == kRowChunks * 16, "rows must be 16 chunks of 16 bytes");
   __shared__ RoundLds<G, D> R;
   __shared__ alignas(16) uint8_t vbuf[kMaxWaves][kVSlab];
-  static_assert(sizeof(EpilogueLds<G, D>) <= sizeof(vbuf), "epilogue state must fit the V slabs");
+  // the waves' final state is stashed above the replay state, so a split
+  // chunk can keep its pass-0 result in LDS while the replay runs
+  constexpr int kEpiOff = 32768;
+  static_assert(sizeof(ReplayLds<D>) <= kEpiOff, "replay state must fit below the stash");
+  static_assert(kEpiOff + sizeof(EpilogueLds<G, D>) <= sizeof(vbuf), "stash must fit the V slabs");
 
   constexpr int W = kMaxWaves;  // waves per work item
   const int tid = threadIdx.x;
@@ -408,7 +437,15 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
   // ---- work item --------------------------------------------------------
   const int n_units = a.batch * a.hkv;
   const int n_items = n_units * a.max_chunks;
-  const int item = blockIdx.x;
+  // Split ART hands out work items in ticket order, chunk-major: an item's
+  // predecessor chunk always holds a smaller ticket, so it is running or done
+  // when the item waits for its carry.
+  int item = blockIdx.x;
+  if constexpr (SPLIT) {
+    if (tid == 0) R.ticket = (int)atomicAdd(&a.ws->ticket, 1u);
+    __syncthreads();
+    item = uni(R.ticket);
+  }
   if (item == 0 && tid == 0) {
     a.ws->magic = kWsMagic;
     a.ws->n_items = n_items;
@@ -477,7 +514,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
     const int zp = uni(R.zero_pos);
     __syncthreads();
     if (bad) {
-      if (tid == 0) a.items[item] = ItemState{ART_ERR_DEVICE_INPUT, 0};
+      if (tid == 0) a.items[item] = ItemState{ART_ERR_DEVICE_INPUT, -1};
       if (chunk == 0) {
         for (int i = tid; i < G * D; i += kWave * kMaxWaves) out_rows[i] = 0.f;
         if (tid == 0) {
@@ -613,309 +650,520 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
   int bad_page = 0;
   int issued = 0;
   int stop = -1;  // traversal blocks processed at the stop (ART mode)
-  BlockAddr cur;
-  if (t_begin + wid < t_end) {
-    cur = block_addr<ROW, PAGED>(u, uni(block_at(u, a.order, t_begin + wid)), bad_page);
-    load_k(cur, 0.f);
-    load_v(cur);
-    ++issued;
-  }
-  int parity = 0;
+  // Split ART: pass 0 walks the whole chunk speculatively, storing block
+  // summaries; the look-back replay then decides the stop; if it lies inside
+  // the chunk, pass 1 recomputes the chunk's output up to the stop.
+  const bool split = SPLIT && art_mode && !single;
+  bool discard = false;  // the unit stopped before this chunk
+  int t_stop = t_end;
 
-  for (int t0 = t_begin; t0 < t_end; t0 += W) {
-    const int t = t0 + wid;
-    const bool active = t < t_end;
-    const int n_act = min(W, t_end - t0);
-    const int tn = t + W;
-    const bool has_next = tn < t_end;
-    BlockAddr nxt = cur;
-    if (has_next) nxt = block_addr<ROW, PAGED>(u, uni(block_at(u, a.order, tn)), bad_page);
-
-    float m_new = m_c, alpha = 1.f, lblk = 0.f;
-    f32x4 bacc[NDT];
-    if (active) {
-      const int nvalid = cur.nvalid;
-      // ---- scores S^T[token][head] = k_token . q_head --------------------------
-      wait_v_tied<kLoads>(kr);  // this block's K (its 16 V DMAs were issued after it)
-      f32x4 S[kTiles];
-      static_for<0, kTiles>([&](auto ntc) {
-        constexpr int nt = decltype(ntc)::value;
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (DT == ART_DT_BF16) {
+  // ---- split ART: look-back replay of the stop rule over this chunk -----------
+  // After pass 0 the chunk's block summaries are in the workspace.  Wait for
+  // the predecessor chunk's carry (the prefix state on the probe dims after
+  // its last block, its patience counter and |x|^2), then evaluate every
+  // position of the chunk at once: thread (j, g, hh) forms the prefix
+  // numerators of head g at positions j and j-1 on half hh of the probe dims,
+  // all terms on the chunk's common maximum; eight lanes per position give
+  // |x^(t)|^2 and x^(t).x^(t-1).  The patience scan then runs over the
+  // positions in order.  Returns the chunk's blocks up to and including the
+  // stop, or -1; publishes this chunk's carry (or the stop) for its successor.
+  // The waves' running state (m, l, output) goes to LDS, where the
+  // epilogue merges it; pass-0 results of a split chunk wait there during
+  // the replay.
+  auto& E = *reinterpret_cast<EpilogueLds<G, D>*>(&vbuf[0][kEpiOff]);
+  auto stash_waves = [&]() {
+    wait_vm<0>();  // speculative loads may still be landing in the V slabs
+    __syncthreads();
+    if (lane < 16) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[4 * nt + j]),
-                                                        __builtin_bit_cast(bf16x8, qv[j]), s, 0, 0, 0);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              s = __builtin_amdgcn_mfma_f32_16x16x4f32(u2f(kr[4 * nt + j][e]), u2f(qv[j][e]), s, 0, 0, 0);
-        }
-        S[nt] = s;
-      });
-      // ---- online softmax of head c % G against its running max ---------------
-      const int tb = 4 * lg;  // token of register 0 within each tile
-      float mx = -INFINITY;
-#pragma unroll
-      for (int nt = 0; nt < kTiles; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float sv = (16 * nt + tb + r < nvalid) ? S[nt][r] * c2 : -INFINITY;
-          S[nt][r] = sv;
-          mx = fmaxf(mx, sv);
-        }
-      mx = col_max(mx);
-      if (has_next) {
-        load_k(nxt, mx);
-        ++issued;
-      }
-      m_new = fmaxf(m_c, mx);
-      alpha = __builtin_amdgcn_exp2f(m_c - m_new);
-      float ls = 0.f;
-#pragma unroll
-      for (int nt = 0; nt < kTiles; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(S[nt][r] - m_new);
-          S[nt][r] = p;
-          ls += p;
-        }
-      lblk = col_sum(ls);
-      // ---- P V on MFMA ---------------------------------------------------------
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) bacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // V of this block: the 16 K loads of the next block (if any) were issued after it
-      if (has_next)
-        wait_vm<kLoads>();
-      else
-        wait_vm<0>();
-      const bool partial = nvalid < kBlk;  // weights of the tail tokens are 0; their V may be garbage
-      if constexpr (DT == ART_DT_BF16) {
-        // A operand of tile pair jp: element e < 4 is token 16(2jp) + 4lg + e,
-        // element e >= 4 is token 16(2jp+1) + 4lg + e - 4, split as P = hi + lo
-        u32x4 ph[2], pl[2];
-#pragma unroll
-        for (int jp = 0; jp < 2; ++jp)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int nt = 2 * jp + hh;
-            const uint32_t w0 = pk_bf16(S[nt][0], S[nt][1]);
-            const uint32_t w1 = pk_bf16(S[nt][2], S[nt][3]);
-            ph[jp][2 * hh] = w0;
-            ph[jp][2 * hh + 1] = w1;
-            pl[jp][2 * hh] = pk_bf16(S[nt][0] - bf16_lo(w0), S[nt][1] - bf16_hi(w0));
-            pl[jp][2 * hh + 1] = pk_bf16(S[nt][2] - bf16_lo(w1), S[nt][3] - bf16_hi(w1));
-          }
-        // B operand of (tile pair jp, dim tile dt): two transposed reads,
-        // tokens of tile 2jp then tile 2jp+1, dims 16dt + c
-        auto read_b = [&](int jp, int dt, bool mask) -> bf16x8 {
-          const auto* pv = vb + tr_lane + (((uint32_t)(32 * dt)) ^ tr_x);
-          s16x4 v0 = lds_read_tr(pv + (2 * jp) * 4096);
-          s16x4 v1 = lds_read_tr(pv + (2 * jp + 1) * 4096);
-          if (mask) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              if (32 * jp + tb + e >= nvalid) v0[e] = 0;
-              if (32 * jp + 16 + tb + e >= nvalid) v1[e] = 0;
-            }
-          }
-          return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-        };
-        // per tile pair and group of four dim tiles: the reads first, then the
-        // hi MFMAs, then the lo MFMAs (four independent accumulator chains)
-        auto pv_pass = [&](int jp, bool mask) {
-#pragma unroll
-          for (int d0 = 0; d0 < NDT; d0 += 4) {
-            bf16x8 bv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) bv[i] = read_b(jp, d0 + i, mask);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              bacc[d0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ph[jp]), bv[i],
-                                                                     bacc[d0 + i], 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              bacc[d0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pl[jp]), bv[i],
-                                                                     bacc[d0 + i], 0, 0, 0);
-          }
-        };
-        if (!partial) {
-          pv_pass(0, false);
-          pv_pass(1, false);
-        } else {  // the last block of a sequence: zero the tail tokens' values
-          pv_pass(0, true);
-          pv_pass(1, true);
-        }
-      } else {
-        // fp32: k = lg of step (nt, r) is token 16nt + 4lg + r; B element
-        // (token, dim 16dt + c) read directly from the slab
-        const auto* vf = (const __attribute__((address_space(3))) float*)vb;
-#pragma unroll
-        for (int nt = 0; nt < kTiles; ++nt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int tok = 16 * nt + tb + r;
-            const int zsw = (2 * r) ^ (8 * (lg & 1));
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-              const int pos = (4 * dt + (c >> 2)) ^ zsw;
-              float v = vf[((4 * nt + lg) * 1024 + r * 256 + pos * 16 + 4 * (c & 3)) >> 2];
-              if (tok >= nvalid) v = 0.f;
-              bacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(S[nt][r], v, bacc[dt], 0, 0, 0);
-            }
-          }
-      }
-      if (has_next) load_v(nxt);
+      for (int dt = 0; dt < NDT; ++dt) *(f32x4*)&E.acc[wid][16 * dt + c][0] = acc[dt];
     }
-
-    int stop_round = -1;  // this round's stop, as a traversal count
-    if (art_mode) {
-      // ---- publish the block summary ------------------------------------------
-      // probe dims 4p: lanes c = 0, 4, 8, 12 of row 0 hold dims 16dt + c for
-      // heads r % G in register r
-      Summary<D>& sw = R.sum[parity][wid];
-      if (active) {
-        if (lane < 16 && (c & 3) == 0) {
+    if (lane < G) {
+      E.m[wid][lane] = m_c;
+      E.l[wid][lane] = l_c;
+    }
+    if (lane == 0) {
+      E.issued[wid] = issued;
+      E.bad[wid] = bad_page;
+    }
+    __syncthreads();
+  };
+  int dev_status = item_status;
+  auto split_replay = [&]() -> int {
+    ReplayLds<D>& RL = *reinterpret_cast<ReplayLds<D>*>(&vbuf[0][0]);
+    CarryRec<D>* carries = reinterpret_cast<CarryRec<D>*>(a.carries) + (size_t)unit * a.max_chunks;
+    const int Cn = t_end - t_begin;
+    wait_vm<0>();     // speculative loads have landed in the V slabs
+    __syncthreads();  // this chunk's summaries (written by its own waves) are visible
+    if (tid == 0) {
+      int f = 1;
+      if (chunk > 0) {
+        uint32_t polls = 0;
+        for (;;) {
+          f = ld_sys(&carries[chunk - 1].flag);
+          if (f != 0) break;
+          if (++polls >= a.spin_limit) {
+            f = -1;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(8);
+        }
+      }
+      R.flag = f;
+    }
+    __syncthreads();
+    const int pflag = uni(R.flag);
+    if (pflag == 2) {  // the unit stopped at or before the predecessor's end
+      discard = true;
+      if (tid == 0) st_sys(&carries[chunk].flag, 2);
+      return -1;
+    }
+    if (pflag < 0) dev_status = ART_ERR_TIMEOUT;
+    const bool has_carry = chunk > 0 && pflag > 0;
+    const CarryRec<D>* cin = &carries[chunk > 0 ? chunk - 1 : 0];
+    const Summary<D>* gsum = reinterpret_cast<const Summary<D>*>(a.summaries) + ((size_t)unit * a.max_trav + t_begin);
+    {  // stage [j][q][g] -> [j][g][q]; all loads of a thread are issued before its stores
+      constexpr int kPer = kSplitMax * D / (kWave * kMaxWaves);
+      float v[kPer];
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) *(f32x4*)&sw.ps[4 * dt + (c >> 2)][0] = bacc[dt];
+      for (int r = 0; r < kPer; ++r) {
+        const int i = tid + r * kWave * kMaxWaves;
+        v[r] = i < Cn * D ? gsum[i / D].ps[(i % D) >> 2][i & 3] : 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) {
+        const int i = tid + r * kWave * kMaxWaves;
+        if (i < Cn * D) RL.ps[i / D][i & 3][(i % D) >> 2] = v[r];
+      }
+      if (tid < Cn * 4) {
+        const float mv = gsum[tid >> 2].m[tid & 3], lv = gsum[tid >> 2].l[tid & 3];
+        RL.m[tid >> 2][tid & 3] = mv;
+        RL.l[tid >> 2][tid & 3] = lv;
+      }
+    }
+    if (tid == 0) {
+      RL.stt[0] = has_carry ? ld_sys(&cin->stt_last) : 0.0;
+      RL.counter = has_carry ? ld_sys(&cin->counter) : 0;
+    }
+    __syncthreads();
+    constexpr int NQ = D / 8;  // probe dims per thread
+    const int j = tid >> 3, g = (tid >> 1) & 3, hh = tid & 1;
+    const bool on = j < Cn && g < G;
+    const int jj = j < Cn ? j : 0, gg = g < G ? g : 0;
+    const float Mc = has_carry ? ld_sys(&cin->m[gg]) : -INFINITY;
+    const double Lc = has_carry ? ld_sys(&cin->l[gg]) : 0.0;
+    float Ms = Mc;
+    for (int i = 0; i < Cn; ++i) Ms = fmaxf(Ms, RL.m[i][gg]);
+    const double sc = has_carry ? (double)__builtin_amdgcn_exp2f(Mc - Ms) : 0.0;
+    double P[NQ], Pp[NQ];
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq) {
+      P[qq] = has_carry ? ld_sys(&cin->p[hh * NQ + qq][gg]) * sc : 0.0;
+      Pp[qq] = P[qq];
+    }
+    double L = Lc * sc, Lp = L;
+    for (int i = 0; i < Cn; ++i) {
+      const double si = (double)__builtin_amdgcn_exp2f(RL.m[i][gg] - Ms);
+      const double wi = i <= jj ? si : 0.0, wp = i < jj ? si : 0.0;
+      const double li = (double)RL.l[i][gg];
+      L = fma(li, wi, L);
+      Lp = fma(li, wp, Lp);
+#pragma unroll
+      for (int qq = 0; qq < NQ; ++qq) {
+        const double v = (double)RL.ps[i][gg][hh * NQ + qq];
+        P[qq] = fma(v, wi, P[qq]);
+        Pp[qq] = fma(v, wp, Pp[qq]);
+      }
+    }
+    double A = 0.0, X = 0.0;
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq) {
+      A = fma(P[qq], P[qq], A);
+      X = fma(P[qq], Pp[qq], X);
+    }
+    A += dpp<kQx1>(A);  // the two halves of the probe dims
+    X += dpp<kQx1>(X);
+    const double iL = recip_d(L), iLp = Lp > 0.0 ? recip_d(Lp) : 0.0;
+    double stt = on ? A * (iL * iL) : 0.0, stp = on ? X * (iL * iLp) : 0.0;
+    stt += dpp<kQx2>(stt);  // heads g and g ^ 1
+    stp += dpp<kQx2>(stp);
+    stt += dpp<kHalfMirror>(stt);  // heads {0, 1} and {2, 3}
+    stp += dpp<kHalfMirror>(stp);
+    if (on && (tid & 7) == 0) RL.stt[j + 1] = stt;
+    __syncthreads();
+    if (on && (tid & 7) == 0) {
+      const double spr = RL.stt[j];
+      const bool exists = t_begin + j + 1 >= 2;  // a check exists from the second block on
+      const bool stable = (spr > 0.0) & (stt > 0.0) & crit.scale_ok(spr, stt) & crit.dir_ok(spr, stt, stp);
+      RL.bits[j] = (exists ? 2 : 0) | (stable ? 1 : 0);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int cnt = RL.counter, st = -1;
+      for (int i = 0; i < Cn; ++i) {
+        const int bt = RL.bits[i];
+        if (!(bt & 2)) continue;
+        cnt = (bt & 1) ? cnt + 1 : 0;
+        if (cnt >= a.patience) {
+          st = i + 1;
+          break;
+        }
+      }
+      RL.stop_local = st;
+      RL.counter = cnt;
+    }
+    __syncthreads();
+    const int st = uni(RL.stop_local);
+    if (st < 0) {  // no stop here: publish the prefix state after the chunk's last block
+      CarryRec<D>& co = carries[chunk];
+      if (on && j == Cn - 1) {
+#pragma unroll
+        for (int qq = 0; qq < NQ; ++qq) st_sys(&co.p[hh * NQ + qq][g], P[qq]);
+        if (hh == 0) {
+          st_sys(&co.m[g], Ms);
+          st_sys(&co.l[g], L);
+        }
+      }
+      if (tid == 0) {
+        st_sys(&co.counter, RL.counter);
+        st_sys(&co.stt_last, RL.stt[Cn]);
+      }
+      wait_vm<0>();  // the carry's stores are acknowledged
+      __syncthreads();
+      if (tid == 0) st_sys(&co.flag, 1);
+    } else if (tid == 0) {
+      st_sys(&a.unit_stop[unit], t_begin + st);
+      st_sys(&carries[chunk].flag, 2);
+    }
+    __syncthreads();  // the V slabs are free again
+    return st;
+  };
+
+  if (split && chunk > 0) {  // an earlier chunk already stopped before this one: nothing to do
+    if (tid == 0) R.flag = ld_sys(&a.unit_stop[unit]);
+    __syncthreads();
+    const int us = uni(R.flag);
+    if (us > 0 && us <= t_begin) {
+      discard = true;
+      if (tid == 0) st_sys(&(reinterpret_cast<CarryRec<D>*>(a.carries) + (size_t)unit * a.max_chunks)[chunk].flag, 2);
+    }
+  }
+  bool stashed = false;
+  for (int pass = 0; pass < 2 && !discard; ++pass) {
+    if (pass == 1) {
+      m_c = -INFINITY;
+      l_c = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    BlockAddr cur;
+    if (t_begin + wid < t_stop) {
+      cur = block_addr<ROW, PAGED>(u, uni(block_at(u, a.order, t_begin + wid)), bad_page);
+      load_k(cur, 0.f);
+      load_v(cur);
+      ++issued;
+    }
+    int parity = 0;
+
+    for (int t0 = t_begin; t0 < t_stop; t0 += W) {
+      const int t = t0 + wid;
+      const bool active = t < t_stop;
+      const int n_act = min(W, t_stop - t0);
+      const int tn = t + W;
+      const bool has_next = tn < t_stop;
+      BlockAddr nxt = cur;
+      if (has_next) nxt = block_addr<ROW, PAGED>(u, uni(block_at(u, a.order, tn)), bad_page);
+
+      float m_new = m_c, alpha = 1.f, lblk = 0.f;
+      f32x4 bacc[NDT];
+      if (active) {
+        const int nvalid = cur.nvalid;
+        // ---- scores S^T[token][head] = k_token . q_head --------------------------
+        wait_v_tied<kLoads>(kr);  // this block's K (its 16 V DMAs were issued after it)
+        f32x4 S[kTiles];
+        static_for<0, kTiles>([&](auto ntc) {
+          constexpr int nt = decltype(ntc)::value;
+          f32x4 s = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (DT == ART_DT_BF16) {
+  #pragma unroll
+            for (int j = 0; j < 4; ++j)
+              s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[4 * nt + j]),
+                                                          __builtin_bit_cast(bf16x8, qv[j]), s, 0, 0, 0);
+          } else {
+  #pragma unroll
+            for (int j = 0; j < 4; ++j)
+  #pragma unroll
+              for (int e = 0; e < 4; ++e)
+                s = __builtin_amdgcn_mfma_f32_16x16x4f32(u2f(kr[4 * nt + j][e]), u2f(qv[j][e]), s, 0, 0, 0);
+          }
+          S[nt] = s;
+        });
+        // ---- online softmax of head c % G against its running max ---------------
+        const int tb = 4 * lg;  // token of register 0 within each tile
+        float mx = -INFINITY;
+  #pragma unroll
+        for (int nt = 0; nt < kTiles; ++nt)
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float sv = (16 * nt + tb + r < nvalid) ? S[nt][r] * c2 : -INFINITY;
+            S[nt][r] = sv;
+            mx = fmaxf(mx, sv);
+          }
+        mx = col_max(mx);
+        if (has_next) {
+          load_k(nxt, mx);
+          ++issued;
+        }
+        m_new = fmaxf(m_c, mx);
+        alpha = __builtin_amdgcn_exp2f(m_c - m_new);
+        float ls = 0.f;
+  #pragma unroll
+        for (int nt = 0; nt < kTiles; ++nt)
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float p = __builtin_amdgcn_exp2f(S[nt][r] - m_new);
+            S[nt][r] = p;
+            ls += p;
+          }
+        lblk = col_sum(ls);
+        // ---- P V on MFMA ---------------------------------------------------------
+  #pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) bacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // V of this block: the 16 K loads of the next block (if any) were issued after it
+        if (has_next)
+          wait_vm<kLoads>();
+        else
+          wait_vm<0>();
+        const bool partial = nvalid < kBlk;  // weights of the tail tokens are 0; their V may be garbage
+        if constexpr (DT == ART_DT_BF16) {
+          // A operand of tile pair jp: element e < 4 is token 16(2jp) + 4lg + e,
+          // element e >= 4 is token 16(2jp+1) + 4lg + e - 4, split as P = hi + lo
+          u32x4 ph[2], pl[2];
+  #pragma unroll
+          for (int jp = 0; jp < 2; ++jp)
+  #pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const int nt = 2 * jp + hh;
+              const uint32_t w0 = pk_bf16(S[nt][0], S[nt][1]);
+              const uint32_t w1 = pk_bf16(S[nt][2], S[nt][3]);
+              ph[jp][2 * hh] = w0;
+              ph[jp][2 * hh + 1] = w1;
+              pl[jp][2 * hh] = pk_bf16(S[nt][0] - bf16_lo(w0), S[nt][1] - bf16_hi(w0));
+              pl[jp][2 * hh + 1] = pk_bf16(S[nt][2] - bf16_lo(w1), S[nt][3] - bf16_hi(w1));
+            }
+          // B operand of (tile pair jp, dim tile dt): two transposed reads,
+          // tokens of tile 2jp then tile 2jp+1, dims 16dt + c
+          auto read_b = [&](int jp, int dt, bool mask) -> bf16x8 {
+            const auto* pv = vb + tr_lane + (((uint32_t)(32 * dt)) ^ tr_x);
+            s16x4 v0 = lds_read_tr(pv + (2 * jp) * 4096);
+            s16x4 v1 = lds_read_tr(pv + (2 * jp + 1) * 4096);
+            if (mask) {
+  #pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                if (32 * jp + tb + e >= nvalid) v0[e] = 0;
+                if (32 * jp + 16 + tb + e >= nvalid) v1[e] = 0;
+              }
+            }
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+          };
+          // per tile pair and group of four dim tiles: the reads first, then the
+          // hi MFMAs, then the lo MFMAs (four independent accumulator chains)
+          auto pv_pass = [&](int jp, bool mask) {
+  #pragma unroll
+            for (int d0 = 0; d0 < NDT; d0 += 4) {
+              bf16x8 bv[4];
+  #pragma unroll
+              for (int i = 0; i < 4; ++i) bv[i] = read_b(jp, d0 + i, mask);
+  #pragma unroll
+              for (int i = 0; i < 4; ++i)
+                bacc[d0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ph[jp]), bv[i],
+                                                                       bacc[d0 + i], 0, 0, 0);
+  #pragma unroll
+              for (int i = 0; i < 4; ++i)
+                bacc[d0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pl[jp]), bv[i],
+                                                                       bacc[d0 + i], 0, 0, 0);
+            }
+          };
+          if (!partial) {
+            pv_pass(0, false);
+            pv_pass(1, false);
+          } else {  // the last block of a sequence: zero the tail tokens' values
+            pv_pass(0, true);
+            pv_pass(1, true);
+          }
+        } else {
+          // fp32: k = lg of step (nt, r) is token 16nt + 4lg + r; B element
+          // (token, dim 16dt + c) read directly from the slab
+          const auto* vf = (const __attribute__((address_space(3))) float*)vb;
+  #pragma unroll
+          for (int nt = 0; nt < kTiles; ++nt)
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int tok = 16 * nt + tb + r;
+              const int zsw = (2 * r) ^ (8 * (lg & 1));
+  #pragma unroll
+              for (int dt = 0; dt < NDT; ++dt) {
+                const int pos = (4 * dt + (c >> 2)) ^ zsw;
+                float v = vf[((4 * nt + lg) * 1024 + r * 256 + pos * 16 + 4 * (c & 3)) >> 2];
+                if (tok >= nvalid) v = 0.f;
+                bacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(S[nt][r], v, bacc[dt], 0, 0, 0);
+              }
+            }
+        }
+        if (has_next) load_v(nxt);
+      }
+
+      int stop_round = -1;  // this round's stop, as a traversal count
+      if (split && pass == 0 && active) {
+        // split ART: the block summary goes to the workspace for the replay
+        Summary<D>* gs = reinterpret_cast<Summary<D>*>(a.summaries) + ((size_t)unit * a.max_trav + t);
+        if (lane < 16 && (c & 3) == 0) {
+  #pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) *(f32x4*)&gs->ps[4 * dt + (c >> 2)][0] = bacc[dt];
         }
         if (lane < G) {
-          sw.m[lane] = m_new;
-          sw.l[lane] = lblk;
+          gs->m[lane] = m_new;
+          gs->l[lane] = lblk;
         }
       }
-      lds_barrier();
-      // ---- the round's positions, in order ------------------------------------
-      // Every wave merges the round's block summaries, in traversal order,
-      // onto the carried prefix state on the probe dims (lane (lg, c): head
-      // lg if lg < G, probe dims of chunk c); all waves keep the same state.
-      // All terms are first put on the round's common maximum M, so the scale
-      // factors are independent of one another.  With P^(t) the prefix
-      // numerators and l^(t) the prefix mass of a head, x^(t) = P^(t) / l^(t)
-      // (the ratio is scale free).  A wave keeps the per-lane parts of
-      // |P|^2 at its own position and the one before, and of P^(t).P^(t-1)
-      // at its own, then forms |x^(t)|^2, |x^(t-1)|^2 and x^(t).x^(t-1)
-      // (per-head row sums, divided by that head's mass, summed over heads)
-      // and runs the two tests for its own position only.
-      float mk[kMaxWaves];
-      double lk[kMaxWaves], pk[kMaxWaves][PPC];
-      float M = mP;
-#pragma unroll
-      for (int k = 0; k < kMaxWaves; ++k) {
-        const Summary<D>& s2 = R.sum[parity][k];
-        const bool on = k < n_act;  // slots past the round's end hold stale data
-        mk[k] = on ? s2.m[hg] : -INFINITY;
-        lk[k] = on ? (double)s2.l[hg] : 0.0;
-#pragma unroll
-        for (int i = 0; i < PPC; ++i) pk[k][i] = on ? (double)s2.ps[c * PPC + i][hg] : 0.0;
-        M = fmaxf(M, mk[k]);
-      }
-      const double sP = (double)__builtin_amdgcn_exp2f(mP - M);
-      double L = lP * sP, P[PPC];
-#pragma unroll
-      for (int i = 0; i < PPC; ++i) P[i] = pP[i] * sP;
-      double a_own = 0.0, c_own = 0.0, a_prev = 0.0, L_own = 1.0, L_prev = 0.0;
-#pragma unroll
-      for (int k = 0; k < kMaxWaves; ++k) {
-        const double sk = (double)__builtin_amdgcn_exp2f(mk[k] - M);  // 0 past the round's end
-        double pa = 0.0, pc = 0.0;
-#pragma unroll
-        for (int i = 0; i < PPC; ++i) {
-          const double pn = fma(pk[k][i], sk, P[i]);
-          pa = fma(pn, pn, pa);
-          pc = fma(pn, P[i], pc);
-          P[i] = pn;
+      if (art_mode && !split) {
+        // ---- publish the block summary ------------------------------------------
+        // probe dims 4p: lanes c = 0, 4, 8, 12 of row 0 hold dims 16dt + c for
+        // heads r % G in register r
+        Summary<D>& sw = R.sum[parity][wid];
+        if (active) {
+          if (lane < 16 && (c & 3) == 0) {
+  #pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) *(f32x4*)&sw.ps[4 * dt + (c >> 2)][0] = bacc[dt];
+          }
+          if (lane < G) {
+            sw.m[lane] = m_new;
+            sw.l[lane] = lblk;
+          }
         }
-        const double Ln = fma(lk[k], sk, L);
-        const bool own = k == wid, before = k + 1 == wid;
-        a_own = own ? pa : a_own;
-        c_own = own ? pc : c_own;
-        L_prev = own ? L : L_prev;
-        L_own = own ? Ln : L_own;
-        a_prev = before ? pa : a_prev;
-        L = Ln;
-      }
-      mP = M;
-      lP = L;
-#pragma unroll
-      for (int i = 0; i < PPC; ++i) pP[i] = P[i];
-      if (active) {
-        const double keep = lg < G ? 1.0 : 0.0;  // rows past G carry head 0 again
-        const double io = recip_d(L_own);
-        const double ip = L_prev > 0.0 ? recip_d(L_prev) : 0.0;
-        const double stt = col_sum_d(row_sum_d(a_own) * (io * io * keep));
-        const double stp = col_sum_d(row_sum_d(c_own) * (io * ip * keep));
-        const double spr = wid == 0 ? stt_last : col_sum_d(row_sum_d(a_prev) * (ip * ip * keep));
-        const bool stable =
-            (spr > 0.0) & (stt > 0.0) & crit.scale_ok(spr, stt) & crit.dir_ok(spr, stt, stp);
-        if (lane == 0) {
-          R.chk[parity][wid].stt = stt;
-          R.chk[parity][wid].stable = stable;
+        lds_barrier();
+        // ---- the round's positions, in order ------------------------------------
+        // Every wave merges the round's block summaries, in traversal order,
+        // onto the carried prefix state on the probe dims (lane (lg, c): head
+        // lg if lg < G, probe dims of chunk c); all waves keep the same state.
+        // All terms are first put on the round's common maximum M, so the scale
+        // factors are independent of one another.  With P^(t) the prefix
+        // numerators and l^(t) the prefix mass of a head, x^(t) = P^(t) / l^(t)
+        // (the ratio is scale free).  A wave keeps the per-lane parts of
+        // |P|^2 at its own position and the one before, and of P^(t).P^(t-1)
+        // at its own, then forms |x^(t)|^2, |x^(t-1)|^2 and x^(t).x^(t-1)
+        // (per-head row sums, divided by that head's mass, summed over heads)
+        // and runs the two tests for its own position only.
+        float mk[kMaxWaves];
+        double lk[kMaxWaves], pk[kMaxWaves][PPC];
+        float M = mP;
+  #pragma unroll
+        for (int k = 0; k < kMaxWaves; ++k) {
+          const Summary<D>& s2 = R.sum[parity][k];
+          const bool on = k < n_act;  // slots past the round's end hold stale data
+          mk[k] = on ? s2.m[hg] : -INFINITY;
+          lk[k] = on ? (double)s2.l[hg] : 0.0;
+  #pragma unroll
+          for (int i = 0; i < PPC; ++i) pk[k][i] = on ? (double)s2.ps[c * PPC + i][hg] : 0.0;
+          M = fmaxf(M, mk[k]);
         }
-      }
-      lds_barrier();
-      // ---- patience counter over the round's checks, in traversal order ---------
-      int sbits = 0;  // bit w2: the check at position t0 + w2 passed
-#pragma unroll
-      for (int w2 = 0; w2 < kMaxWaves; ++w2) {
-        const Check ck = R.chk[parity][w2];
-        sbits |= (ck.stable & 1) << w2;
-        if (w2 + 1 == n_act) stt_last = ck.stt;
-      }
-      sbits = uni(sbits);
-      // a check exists from the second traversal block on
-#pragma unroll
-      for (int w2 = 0; w2 < kMaxWaves; ++w2) {
-        const int cnt = t0 + w2 + 1;
-        if (w2 < n_act && cnt >= 2 && stop_round < 0) {
-          counter = ((sbits >> w2) & 1) ? counter + 1 : 0;
-          if (counter >= a.patience) stop_round = cnt;
+        const double sP = (double)__builtin_amdgcn_exp2f(mP - M);
+        double L = lP * sP, P[PPC];
+  #pragma unroll
+        for (int i = 0; i < PPC; ++i) P[i] = pP[i] * sP;
+        double a_own = 0.0, c_own = 0.0, a_prev = 0.0, L_own = 1.0, L_prev = 0.0;
+  #pragma unroll
+        for (int k = 0; k < kMaxWaves; ++k) {
+          const double sk = (double)__builtin_amdgcn_exp2f(mk[k] - M);  // 0 past the round's end
+          double pa = 0.0, pc = 0.0;
+  #pragma unroll
+          for (int i = 0; i < PPC; ++i) {
+            const double pn = fma(pk[k][i], sk, P[i]);
+            pa = fma(pn, pn, pa);
+            pc = fma(pn, P[i], pc);
+            P[i] = pn;
+          }
+          const double Ln = fma(lk[k], sk, L);
+          const bool own = k == wid, before = k + 1 == wid;
+          a_own = own ? pa : a_own;
+          c_own = own ? pc : c_own;
+          L_prev = own ? L : L_prev;
+          L_own = own ? Ln : L_own;
+          a_prev = before ? pa : a_prev;
+          L = Ln;
         }
+        mP = M;
+        lP = L;
+  #pragma unroll
+        for (int i = 0; i < PPC; ++i) pP[i] = P[i];
+        if (active) {
+          const double keep = lg < G ? 1.0 : 0.0;  // rows past G carry head 0 again
+          const double io = recip_d(L_own);
+          const double ip = L_prev > 0.0 ? recip_d(L_prev) : 0.0;
+          const double stt = col_sum_d(row_sum_d(a_own) * (io * io * keep));
+          const double stp = col_sum_d(row_sum_d(c_own) * (io * ip * keep));
+          const double spr = wid == 0 ? stt_last : col_sum_d(row_sum_d(a_prev) * (ip * ip * keep));
+          const bool stable =
+              (spr > 0.0) & (stt > 0.0) & crit.scale_ok(spr, stt) & crit.dir_ok(spr, stt, stp);
+          if (lane == 0) {
+            R.chk[parity][wid].stt = stt;
+            R.chk[parity][wid].stable = stable;
+          }
+        }
+        lds_barrier();
+        // ---- patience counter over the round's checks, in traversal order ---------
+        int sbits = 0;  // bit w2: the check at position t0 + w2 passed
+  #pragma unroll
+        for (int w2 = 0; w2 < kMaxWaves; ++w2) {
+          const Check ck = R.chk[parity][w2];
+          sbits |= (ck.stable & 1) << w2;
+          if (w2 + 1 == n_act) stt_last = ck.stt;
+        }
+        sbits = uni(sbits);
+        // a check exists from the second traversal block on
+  #pragma unroll
+        for (int w2 = 0; w2 < kMaxWaves; ++w2) {
+          const int cnt = t0 + w2 + 1;
+          if (w2 < n_act && cnt >= 2 && stop_round < 0) {
+            counter = ((sbits >> w2) & 1) ? counter + 1 : 0;
+            if (counter >= a.patience) stop_round = cnt;
+          }
+        }
+        stop_round = uni(stop_round);
+        parity ^= 1;
       }
-      stop_round = uni(stop_round);
-      parity ^= 1;
-    }
 
-    // ---- commit this wave's block (unless it lies after the stop) -------------
-    if (active && (stop_round < 0 || t + 1 <= stop_round)) {
-      // row r of the O layout holds head r % G, whose column values sit in lane r % G
-      float al[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) al[r] = lane_f(alpha, r % G);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[dt][r] = fmaf(acc[dt][r], al[r], bacc[dt][r]);
-      m_c = m_new;
-      l_c = fmaf(l_c, alpha, lblk);
+      // ---- commit this wave's block (unless it lies after the stop) -------------
+      if (active && (stop_round < 0 || t + 1 <= stop_round)) {
+        // row r of the O layout holds head r % G, whose column values sit in lane r % G
+        float al[4];
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) al[r] = lane_f(alpha, r % G);
+  #pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) acc[dt][r] = fmaf(acc[dt][r], al[r], bacc[dt][r]);
+        m_c = m_new;
+        l_c = fmaf(l_c, alpha, lblk);
+      }
+      if (stop_round >= 0) {
+        stop = stop_round;
+        break;
+      }
+      cur = nxt;
     }
-    if (stop_round >= 0) {
-      stop = stop_round;
-      break;
-    }
-    cur = nxt;
+    if (!split || pass == 1) break;
+    stash_waves();
+    stashed = true;
+    const int stop_local = split_replay();
+    if (discard || stop_local < 0 || stop_local == t_end - t_begin) break;
+    t_stop = t_begin + stop_local;  // recompute the blocks up to the stop
+    stashed = false;
   }
   if (stop < 0) stop = t_end;
+  if (!stashed) stash_waves();
 
-  // ---- epilogue: merge waves, normalize --------------------------------------
-  wait_vm<0>();  // speculative loads may still be landing in the V slabs
-  __syncthreads();
-  auto& E = *reinterpret_cast<EpilogueLds<G, D>*>(&vbuf[0][0]);
-  if (lane < 16) {
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) *(f32x4*)&E.acc[wid][16 * dt + c][0] = acc[dt];
-  }
-  if (lane < G) {
-    E.m[wid][lane] = m_c;
-    E.l[wid][lane] = l_c;
-  }
-  if (lane == 0) {
-    E.issued[wid] = issued;
-    E.bad[wid] = bad_page;
-  }
-  __syncthreads();
+  // ---- epilogue: merge the stashed waves, normalize -----------------------------
   for (int o = tid; o < G * D; o += kWave * kMaxWaves) {
     const int g = o / D, dim = o % D;
     float M = -INFINITY;
@@ -928,6 +1176,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
       L = fmaf(E.l[w2][g], s, L);
       num = fmaf(E.acc[w2][dim][g], s, num);
     }
+    if (discard) L = 0.f;  // nothing of this chunk counts
     if (single) {
       out_rows[o] = num / L;
     } else {
@@ -945,7 +1194,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
       tot += E.issued[w2];
       bad |= E.bad[w2];
     }
-    a.items[item] = ItemState{bad ? (int)ART_ERR_DEVICE_INPUT : item_status, tot};
+    a.items[item] = ItemState{bad ? (int)ART_ERR_DEVICE_INPUT : dev_status, tot};
     if (single) {
       a.stop_idx[unit] = stop;
       if (a.blocks_issued) a.blocks_issued[unit] = tot;
@@ -971,7 +1220,7 @@ __global__ __launch_bounds__(kWave) void art_combine_kernel(KernelArgs a) {
   if (n_trav <= 0) return;
   const int n_chunks = (n_trav + a.chunk_blocks - 1) / a.chunk_blocks;
   if (n_chunks <= 1) return;  // written directly by the decode kernel
-  if (a.kept_blocks && a.stop_idx[unit] == -1) return;  // bad kept list: already reported
+  if (a.items[unit].issued == -1) return;  // kept list rejected: already reported
   const float* part = a.partials + (size_t)unit * a.max_chunks * G * (D + 2);
   for (int g = 0; g < G; ++g) {
     float M = -INFINITY;
@@ -991,7 +1240,12 @@ __global__ __launch_bounds__(kWave) void art_combine_kernel(KernelArgs a) {
     if (D > kWave) dst[kWave + threadIdx.x] = o1 / L;
   }
   if (threadIdx.x == 0) {
-    a.stop_idx[unit] = n_trav;
+    int stop = n_trav;
+    if (a.split_art) {
+      const int us = a.unit_stop[unit];
+      if (us > 0) stop = us;
+    }
+    a.stop_idx[unit] = stop;
     if (a.blocks_issued) {
       int tot = 0;
       for (int k = 0; k < n_chunks; ++k) tot += a.items[(size_t)k * a.batch * a.hkv + unit].issued;
@@ -1006,7 +1260,10 @@ __global__ __launch_bounds__(kWave) void art_combine_kernel(KernelArgs a) {
 template <int DT, int G, bool PAGED>
 static hipError_t launch_t(const KernelArgs& a, int grid, int waves, hipStream_t s) {
   (void)waves;
-  hipLaunchKernelGGL((art_decode_kernel<DT, G, PAGED>), dim3(grid), dim3(kWave * kMaxWaves), 0, s, a);
+  if (a.split_art)
+    hipLaunchKernelGGL((art_decode_kernel<DT, G, PAGED, true>), dim3(grid), dim3(kWave * kMaxWaves), 0, s, a);
+  else
+    hipLaunchKernelGGL((art_decode_kernel<DT, G, PAGED, false>), dim3(grid), dim3(kWave * kMaxWaves), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.max_chunks > 1) {
@@ -1021,8 +1278,28 @@ static hipError_t launch_g(const KernelArgs& a, int grid, int waves, hipStream_t
   return a.page_size ? launch_t<DT, G, true>(a, grid, waves, s) : launch_t<DT, G, false>(a, grid, waves, s);
 }
 
+// Split ART: zero the ticket, the per-unit stops and the carry flags (a
+// kernel rather than a memset, so the call stays safe to capture in a graph).
+template <int D>
+__global__ void art_split_init_kernel(KernelArgs a) {
+  const int n_units = a.batch * a.hkv;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i == 0) a.ws->ticket = 0;
+  if (i < n_units) a.unit_stop[i] = 0;
+  if (i < n_units * a.max_chunks) reinterpret_cast<CarryRec<D>*>(a.carries)[i].flag = 0;
+}
+
 hipError_t launch(const KernelArgs& a, hipStream_t s) {
   const int n_units = a.batch * a.hkv;
+  if (a.split_art) {
+    const int n = n_units * a.max_chunks;
+    if (a.dtype == ART_DT_BF16)
+      hipLaunchKernelGGL(art_split_init_kernel<128>, dim3((n + 255) / 256), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(art_split_init_kernel<64>, dim3((n + 255) / 256), dim3(256), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int grid = n_units * a.max_chunks;
   const int waves = a.waves < 1 ? 1 : (a.waves > kMaxWaves ? kMaxWaves : a.waves);
   const int G = a.hq / a.hkv;

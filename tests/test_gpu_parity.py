@@ -13,6 +13,8 @@ from workloads import config, make_workload, scaled
 
 pytestmark = pytest.mark.gpu
 
+SPLIT_MAX = 32  # longest split-ART chunk
+
 
 @pytest.fixture(scope="module")
 def torch_cuda():
@@ -31,7 +33,8 @@ def check(w, mode=1, tag="", **kw):
     log(f"   {rep}")
     assert rep.ok(), (rep.unexcused[:5], rep.bad_outputs[:5])
     Tp = w.traversal_lengths()
-    assert np.all(issued >= stop) and np.all(issued <= Tp), "blocks_issued out of range"
+    # split ART may re-read up to one chunk (32 blocks) to recompute the stop chunk
+    assert np.all(issued >= stop) and np.all(issued <= Tp + SPLIT_MAX), "blocks_issued out of range"
     return out, stop, issued, rep
 
 
@@ -49,7 +52,8 @@ def test_scaled_configs(torch_cuda, n, reading, mode):
 def test_forced_stop_after_p_plus_one(torch_cuda, p):
     """eps huge: every check is stable, so the stop is at min(T', p+1)."""
     w = make_workload(scaled(3, "B"))
-    _, stop, issued, _ = check(w, tag="huge eps", eps_scale=1e30, eps_dir=1e30, patience=p)
+    # one work item per unit (in-round stopping; split ART is tested below)
+    _, stop, issued, _ = check(w, tag="huge eps", eps_scale=1e30, eps_dir=1e30, patience=p, split_blocks=10 ** 6)
     Tp = w.traversal_lengths()
     np.testing.assert_array_equal(stop, np.minimum(Tp, p + 1))
     # loads stop: the round holding the stop and the prefetch of the next round
@@ -182,11 +186,53 @@ def test_full_size_sampled(torch_cuda, n, reading):
     patiences = (1, 2, 4) if n == 4 else (w.spec.patience,)
     from workloads.device import to_device
     dev = to_device(w)
+    splits = (0, 32) if n in (2, 5) else (0,)  # few units: also ordered split ART
     for p in patiences:
-        out, stop, issued, err = run_gpu(w, patience=p, dev=dev)
-        assert err == 0
-        rep, _ = compare(w, out, stop, units=units, patience=p)
-        log(f"   p={p} {rep} skipped={1 - stop.sum() / w.traversal_lengths().sum():.3f}")
-        assert rep.ok(), (rep.unexcused[:5], rep.bad_outputs[:5])
-        assert np.all((stop >= 1) & (stop <= w.traversal_lengths()))
+        for split in splits:
+            out, stop, issued, err = run_gpu(w, patience=p, dev=dev, split_blocks=split)
+            assert err == 0
+            rep, _ = compare(w, out, stop, units=units, patience=p)
+            log(f"   p={p} split={split} {rep} skipped={1 - stop.sum() / w.traversal_lengths().sum():.3f}")
+            assert rep.ok(), (rep.unexcused[:5], rep.bad_outputs[:5])
+            assert np.all((stop >= 1) & (stop <= w.traversal_lengths()))
     del dev
+
+
+# ---------------------------------------------------------------------------
+# ordered split ART (chunks with look-back) against the oracle
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("split", [4, 8, 16, 32])
+def test_split_art_firing(torch_cuda, split):
+    """Few units at long context, forced chunk lengths: the stop is found by
+    the look-back replay and the stop chunk is recomputed."""
+    w = make_workload(config(2, "B", batch=2, num_q_heads=8, num_kv_heads=2, ctx=(20000, 32768)))
+    _, stop, _, _ = check(w, tag=f"split ART {split}", split_blocks=split)
+    assert np.all(stop < w.traversal_lengths())
+
+
+@pytest.mark.parametrize("p", [1, 2, 3])
+def test_split_art_stop_in_first_chunk(torch_cuda, p):
+    w = make_workload(config(2, "B", batch=1, num_q_heads=8, num_kv_heads=2, ctx=(12000, 12000)))
+    _, stop, _, _ = check(w, tag="split ART early stop", split_blocks=8, eps_scale=1e30, eps_dir=1e30, patience=p)
+    np.testing.assert_array_equal(stop, np.minimum(w.traversal_lengths(), p + 1))
+
+
+def test_split_art_no_stop(torch_cuda):
+    """eps 0: every chunk passes its carry on; the output is full attention."""
+    w = make_workload(config(2, "B", batch=1, num_q_heads=8, num_kv_heads=2, ctx=(9000, 9000)))
+    _, stop, issued, _ = check(w, tag="split ART eps 0", split_blocks=8, eps_scale=0.0, eps_dir=0.0)
+    np.testing.assert_array_equal(stop, w.traversal_lengths())
+
+
+@pytest.mark.parametrize("order", [orc.ORDER_NATURAL, orc.ORDER_GIVEN])
+def test_split_art_orders(torch_cuda, order):
+    s = config(5, "B", batch=1, num_q_heads=8, num_kv_heads=2, ctx=(16384, 16384))
+    w = make_workload(s)
+    if order == orc.ORDER_GIVEN:
+        rng = np.random.default_rng(5)
+        kb = w.kept_blocks.copy()
+        for h in range(s.num_kv_heads):
+            n = int(w.kept_count[0, h])
+            kb[0, h, :n] = rng.permutation(kb[0, h, :n])
+        w.kept_blocks = kb
+    check(w, tag=f"split ART order {order}", order=order, split_blocks=16, eps_scale=2e-2, eps_dir=2e-3)
