@@ -76,6 +76,15 @@ ORDER_GIVEN = 2
 MODE_FULL = 0
 MODE_ART = 1
 
+# Ablation and measurement switches (the library's art_params.flags bits).
+# The pages attribute the method's robustness to requiring both metrics at
+# once (gist.science explainer, section 2.2) and measure the detector's own
+# cost with termination disabled (same explainer, experiments); these
+# switches take one metric out, or keep the detector but never stop.
+FLAG_NO_SCALE = 1     # the magnitude test always passes
+FLAG_NO_DIR = 2       # the direction test always passes
+FLAG_DETECT_ONLY = 4  # evaluate the rule, report its stop, attend over every block
+
 PROBE_STRIDE = 4  # R5
 
 
@@ -208,17 +217,22 @@ def threshold(eps: float) -> float:
 # dual threshold + patience [GIST-2.2], [GIST-2.3], R3, R7
 # ---------------------------------------------------------------------------
 def stop_index(d_scale: np.ndarray, d_dir: np.ndarray, valid: np.ndarray,
-               eps_scale: float, eps_dir: float, patience: int, mode: int = MODE_ART) -> int:
-    """Number of traversal blocks processed before the criterion fires."""
+               eps_scale: float, eps_dir: float, patience: int, mode: int = MODE_ART,
+               flags: int = 0) -> int:
+    """Number of traversal blocks processed before the criterion fires.
+
+    ``flags`` may switch one metric's test off (FLAG_NO_SCALE, FLAG_NO_DIR);
+    a zero-norm probe still never counts as stable."""
     T = len(d_scale)
     if mode == MODE_FULL or T == 0:
         return T
     if patience < 1:
         raise ValueError("patience must be >= 1")
     tau, phi = threshold(eps_scale), threshold(eps_dir)
+    use_scale, use_dir = not (flags & FLAG_NO_SCALE), not (flags & FLAG_NO_DIR)
     count = 0
     for t in range(1, T):                   # check for traversal step t+1 (1-based)
-        stable = bool(valid[t]) and d_scale[t] < tau and d_dir[t] < phi
+        stable = bool(valid[t]) and (not use_scale or d_scale[t] < tau) and (not use_dir or d_dir[t] < phi)
         count = count + 1 if stable else 0
         if count >= patience:
             return t + 1
@@ -241,15 +255,19 @@ class UnitResult:
 
 def art_unit(q: np.ndarray, K: np.ndarray, V: np.ndarray, n_ctx: int, block_size: int,
              eps_scale: float, eps_dir: float, patience: int, order: int = ORDER_RECENT_FIRST,
-             kept: Optional[Sequence[int]] = None, mode: int = MODE_ART) -> UnitResult:
-    """ART for one (batch, kv head) unit; q [G, d], K/V [n_ctx, d] in float64."""
+             kept: Optional[Sequence[int]] = None, mode: int = MODE_ART, flags: int = 0) -> UnitResult:
+    """ART for one (batch, kv head) unit; q [G, d], K/V [n_ctx, d] in float64.
+
+    With FLAG_DETECT_ONLY the stop is reported but the output covers every
+    traversal block (O^(T'))."""
     T = (n_ctx + block_size - 1) // block_size
     pi = traversal(T, kept, order)
     O, mass = prefix_outputs(q, K, V, n_ctx, pi, block_size)
     x = probe(O)
     ds, dd, dds, valid = stability_trace(x)
-    stop = stop_index(ds, dd, valid, eps_scale, eps_dir, patience, mode)
-    out = O[stop - 1] if stop > 0 else np.zeros(q.shape)
+    stop = stop_index(ds, dd, valid, eps_scale, eps_dir, patience, mode, flags)
+    last = len(pi) if (flags & FLAG_DETECT_ONLY) else stop
+    out = O[last - 1] if last > 0 else np.zeros(q.shape)
     return UnitResult(out, stop, len(pi), pi, O, ds, dd, dds, valid, mass)
 
 
@@ -274,7 +292,7 @@ def gather_unit(k: np.ndarray, v: np.ndarray, b: int, h: int, n_ctx: int,
 def art_decode(q, k, v, context_lens, dtype: str, num_kv_heads: int, block_size: int,
                eps_scale: float, eps_dir: float, patience: int, order: int, mode: int,
                page_size: int = 0, block_table=None, kept_blocks=None, kept_count=None,
-               units=None, keep_results: bool = False):
+               units=None, keep_results: bool = False, flags: int = 0):
     """Oracle for the whole call (or a subset of units).
 
     Returns out [B, Hq, d] float64 (rows of skipped units are NaN), stop
@@ -294,7 +312,7 @@ def art_decode(q, k, v, context_lens, dtype: str, num_kv_heads: int, block_size:
         if kept_blocks is not None:
             kept = kept_blocks[b, h, : int(kept_count[b, h])]
         r = art_unit(widen(q[b, h * G:(h + 1) * G], dtype), widen(Ks, dtype), widen(Vs, dtype), n,
-                     block_size, eps_scale, eps_dir, patience, order, kept, mode)
+                     block_size, eps_scale, eps_dir, patience, order, kept, mode, flags)
         out[b, h * G:(h + 1) * G] = r.out
         stop[b, h] = r.stop
         if keep_results:
@@ -303,7 +321,7 @@ def art_decode(q, k, v, context_lens, dtype: str, num_kv_heads: int, block_size:
 
 
 def art_decode_workload(w, mode: int = MODE_ART, patience: Optional[int] = None, units=None,
-                        keep_results: bool = False, eps_scale=None, eps_dir=None, order=None):
+                        keep_results: bool = False, eps_scale=None, eps_dir=None, order=None, flags: int = 0):
     """Convenience wrapper over a ``workloads.Workload``-shaped object."""
     s = w.spec
     return art_decode(w.q, w.k, w.v, w.context_lens, s.dtype, s.num_kv_heads, s.block_size,
@@ -311,7 +329,7 @@ def art_decode_workload(w, mode: int = MODE_ART, patience: Optional[int] = None,
                       s.eps_dir if eps_dir is None else eps_dir,
                       s.patience if patience is None else patience,
                       s.order if order is None else order, mode, s.page_size, w.block_table,
-                      w.kept_blocks, w.kept_count, units, keep_results)
+                      w.kept_blocks, w.kept_count, units, keep_results, flags)
 
 
 def relative_margin(d: np.ndarray, eps: float) -> np.ndarray:

@@ -156,6 +156,54 @@ def test_patience_counting_on_a_hand_trace():
     assert orc.stop_index(ds, dd2, valid, 1e-3, 1e-4, 2) == 6
 
 
+def test_ablation_switches_on_a_hand_trace():
+    """Checks t=2..8 where the scale test fails at t=4 and the direction test
+    fails at t=6 (each alone).  Both metrics: p=2 stops at t=3; with p=3 the
+    passing runs are {2,3}, {5}, {7,8}, so it runs to T'=8.  Scale test off:
+    only t=6 fails, run {2..5} -> p=3 stops at t=4.  Direction test off: only
+    t=4 fails, runs {2,3}, {5..8} -> stops at t=7.  Both off: every valid
+    check passes -> stops at t=4; an invalid (zero) probe at t=3 still resets
+    the counter -> stops at t=6."""
+    lo, hi = 1e-6, 1.0
+    ds = np.array([np.nan, lo, lo, hi, lo, lo, lo, lo])
+    dd = np.array([np.nan, lo, lo, lo, lo, hi, lo, lo])
+    valid = np.array([False] + [True] * 7)
+    f = orc.stop_index
+    assert f(ds, dd, valid, 1e-3, 1e-4, 2) == 3
+    assert f(ds, dd, valid, 1e-3, 1e-4, 3) == 8
+    assert f(ds, dd, valid, 1e-3, 1e-4, 3, flags=orc.FLAG_NO_SCALE) == 4
+    assert f(ds, dd, valid, 1e-3, 1e-4, 3, flags=orc.FLAG_NO_DIR) == 7
+    assert f(ds, dd, valid, 1e-3, 1e-4, 3, flags=orc.FLAG_NO_SCALE | orc.FLAG_NO_DIR) == 4
+    # a zero-norm probe is still never stable with both tests off
+    valid2 = valid.copy(); valid2[2] = False
+    assert f(ds, dd, valid2, 1e-3, 1e-4, 3, flags=orc.FLAG_NO_SCALE | orc.FLAG_NO_DIR) == 6
+
+
+def test_detect_only_reports_the_stop_and_attends_everywhere():
+    w = make_workload(scaled(3, "B"))
+    eps = dict(eps_scale=5e-2, eps_dir=5e-3)
+    out_a, stop_a, _ = orc.art_decode_workload(w, **eps)
+    out_d, stop_d, res = orc.art_decode_workload(w, flags=orc.FLAG_DETECT_ONLY, keep_results=True, **eps)
+    np.testing.assert_array_equal(stop_d, stop_a)
+    out_f, stop_f, _ = orc.art_decode_workload(w, mode=orc.MODE_FULL)
+    for (b, h), r in res.items():
+        np.testing.assert_array_equal(r.out, r.O[-1])
+    # attending to every block is full decode, whatever was detected
+    np.testing.assert_allclose(out_d, out_f, rtol=0, atol=1e-12)
+    assert np.any(stop_a < stop_f), "the workload should fire somewhere"
+
+
+def test_ablation_never_stops_later():
+    """Taking a test out can only add passing checks."""
+    w = make_workload(scaled(3, "B"))
+    eps = dict(eps_scale=5e-2, eps_dir=5e-3)
+    _, s_both, _ = orc.art_decode_workload(w, **eps)
+    _, s_ns, _ = orc.art_decode_workload(w, flags=orc.FLAG_NO_SCALE, **eps)
+    _, s_nd, _ = orc.art_decode_workload(w, flags=orc.FLAG_NO_DIR, **eps)
+    assert np.all(s_ns <= s_both) and np.all(s_nd <= s_both)
+    assert np.any(s_ns < s_both) or np.any(s_nd < s_both), "an ablation should change a stop"
+
+
 def test_strict_comparison_at_threshold():
     """A metric exactly at its threshold is not stable (reading R3)."""
     tau = orc.threshold(1e-3)
