@@ -25,7 +25,12 @@ Reported (one JSON line on stdout):
                  while the kernel sources still match it
   cpu_baseline   the fp64 numpy oracle over every unit of the same workload
   extra fields   full-attention mode and generator reading "A" on the same
-                 shapes, % KV blocks skipped, effective tokens/s
+                 shapes, % KV blocks skipped, effective tokens/s;
+                 detector_overhead: detect-only (detector on, termination
+                 off) against full mode at the same launch shape;
+                 ablation: blocks skipped and output error against full
+                 decode with the scale test, the direction test or
+                 patience taken out
 
 Other modes (no timing line):
   --summarize-pmc FETCH_DIR WRITE_DIR   turn two rocprofv3 --pmc runs of
@@ -117,14 +122,18 @@ def accounting(w, stop, issued):
     return kv_bytes(issued) + per_unit + pages, kv_bytes(stop) + per_unit + pages, kv_bytes
 
 
-def time_steps(dec, dev, w, mode, steps, warmup, split_blocks, flush):
-    import torch
+def decode_kwargs(dev, w, mode, split_blocks, stream, flags=0, patience=None):
     s = w.spec
+    return dict(dtype=dev.dtype_code, page_size=dev.page_size, block_table=dev.block_table,
+                kept_blocks=dev.kept_blocks, kept_count=dev.kept_count, eps_scale=s.eps_scale, eps_dir=s.eps_dir,
+                patience=s.patience if patience is None else patience, order=s.order, mode=mode,
+                split_blocks=split_blocks, flags=flags, stream=stream.cuda_stream)
+
+
+def time_steps(dec, dev, w, mode, steps, warmup, split_blocks, flush, flags=0):
+    import torch
     stream = torch.cuda.current_stream()
-    kw = dict(dtype=dev.dtype_code, page_size=dev.page_size, block_table=dev.block_table,
-              kept_blocks=dev.kept_blocks, kept_count=dev.kept_count, eps_scale=s.eps_scale, eps_dir=s.eps_dir,
-              patience=s.patience, order=s.order, mode=mode, split_blocks=split_blocks,
-              stream=stream.cuda_stream)
+    kw = decode_kwargs(dev, w, mode, split_blocks, stream, flags)
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if flush else None
     r = dec.decode(dev.q, dev.k, dev.v, dev.context_lens, **kw)
     for _ in range(warmup):
@@ -151,10 +160,11 @@ def time_steps(dec, dev, w, mode, steps, warmup, split_blocks, flush):
                 issued=r.blocks_issued.cpu().numpy().astype(np.int64))
 
 
-def measure(dec, w, mode, args, dev=None):
+def measure(dec, w, mode, args, dev=None, flags=0, split_blocks=None):
     from workloads.device import to_device
     dev = dev or to_device(w)
-    t = time_steps(dec, dev, w, mode, args.steps, args.warmup, args.split_blocks, not args.no_flush)
+    sb = args.split_blocks if split_blocks is None else split_blocks
+    t = time_steps(dec, dev, w, mode, args.steps, args.warmup, sb, not args.no_flush, flags)
     loaded, algo, _ = accounting(w, t["stop"], t["issued"])
     sec = t["ms_mean"] * 1e-3
     Tp = w.traversal_lengths()
@@ -167,6 +177,34 @@ def measure(dec, w, mode, args, dev=None):
                context_tokens_per_s=float(w.context_lens.astype(np.int64).sum()) / sec)
     res["pct_of_peak"] = res["gbs_loaded"] / HBM_PEAK_GBS
     return res, t, dev
+
+
+def ablation_report(dec, dev, w, split_blocks, full_out):
+    """Stop-rule variants on the same workload, one call each: KV blocks
+    skipped and the output error against full decode per (batch, kv head)
+    unit (relative L2 over the unit's query heads)."""
+    import torch
+    from kv_cache_early_amd import ART_FLAG_NO_DIR, ART_FLAG_NO_SCALE
+    s = w.spec
+    Tp = w.traversal_lengths()
+    ref = full_out.astype(np.float64).reshape(s.batch, s.num_kv_heads, -1)
+    ref_n = np.linalg.norm(ref, axis=2)
+    rows = {}
+    for name, flags, p in (("art", 0, None), ("no_scale_test", ART_FLAG_NO_SCALE, None),
+                           ("no_direction_test", ART_FLAG_NO_DIR, None), ("no_patience", 0, 1)):
+        r = dec.decode(dev.q, dev.k, dev.v, dev.context_lens,
+                       **decode_kwargs(dev, w, 1, split_blocks, torch.cuda.current_stream(), flags, p))
+        torch.cuda.synchronize()
+        if dec.device_error() != 0:
+            raise RuntimeError(f"device error {dec.device_error()} in ablation {name}")
+        out = r.out.cpu().numpy().astype(np.float64).reshape(s.batch, s.num_kv_heads, -1)
+        stop = r.stop_idx.cpu().numpy().astype(np.int64)
+        rel = np.linalg.norm(out - ref, axis=2) / np.maximum(ref_n, 1e-30)
+        rows[name] = dict(patience=s.patience if p is None else p,
+                          pct_blocks_skipped=round(float(1 - stop.sum() / Tp.sum()), 4),
+                          rel_l2_mean=float(f"{rel.mean():.3e}"), rel_l2_max=float(f"{rel.max():.3e}"),
+                          frac_units_rel_l2_over_1e_2=round(float((rel > 1e-2).mean()), 4))
+    return rows
 
 
 def copy_leg(mib, steps):
@@ -358,10 +396,27 @@ def main():
           f"skip {head['pct_blocks_skipped']:.3f}", file=sys.stderr, flush=True)
     extra = {}
     if not args.skip_extra and args.only is None:
-        full_res, _, _ = measure(dec, w, 0, args, dev=dev)
+        full_res, full_t, _ = measure(dec, w, 0, args, dev=dev)
         extra["full_mode"] = {k: round(full_res[k], 4) for k in ("ms", "gbs_loaded", "pct_of_peak",
                                                                  "effective_tokens_per_s")}
         print(f"[bench] full: {full_res['ms']:.3f} ms {full_res['gbs_loaded']:.0f} GB/s", file=sys.stderr, flush=True)
+        if head_mode == 1:
+            from kv_cache_early_amd import ART_FLAG_DETECT_ONLY
+            # same launch shape on both sides (one work item per unit, as ART
+            # mode runs here): the difference is the detector alone
+            one = 10 ** 9
+            f1, _, _ = measure(dec, w, 0, args, dev=dev, split_blocks=one)
+            det, det_t, _ = measure(dec, w, 1, args, dev=dev, flags=ART_FLAG_DETECT_ONLY, split_blocks=one)
+            extra["detector_overhead"] = dict(
+                full_one_item_ms=round(f1["ms"], 4), detect_only_ms=round(det["ms"], 4),
+                overhead=round(det["ms"] / f1["ms"] - 1, 4),
+                stops_equal_art=bool(np.array_equal(det_t["stop"], head_t["stop"])),
+                note="detector on, termination off (every block read) against full mode, both one work item "
+                     "per (batch, kv head) unit")
+            print(f"[bench] detect-only: {det['ms']:.3f} ms vs full one-item {f1['ms']:.3f} ms "
+                  f"(overhead {det['ms'] / f1['ms'] - 1:+.3%})", file=sys.stderr, flush=True)
+            extra["ablation"] = ablation_report(dec, dev, w, args.split_blocks, full_t["out"])
+            print(f"[bench] ablation: {extra['ablation']}", file=sys.stderr, flush=True)
     traffic = traffic_from_summary() if head_mode == 1 else None
     roof = dict(bound="hbm", achieved=round(head["gbs_algorithmic"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(head["gbs_algorithmic"] / HBM_PEAK_GBS, 4),

@@ -85,6 +85,18 @@ typedef enum { ART_ORDER_NATURAL = 0, ART_ORDER_RECENT_FIRST = 1, ART_ORDER_GIVE
 
 typedef enum { ART_MODE_FULL = 0, ART_MODE_ART = 1 } art_mode;
 
+/* Switches of the stop rule (art_params.flags, ART mode only), for the
+ * detector-overhead and ablation measurements of the gist.science
+ * explainer's experiments section:
+ *  - NO_SCALE, NO_DIR take the magnitude test or the direction test out of
+ *    the stability check (a zero-norm probe is still never stable);
+ *    patience 1 is the no-patience ablation.
+ *  - DETECT_ONLY runs the detector but never terminates: every block is
+ *    read and attended to (out is full decode), stop_idx reports where the
+ *    rule would have stopped (T' if nowhere), blocks_issued counts every
+ *    block read. */
+typedef enum { ART_FLAG_NO_SCALE = 1, ART_FLAG_NO_DIR = 2, ART_FLAG_DETECT_ONLY = 4 } art_flag;
+
 typedef struct {
   int32_t block_size;    /* tokens per ART block (64)                        */
   float eps_scale;       /* tau: threshold on d_scale, >= 0, finite          */
@@ -100,6 +112,7 @@ typedef struct {
                             of the stop rule on the predecessor's carry, and
                             a recompute of the chunk holding the stop);
                             blocks_issued then counts the re-read blocks     */
+  int32_t flags;         /* OR of art_flag; must be 0 in full mode           */
 } art_params;
 
 typedef struct {

@@ -42,6 +42,8 @@ art_status validate(const art_shape* sp, const art_params* pp) {
   if (!finite_nonneg(p.eps_scale) || !finite_nonneg(p.eps_dir)) return ART_ERR_INVALID_ARG;
   if (p.order < ART_ORDER_NATURAL || p.order > ART_ORDER_GIVEN) return ART_ERR_INVALID_ARG;
   if (p.mode != ART_MODE_FULL && p.mode != ART_MODE_ART) return ART_ERR_INVALID_ARG;
+  constexpr int32_t kAllFlags = ART_FLAG_NO_SCALE | ART_FLAG_NO_DIR | ART_FLAG_DETECT_ONLY;
+  if ((p.flags & ~kAllFlags) != 0 || (p.mode == ART_MODE_FULL && p.flags != 0)) return ART_ERR_INVALID_ARG;
   if (p.order == ART_ORDER_GIVEN && s.max_kept == 0) return ART_ERR_INVALID_ARG;
   if (s.page_size > 0 && s.page_size % 16 != 0) return ART_ERR_INVALID_ARG;
   // supported set
@@ -171,7 +173,19 @@ art_status art_decode(const art_shape* shape, const art_params* params, const vo
     a.crit_c2 = (1.0 - phi) * (1.0 - phi);
     a.crit_tau_lt1 = tau < 1.0;
     a.crit_phi_le1 = phi <= 1.0;
+    // A test taken out always passes for a non-zero probe: an infinite upper
+    // bound on |x_t|^2 / |x_{t-1}|^2, and for the direction the (1 - eps_dir)
+    // > 0 branch off with an infinite bound on the negative side.
+    if (p.flags & ART_FLAG_NO_SCALE) {
+      a.crit_hi = INFINITY;
+      a.crit_tau_lt1 = 0;
+    }
+    if (p.flags & ART_FLAG_NO_DIR) {
+      a.crit_c2 = INFINITY;
+      a.crit_phi_le1 = 0;
+    }
   }
+  a.detect_only = (p.flags & ART_FLAG_DETECT_ONLY) ? 1 : 0;
   a.order = p.order;
   a.mode = p.mode;
   a.chunk_blocks = chunk;

@@ -37,7 +37,8 @@ struct alignas(16) Summary {
 // published for the next chunk (look-back).
 template <int D>
 struct alignas(16) CarryRec {
-  int32_t flag;        // 0 not yet; 1 ready (no stop so far); 2 stopped at or before this chunk's end
+  int32_t flag;        // 0 not yet; 1 ready (no stop so far); 2 stopped at or before this chunk's end;
+                       // 3 ready, a stop was detected at or before this chunk's end (detect-only)
   int32_t counter;     // consecutive stable checks at the chunk's end
   double stt_last;     // |x|^2 at the chunk's last position
   float m[4];          // reference max per head (log2 domain)
@@ -55,6 +56,7 @@ struct KernelArgs {
   // squared forms of the thresholds (see the stability tests in the kernel)
   double crit_hi, crit_lo, crit_c2;  // (1+eps_scale)^2, (1-eps_scale)^2, (1-eps_dir)^2
   int32_t crit_tau_lt1, crit_phi_le1; // eps_scale < 1, eps_dir <= 1
+  int32_t detect_only;   // record the stop, never terminate
   int32_t split_art;     // ART mode with several chunks per unit (look-back)
   int32_t max_trav;      // traversal blocks per unit bound (summary row stride)
   int32_t chunk_blocks;  // traversal blocks per work item

@@ -560,6 +560,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const bool art_mode = a.mode == ART_MODE_ART;
+  const bool detect_only = art_mode && a.detect_only != 0;  // record the stop, read every block
   // prefix state on the probe dims (same in every wave): running max, mass and
   // numerators for head hg = lg (lanes with lg >= G carry head 0 unused),
   // the previous probe's squared norm, and the patience counter
@@ -650,6 +651,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
   int bad_page = 0;
   int issued = 0;
   int stop = -1;  // traversal blocks processed at the stop (ART mode)
+  int detected = -1;  // detect-only: the first stop the rule reached
   // Split ART: pass 0 walks the whole chunk speculatively, storing block
   // summaries; the look-back replay then decides the stop; if it lies inside
   // the chunk, pass 1 recomputes the chunk's output up to the stop.
@@ -713,6 +715,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
     }
     __syncthreads();
     const int pflag = uni(R.flag);
+    const bool upstream = pflag == 3;  // detect-only: a stop was already detected
     if (pflag == 2) {  // the unit stopped at or before the predecessor's end
       discard = true;
       if (tid == 0) st_sys(&carries[chunk].flag, 2);
@@ -814,7 +817,10 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
     }
     __syncthreads();
     const int st = uni(RL.stop_local);
-    if (st < 0) {  // no stop here: publish the prefix state after the chunk's last block
+    const bool stop_here = st >= 0 && !upstream;
+    // With no stop here, or in detect-only mode (which never terminates), the
+    // prefix state after the chunk's last block goes to the successor.
+    if (st < 0 || detect_only) {
       CarryRec<D>& co = carries[chunk];
       if (on && j == Cn - 1) {
 #pragma unroll
@@ -827,19 +833,20 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
       if (tid == 0) {
         st_sys(&co.counter, RL.counter);
         st_sys(&co.stt_last, RL.stt[Cn]);
+        if (stop_here) st_sys(&a.unit_stop[unit], t_begin + st);  // detect-only: the first stop
       }
       wait_vm<0>();  // the carry's stores are acknowledged
       __syncthreads();
-      if (tid == 0) st_sys(&co.flag, 1);
+      if (tid == 0) st_sys(&co.flag, (stop_here || upstream) ? 3 : 1);
     } else if (tid == 0) {
       st_sys(&a.unit_stop[unit], t_begin + st);
       st_sys(&carries[chunk].flag, 2);
     }
     __syncthreads();  // the V slabs are free again
-    return st;
+    return detect_only ? -1 : st;
   };
 
-  if (split && chunk > 0) {  // an earlier chunk already stopped before this one: nothing to do
+  if (split && chunk > 0 && !detect_only) {  // an earlier chunk already stopped before this one: nothing to do
     if (tid == 0) R.flag = ld_sys(&a.unit_stop[unit]);
     __syncthreads();
     const int us = uni(R.flag);
@@ -1131,6 +1138,10 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
         }
         stop_round = uni(stop_round);
         parity ^= 1;
+        if (detect_only) {  // keep the first stop, terminate nothing
+          if (detected < 0) detected = stop_round;
+          stop_round = -1;
+        }
       }
 
       // ---- commit this wave's block (unless it lies after the stop) -------------
@@ -1160,7 +1171,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
     t_stop = t_begin + stop_local;  // recompute the blocks up to the stop
     stashed = false;
   }
-  if (stop < 0) stop = t_end;
+  if (stop < 0) stop = detected >= 0 ? detected : t_end;
   if (!stashed) stash_waves();
 
   // ---- epilogue: merge the stashed waves, normalize -----------------------------

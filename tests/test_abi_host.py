@@ -46,7 +46,7 @@ def good_shape(**kw):
 
 def good_params(**kw):
     d = dict(eps_scale=1e-3, eps_dir=1e-4, patience=2, order=art.ART_ORDER_RECENT_FIRST, mode=art.ART_MODE_ART,
-             block_size=64, split_blocks=0)
+             block_size=64, split_blocks=0, flags=0)
     d.update(kw)
     return art.make_params(**d)
 
@@ -79,6 +79,9 @@ CASES = [
     ("bad mode", dict(params=good_params(mode=2)), art.ART_ERR_INVALID_ARG),
     ("given without kept list", dict(params=good_params(order=art.ART_ORDER_GIVEN)), art.ART_ERR_INVALID_ARG),
     ("negative split", dict(params=good_params(split_blocks=-1)), art.ART_ERR_INVALID_ARG),
+    ("unknown flag", dict(params=good_params(flags=8)), art.ART_ERR_INVALID_ARG),
+    ("flags in full mode", dict(params=good_params(mode=art.ART_MODE_FULL, flags=art.ART_FLAG_DETECT_ONLY)),
+     art.ART_ERR_INVALID_ARG),
     ("kept without count", dict(shape=good_shape(max_kept=8), kept=FAKE), art.ART_ERR_INVALID_ARG),
     ("count without kept", dict(kc=FAKE), art.ART_ERR_INVALID_ARG),
     ("kept list but max_kept 0", dict(kept=FAKE, kc=FAKE), art.ART_ERR_INVALID_ARG),

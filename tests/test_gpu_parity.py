@@ -28,7 +28,7 @@ def check(w, mode=1, tag="", **kw):
     log(f"[case] {tag or w.spec.name} reading={w.spec.reading} mode={mode} {kw}")
     out, stop, issued, err = run_gpu(w, mode=mode, **kw)
     assert err == 0, f"device error {err}"
-    ckw = {k: v for k, v in kw.items() if k in ("patience", "eps_scale", "eps_dir", "order")}
+    ckw = {k: v for k, v in kw.items() if k in ("patience", "eps_scale", "eps_dir", "order", "flags")}
     rep, res = compare(w, out, stop, mode=mode, **ckw)
     log(f"   {rep}")
     assert rep.ok(), (rep.unexcused[:5], rep.bad_outputs[:5])
@@ -236,3 +236,44 @@ def test_split_art_orders(torch_cuda, order):
             kb[0, h, :n] = rng.permutation(kb[0, h, :n])
         w.kept_blocks = kb
     check(w, tag=f"split ART order {order}", order=order, split_blocks=16, eps_scale=2e-2, eps_dir=2e-3)
+
+
+# ---------------------------------------------------------------------------
+# stop-rule switches: ablations and detect-only
+# ---------------------------------------------------------------------------
+ABLATIONS = [orc.FLAG_NO_SCALE, orc.FLAG_NO_DIR, orc.FLAG_NO_SCALE | orc.FLAG_NO_DIR]
+
+
+@pytest.mark.parametrize("flags", ABLATIONS)
+@pytest.mark.parametrize("split", [0, 8])
+def test_ablation_flags(torch_cuda, flags, split):
+    """One test of the stability check taken out: the stops follow the
+    oracle's ablated rule, in one work item per unit and in split ART."""
+    w = make_workload(scaled(3, "B"))
+    sb = 10 ** 6 if split == 0 else split
+    _, stop, _, _ = check(w, tag=f"ablation flags={flags} split={split}", flags=flags, split_blocks=sb,
+                          eps_scale=5e-2, eps_dir=5e-3)
+    assert np.all(stop <= w.traversal_lengths())
+
+
+@pytest.mark.parametrize("split", [0, 4, 8, 32])
+def test_detect_only(torch_cuda, split):
+    """Detect-only reads every block once: the output is full decode, the stop
+    is the one ART mode finds, blocks_issued is T'."""
+    w = make_workload(config(2, "B", batch=2, num_q_heads=8, num_kv_heads=2, ctx=(20000, 32768)))
+    sb = 10 ** 6 if split == 0 else split
+    eps = dict(eps_scale=5e-2, eps_dir=5e-3)
+    _, stop_d, issued, _ = check(w, tag=f"detect-only split={split}", flags=orc.FLAG_DETECT_ONLY, split_blocks=sb,
+                                 **eps)
+    Tp = w.traversal_lengths()
+    np.testing.assert_array_equal(issued, Tp)
+    _, stop_a, _, _ = check(w, tag=f"ART split={split}", split_blocks=sb, **eps)
+    np.testing.assert_array_equal(stop_d, stop_a)
+    assert np.any(stop_d < Tp), "the rule should fire somewhere"
+
+
+def test_detect_only_never_fires(torch_cuda):
+    w = make_workload(scaled(3, "B"))
+    _, stop, issued, _ = check(w, tag="detect-only eps 0", flags=orc.FLAG_DETECT_ONLY, eps_scale=0.0, eps_dir=0.0)
+    np.testing.assert_array_equal(stop, w.traversal_lengths())
+    np.testing.assert_array_equal(issued, w.traversal_lengths())
