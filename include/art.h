@@ -113,6 +113,12 @@ typedef struct {
                             a recompute of the chunk holding the stop);
                             blocks_issued then counts the re-read blocks     */
   int32_t flags;         /* OR of art_flag; must be 0 in full mode           */
+  int32_t pairing;       /* ART mode with one work item per unit: 0 =
+                            library's choice (one), 1 = one unit per workgroup,
+                            2 = two units per workgroup walked in lockstep
+                            (the two units sharing a CU then advance at the
+                            same pace); ignored otherwise.  Results do not
+                            depend on it.                                    */
 } art_params;
 
 typedef struct {

@@ -40,7 +40,7 @@ EXPORTS = ("art_workspace_size", "art_decode", "art_last_error", "art_status_str
 class art_params(ctypes.Structure):
     _fields_ = [("block_size", ctypes.c_int32), ("eps_scale", ctypes.c_float), ("eps_dir", ctypes.c_float),
                 ("patience", ctypes.c_int32), ("order", ctypes.c_int32), ("mode", ctypes.c_int32),
-                ("split_blocks", ctypes.c_int32), ("flags", ctypes.c_int32)]
+                ("split_blocks", ctypes.c_int32), ("flags", ctypes.c_int32), ("pairing", ctypes.c_int32)]
 
 
 class art_shape(ctypes.Structure):
@@ -94,8 +94,8 @@ def make_shape(batch, num_q_heads, num_kv_heads, head_dim, dtype, page_size=0, m
 
 
 def make_params(eps_scale=1e-3, eps_dir=1e-4, patience=2, order=ART_ORDER_RECENT_FIRST, mode=ART_MODE_ART,
-                block_size=64, split_blocks=0, flags=0) -> art_params:
-    return art_params(block_size, eps_scale, eps_dir, patience, order, mode, split_blocks, flags)
+                block_size=64, split_blocks=0, flags=0, pairing=0) -> art_params:
+    return art_params(block_size, eps_scale, eps_dir, patience, order, mode, split_blocks, flags, pairing)
 
 
 def workspace_size(shape: art_shape, params: art_params) -> int:
@@ -149,7 +149,7 @@ class ArtDecoder:
 
     def decode(self, q, k, v, context_lens, *, dtype: int, page_size: int = 0, block_table=None,
                kept_blocks=None, kept_count=None, eps_scale=1e-3, eps_dir=1e-4, patience=2,
-               order=ART_ORDER_RECENT_FIRST, mode=ART_MODE_ART, block_size=64, split_blocks=0, flags=0,
+               order=ART_ORDER_RECENT_FIRST, mode=ART_MODE_ART, block_size=64, split_blocks=0, flags=0, pairing=0,
                out=None, stop_idx=None, blocks_issued=None, stream=None) -> DecodeResult:
         torch = self.torch
         B, Hq, d = q.shape
@@ -162,7 +162,7 @@ class ArtDecoder:
                            max_pages=block_table.shape[1] if block_table is not None else 0,
                            num_pages=k.shape[0] if page_size else 0,
                            max_kept=kept_blocks.shape[2] if kept_blocks is not None else 0)
-        params = make_params(eps_scale, eps_dir, patience, order, mode, block_size, split_blocks, flags)
+        params = make_params(eps_scale, eps_dir, patience, order, mode, block_size, split_blocks, flags, pairing)
         nbytes = workspace_size(shape, params)
         if nbytes == 0:
             raise ArtError(ART_ERR_INVALID_ARG, "art_workspace_size")

@@ -307,6 +307,7 @@ struct UnitView {
   int n_trav;            // T'
   int zero_pos;          // GIVEN order: position of block 0 in the list, or -1
   int log2_page;         // paged: log2(page size)
+  int row_pages;         // paged: entries per block-table row (max_pages)
   int hkv, h;
   int num_pages;
 };
@@ -367,6 +368,40 @@ __device__ __forceinline__ BlockAddr block_addr(const UnitView& u, int j, int& b
   return ba;
 }
 
+// Paged rows of block j from one 16-byte scalar load instead of four
+// dependent ones.  The four block-table entries starting at
+// min((64 j) >> log2(page), max_pages - 4) hold the pages of all four
+// 16-token groups of block j, also those clamped to the sequence's last
+// page: the groups' pages are consecutive from (64 j) >> log2(page), and the
+// window only moves back from the row's end when it would pass it.  Rows of
+// fewer than 4 entries take the per-group path.
+template <int ROW, bool PAGED>
+__device__ __forceinline__ BlockAddr block_addr4(const UnitView& u, int j, int& bad) {
+  if constexpr (PAGED) {
+    if (u.row_pages >= 4) {
+      const int base = min((j * kBlk) >> u.log2_page, u.row_pages - 4);
+      const int32_t* w = u.bt + base;
+      const int e[4] = {sload(w), sload(w + 1), sload(w + 2), sload(w + 3)};  // merged into one load
+      BlockAddr ba;
+      ba.j = j;
+      ba.nvalid = min(kBlk, u.n_ctx - j * kBlk);
+      const int pmask = (1 << u.log2_page) - 1;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int tok = j * kBlk + 16 * g;
+        const int idx = min(tok >> u.log2_page, u.n_pages - 1) - base;  // in [0, 3]
+        int pg = idx == 0 ? e[0] : (idx == 1 ? e[1] : (idx == 2 ? e[2] : e[3]));
+        const bool oob = (unsigned)pg >= (unsigned)u.num_pages;
+        bad |= oob;
+        pg = oob ? 0 : pg;
+        ba.row[g] = (((uint32_t)pg * (uint32_t)u.hkv + (uint32_t)u.h) << u.log2_page) + (uint32_t)(tok & pmask);
+      }
+      return ba;
+    }
+  }
+  return block_addr<ROW, PAGED>(u, j, bad);
+}
+
 // ---------------------------------------------------------------------------
 // LDS layout (one workgroup)
 // ---------------------------------------------------------------------------
@@ -383,6 +418,7 @@ struct alignas(16) RoundLds {
   int zero_pos;
   int ticket;                         // split ART: this workgroup's work item
   int flag;                           // split ART: predecessor's carry flag / early stop
+  int live;                           // two units per workgroup: positions left after the last round
 };
 // Split ART look-back replay state (reuses the V slabs): the chunk's block
 // summaries transposed to [block][head][probe dim], |x|^2 per position and
@@ -412,24 +448,34 @@ struct alignas(16) EpilogueLds {     // per-wave final state (reuses the V slabs
 // ---------------------------------------------------------------------------
 // SPLIT: the ordered split-ART instantiation (ticket order, look-back replay,
 // recompute); the other instantiation serves full mode and single-chunk ART.
-template <int DT, int G, bool PAGED, bool SPLIT>
-__global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(KernelArgs a) {
+// TEAMS = 2 (single-chunk ART only): a workgroup of two teams of 4 waves
+// walks two units, one per team, in lockstep: both teams meet at every
+// round's barriers, so the two units on a CU advance at the same pace (two
+// separate workgroups on one CU do not: the older one's loads are served
+// first and the younger unit falls far behind).  A team whose unit is done,
+// or that has no unit, stays idle in the loop until both are done.
+template <int DT, int G, bool PAGED, bool SPLIT, int TEAMS>
+__global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_decode_kernel(KernelArgs a) {
+  static_assert(TEAMS == 1 || (TEAMS == 2 && !SPLIT), "two teams only in single-chunk ART");
   using GE = Geo<DT>;
   constexpr int D = GE::D, ES = GE::ES, PPC = GE::PPC;
   constexpr int NDT = D / 16;  // 16-dim output tiles
   constexpr int ROW = D * ES;
   static_assert(ROW == kRowChunks * 16, "rows must be 16 chunks of 16 bytes");
-  __shared__ RoundLds<G, D> R;
-  __shared__ alignas(16) uint8_t vbuf[kMaxWaves][kVSlab];
+  __shared__ RoundLds<G, D> R_all[TEAMS];
+  __shared__ alignas(16) uint8_t vbuf_all[TEAMS][kMaxWaves][kVSlab];
   // the waves' final state is stashed above the replay state, so a split
   // chunk can keep its pass-0 result in LDS while the replay runs
   constexpr int kEpiOff = 32768;
   static_assert(sizeof(ReplayLds<D>) <= kEpiOff, "replay state must fit below the stash");
-  static_assert(kEpiOff + sizeof(EpilogueLds<G, D>) <= sizeof(vbuf), "stash must fit the V slabs");
+  static_assert(kEpiOff + sizeof(EpilogueLds<G, D>) <= sizeof(vbuf_all[0]), "stash must fit the V slabs");
 
   constexpr int W = kMaxWaves;  // waves per work item
-  const int tid = threadIdx.x;
+  const int team = TEAMS == 1 ? 0 : uni((int)(threadIdx.x >> 8));
+  const int tid = threadIdx.x & (kWave * kMaxWaves - 1);  // thread within the team
   const int wid = uni(tid >> 6);
+  RoundLds<G, D>& R = R_all[team];
+  auto& vbuf = vbuf_all[team];
   const int lane = threadIdx.x & 63;
   const int lg = lane >> 4;
   const int c = lane & 15;
@@ -440,13 +486,17 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
   // Split ART hands out work items in ticket order, chunk-major: an item's
   // predecessor chunk always holds a smaller ticket, so it is running or done
   // when the item waits for its carry.
-  int item = blockIdx.x;
+  int item = blockIdx.x * TEAMS + team;
+  // two teams: an odd unit count leaves the last team without a unit
+  const bool phantom = TEAMS == 2 && item >= n_items;
+  if (phantom) item = n_items - 1;
+  bool idle = phantom;  // two teams: nothing to walk (outputs already written)
   if constexpr (SPLIT) {
     if (tid == 0) R.ticket = (int)atomicAdd(&a.ws->ticket, 1u);
     __syncthreads();
     item = uni(R.ticket);
   }
-  if (item == 0 && tid == 0) {
+  if (item == 0 && tid == 0 && !phantom) {
     a.ws->magic = kWsMagic;
     a.ws->n_items = n_items;
   }
@@ -469,12 +519,14 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
   u.n_blocks = (u.n_ctx + kBlk - 1) / kBlk;
   if constexpr (PAGED) {
     u.log2_page = 31 - __builtin_clz(a.page_size);
+    u.row_pages = a.max_pages;
     u.n_pages = (u.n_ctx + a.page_size - 1) >> u.log2_page;
     u.bt = a.block_table + (size_t)b * a.max_pages;
     u.k = (const char*)a.k;
     u.v = (const char*)a.v;
   } else {
     u.log2_page = 0;
+    u.row_pages = 0;
     u.n_pages = 0;
     u.bt = nullptr;
     const size_t base = ((size_t)b * a.hkv + h) * (size_t)a.max_ctx * ROW;
@@ -513,7 +565,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
     const int bad = uni(R.bad);
     const int zp = uni(R.zero_pos);
     __syncthreads();
-    if (bad) {
+    if (bad && !phantom) {
       if (tid == 0) a.items[item] = ItemState{ART_ERR_DEVICE_INPUT, -1};
       if (chunk == 0) {
         for (int i = tid; i < G * D; i += kWave * kMaxWaves) out_rows[i] = 0.f;
@@ -522,15 +574,18 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
           if (a.blocks_issued) a.blocks_issued[unit] = 0;
         }
       }
-      return;
+    }
+    if (bad) {
+      if constexpr (TEAMS == 1) return;
+      idle = true;
     }
     u.zero_pos = zp == 0x7fffffff ? -1 : zp;
   }
   const int item_status = bad_input ? ART_ERR_DEVICE_INPUT : ART_OK;
-  if (u.n_trav <= 0 || t_begin >= u.n_trav) {  // nothing (left) to attend to
+  if (!idle && (u.n_trav <= 0 || t_begin >= u.n_trav)) {  // nothing (left) to attend to
     if (tid == 0) a.items[item] = ItemState{item_status, 0};
   }
-  if (u.n_trav <= 0) {  // out = 0, stop = 0
+  if (!idle && u.n_trav <= 0) {  // out = 0, stop = 0
     if (chunk == 0) {
       for (int i = tid; i < G * D; i += kWave * kMaxWaves) out_rows[i] = 0.f;
       if (tid == 0) {
@@ -538,9 +593,13 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
         if (a.blocks_issued) a.blocks_issued[unit] = 0;
       }
     }
-    return;
+    if constexpr (TEAMS == 1) return;
+    idle = true;
   }
-  if (t_begin >= t_end) return;  // chunk past this unit's traversal
+  if (t_begin >= t_end) {  // chunk past this unit's traversal
+    if constexpr (TEAMS == 1) return;
+    idle = true;
+  }
 
   // ---- query operand (B of S^T = K q^T): k-step j, lane (lg, c) holds the
   // 16 bytes of chunk 4j + lg of head c % G (heads replicated over columns)
@@ -657,7 +716,10 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
   // the chunk, pass 1 recomputes the chunk's output up to the stop.
   const bool split = SPLIT && art_mode && !single;
   bool discard = false;  // the unit stopped before this chunk
-  int t_stop = t_end;
+  int t_stop = idle ? t_begin : t_end;
+  if constexpr (TEAMS == 2) {
+    if (tid == 0) R.live = idle ? 0 : 1;  // read after the first round's first barrier
+  }
 
   // ---- split ART: look-back replay of the stop rule over this chunk -----------
   // After pass 0 the chunk's block summaries are in the workspace.  Wait for
@@ -865,21 +927,22 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
     }
     BlockAddr cur;
     if (t_begin + wid < t_stop) {
-      cur = block_addr<ROW, PAGED>(u, uni(block_at(u, a.order, t_begin + wid)), bad_page);
+      cur = block_addr4<ROW, PAGED>(u, uni(block_at(u, a.order, t_begin + wid)), bad_page);
       load_k(cur, 0.f);
       load_v(cur);
       ++issued;
     }
     int parity = 0;
 
-    for (int t0 = t_begin; t0 < t_stop; t0 += W) {
+    // two teams: the loop ends for both at once, on the liveness flags (below)
+    for (int t0 = t_begin; (TEAMS == 2 && art_mode) || t0 < t_stop; t0 += W) {
       const int t = t0 + wid;
       const bool active = t < t_stop;
       const int n_act = min(W, t_stop - t0);
       const int tn = t + W;
       const bool has_next = tn < t_stop;
       BlockAddr nxt = cur;
-      if (has_next) nxt = block_addr<ROW, PAGED>(u, uni(block_at(u, a.order, tn)), bad_page);
+      if (has_next) nxt = block_addr4<ROW, PAGED>(u, uni(block_at(u, a.order, tn)), bad_page);
 
       float m_new = m_c, alpha = 1.f, lblk = 0.f;
       f32x4 bacc[NDT];
@@ -1017,7 +1080,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
               }
             }
         }
-        if (has_next) load_v(nxt);
+        if (has_next && !(art_mode && !split)) load_v(nxt);  // in-round ART: after the summary reads below
       }
 
       int stop_round = -1;  // this round's stop, as a traversal count
@@ -1049,6 +1112,14 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
           }
         }
         lds_barrier();
+        bool team_live = true;
+        if constexpr (TEAMS == 2) {
+          // liveness of both teams after the previous round (written before
+          // its end, read here after a barrier): when neither has positions
+          // left, this round is empty for both and the walk ends
+          if (!uni(R_all[0].live | R_all[1].live)) break;
+          team_live = uni(R.live) != 0;
+        }
         // ---- the round's positions, in order ------------------------------------
         // Every wave merges the round's block summaries, in traversal order,
         // onto the carried prefix state on the probe dims (lane (lg, c): head
@@ -1061,6 +1132,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
         // at its own, then forms |x^(t)|^2, |x^(t-1)|^2 and x^(t).x^(t-1)
         // (per-head row sums, divided by that head's mass, summed over heads)
         // and runs the two tests for its own position only.
+        if (team_live) {
         float mk[kMaxWaves];
         double lk[kMaxWaves], pk[kMaxWaves][PPC];
         float M = mP;
@@ -1074,6 +1146,10 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
           for (int i = 0; i < PPC; ++i) pk[k][i] = on ? (double)s2.ps[c * PPC + i][hg] : 0.0;
           M = fmaxf(M, mk[k]);
         }
+        // this wave's next V goes out only now: DMAs landing in LDS would slow
+        // the summary reads above
+        wait_lgkm0();
+        if (has_next) load_v(nxt);
         const double sP = (double)__builtin_amdgcn_exp2f(mP - M);
         double L = lP * sP, P[PPC];
   #pragma unroll
@@ -1117,8 +1193,10 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
             R.chk[parity][wid].stable = stable;
           }
         }
+        }  // team_live
         lds_barrier();
         // ---- patience counter over the round's checks, in traversal order ---------
+        if (team_live) {
         int sbits = 0;  // bit w2: the check at position t0 + w2 passed
   #pragma unroll
         for (int w2 = 0; w2 < kMaxWaves; ++w2) {
@@ -1137,10 +1215,14 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
           }
         }
         stop_round = uni(stop_round);
+        }  // team_live
         parity ^= 1;
         if (detect_only) {  // keep the first stop, terminate nothing
           if (detected < 0) detected = stop_round;
           stop_round = -1;
+        }
+        if constexpr (TEAMS == 2) {  // read by both teams after the next round's first barrier
+          if (tid == 0) R.live = (team_live && stop_round < 0 && t0 + W < t_stop) ? 1 : 0;
         }
       }
 
@@ -1159,7 +1241,8 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
       }
       if (stop_round >= 0) {
         stop = stop_round;
-        break;
+        if constexpr (TEAMS == 1) break;
+        t_stop = stop_round;  // two teams: idle until the other team is done
       }
       cur = nxt;
     }
@@ -1175,7 +1258,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
   if (!stashed) stash_waves();
 
   // ---- epilogue: merge the stashed waves, normalize -----------------------------
-  for (int o = tid; o < G * D; o += kWave * kMaxWaves) {
+  for (int o = tid; o < G * D && !idle; o += kWave * kMaxWaves) {
     const int g = o / D, dim = o % D;
     float M = -INFINITY;
     for (int w2 = 0; w2 < W; ++w2)
@@ -1199,7 +1282,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves, 2) void art_decode_kernel(Kernel
       }
     }
   }
-  if (tid == 0) {
+  if (tid == 0 && !idle) {
     int tot = 0, bad = 0;
     for (int w2 = 0; w2 < W; ++w2) {
       tot += E.issued[w2];
@@ -1272,9 +1355,12 @@ template <int DT, int G, bool PAGED>
 static hipError_t launch_t(const KernelArgs& a, int grid, int waves, hipStream_t s) {
   (void)waves;
   if (a.split_art)
-    hipLaunchKernelGGL((art_decode_kernel<DT, G, PAGED, true>), dim3(grid), dim3(kWave * kMaxWaves), 0, s, a);
+    hipLaunchKernelGGL((art_decode_kernel<DT, G, PAGED, true, 1>), dim3(grid), dim3(kWave * kMaxWaves), 0, s, a);
+  else if (a.pair)  // one work item per unit, two per workgroup
+    hipLaunchKernelGGL((art_decode_kernel<DT, G, PAGED, false, 2>), dim3((grid + 1) / 2), dim3(2 * kWave * kMaxWaves),
+                       0, s, a);
   else
-    hipLaunchKernelGGL((art_decode_kernel<DT, G, PAGED, false>), dim3(grid), dim3(kWave * kMaxWaves), 0, s, a);
+    hipLaunchKernelGGL((art_decode_kernel<DT, G, PAGED, false, 1>), dim3(grid), dim3(kWave * kMaxWaves), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.max_chunks > 1) {
@@ -1302,6 +1388,7 @@ __global__ void art_split_init_kernel(KernelArgs a) {
 
 hipError_t launch(const KernelArgs& a, hipStream_t s) {
   const int n_units = a.batch * a.hkv;
+  if (a.pair && (a.max_chunks != 1 || a.mode != ART_MODE_ART || a.split_art)) return hipErrorInvalidValue;
   if (a.split_art) {
     const int n = n_units * a.max_chunks;
     if (a.dtype == ART_DT_BF16)

@@ -32,7 +32,7 @@ def log(*a):
 
 
 def run_gpu(w, mode=1, patience=None, eps_scale=None, eps_dir=None, order=None, split_blocks=0, dev=None,
-            decoder=None, flags=0):
+            decoder=None, flags=0, pairing=0):
     """Upload (unless ``dev`` is given) and run art_decode; returns numpy arrays."""
     import torch
     from kv_cache_early_amd import ArtDecoder
@@ -44,7 +44,8 @@ def run_gpu(w, mode=1, patience=None, eps_scale=None, eps_dir=None, order=None, 
                    eps_scale=s.eps_scale if eps_scale is None else eps_scale,
                    eps_dir=s.eps_dir if eps_dir is None else eps_dir,
                    patience=s.patience if patience is None else patience,
-                   order=s.order if order is None else order, mode=mode, split_blocks=split_blocks, flags=flags)
+                   order=s.order if order is None else order, mode=mode, split_blocks=split_blocks, flags=flags,
+                   pairing=pairing)
     torch.cuda.synchronize()
     err = dec.device_error()
     return (r.out.cpu().numpy().astype(np.float64), r.stop_idx.cpu().numpy().astype(np.int64),

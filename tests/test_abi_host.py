@@ -46,7 +46,7 @@ def good_shape(**kw):
 
 def good_params(**kw):
     d = dict(eps_scale=1e-3, eps_dir=1e-4, patience=2, order=art.ART_ORDER_RECENT_FIRST, mode=art.ART_MODE_ART,
-             block_size=64, split_blocks=0, flags=0)
+             block_size=64, split_blocks=0, flags=0, pairing=0)
     d.update(kw)
     return art.make_params(**d)
 
@@ -80,6 +80,7 @@ CASES = [
     ("given without kept list", dict(params=good_params(order=art.ART_ORDER_GIVEN)), art.ART_ERR_INVALID_ARG),
     ("negative split", dict(params=good_params(split_blocks=-1)), art.ART_ERR_INVALID_ARG),
     ("unknown flag", dict(params=good_params(flags=8)), art.ART_ERR_INVALID_ARG),
+    ("bad pairing", dict(params=good_params(pairing=3)), art.ART_ERR_INVALID_ARG),
     ("flags in full mode", dict(params=good_params(mode=art.ART_MODE_FULL, flags=art.ART_FLAG_DETECT_ONLY)),
      art.ART_ERR_INVALID_ARG),
     ("kept without count", dict(shape=good_shape(max_kept=8), kept=FAKE), art.ART_ERR_INVALID_ARG),

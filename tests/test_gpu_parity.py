@@ -277,3 +277,75 @@ def test_detect_only_never_fires(torch_cuda):
     _, stop, issued, _ = check(w, tag="detect-only eps 0", flags=orc.FLAG_DETECT_ONLY, eps_scale=0.0, eps_dir=0.0)
     np.testing.assert_array_equal(stop, w.traversal_lengths())
     np.testing.assert_array_equal(issued, w.traversal_lengths())
+
+
+# ---------------------------------------------------------------------------
+# two units per workgroup (lockstep teams) against one unit per workgroup
+# ---------------------------------------------------------------------------
+def _pair_case(case):
+    s3 = scaled(3, "B")
+    kw = {}
+    if case == "scaled":
+        w = make_workload(s3)
+    elif case == "odd units":  # 3 units: the second workgroup's second team has none
+        w = make_workload(replace(s3, batch=3, num_q_heads=4, num_kv_heads=1))
+        kw = dict(eps_scale=5e-2, eps_dir=5e-3)
+    elif case == "edge lengths":  # empty and one-block units next to long ones
+        lens = np.array([0, 1, 63, 64, 65, 127, 129, 1000], dtype=np.int32)
+        w = make_workload(replace(s3, batch=8), context_lens=lens)
+        kw = dict(eps_scale=5e-2, eps_dir=5e-3, patience=1)
+    elif case == "bad kept list":  # one team's unit is rejected, its partner runs
+        w = make_workload(scaled(5, "B"))
+        w.kept_blocks = w.kept_blocks.copy()
+        w.kept_blocks[0, 1, 3] = 10 ** 6
+    elif case == "forced stop":  # partners stop at different rounds
+        w = make_workload(s3)
+        kw = dict(eps_scale=1e30, eps_dir=1e30, patience=2)
+    elif case == "detect-only":
+        w = make_workload(s3)
+        kw = dict(eps_scale=5e-2, eps_dir=5e-3, flags=orc.FLAG_DETECT_ONLY)
+    elif case == "natural order":
+        w = make_workload(s3)
+        kw = dict(order=orc.ORDER_NATURAL, eps_scale=5e-2, eps_dir=5e-3)
+    else:
+        raise ValueError(case)
+    return w, kw
+
+
+PAIR_CASES = ["scaled", "odd units", "edge lengths", "bad kept list", "forced stop", "detect-only", "natural order"]
+
+
+@pytest.mark.parametrize("case", PAIR_CASES)
+def test_two_units_per_workgroup(torch_cuda, case):
+    """Lockstep teams change scheduling only: outputs, stops and issued
+    counts equal the one-unit-per-workgroup kernel's bit for bit, and the
+    oracle's within the parity bar."""
+    from kv_cache_early_amd import art
+    w, kw = _pair_case(case)
+    log(f"[case] pairing {case}: one unit per workgroup")
+    o1, s1, i1, e1 = run_gpu(w, pairing=1, **kw)
+    log(f"[case] pairing {case}: two units per workgroup")
+    o2, s2, i2, e2 = run_gpu(w, pairing=2, **kw)
+    assert e1 == e2
+    np.testing.assert_array_equal(s2, s1)
+    np.testing.assert_array_equal(i2, i1)
+    np.testing.assert_array_equal(o2, o1)
+    ckw = {k: v for k, v in kw.items() if k in ("patience", "eps_scale", "eps_dir", "order", "flags")}
+    units = None
+    if case == "bad kept list":
+        assert e2 == art.ART_ERR_DEVICE_INPUT and s2[0, 1] == -1
+        units = [(b, h) for b in range(w.spec.batch) for h in range(w.spec.num_kv_heads) if (b, h) != (0, 1)]
+    else:
+        assert e2 == 0
+    rep, _ = compare(w, o2, s2, units=units, **ckw)
+    log(f"   {rep}")
+    assert rep.ok(), (rep.unexcused[:5], rep.bad_outputs[:5])
+
+
+def test_pairing_is_ignored_in_full_mode(torch_cuda):
+    w = make_workload(scaled(3, "A"))
+    log("[case] pairing 2 in full mode")
+    o1, s1, i1, _ = run_gpu(w, mode=0, pairing=1)
+    o2, s2, i2, _ = run_gpu(w, mode=0, pairing=2)
+    np.testing.assert_array_equal(o2, o1)
+    np.testing.assert_array_equal(s2, s1)
