@@ -161,8 +161,10 @@ size_t art_workspace_size(const art_shape* shape, const art_params* params);
  *                 rewrites what it reads, so no initialisation or per-call
  *                 clearing is needed and the call enqueues no memset)
  *
- * ART_MODE_ART enqueues one kernel; ART_MODE_FULL with more than one chunk
- * per unit enqueues the decode kernel and an LSE-combine kernel.
+ * ART_MODE_ART with one work item per unit enqueues one kernel; ordered
+ * split ART enqueues an init kernel, the decode kernel and an LSE-combine
+ * kernel; ART_MODE_FULL with more than one chunk per unit enqueues the
+ * decode kernel and the combine kernel.
  */
 art_status art_decode(const art_shape* shape, const art_params* params,
                       const void* q, const void* k, const void* v,
@@ -171,13 +173,69 @@ art_status art_decode(const art_shape* shape, const art_params* params,
                       float* out, int32_t* stop_idx, int32_t* blocks_issued,
                       void* workspace, size_t workspace_bytes, void* stream);
 
-/* Device-side error recorded by the last art_decode that enqueued work on
- * `workspace` (ART_OK, ART_ERR_TIMEOUT or ART_ERR_DEVICE_INPUT; the most
- * severe over its work items).  ART_OK if no launch has used the workspace.
+/* Device-side error recorded by the last call (art_decode, art_block_means
+ * or art_select_blocks) that enqueued work on `workspace` (ART_OK,
+ * ART_ERR_TIMEOUT or ART_ERR_DEVICE_INPUT; the most severe over its work
+ * items).  ART_OK if no launch has used the workspace.
  * Synchronous (device-to-host copies of the workspace's status words); call
  * after synchronizing the decode's stream.  `workspace_bytes` bounds what is
  * read: ART_ERR_WORKSPACE if the recorded work does not fit in it. */
 art_status art_last_error(const void* workspace, size_t workspace_bytes);
+
+/* ---- key-based block selection and importance-first traversal ----------
+ *
+ * The gist.science explainer (section 2.4) composes ART with KV-cache
+ * managers through the traversal sequence, naming importance-first as one
+ * order.  The importance of block j of unit (b, h) is taken as
+ *   s_j = qbar . kbar_j,
+ * qbar = the mean of the unit's G query rows, kbar_j = the mean of the
+ * block's valid key rows (64-token blocks).  A kept list keeps the first
+ * `sink` blocks, the `recent` most recent blocks, and fills up to
+ * n = min(T, ceil(keep_frac * T)) blocks with the highest s_j, ties to the
+ * lower block index (T = ceil(len / 64)).  ART_SELECT_ASCENDING writes the
+ * list in ascending block order (for ART_ORDER_NATURAL / RECENT_FIRST);
+ * ART_SELECT_IMPORTANCE writes it by decreasing s_j, ties to the lower
+ * index (for ART_ORDER_GIVEN: an importance-first traversal; with
+ * keep_frac = 1 it orders every block). */
+typedef enum { ART_SELECT_ASCENDING = 0, ART_SELECT_IMPORTANCE = 1 } art_select_order;
+
+typedef struct {
+  float keep_frac;  /* (0, 1]                                               */
+  int32_t sink;     /* leading blocks always kept, >= 0                     */
+  int32_t recent;   /* most recent blocks always kept, >= 0                 */
+  int32_t order;    /* art_select_order of the written list                 */
+} art_select_params;
+
+/* Workspace bytes for art_block_means and art_select_blocks on `shape`
+ * (0 on an invalid shape).  Same rules as art_decode's workspace: device
+ * memory, 256-byte aligned, no initialisation needed; art_last_error reads
+ * the status they record. */
+size_t art_select_workspace_size(const art_shape* shape);
+
+/* Block-mean keys.  For every unit (b, h) and block j < ceil(len_b / 64):
+ *   means[((b * Hkv + h) * max_blocks + j) * d + i] = mean over the block's
+ *   valid tokens of K[token][i]            (fp32, written)
+ * Entries for j >= ceil(len_b / 64) are not written.  K, context_lens and
+ * block_table as for art_decode (shape.max_kept is ignored); max_blocks >=
+ * ceil(capacity / 64), capacity = max_ctx (contiguous) or max_pages *
+ * page_size (paged).  Reads every key once; meant to run when blocks are
+ * written, not per decode step.  Lengths outside [0, capacity] are clamped
+ * and page ids outside the pool read page 0; both are reported as
+ * ART_ERR_DEVICE_INPUT by art_last_error. */
+art_status art_block_means(const art_shape* shape, const void* k, const int32_t* context_lens,
+                           const int32_t* block_table, float* means, int32_t max_blocks,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Kept lists from block-mean keys (see above): for every unit writes
+ * kept_blocks[(b * Hkv + h) * shape.max_kept + i] for i < n, and
+ * kept_count[b * Hkv + h] = n.  q as for art_decode; means as written by
+ * art_block_means with the same max_blocks.  Requires shape.max_kept >=
+ * min(T_max, ceil(keep_frac * T_max)) for T_max = ceil(capacity / 64), and
+ * T_max <= 4096 (ART_ERR_UNSUPPORTED otherwise). */
+art_status art_select_blocks(const art_shape* shape, const art_select_params* params, const void* q,
+                             const float* means, int32_t max_blocks, const int32_t* context_lens,
+                             int32_t* kept_blocks, int32_t* kept_count,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static English description of a status code. */
 const char* art_status_string(art_status status);

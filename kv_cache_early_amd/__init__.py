@@ -6,5 +6,5 @@ ctypes binding.
 """
 from . import art  # noqa: F401
 from .art import (ART_DT_BF16, ART_DT_F32, ART_FLAG_DETECT_ONLY, ART_FLAG_NO_DIR, ART_FLAG_NO_SCALE,  # noqa: F401
-                  ART_MODE_ART, ART_MODE_FULL, ART_ORDER_GIVEN, ART_ORDER_NATURAL, ART_ORDER_RECENT_FIRST, ArtDecoder,
-                  ArtError, DecodeResult)
+                  ART_MODE_ART, ART_MODE_FULL, ART_ORDER_GIVEN, ART_ORDER_NATURAL, ART_ORDER_RECENT_FIRST,
+                  ART_SELECT_ASCENDING, ART_SELECT_IMPORTANCE, ArtDecoder, ArtError, DecodeResult)

@@ -33,8 +33,11 @@ ART_MODE_ART = 1
 ART_FLAG_NO_SCALE = 1
 ART_FLAG_NO_DIR = 2
 ART_FLAG_DETECT_ONLY = 4
+ART_SELECT_ASCENDING = 0
+ART_SELECT_IMPORTANCE = 1
 
-EXPORTS = ("art_workspace_size", "art_decode", "art_last_error", "art_status_string", "art_probe_stride")
+EXPORTS = ("art_workspace_size", "art_decode", "art_last_error", "art_status_string", "art_probe_stride",
+           "art_select_workspace_size", "art_block_means", "art_select_blocks")
 
 
 class art_params(ctypes.Structure):
@@ -48,6 +51,11 @@ class art_shape(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("max_ctx", ctypes.c_int32), ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int32),
                 ("max_kept", ctypes.c_int32)]
+
+
+class art_select_params(ctypes.Structure):
+    _fields_ = [("keep_frac", ctypes.c_float), ("sink", ctypes.c_int32), ("recent", ctypes.c_int32),
+                ("order", ctypes.c_int32)]
 
 
 class ArtError(RuntimeError):
@@ -79,6 +87,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.art_status_string.restype = ctypes.c_char_p
     lib.art_probe_stride.argtypes = []
     lib.art_probe_stride.restype = ctypes.c_int32
+    lib.art_select_workspace_size.argtypes = [ctypes.POINTER(art_shape)]
+    lib.art_select_workspace_size.restype = ctypes.c_size_t
+    lib.art_block_means.argtypes = [ctypes.POINTER(art_shape), vp, vp, vp, vp, ctypes.c_int32, vp, ctypes.c_size_t, vp]
+    lib.art_block_means.restype = ctypes.c_int
+    lib.art_select_blocks.argtypes = [ctypes.POINTER(art_shape), ctypes.POINTER(art_select_params), vp, vp,
+                                      ctypes.c_int32, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.art_select_blocks.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -113,6 +128,25 @@ def decode_raw(shape: art_shape, params: art_params, q, k, v, context_lens, bloc
                                  _ptr(context_lens), _ptr(block_table), _ptr(kept_blocks), _ptr(kept_count),
                                  _ptr(out), _ptr(stop_idx), _ptr(blocks_issued), _ptr(workspace),
                                  workspace_bytes, stream))
+
+
+def select_workspace_size(shape: art_shape) -> int:
+    return int(load().art_select_workspace_size(ctypes.byref(shape)))
+
+
+def block_means_raw(shape: art_shape, k, context_lens, block_table, means, max_blocks: int, workspace,
+                    workspace_bytes: int, stream: Optional[int]) -> int:
+    """Call art_block_means with raw device pointers taken from tensors; returns the status."""
+    return int(load().art_block_means(ctypes.byref(shape), _ptr(k), _ptr(context_lens), _ptr(block_table),
+                                      _ptr(means), int(max_blocks), _ptr(workspace), workspace_bytes, stream))
+
+
+def select_blocks_raw(shape: art_shape, params: art_select_params, q, means, max_blocks: int, context_lens,
+                      kept_blocks, kept_count, workspace, workspace_bytes: int, stream: Optional[int]) -> int:
+    """Call art_select_blocks with raw device pointers taken from tensors; returns the status."""
+    return int(load().art_select_blocks(ctypes.byref(shape), ctypes.byref(params), _ptr(q), _ptr(means),
+                                        int(max_blocks), _ptr(context_lens), _ptr(kept_blocks), _ptr(kept_count),
+                                        _ptr(workspace), workspace_bytes, stream))
 
 
 def last_error(workspace, workspace_bytes: int) -> int:
@@ -180,6 +214,60 @@ class ArtDecoder:
         if st != ART_OK:
             raise ArtError(st)
         return DecodeResult(out, stop_idx, blocks_issued)
+
+    def block_means(self, k, context_lens, *, num_q_heads: int, dtype: int, page_size: int = 0,
+                    block_table=None, max_blocks: Optional[int] = None, out=None, stream=None):
+        """art_block_means: fp32 [B, Hkv, max_blocks, d] block-mean keys (rows past
+        a sequence's blocks are left as they are)."""
+        torch = self.torch
+        B, Hkv, d = context_lens.shape[0], k.shape[1], k.shape[3]
+        max_ctx = k.shape[2] if page_size == 0 else 0
+        max_pages = block_table.shape[1] if block_table is not None else 0
+        cap = max_ctx if page_size == 0 else max_pages * page_size
+        mb = (cap + 63) // 64 if max_blocks is None else max_blocks
+        shape = make_shape(B, num_q_heads, Hkv, d, dtype, page_size, max_ctx=max_ctx, max_pages=max_pages,
+                           num_pages=k.shape[0] if page_size else 0)
+        nbytes = select_workspace_size(shape)
+        if nbytes == 0:
+            raise ArtError(ART_ERR_INVALID_ARG, "art_select_workspace_size")
+        ws = self.workspace(nbytes)
+        if out is None:
+            out = torch.zeros((B, Hkv, mb, d), dtype=torch.float32, device=self.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device).cuda_stream
+        st = block_means_raw(shape, k, context_lens, block_table, out, mb, ws, ws.numel(), stream)
+        if st != ART_OK:
+            raise ArtError(st, "art_block_means")
+        return out
+
+    def select_blocks(self, q, means, context_lens, *, dtype: int, keep_frac: float, sink: int, recent: int,
+                      order: int = ART_SELECT_ASCENDING, page_size: int = 0, max_ctx: int = 0, max_pages: int = 0,
+                      max_kept: Optional[int] = None, stream=None):
+        """art_select_blocks: (kept_blocks int32 [B, Hkv, max_kept], kept_count int32 [B, Hkv])."""
+        import math
+        torch = self.torch
+        B, Hq, d = q.shape
+        Hkv, mb = means.shape[1], means.shape[2]
+        cap = max_ctx if page_size == 0 else max_pages * page_size
+        tmax = (cap + 63) // 64
+        if max_kept is None:
+            max_kept = max(1, min(tmax, math.ceil(float(ctypes.c_float(keep_frac).value) * tmax)))
+        shape = make_shape(B, Hq, Hkv, d, dtype, page_size, max_ctx=max_ctx, max_pages=max_pages,
+                           num_pages=1 if page_size else 0, max_kept=max_kept)
+        nbytes = select_workspace_size(shape)
+        if nbytes == 0:
+            raise ArtError(ART_ERR_INVALID_ARG, "art_select_workspace_size")
+        ws = self.workspace(nbytes)
+        kept_blocks = torch.full((B, Hkv, max_kept), -1, dtype=torch.int32, device=self.device)
+        kept_count = torch.empty((B, Hkv), dtype=torch.int32, device=self.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device).cuda_stream
+        params = art_select_params(keep_frac, sink, recent, order)
+        st = select_blocks_raw(shape, params, q, means, mb, context_lens, kept_blocks, kept_count, ws, ws.numel(),
+                               stream)
+        if st != ART_OK:
+            raise ArtError(st, "art_select_blocks")
+        return kept_blocks, kept_count
 
     def device_error(self) -> int:
         """Device-side status of the last decode (synchronizes the device first)."""

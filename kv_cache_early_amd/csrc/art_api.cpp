@@ -29,15 +29,34 @@ int64_t max_traversal(const art_shape& s) {
   return (tokens + kBlockTokens - 1) / kBlockTokens;
 }
 
-art_status validate(const art_shape* sp, const art_params* pp) {
-  if (!sp || !pp) return ART_ERR_INVALID_ARG;
+// Shape rules shared by every entry point.
+art_status validate_shape(const art_shape* sp) {
+  if (!sp) return ART_ERR_INVALID_ARG;
   const art_shape& s = *sp;
-  const art_params& p = *pp;
   if (s.batch < 0 || s.num_q_heads <= 0 || s.num_kv_heads <= 0 || s.head_dim <= 0) return ART_ERR_INVALID_ARG;
   if (s.num_q_heads % s.num_kv_heads != 0) return ART_ERR_INVALID_ARG;
   if (s.dtype != ART_DT_F32 && s.dtype != ART_DT_BF16) return ART_ERR_INVALID_ARG;
   if (s.page_size < 0 || s.max_ctx < 0 || s.max_pages < 0 || s.num_pages < 0 || s.max_kept < 0)
     return ART_ERR_INVALID_ARG;
+  if (s.page_size > 0 && s.page_size % 16 != 0) return ART_ERR_INVALID_ARG;
+  const int G = s.num_q_heads / s.num_kv_heads;
+  if (!((s.dtype == ART_DT_BF16 && s.head_dim == 128) || (s.dtype == ART_DT_F32 && s.head_dim == 64)))
+    return ART_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4) return ART_ERR_UNSUPPORTED;
+  if (s.page_size > 0 && (s.page_size & (s.page_size - 1)) != 0) return ART_ERR_UNSUPPORTED;  // powers of two
+  // index ranges the kernels compute in 32-bit
+  const int64_t units = (int64_t)s.batch * s.num_kv_heads;
+  if (units > (1 << 26) || max_traversal(s) > (1 << 24)) return ART_ERR_UNSUPPORTED;
+  // paged pool rows (page * Hkv + h) * page_size + slot are 32-bit in the kernels
+  if (s.page_size > 0 && (int64_t)s.num_pages * s.num_kv_heads * s.page_size > (int64_t)UINT32_MAX)
+    return ART_ERR_UNSUPPORTED;
+  return ART_OK;
+}
+
+art_status validate(const art_shape* sp, const art_params* pp) {
+  if (!sp || !pp) return ART_ERR_INVALID_ARG;
+  const art_shape& s = *sp;
+  const art_params& p = *pp;
   if (p.block_size <= 0 || p.patience < 1 || p.split_blocks < 0) return ART_ERR_INVALID_ARG;
   if (!finite_nonneg(p.eps_scale) || !finite_nonneg(p.eps_dir)) return ART_ERR_INVALID_ARG;
   if (p.order < ART_ORDER_NATURAL || p.order > ART_ORDER_GIVEN) return ART_ERR_INVALID_ARG;
@@ -46,20 +65,9 @@ art_status validate(const art_shape* sp, const art_params* pp) {
   if ((p.flags & ~kAllFlags) != 0 || (p.mode == ART_MODE_FULL && p.flags != 0)) return ART_ERR_INVALID_ARG;
   if (p.pairing < 0 || p.pairing > 2) return ART_ERR_INVALID_ARG;
   if (p.order == ART_ORDER_GIVEN && s.max_kept == 0) return ART_ERR_INVALID_ARG;
-  if (s.page_size > 0 && s.page_size % 16 != 0) return ART_ERR_INVALID_ARG;
-  // supported set
-  const int G = s.num_q_heads / s.num_kv_heads;
-  if (!((s.dtype == ART_DT_BF16 && s.head_dim == 128) || (s.dtype == ART_DT_F32 && s.head_dim == 64)))
-    return ART_ERR_UNSUPPORTED;
-  if (G != 1 && G != 2 && G != 4) return ART_ERR_UNSUPPORTED;
+  const art_status st = validate_shape(sp);
+  if (st != ART_OK) return st;
   if (p.block_size != kBlockTokens) return ART_ERR_UNSUPPORTED;
-  if (s.page_size > 0 && (s.page_size & (s.page_size - 1)) != 0) return ART_ERR_UNSUPPORTED;  // powers of two
-  // index ranges the kernels compute in 32-bit
-  const int64_t units = (int64_t)s.batch * s.num_kv_heads;
-  if (units > (1 << 26) || max_traversal(s) > (1 << 24)) return ART_ERR_UNSUPPORTED;
-  // paged pool rows (page * Hkv + h) * page_size + slot are 32-bit in the kernels
-  if (s.page_size > 0 && (int64_t)s.num_pages * s.num_kv_heads * s.page_size > (int64_t)UINT32_MAX)
-    return ART_ERR_UNSUPPORTED;
   return ART_OK;
 }
 
@@ -97,6 +105,24 @@ int chunk_blocks(const art_shape& s, const art_params& p) {
   c = (c + kWavesPerItem - 1) / kWavesPerItem * kWavesPerItem;
   return (int)std::min<int64_t>(c, tmax);
 }
+
+// Blocks a sequence can hold: ceil(capacity / 64), capacity = max_ctx or
+// max_pages * page_size (the kept list does not matter for selection).
+int64_t capacity_blocks(const art_shape& s) {
+  const int64_t tokens = s.page_size == 0 ? (int64_t)s.max_ctx : (int64_t)s.max_pages * s.page_size;
+  return (tokens + kBlockTokens - 1) / kBlockTokens;
+}
+
+// Selection workspace: the header and one ItemState per workgroup of the
+// larger of the two launches (block means: four blocks per workgroup).
+size_t select_ws_bytes(const art_shape& s) {
+  const int64_t units = (int64_t)s.batch * s.num_kv_heads;
+  const int64_t groups = std::max<int64_t>(1, (capacity_blocks(s) + 3) / 4);
+  return round256(sizeof(art::WsHeader)) +
+         round256(sizeof(art::ItemState) * (size_t)std::max<int64_t>(1, units * groups));
+}
+
+constexpr int64_t kSelectSortMax = 4096;  // blocks per unit the selection kernel sorts
 
 art::WsLayout layout(const art_shape& s, const art_params& p, int chunk, int max_chunks) {
   art::WsLayout L{};
@@ -228,6 +254,97 @@ art_status art_decode(const art_shape* shape, const art_params* params, const vo
   return e == hipSuccess ? ART_OK : ART_ERR_HIP;
 }
 
+size_t art_select_workspace_size(const art_shape* shape) {
+  if (validate_shape(shape) != ART_OK) return 0;
+  return select_ws_bytes(*shape);
+}
+
+art_status art_block_means(const art_shape* shape, const void* k, const int32_t* context_lens,
+                           const int32_t* block_table, float* means, int32_t max_blocks, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  art_status st = validate_shape(shape);
+  if (st != ART_OK) return st;
+  const art_shape& s = *shape;
+  if (s.batch == 0) return ART_OK;
+  if (!k || !context_lens || !means) return ART_ERR_INVALID_ARG;
+  if (s.page_size > 0 && (!block_table || s.max_pages <= 0 || s.num_pages <= 0)) return ART_ERR_INVALID_ARG;
+  if (s.page_size == 0 && block_table) return ART_ERR_INVALID_ARG;
+  const int64_t tmax = capacity_blocks(s);
+  if (max_blocks < tmax || max_blocks <= 0) return ART_ERR_INVALID_ARG;
+  const int64_t units = (int64_t)s.batch * s.num_kv_heads;
+  const int64_t groups = std::max<int64_t>(1, (tmax + 3) / 4);
+  if (units * groups > INT32_MAX) return ART_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < select_ws_bytes(s) || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return ART_ERR_WORKSPACE;
+  art::SelectArgs a{};
+  a.batch = s.batch;
+  a.hq = s.num_q_heads;
+  a.hkv = s.num_kv_heads;
+  a.dtype = s.dtype;
+  a.page_size = s.page_size;
+  a.max_ctx = s.max_ctx;
+  a.max_pages = s.max_pages;
+  a.num_pages = s.num_pages;
+  a.max_blocks = max_blocks;
+  a.t_max = (int)tmax;
+  a.groups = (int)groups;
+  a.k = k;
+  a.context_lens = context_lens;
+  a.block_table = block_table;
+  a.means = means;
+  char* w = static_cast<char*>(workspace);
+  a.ws = reinterpret_cast<art::WsHeader*>(w);
+  a.items = reinterpret_cast<art::ItemState*>(w + round256(sizeof(art::WsHeader)));
+  return art::launch_block_means(a, static_cast<hipStream_t>(stream)) == hipSuccess ? ART_OK : ART_ERR_HIP;
+}
+
+art_status art_select_blocks(const art_shape* shape, const art_select_params* params, const void* q,
+                             const float* means, int32_t max_blocks, const int32_t* context_lens,
+                             int32_t* kept_blocks, int32_t* kept_count, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  art_status st = validate_shape(shape);
+  if (st != ART_OK) return st;
+  if (!params) return ART_ERR_INVALID_ARG;
+  const art_shape& s = *shape;
+  const art_select_params& p = *params;
+  if (!(p.keep_frac > 0.f && p.keep_frac <= 1.f) || p.sink < 0 || p.recent < 0) return ART_ERR_INVALID_ARG;
+  if (p.order != ART_SELECT_ASCENDING && p.order != ART_SELECT_IMPORTANCE) return ART_ERR_INVALID_ARG;
+  if (s.batch == 0) return ART_OK;
+  if (!q || !means || !context_lens || !kept_blocks || !kept_count) return ART_ERR_INVALID_ARG;
+  const int64_t tmax = capacity_blocks(s);
+  if (max_blocks < tmax || max_blocks <= 0) return ART_ERR_INVALID_ARG;
+  if (tmax > kSelectSortMax) return ART_ERR_UNSUPPORTED;
+  const int64_t need = std::min<int64_t>(tmax, (int64_t)std::ceil((double)p.keep_frac * (double)tmax));
+  if (s.max_kept < need) return ART_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < select_ws_bytes(s) || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return ART_ERR_WORKSPACE;
+  art::SelectArgs a{};
+  a.batch = s.batch;
+  a.hq = s.num_q_heads;
+  a.hkv = s.num_kv_heads;
+  a.dtype = s.dtype;
+  a.page_size = s.page_size;
+  a.max_ctx = s.max_ctx;
+  a.max_pages = s.max_pages;
+  a.num_pages = s.num_pages;
+  a.max_kept = s.max_kept;
+  a.max_blocks = max_blocks;
+  a.t_max = (int)tmax;
+  a.keep_frac = p.keep_frac;
+  a.sink = p.sink;
+  a.recent = p.recent;
+  a.order = p.order;
+  a.q = q;
+  a.context_lens = context_lens;
+  a.means = const_cast<float*>(means);
+  a.kept_blocks = kept_blocks;
+  a.kept_count = kept_count;
+  char* w = static_cast<char*>(workspace);
+  a.ws = reinterpret_cast<art::WsHeader*>(w);
+  a.items = reinterpret_cast<art::ItemState*>(w + round256(sizeof(art::WsHeader)));
+  return art::launch_select(a, static_cast<hipStream_t>(stream)) == hipSuccess ? ART_OK : ART_ERR_HIP;
+}
+
 art_status art_last_error(const void* workspace, size_t workspace_bytes) {
   if (!workspace || workspace_bytes < sizeof(art::WsHeader)) return ART_ERR_INVALID_ARG;
   art::WsHeader h;
@@ -252,7 +369,7 @@ const char* art_status_string(art_status status) {
     case ART_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case ART_ERR_HIP: return "HIP runtime or launch failure";
     case ART_ERR_TIMEOUT: return "split look-back wait timed out on the device";
-    case ART_ERR_DEVICE_INPUT: return "kept list out of range or not strictly ascending";
+    case ART_ERR_DEVICE_INPUT: return "device-side input out of range (context length, page id or kept list)";
   }
   return "unknown status";
 }

@@ -92,4 +92,25 @@ struct WsLayout {
 
 hipError_t launch(const KernelArgs& a, hipStream_t stream);
 
+// Key-based block selection (block-mean keys, kept lists).
+struct SelectArgs {
+  int32_t batch, hq, hkv, dtype, page_size, max_ctx, max_pages, num_pages, max_kept;
+  int32_t max_blocks;     // row stride (blocks) of `means`
+  int32_t t_max;          // ceil(capacity / 64)
+  int32_t groups;         // block-means launch: workgroups per unit (4 blocks each)
+  float keep_frac;
+  int32_t sink, recent, order;
+  const void* q;
+  const void* k;
+  const int32_t* context_lens;
+  const int32_t* block_table;
+  float* means;           // [B][Hkv][max_blocks][d]
+  int32_t* kept_blocks;   // [B][Hkv][max_kept]
+  int32_t* kept_count;    // [B][Hkv]
+  WsHeader* ws;
+  ItemState* items;       // one per work item (workgroup) of the launch
+};
+hipError_t launch_block_means(const SelectArgs& a, hipStream_t stream);
+hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+
 }  // namespace art

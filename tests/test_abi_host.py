@@ -124,3 +124,72 @@ def test_workspace_size():
     assert art.workspace_size(good_shape(head_dim=96), p) == 0
     full_split = art.workspace_size(s, good_params(mode=art.ART_MODE_FULL, split_blocks=4))
     assert full_split > n  # room for the split partials
+
+
+# ---------------------------------------------------------------------------
+# block selection entry points: host-side rejections (nothing is enqueued)
+# ---------------------------------------------------------------------------
+def sel_params(**kw):
+    d = dict(keep_frac=0.5, sink=1, recent=4, order=art.ART_SELECT_ASCENDING)
+    d.update(kw)
+    return art.art_select_params(**d)
+
+
+def call_means(shape=None, k=FAKE, lens=FAKE, bt=FAKE, means=FAKE, max_blocks=1024, ws=FAKE * 16,
+               ws_bytes=1 << 30):
+    shape = shape or good_shape()
+    return art.load().art_block_means(ctypes.byref(shape), k, lens, bt, means, max_blocks, ws, ws_bytes, None)
+
+
+def call_select(shape=None, params=None, q=FAKE, means=FAKE, max_blocks=1024, lens=FAKE, kb=FAKE, kc=FAKE,
+                ws=FAKE * 16, ws_bytes=1 << 30):
+    shape = shape or good_shape(max_kept=512)
+    params = params or sel_params()
+    return art.load().art_select_blocks(ctypes.byref(shape), ctypes.byref(params), q, means, max_blocks, lens, kb, kc,
+                                        ws, ws_bytes, None)
+
+
+MEANS_CASES = [
+    ("null k", dict(k=None), art.ART_ERR_INVALID_ARG),
+    ("null means", dict(means=None), art.ART_ERR_INVALID_ARG),
+    ("max_blocks below capacity", dict(max_blocks=15), art.ART_ERR_INVALID_ARG),
+    ("paged without table", dict(bt=None), art.ART_ERR_INVALID_ARG),
+    ("bad dtype", dict(shape=good_shape(dtype=7)), art.ART_ERR_INVALID_ARG),
+    ("head_dim 96", dict(shape=good_shape(head_dim=96)), art.ART_ERR_UNSUPPORTED),
+    ("small workspace", dict(ws_bytes=64), art.ART_ERR_WORKSPACE),
+    ("misaligned workspace", dict(ws=FAKE * 16 + 8), art.ART_ERR_WORKSPACE),
+]
+
+
+@pytest.mark.parametrize("name,kw,expect", MEANS_CASES, ids=[c[0] for c in MEANS_CASES])
+def test_block_means_rejects(name, kw, expect):
+    assert call_means(**kw) == expect
+
+
+SELECT_CASES = [
+    ("keep_frac 0", dict(params=sel_params(keep_frac=0.0)), art.ART_ERR_INVALID_ARG),
+    ("keep_frac above 1", dict(params=sel_params(keep_frac=1.5)), art.ART_ERR_INVALID_ARG),
+    ("keep_frac nan", dict(params=sel_params(keep_frac=math.nan)), art.ART_ERR_INVALID_ARG),
+    ("negative sink", dict(params=sel_params(sink=-1)), art.ART_ERR_INVALID_ARG),
+    ("bad order", dict(params=sel_params(order=2)), art.ART_ERR_INVALID_ARG),
+    ("max_kept too small", dict(shape=good_shape(max_kept=3)), art.ART_ERR_INVALID_ARG),
+    ("null kept_count", dict(kc=None), art.ART_ERR_INVALID_ARG),
+    ("max_blocks below capacity", dict(max_blocks=15), art.ART_ERR_INVALID_ARG),
+    ("more than 4096 blocks", dict(shape=good_shape(max_pages=20000, max_kept=20000), max_blocks=5000),
+     art.ART_ERR_UNSUPPORTED),
+    ("small workspace", dict(ws_bytes=64), art.ART_ERR_WORKSPACE),
+]
+
+
+@pytest.mark.parametrize("name,kw,expect", SELECT_CASES, ids=[c[0] for c in SELECT_CASES])
+def test_select_blocks_rejects(name, kw, expect):
+    assert call_select(**kw) == expect
+
+
+def test_select_workspace_size():
+    s = good_shape()  # 2 units, 64 pages of 16 tokens = 16 blocks -> 4 groups per unit
+    n = art.select_workspace_size(s)
+    assert n >= 256 + 8 * 2 * 4 and n % 256 == 0
+    assert art.select_workspace_size(good_shape(dtype=7)) == 0
+    assert call_means(shape=good_shape(batch=0)) == art.ART_OK  # empty batch: nothing enqueued
+    assert call_select(shape=good_shape(batch=0, max_kept=512)) == art.ART_OK
