@@ -30,7 +30,9 @@ Reported (one JSON line on stdout):
                  off) against full mode at the same launch shape;
                  ablation: blocks skipped and output error against full
                  decode with the scale test, the direction test or
-                 patience taken out
+                 patience taken out;
+                 importance_first: block-mean keys and the importance
+                 order on the GPU, then ART over that order
 
 Other modes (no timing line):
   --summarize-pmc FETCH_DIR WRITE_DIR   turn two rocprofv3 --pmc runs of
@@ -122,18 +124,18 @@ def accounting(w, stop, issued):
     return kv_bytes(issued) + per_unit + pages, kv_bytes(stop) + per_unit + pages, kv_bytes
 
 
-def decode_kwargs(dev, w, mode, split_blocks, stream, flags=0, patience=None):
+def decode_kwargs(dev, w, mode, split_blocks, stream, flags=0, patience=None, order=None):
     s = w.spec
     return dict(dtype=dev.dtype_code, page_size=dev.page_size, block_table=dev.block_table,
                 kept_blocks=dev.kept_blocks, kept_count=dev.kept_count, eps_scale=s.eps_scale, eps_dir=s.eps_dir,
-                patience=s.patience if patience is None else patience, order=s.order, mode=mode,
-                split_blocks=split_blocks, flags=flags, stream=stream.cuda_stream)
+                patience=s.patience if patience is None else patience, order=s.order if order is None else order,
+                mode=mode, split_blocks=split_blocks, flags=flags, stream=stream.cuda_stream)
 
 
-def time_steps(dec, dev, w, mode, steps, warmup, split_blocks, flush, flags=0):
+def time_steps(dec, dev, w, mode, steps, warmup, split_blocks, flush, flags=0, order=None):
     import torch
     stream = torch.cuda.current_stream()
-    kw = decode_kwargs(dev, w, mode, split_blocks, stream, flags)
+    kw = decode_kwargs(dev, w, mode, split_blocks, stream, flags, order=order)
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if flush else None
     r = dec.decode(dev.q, dev.k, dev.v, dev.context_lens, **kw)
     for _ in range(warmup):
@@ -160,11 +162,11 @@ def time_steps(dec, dev, w, mode, steps, warmup, split_blocks, flush, flags=0):
                 issued=r.blocks_issued.cpu().numpy().astype(np.int64))
 
 
-def measure(dec, w, mode, args, dev=None, flags=0, split_blocks=None):
+def measure(dec, w, mode, args, dev=None, flags=0, split_blocks=None, order=None):
     from workloads.device import to_device
     dev = dev or to_device(w)
     sb = args.split_blocks if split_blocks is None else split_blocks
-    t = time_steps(dec, dev, w, mode, args.steps, args.warmup, sb, not args.no_flush, flags)
+    t = time_steps(dec, dev, w, mode, args.steps, args.warmup, sb, not args.no_flush, flags, order)
     loaded, algo, _ = accounting(w, t["stop"], t["issued"])
     sec = t["ms_mean"] * 1e-3
     Tp = w.traversal_lengths()
@@ -205,6 +207,59 @@ def ablation_report(dec, dev, w, split_blocks, full_out):
                           rel_l2_mean=float(f"{rel.mean():.3e}"), rel_l2_max=float(f"{rel.max():.3e}"),
                           frac_units_rel_l2_over_1e_2=round(float((rel > 1e-2).mean()), 4))
     return rows
+
+
+def time_call(fn, steps, flush):
+    """Mean ms of `fn()` over `steps` calls (HIP events on the current
+    stream, the caches evicted before each call unless `flush` is false)."""
+    import torch
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if flush else None
+    fn()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(steps):
+        if scratch is not None:
+            scratch.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        r = fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    return float(np.mean(ms)), r
+
+
+def importance_report(dec, dev, w, args, head, full_out):
+    """Importance-first traversal on the same workload: block-mean keys and
+    the importance order of every block, both on the GPU, then ART walking
+    that order (ART_ORDER_GIVEN), against recency-first ART (`head`)."""
+    from dataclasses import replace as dc_replace
+    from kv_cache_early_amd import ART_DT_BF16, ART_ORDER_GIVEN, ART_SELECT_IMPORTANCE
+    s = w.spec
+    mp = int(dev.block_table.shape[1])
+    steps = max(3, args.steps // 3)
+    means_ms, means = time_call(lambda: dec.block_means(dev.k, dev.context_lens, num_q_heads=s.num_q_heads,
+                                                        dtype=dev.dtype_code, page_size=dev.page_size,
+                                                        block_table=dev.block_table), steps, not args.no_flush)
+    sel_ms, (kb, kc) = time_call(lambda: dec.select_blocks(dev.q, means, dev.context_lens, dtype=dev.dtype_code,
+                                                           keep_frac=1.0, sink=0, recent=0,
+                                                           order=ART_SELECT_IMPORTANCE, page_size=dev.page_size,
+                                                           max_pages=mp), steps, not args.no_flush)
+    if dec.device_error() != 0:
+        raise RuntimeError("device error in block selection")
+    k_bytes = int(w.context_lens.astype(np.int64).sum()) * s.num_kv_heads * s.head_dim * (2 if dev.dtype_code == ART_DT_BF16 else 4)
+    dev_imp = dc_replace(dev, kept_blocks=kb, kept_count=kc)
+    imp, imp_t, _ = measure(dec, w, 1, args, dev=dev_imp, order=ART_ORDER_GIVEN)
+    ref = full_out.astype(np.float64).reshape(s.batch, s.num_kv_heads, -1)
+    got = imp_t["out"].astype(np.float64).reshape(s.batch, s.num_kv_heads, -1)
+    rel = np.linalg.norm(got - ref, axis=2) / np.maximum(np.linalg.norm(ref, axis=2), 1e-30)
+    return dict(block_means_ms=round(means_ms, 4), block_means_gbs=round(k_bytes / (means_ms * 1e-3) / 1e9, 1),
+                select_ms=round(sel_ms, 4), art_ms=round(imp["ms"], 4),
+                pct_blocks_skipped=round(imp["pct_blocks_skipped"], 4),
+                recency_first_pct_blocks_skipped=round(head["pct_blocks_skipped"], 4),
+                rel_l2_vs_full_mean=float(f"{rel.mean():.3e}"),
+                note="block means read every key once (meant for when blocks are written); the selection and "
+                     "the ART call are per decode step")
 
 
 def copy_leg(mib, steps):
@@ -417,6 +472,8 @@ def main():
                   f"(overhead {det['ms'] / f1['ms'] - 1:+.3%})", file=sys.stderr, flush=True)
             extra["ablation"] = ablation_report(dec, dev, w, args.split_blocks, full_t["out"])
             print(f"[bench] ablation: {extra['ablation']}", file=sys.stderr, flush=True)
+            extra["importance_first"] = importance_report(dec, dev, w, args, head, full_t["out"])
+            print(f"[bench] importance-first: {extra['importance_first']}", file=sys.stderr, flush=True)
     traffic = traffic_from_summary() if head_mode == 1 else None
     roof = dict(bound="hbm", achieved=round(head["gbs_algorithmic"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(head["gbs_algorithmic"] / HBM_PEAK_GBS, 4),
