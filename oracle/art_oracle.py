@@ -55,6 +55,10 @@ below and listed with its reason in the design notes):
 * R13 scale 1/sqrt(d); no mask inside the cache beyond the context length.
 * Thresholds are single-precision values (as passed through the C ABI)
       compared in double precision.
+* R28 multi-row queries (Q with M rows per sequence, Eq. (1)): the M*G query
+      vectors of a unit share its traversal and its one stop; the probe
+      concatenates all of them (row by row, head by head), as R6 does for
+      the G heads.
 
 Numerics: all arithmetic in float64 on exactly widened inputs.  O^(t) is
 computed from per-block weighted sums and their prefix sums with one shift
@@ -318,6 +322,28 @@ def art_decode(q, k, v, context_lens, dtype: str, num_kv_heads: int, block_size:
         if keep_results:
             results[(b, h)] = r
     return out, stop, results
+
+
+def art_decode_rows(q_rows, k, v, context_lens, dtype: str, num_kv_heads: int, block_size: int,
+                    eps_scale: float, eps_dir: float, patience: int, order: int, mode: int,
+                    page_size: int = 0, block_table=None, kept_blocks=None, kept_count=None,
+                    units=None, keep_results: bool = False, flags: int = 0):
+    """Multi-row queries (R28): q_rows [B, M, Hq, d], M query rows per
+    sequence against the same cached context.  The M*G query vectors of unit
+    (b, h), taken row by row (row i, head g at position i*G + g), share the
+    unit's traversal and its one stop decision, exactly as the G heads of a
+    GQA group do [ART-3.1 Eq. (1) with Q of M*G rows; GIST-2.2 on their
+    concatenated probe].  Returns out [B, M, Hq, d], stop [B, Hkv] and the
+    per-unit results (their rows in that order)."""
+    B, M, Hq, d = q_rows.shape
+    G = Hq // num_kv_heads
+    q_units = (np.asarray(q_rows).reshape(B, M, num_kv_heads, G, d).transpose(0, 2, 1, 3, 4)
+               .reshape(B, num_kv_heads * M * G, d))
+    out, stop, res = art_decode(q_units, k, v, context_lens, dtype, num_kv_heads, block_size, eps_scale, eps_dir,
+                                patience, order, mode, page_size, block_table, kept_blocks, kept_count, units,
+                                keep_results, flags)
+    out = out.reshape(B, num_kv_heads, M, G, d).transpose(0, 2, 1, 3, 4).reshape(B, M, Hq, d)
+    return out, stop, res
 
 
 def art_decode_workload(w, mode: int = MODE_ART, patience: Optional[int] = None, units=None,

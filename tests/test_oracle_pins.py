@@ -419,3 +419,64 @@ def test_hand_derived_worked_example():
             assert r.d_scale[t] == pytest.approx(eval(ex["d_scale"][t], ev), rel=1e-12, abs=1e-15)
             assert r.d_dir[t] == pytest.approx(eval(ex["d_dir"][t], ev), rel=1e-10, abs=1e-15)
         assert r.stop == case["stop"], case
+
+
+# ---------------------------------------------------------------------------
+# multi-row queries (R28)
+# ---------------------------------------------------------------------------
+def _rows_case(M, seed=21):
+    rng = np.random.default_rng(seed)
+    B, Hkv, G, d, n = 2, 2, 2, 64, 700
+    q = rng.standard_normal((B, M, Hkv * G, d))
+    k = rng.standard_normal((B, Hkv, n, d))
+    v = rng.standard_normal((B, Hkv, n, d))
+    lens = np.array([700, 455], dtype=np.int32)
+    return q, k, v, lens, Hkv
+
+
+def _rows(q, k, v, lens, Hkv, **kw):
+    return orc.art_decode_rows(q.astype(np.float32), k.astype(np.float32), v.astype(np.float32), lens, "f32", Hkv,
+                               64, kw.get("es", 5e-2), kw.get("ed", 5e-3), 2, orc.ORDER_RECENT_FIRST, orc.MODE_ART)
+
+
+def test_rows_identical_rows_change_nothing():
+    """M identical rows: the concatenated probe is the single-row probe
+    repeated, so both metrics (ratios of norms and a cosine) and the stop are
+    those of one row, and every row's output is the one-row output."""
+    q, k, v, lens, Hkv = _rows_case(1)
+    out1, stop1, _ = _rows(q, k, v, lens, Hkv)
+    q3 = np.repeat(q, 3, axis=1)
+    out3, stop3, _ = _rows(q3, k, v, lens, Hkv)
+    np.testing.assert_array_equal(stop3, stop1)
+    for i in range(3):
+        np.testing.assert_allclose(out3[:, i], out1[:, 0], rtol=1e-12, atol=1e-14)
+
+
+def test_rows_permutation_invariance():
+    """Permuting the rows permutes the outputs and keeps the stop: norms and
+    dot products of the concatenated probe do not depend on its order."""
+    q, k, v, lens, Hkv = _rows_case(3)
+    out, stop, _ = _rows(q, k, v, lens, Hkv)
+    perm = [2, 0, 1]
+    outp, stopp, _ = _rows(q[:, perm], k, v, lens, Hkv)
+    np.testing.assert_array_equal(stopp, stop)
+    np.testing.assert_allclose(outp, out[:, perm], rtol=1e-12, atol=1e-14)
+
+
+def test_rows_full_mode_is_per_row_attention():
+    """Full mode: every row's output is plain softmax attention of that row
+    over the whole context (a library routine, row by row)."""
+    q, k, v, lens, Hkv = _rows_case(2)
+    out, stop, _ = orc.art_decode_rows(q.astype(np.float32), k.astype(np.float32), v.astype(np.float32), lens, "f32",
+                                       Hkv, 64, 1e-3, 1e-4, 2, orc.ORDER_RECENT_FIRST, orc.MODE_FULL)
+    G = q.shape[2] // Hkv
+    for b in range(2):
+        n = int(lens[b])
+        for i in range(2):
+            for hq in range(q.shape[2]):
+                h = hq // G
+                qq = q[b, i, hq].astype(np.float32).astype(np.float64)
+                K = k[b, h, :n].astype(np.float32).astype(np.float64)
+                V = v[b, h, :n].astype(np.float32).astype(np.float64)
+                ref = sdpa64(qq[None], K, V, np.zeros(n))[0]
+                np.testing.assert_allclose(out[b, i, hq], ref, rtol=1e-11, atol=1e-13)

@@ -324,6 +324,20 @@ def make_workload(spec: Spec, threads: Optional[int] = None, context_lens=None) 
                     meta={"reading": spec.reading, "seed": spec.seed})
 
 
+def multi_row_queries(w: Workload, rows: int, spread: float = 0.5) -> np.ndarray:
+    """Query rows [B, rows, Hq, d] in storage format for multi-row decode:
+    row 0 is the workload's own query, row i >= 1 adds spread * N(0, 1)
+    noise (seeded per workload and row), like the nearby draft tokens of a
+    speculative step."""
+    s = w.spec
+    base = storage_to_f64(w.q, s.dtype)
+    out = [w.q]
+    for i in range(1, rows):
+        rng = np.random.default_rng([s.seed, 104729, i])
+        out.append(_store(base + spread * rng.standard_normal(base.shape), s.dtype))
+    return np.stack(out, axis=1)
+
+
 def scaled(n: int, reading: Optional[str] = None, **overrides) -> Spec:
     """Small versions of the five configurations, for CPU-checkable parity.
 
