@@ -135,6 +135,15 @@ typedef struct {
                              context_lens[b] <= max_pages * page_size        */
   int32_t num_pages;      /* paged: pages in the pool (bounds check only)    */
   int32_t max_kept;       /* row stride of kept_blocks; 0 = no kept list     */
+  int32_t q_rows;         /* M query rows per sequence (0 is read as 1): q
+                             and out are [B][M][Hq][d].  The M * G query
+                             vectors of a unit (G = Hq / Hkv) share its
+                             traversal and its one stop, their probes
+                             concatenated row by row (ART paper section 3.1
+                             writes Q with any number of rows; per-row or
+                             per-block stopping is not fixed by the pages).
+                             M * G must be 1, 2, 4, 8 or 16; above 4, split
+                             ART and pairing are not available.              */
 } art_shape;
 
 /* Bytes of device workspace art_decode needs for this shape and params
@@ -143,7 +152,7 @@ size_t art_workspace_size(const art_shape* shape, const art_params* params);
 
 /* Blockwise ART decode attention (see the top of this file).
  *
- *   q             [B][Hq][d] in `dtype`
+ *   q             [B][M][Hq][d] in `dtype` (M = q_rows; [B][Hq][d] when 1)
  *   k, v          contiguous [B][Hkv][max_ctx][d] or paged
  *                 [num_pages][Hkv][page_size][d], in `dtype`
  *   context_lens  int32 [B], 0 <= len (bounded as described in art_shape)
@@ -153,7 +162,7 @@ size_t art_workspace_size(const art_shape* shape, const art_params* params);
  *                 strictly ascending for NATURAL/RECENT_FIRST, distinct and
  *                 in [0, ceil(len/block_size)) for all orders
  *   kept_count    int32 [B][Hkv] entries used per unit (NULL iff kept_blocks)
- *   out           fp32 [B][Hq][d]                  (written)
+ *   out           fp32 [B][M][Hq][d]               (written)
  *   stop_idx      int32 [B][Hkv]                   (written)
  *   blocks_issued int32 [B][Hkv] or NULL           (written)
  *   workspace     device buffer of >= art_workspace_size() bytes, 256-byte
@@ -229,7 +238,7 @@ art_status art_block_means(const art_shape* shape, const void* k, const int32_t*
 /* Kept lists from block-mean keys (see above): for every unit writes
  * kept_blocks[(b * Hkv + h) * shape.max_kept + i] for i < n, and
  * kept_count[b * Hkv + h] = n.  q as for art_decode; means as written by
- * art_block_means with the same max_blocks.  Requires shape.max_kept >=
+ * art_block_means with the same max_blocks; shape.q_rows 0 or 1.  Requires shape.max_kept >=
  * min(T_max, ceil(keep_frac * T_max)) for T_max = ceil(capacity / 64), and
  * T_max <= 4096 (ART_ERR_UNSUPPORTED otherwise). */
 art_status art_select_blocks(const art_shape* shape, const art_select_params* params, const void* q,

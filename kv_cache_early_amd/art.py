@@ -50,7 +50,7 @@ class art_shape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("max_ctx", ctypes.c_int32), ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int32),
-                ("max_kept", ctypes.c_int32)]
+                ("max_kept", ctypes.c_int32), ("q_rows", ctypes.c_int32)]
 
 
 class art_select_params(ctypes.Structure):
@@ -103,9 +103,9 @@ def status_string(status: int) -> str:
 
 
 def make_shape(batch, num_q_heads, num_kv_heads, head_dim, dtype, page_size=0, max_ctx=0, max_pages=0,
-               num_pages=0, max_kept=0) -> art_shape:
+               num_pages=0, max_kept=0, q_rows=1) -> art_shape:
     return art_shape(batch, num_q_heads, num_kv_heads, head_dim, dtype, page_size, max_ctx, max_pages,
-                     num_pages, max_kept)
+                     num_pages, max_kept, q_rows)
 
 
 def make_params(eps_scale=1e-3, eps_dir=1e-4, patience=2, order=ART_ORDER_RECENT_FIRST, mode=ART_MODE_ART,
@@ -186,7 +186,10 @@ class ArtDecoder:
                order=ART_ORDER_RECENT_FIRST, mode=ART_MODE_ART, block_size=64, split_blocks=0, flags=0, pairing=0,
                out=None, stop_idx=None, blocks_issued=None, stream=None) -> DecodeResult:
         torch = self.torch
-        B, Hq, d = q.shape
+        if q.dim() == 4:  # [B, M, Hq, d]: M query rows per sequence
+            B, M, Hq, d = q.shape
+        else:
+            (B, Hq, d), M = q.shape, 1
         Hkv = k.shape[1]
         for t in (q, k, v, context_lens, block_table, kept_blocks, kept_count):
             if t is not None and not t.is_contiguous():
@@ -195,14 +198,15 @@ class ArtDecoder:
                            max_ctx=k.shape[2] if page_size == 0 else 0,
                            max_pages=block_table.shape[1] if block_table is not None else 0,
                            num_pages=k.shape[0] if page_size else 0,
-                           max_kept=kept_blocks.shape[2] if kept_blocks is not None else 0)
+                           max_kept=kept_blocks.shape[2] if kept_blocks is not None else 0, q_rows=M)
         params = make_params(eps_scale, eps_dir, patience, order, mode, block_size, split_blocks, flags, pairing)
         nbytes = workspace_size(shape, params)
-        if nbytes == 0:
-            raise ArtError(ART_ERR_INVALID_ARG, "art_workspace_size")
+        if nbytes == 0:  # invalid shape or params: art_decode names the reason before using anything
+            raise ArtError(decode_raw(shape, params, q, k, v, context_lens, block_table, kept_blocks, kept_count,
+                                      q, q, None, None, 0, None))
         ws = self.workspace(nbytes)
         if out is None:
-            out = torch.empty((B, Hq, d), dtype=torch.float32, device=self.device)
+            out = torch.empty(tuple(q.shape), dtype=torch.float32, device=self.device)
         if stop_idx is None:
             stop_idx = torch.empty((B, Hkv), dtype=torch.int32, device=self.device)
         if blocks_issued is None:

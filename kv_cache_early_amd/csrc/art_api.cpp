@@ -29,6 +29,9 @@ int64_t max_traversal(const art_shape& s) {
   return (tokens + kBlockTokens - 1) / kBlockTokens;
 }
 
+// Query rows per sequence (0 is read as 1).
+int rows_of(const art_shape& s) { return s.q_rows > 0 ? s.q_rows : 1; }
+
 // Shape rules shared by every entry point.
 art_status validate_shape(const art_shape* sp) {
   if (!sp) return ART_ERR_INVALID_ARG;
@@ -39,10 +42,11 @@ art_status validate_shape(const art_shape* sp) {
   if (s.page_size < 0 || s.max_ctx < 0 || s.max_pages < 0 || s.num_pages < 0 || s.max_kept < 0)
     return ART_ERR_INVALID_ARG;
   if (s.page_size > 0 && s.page_size % 16 != 0) return ART_ERR_INVALID_ARG;
-  const int G = s.num_q_heads / s.num_kv_heads;
+  if (s.q_rows < 0) return ART_ERR_INVALID_ARG;
+  const int64_t GQ = (int64_t)(s.num_q_heads / s.num_kv_heads) * rows_of(s);  // query vectors per unit
   if (!((s.dtype == ART_DT_BF16 && s.head_dim == 128) || (s.dtype == ART_DT_F32 && s.head_dim == 64)))
     return ART_ERR_UNSUPPORTED;
-  if (G != 1 && G != 2 && G != 4) return ART_ERR_UNSUPPORTED;
+  if (GQ != 1 && GQ != 2 && GQ != 4 && GQ != 8 && GQ != 16) return ART_ERR_UNSUPPORTED;
   if (s.page_size > 0 && (s.page_size & (s.page_size - 1)) != 0) return ART_ERR_UNSUPPORTED;  // powers of two
   // index ranges the kernels compute in 32-bit
   const int64_t units = (int64_t)s.batch * s.num_kv_heads;
@@ -68,6 +72,10 @@ art_status validate(const art_shape* sp, const art_params* pp) {
   const art_status st = validate_shape(sp);
   if (st != ART_OK) return st;
   if (p.block_size != kBlockTokens) return ART_ERR_UNSUPPORTED;
+  // ordered split ART keeps at most 4 query vectors per unit
+  const int GQ = (s.num_q_heads / s.num_kv_heads) * rows_of(s);
+  if (GQ > 4 && p.mode == ART_MODE_ART && p.split_blocks > 0 && p.split_blocks < max_traversal(s))
+    return ART_ERR_UNSUPPORTED;
   return ART_OK;
 }
 
@@ -127,7 +135,7 @@ constexpr int64_t kSelectSortMax = 4096;  // blocks per unit the selection kerne
 art::WsLayout layout(const art_shape& s, const art_params& p, int chunk, int max_chunks) {
   art::WsLayout L{};
   const int64_t units = (int64_t)s.batch * s.num_kv_heads;
-  const int G = s.num_q_heads / s.num_kv_heads;
+  const int G = (s.num_q_heads / s.num_kv_heads) * rows_of(s);  // query vectors per unit
   const int d = s.head_dim;
   L.header = round256(sizeof(art::WsHeader));
   L.items = round256(sizeof(art::ItemState) * (size_t)std::max<int64_t>(units * max_chunks, 1));
@@ -218,7 +226,9 @@ art_status art_decode(const art_shape* shape, const art_params* params, const vo
   // units, two per CU) it measured about 4% slower than one unit per
   // workgroup (the lockstep rounds wait for the slower of eight waves), and
   // with fewer units than two per CU it would leave CUs idle.
-  a.pair = (p.mode == ART_MODE_ART && max_chunks == 1 && p.pairing == 2) ? 1 : 0;
+  a.rows = rows_of(s);
+  a.gh = s.num_q_heads / s.num_kv_heads;
+  a.pair = (p.mode == ART_MODE_ART && max_chunks == 1 && p.pairing == 2 && a.rows * a.gh <= 4) ? 1 : 0;
   a.order = p.order;
   a.mode = p.mode;
   a.chunk_blocks = chunk;
@@ -309,6 +319,7 @@ art_status art_select_blocks(const art_shape* shape, const art_select_params* pa
   const art_select_params& p = *params;
   if (!(p.keep_frac > 0.f && p.keep_frac <= 1.f) || p.sink < 0 || p.recent < 0) return ART_ERR_INVALID_ARG;
   if (p.order != ART_SELECT_ASCENDING && p.order != ART_SELECT_IMPORTANCE) return ART_ERR_INVALID_ARG;
+  if (rows_of(s) != 1) return ART_ERR_INVALID_ARG;  // q is [B][Hq][d] here
   if (s.batch == 0) return ART_OK;
   if (!q || !means || !context_lens || !kept_blocks || !kept_count) return ART_ERR_INVALID_ARG;
   const int64_t tmax = capacity_blocks(s);

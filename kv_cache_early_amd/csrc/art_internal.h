@@ -24,13 +24,14 @@ struct ItemState {
   int32_t issued;      // blocks whose loads the item issued (-1: kept list rejected)
 };
 
-// Summary of one ART block on the probe dims (probe dim 4p of head g at
-// ps[p][g]), relative to the block's own score maximum m (log2 domain).
-template <int D>
+// Summary of one ART block on the probe dims (probe dim 4p of query vector g
+// at ps[p][g]), relative to the block's own score maximum m (log2 domain).
+// GS query vectors (4 for up to four per unit).
+template <int D, int GS = 4>
 struct alignas(16) Summary {
-  float m[4];          // reference max per head
-  float l[4];          // softmax mass per head relative to m
-  float ps[D / 4][4];  // sums on the probe dims relative to m
+  float m[GS];          // reference max per query vector
+  float l[GS];          // softmax mass per query vector relative to m
+  float ps[D / 4][GS];  // sums on the probe dims relative to m
 };
 
 // Split ART: prefix state of a unit after the last block of one chunk,
@@ -58,6 +59,8 @@ struct KernelArgs {
   int32_t crit_tau_lt1, crit_phi_le1; // eps_scale < 1, eps_dir <= 1
   int32_t detect_only;   // record the stop, never terminate
   int32_t pair;          // two units per workgroup (single-chunk ART)
+  int32_t rows;          // query rows per sequence (q and out are [B][rows][Hq][d])
+  int32_t gh;            // query heads per kv head (Hq / Hkv); a unit has rows * gh query vectors
   int32_t split_art;     // ART mode with several chunks per unit (look-back)
   int32_t max_trav;      // traversal blocks per unit bound (summary row stride)
   int32_t chunk_blocks;  // traversal blocks per work item

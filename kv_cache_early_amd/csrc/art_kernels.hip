@@ -412,7 +412,10 @@ struct alignas(16) Check {     // one position's stability test, published by it
 };
 template <int G, int D>
 struct alignas(16) RoundLds {
-  Summary<D> sum[2][kMaxWaves];      // by round parity
+  // by round parity; more than 4 query vectors per unit: one buffer (every
+  // read of a round's summaries happens before its second barrier, every
+  // write of the next round's after it)
+  Summary<D, (G > 4 ? G : 4)> sum[G > 4 ? 1 : 2][kMaxWaves];
   Check chk[2][kMaxWaves];            // by round parity: per position
   int bad;
   int zero_pos;
@@ -436,11 +439,12 @@ struct alignas(16) ReplayLds {
 };
 template <int G, int D>
 struct alignas(16) EpilogueLds {     // per-wave final state (reuses the V slabs)
-  float m[kMaxWaves][4];
-  float l[kMaxWaves][4];
+  static constexpr int GS = G > 4 ? G : 4;
+  float m[kMaxWaves][GS];
+  float l[kMaxWaves][GS];
   int issued[kMaxWaves];
   int bad[kMaxWaves];
-  float acc[kMaxWaves][D][4];        // [wave][dim][head]
+  float acc[kMaxWaves][D][GS];       // [wave][dim][query vector]
 };
 
 // ---------------------------------------------------------------------------
@@ -457,6 +461,11 @@ struct alignas(16) EpilogueLds {     // per-wave final state (reuses the V slabs
 template <int DT, int G, bool PAGED, bool SPLIT, int TEAMS>
 __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_decode_kernel(KernelArgs a) {
   static_assert(TEAMS == 1 || (TEAMS == 2 && !SPLIT), "two teams only in single-chunk ART");
+  // G is the number of query vectors of a unit: rows * (Hq / Hkv).  Up to 4
+  // they fill the 16 MFMA columns by repetition; 8 or 16 (multi-row queries)
+  // take the columns and output rows one for one, with the criterion below
+  // laid out per query vector (no split ART, no pairing).
+  static_assert(G == 1 || G == 2 || G == 4 || ((G == 8 || G == 16) && !SPLIT && TEAMS == 1), "query vectors per unit");
   using GE = Geo<DT>;
   constexpr int D = GE::D, ES = GE::ES, PPC = GE::PPC;
   constexpr int NDT = D / 16;  // 16-dim output tiles
@@ -466,8 +475,8 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
   __shared__ alignas(16) uint8_t vbuf_all[TEAMS][kMaxWaves][kVSlab];
   // the waves' final state is stashed above the replay state, so a split
   // chunk can keep its pass-0 result in LDS while the replay runs
-  constexpr int kEpiOff = 32768;
-  static_assert(sizeof(ReplayLds<D>) <= kEpiOff, "replay state must fit below the stash");
+  constexpr int kEpiOff = SPLIT ? 32768 : 0;
+  static_assert(!SPLIT || sizeof(ReplayLds<D>) <= kEpiOff, "replay state must fit below the stash");
   static_assert(kEpiOff + sizeof(EpilogueLds<G, D>) <= sizeof(vbuf_all[0]), "stash must fit the V slabs");
 
   constexpr int W = kMaxWaves;  // waves per work item
@@ -543,7 +552,11 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
   const int t_begin = chunk * a.chunk_blocks;
   const int t_end = min(u.n_trav, t_begin + a.chunk_blocks);
   const bool single = a.chunk_blocks >= u.n_trav;  // whole traversal in this work item
-  float* out_rows = a.out + ((size_t)b * a.hq + h * G) * D;
+  // query vector g of the unit: row g / gh, head h * gh + g % gh
+  auto q_index = [&](int g) -> size_t {
+    return ((size_t)b * a.rows + g / a.gh) * a.hq + (size_t)h * a.gh + g % a.gh;
+  };
+  auto out_at = [&](int i) -> float& { return a.out[q_index(i / D) * D + i % D]; };  // i = g * D + dim
 
   // ---- kept list: validate (device input) and find block 0 --------------
   if (u.kept) {
@@ -568,7 +581,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
     if (bad && !phantom) {
       if (tid == 0) a.items[item] = ItemState{ART_ERR_DEVICE_INPUT, -1};
       if (chunk == 0) {
-        for (int i = tid; i < G * D; i += kWave * kMaxWaves) out_rows[i] = 0.f;
+        for (int i = tid; i < G * D; i += kWave * kMaxWaves) out_at(i) = 0.f;
         if (tid == 0) {
           a.stop_idx[unit] = -1;
           if (a.blocks_issued) a.blocks_issued[unit] = 0;
@@ -587,7 +600,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
   }
   if (!idle && u.n_trav <= 0) {  // out = 0, stop = 0
     if (chunk == 0) {
-      for (int i = tid; i < G * D; i += kWave * kMaxWaves) out_rows[i] = 0.f;
+      for (int i = tid; i < G * D; i += kWave * kMaxWaves) out_at(i) = 0.f;
       if (tid == 0) {
         a.stop_idx[unit] = 0;
         if (a.blocks_issued) a.blocks_issued[unit] = 0;
@@ -605,7 +618,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
   // 16 bytes of chunk 4j + lg of head c % G (heads replicated over columns)
   u32x4 qv[4];
   {
-    const char* qrow = (const char*)a.q + (((size_t)b * a.hq + h * G + c % G) * D) * ES;
+    const char* qrow = (const char*)a.q + q_index(c % G) * D * ES;
 #pragma unroll
     for (int j = 0; j < 4; ++j) qv[j] = *(const u32x4*)(qrow + (4 * j + lg) * 16);
   }
@@ -630,6 +643,15 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
   for (int k = 0; k < PPC; ++k) pP[k] = 0.0;
   double stt_last = 0.0;
   int counter = 0;
+  // more than 4 query vectors per unit: lane = (query vector hq, chunk cq),
+  // LPH lanes per vector, PPCQ of its probe dims per lane
+  constexpr int LPH = G > 4 ? kWave / G : 16;
+  constexpr int PPCQ = G > 4 ? (D / 4) / LPH : 1;
+  const int hq = lane / LPH, cq = lane % LPH;
+  float mPq = -INFINITY;
+  double lPq = 0.0, pPq[PPCQ];
+#pragma unroll
+  for (int k = 0; k < PPCQ; ++k) pPq[k] = 0.0;
   const Criterion crit{a.crit_hi, a.crit_lo, a.crit_c2, a.crit_tau_lt1 != 0, a.crit_phi_le1 != 0};
 
   // ---- loads ---------------------------------------------------------------
@@ -741,6 +763,10 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
     if (lane < 16) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) *(f32x4*)&E.acc[wid][16 * dt + c][0] = acc[dt];
+    }
+    if (G > 4 && lane >= 16 && lg < G / 4) {  // rows 4 lg .. 4 lg + 3 hold query vectors of their own
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) *(f32x4*)&E.acc[wid][16 * dt + c][4 * lg] = acc[dt];
     }
     if (lane < G) {
       E.m[wid][lane] = m_c;
@@ -1097,6 +1123,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
         }
       }
       if (art_mode && !split) {
+        if constexpr (G <= 4) {
         // ---- publish the block summary ------------------------------------------
         // probe dims 4p: lanes c = 0, 4, 8, 12 of row 0 hold dims 16dt + c for
         // heads r % G in register r
@@ -1224,14 +1251,116 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
         if constexpr (TEAMS == 2) {  // read by both teams after the next round's first barrier
           if (tid == 0) R.live = (team_live && stop_round < 0 && t0 + W < t_stop) ? 1 : 0;
         }
+              } else {
+        // ---- more than 4 query vectors (multi-row queries) ------------------------
+        // publish: probe dim 4p of query vector 4 lg + r is register r of
+        // lane (lg, 4 (p % 4)), tile p / 4 (rows 4 lg .. 4 lg + 3 of the O layout)
+        auto& sw = R.sum[0][wid];
+        if (active) {
+          if ((c & 3) == 0 && lg < G / 4) {
+  #pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) *(f32x4*)&sw.ps[4 * dt + (c >> 2)][4 * lg] = bacc[dt];
+          }
+          if (lane < G) {
+            sw.m[lane] = m_new;
+            sw.l[lane] = lblk;
+          }
+        }
+        lds_barrier();
+        // The round's positions in order, as in the path above, but each lane
+        // carries one query vector's prefix state on its share of the probe
+        // dims, and the summaries are merged one at a time (register budget).
+        float mk[kMaxWaves];
+        float M = mPq;
+  #pragma unroll
+        for (int k = 0; k < kMaxWaves; ++k) {
+          mk[k] = k < n_act ? R.sum[0][k].m[hq] : -INFINITY;  // slots past the round's end hold stale data
+          M = fmaxf(M, mk[k]);
+        }
+        const double sP = (double)__builtin_amdgcn_exp2f(mPq - M);
+        double L = lPq * sP, P[PPCQ];
+  #pragma unroll
+        for (int i = 0; i < PPCQ; ++i) P[i] = pPq[i] * sP;
+        double a_own = 0.0, c_own = 0.0, a_prev = 0.0, L_own = 1.0, L_prev = 0.0;
+  #pragma unroll
+        for (int k = 0; k < kMaxWaves; ++k) {
+          const bool on = k < n_act;
+          const double sk = (double)__builtin_amdgcn_exp2f(mk[k] - M);  // 0 past the round's end
+          const double lk = on ? (double)R.sum[0][k].l[hq] : 0.0;
+          double pa = 0.0, pc = 0.0;
+  #pragma unroll
+          for (int i = 0; i < PPCQ; ++i) {
+            const double pv = on ? (double)R.sum[0][k].ps[cq * PPCQ + i][hq] : 0.0;
+            const double pn = fma(pv, sk, P[i]);
+            pa = fma(pn, pn, pa);
+            pc = fma(pn, P[i], pc);
+            P[i] = pn;
+          }
+          const double Ln = fma(lk, sk, L);
+          const bool own = k == wid, before = k + 1 == wid;
+          a_own = own ? pa : a_own;
+          c_own = own ? pc : c_own;
+          L_prev = own ? L : L_prev;
+          L_own = own ? Ln : L_own;
+          a_prev = before ? pa : a_prev;
+          L = Ln;
+        }
+        mPq = M;
+        lPq = L;
+  #pragma unroll
+        for (int i = 0; i < PPCQ; ++i) pPq[i] = P[i];
+        if (has_next) load_v(nxt);  // after the summary reads (it waits for them)
+        if (active) {
+          // each lane scales its own query vector's part; the sums run over all lanes
+          const double io = recip_d(L_own);
+          const double ip = L_prev > 0.0 ? recip_d(L_prev) : 0.0;
+          const double stt = col_sum_d(row_sum_d(a_own * (io * io)));
+          const double stp = col_sum_d(row_sum_d(c_own * (io * ip)));
+          const double spr = wid == 0 ? stt_last : col_sum_d(row_sum_d(a_prev * (ip * ip)));
+          const bool stable =
+              (spr > 0.0) & (stt > 0.0) & crit.scale_ok(spr, stt) & crit.dir_ok(spr, stt, stp);
+          if (lane == 0) {
+            R.chk[parity][wid].stt = stt;
+            R.chk[parity][wid].stable = stable;
+          }
+        }
+        lds_barrier();
+        // ---- patience counter over the round's checks, in traversal order ---------
+        int sbits = 0;
+  #pragma unroll
+        for (int w2 = 0; w2 < kMaxWaves; ++w2) {
+          const Check ck = R.chk[parity][w2];
+          sbits |= (ck.stable & 1) << w2;
+          if (w2 + 1 == n_act) stt_last = ck.stt;
+        }
+        sbits = uni(sbits);
+  #pragma unroll
+        for (int w2 = 0; w2 < kMaxWaves; ++w2) {
+          const int cnt = t0 + w2 + 1;
+          if (w2 < n_act && cnt >= 2 && stop_round < 0) {
+            counter = ((sbits >> w2) & 1) ? counter + 1 : 0;
+            if (counter >= a.patience) stop_round = cnt;
+          }
+        }
+        stop_round = uni(stop_round);
+        parity ^= 1;
+        if (detect_only) {
+          if (detected < 0) detected = stop_round;
+          stop_round = -1;
+        }
+        }
       }
-
       // ---- commit this wave's block (unless it lies after the stop) -------------
       if (active && (stop_round < 0 || t + 1 <= stop_round)) {
         // row r of the O layout holds head r % G, whose column values sit in lane r % G
         float al[4];
   #pragma unroll
-        for (int r = 0; r < 4; ++r) al[r] = lane_f(alpha, r % G);
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (G <= 4)
+            al[r] = lane_f(alpha, r % G);
+          else  // row 4 lg + r is query vector (4 lg + r) % G
+            al[r] = __shfl(alpha, (4 * lg + r) % G);
+        }
   #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
   #pragma unroll
@@ -1272,7 +1401,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
     }
     if (discard) L = 0.f;  // nothing of this chunk counts
     if (single) {
-      out_rows[o] = num / L;
+      out_at(o) = num / L;
     } else {
       float* part = a.partials + ((size_t)unit * a.max_chunks + chunk) * G * (D + 2) + g * (D + 2);
       part[2 + dim] = num;
@@ -1329,7 +1458,7 @@ __global__ __launch_bounds__(kWave) void art_combine_kernel(KernelArgs a) {
       o0 = fmaf(pk[2 + threadIdx.x], w, o0);
       if (D > kWave) o1 = fmaf(pk[2 + kWave + threadIdx.x], w, o1);
     }
-    float* dst = a.out + ((size_t)b * a.hq + h * G + g) * D;
+    float* dst = a.out + (((size_t)b * a.rows + g / a.gh) * a.hq + (size_t)h * a.gh + g % a.gh) * D;
     dst[threadIdx.x] = o0 / L;
     if (D > kWave) dst[kWave + threadIdx.x] = o1 / L;
   }
@@ -1354,13 +1483,19 @@ __global__ __launch_bounds__(kWave) void art_combine_kernel(KernelArgs a) {
 template <int DT, int G, bool PAGED>
 static hipError_t launch_t(const KernelArgs& a, int grid, int waves, hipStream_t s) {
   (void)waves;
-  if (a.split_art)
-    hipLaunchKernelGGL((art_decode_kernel<DT, G, PAGED, true, 1>), dim3(grid), dim3(kWave * kMaxWaves), 0, s, a);
-  else if (a.pair)  // one work item per unit, two per workgroup
-    hipLaunchKernelGGL((art_decode_kernel<DT, G, PAGED, false, 2>), dim3((grid + 1) / 2), dim3(2 * kWave * kMaxWaves),
-                       0, s, a);
-  else
+  if constexpr (G <= 4) {
+    if (a.split_art) {
+      hipLaunchKernelGGL((art_decode_kernel<DT, G, PAGED, true, 1>), dim3(grid), dim3(kWave * kMaxWaves), 0, s, a);
+    } else if (a.pair) {  // one work item per unit, two per workgroup
+      hipLaunchKernelGGL((art_decode_kernel<DT, G, PAGED, false, 2>), dim3((grid + 1) / 2),
+                         dim3(2 * kWave * kMaxWaves), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((art_decode_kernel<DT, G, PAGED, false, 1>), dim3(grid), dim3(kWave * kMaxWaves), 0, s, a);
+    }
+  } else {  // more than 4 query vectors per unit: neither split ART nor pairing
+    if (a.split_art || a.pair) return hipErrorInvalidValue;
     hipLaunchKernelGGL((art_decode_kernel<DT, G, PAGED, false, 1>), dim3(grid), dim3(kWave * kMaxWaves), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.max_chunks > 1) {
@@ -1400,15 +1535,25 @@ hipError_t launch(const KernelArgs& a, hipStream_t s) {
   }
   const int grid = n_units * a.max_chunks;
   const int waves = a.waves < 1 ? 1 : (a.waves > kMaxWaves ? kMaxWaves : a.waves);
-  const int G = a.hq / a.hkv;
+  const int G = a.rows * a.gh;  // query vectors per unit
   if (a.dtype == ART_DT_BF16) {
-    if (G == 1) return launch_g<ART_DT_BF16, 1>(a, grid, waves, s);
-    if (G == 2) return launch_g<ART_DT_BF16, 2>(a, grid, waves, s);
-    return launch_g<ART_DT_BF16, 4>(a, grid, waves, s);
+    switch (G) {
+      case 1: return launch_g<ART_DT_BF16, 1>(a, grid, waves, s);
+      case 2: return launch_g<ART_DT_BF16, 2>(a, grid, waves, s);
+      case 4: return launch_g<ART_DT_BF16, 4>(a, grid, waves, s);
+      case 8: return launch_g<ART_DT_BF16, 8>(a, grid, waves, s);
+      case 16: return launch_g<ART_DT_BF16, 16>(a, grid, waves, s);
+      default: return hipErrorInvalidValue;
+    }
   }
-  if (G == 1) return launch_g<ART_DT_F32, 1>(a, grid, waves, s);
-  if (G == 2) return launch_g<ART_DT_F32, 2>(a, grid, waves, s);
-  return launch_g<ART_DT_F32, 4>(a, grid, waves, s);
+  switch (G) {
+    case 1: return launch_g<ART_DT_F32, 1>(a, grid, waves, s);
+    case 2: return launch_g<ART_DT_F32, 2>(a, grid, waves, s);
+    case 4: return launch_g<ART_DT_F32, 4>(a, grid, waves, s);
+    case 8: return launch_g<ART_DT_F32, 8>(a, grid, waves, s);
+    case 16: return launch_g<ART_DT_F32, 16>(a, grid, waves, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace art

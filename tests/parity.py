@@ -32,14 +32,14 @@ def log(*a):
 
 
 def run_gpu(w, mode=1, patience=None, eps_scale=None, eps_dir=None, order=None, split_blocks=0, dev=None,
-            decoder=None, flags=0, pairing=0):
+            decoder=None, flags=0, pairing=0, q=None):
     """Upload (unless ``dev`` is given) and run art_decode; returns numpy arrays."""
     import torch
     from kv_cache_early_amd import ArtDecoder
     s = w.spec
     dev = dev or to_device(w)
     dec = decoder or ArtDecoder()
-    r = dec.decode(dev.q, dev.k, dev.v, dev.context_lens, dtype=dev.dtype_code, page_size=dev.page_size,
+    r = dec.decode(dev.q if q is None else q, dev.k, dev.v, dev.context_lens, dtype=dev.dtype_code, page_size=dev.page_size,
                    block_table=dev.block_table, kept_blocks=dev.kept_blocks, kept_count=dev.kept_count,
                    eps_scale=s.eps_scale if eps_scale is None else eps_scale,
                    eps_dir=s.eps_dir if eps_dir is None else eps_dir,
@@ -72,15 +72,27 @@ class Report:
 
 
 def compare(w, out_gpu, stop_gpu, units=None, mode=1, patience=None, eps_scale=None, eps_dir=None, order=None,
-            flags=0):
-    """Compare GPU results with the oracle on ``units`` (default: all)."""
+            flags=0, q_rows=None):
+    """Compare GPU results with the oracle on ``units`` (default: all).
+
+    ``q_rows`` [B, M, Hq, d] (storage format) compares a multi-row call:
+    ``out_gpu`` is then [B, M, Hq, d]."""
     s = w.spec
     es = s.eps_scale if eps_scale is None else eps_scale
     ed = s.eps_dir if eps_dir is None else eps_dir
-    _, _, res = orc.art_decode_workload(w, mode=mode, patience=patience, units=units, keep_results=True,
-                                        eps_scale=es, eps_dir=ed, order=order, flags=flags)
+    if q_rows is None:
+        _, _, res = orc.art_decode_workload(w, mode=mode, patience=patience, units=units, keep_results=True,
+                                            eps_scale=es, eps_dir=ed, order=order, flags=flags)
+    else:
+        _, _, res = orc.art_decode_rows(q_rows, w.k, w.v, w.context_lens, s.dtype, s.num_kv_heads, s.block_size,
+                                        es, ed, s.patience if patience is None else patience,
+                                        s.order if order is None else order, mode, s.page_size, w.block_table,
+                                        w.kept_blocks, w.kept_count, units, True, flags)
+        M = q_rows.shape[1]
+        out_gpu = out_gpu.reshape(s.batch, M, s.num_kv_heads, s.group, -1).transpose(0, 2, 1, 3, 4).reshape(
+            s.batch, s.num_kv_heads * M * s.group, -1)
     detect_only = bool(flags & orc.FLAG_DETECT_ONLY)
-    G = s.group
+    G = s.group * (1 if q_rows is None else q_rows.shape[1])  # query vectors per unit
     rep = Report()
     for (b, h), r in res.items():
         rep.units += 1

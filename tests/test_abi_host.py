@@ -39,7 +39,7 @@ def test_status_strings_and_probe_stride():
 
 def good_shape(**kw):
     d = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, dtype=art.ART_DT_BF16, page_size=16,
-             max_ctx=0, max_pages=64, num_pages=200, max_kept=0)
+             max_ctx=0, max_pages=64, num_pages=200, max_kept=0, q_rows=1)
     d.update(kw)
     return art.make_shape(**d)
 
@@ -66,7 +66,11 @@ CASES = [
     ("bad dtype", dict(shape=good_shape(dtype=7)), art.ART_ERR_INVALID_ARG),
     ("head_dim 96", dict(shape=good_shape(head_dim=96)), art.ART_ERR_UNSUPPORTED),
     ("bf16 d64", dict(shape=good_shape(head_dim=64)), art.ART_ERR_UNSUPPORTED),
-    ("group 8", dict(shape=good_shape(num_q_heads=16)), art.ART_ERR_UNSUPPORTED),
+    ("32 query vectors per unit", dict(shape=good_shape(num_q_heads=16, q_rows=4)), art.ART_ERR_UNSUPPORTED),
+    ("group 3", dict(shape=good_shape(num_q_heads=6, num_kv_heads=2)), art.ART_ERR_UNSUPPORTED),
+    ("negative q_rows", dict(shape=good_shape(q_rows=-1)), art.ART_ERR_INVALID_ARG),
+    ("split ART above 4 query vectors", dict(shape=good_shape(q_rows=2), params=good_params(split_blocks=4)),
+     art.ART_ERR_UNSUPPORTED),
     ("block_size 32", dict(params=good_params(block_size=32)), art.ART_ERR_UNSUPPORTED),
     ("block_size 0", dict(params=good_params(block_size=0)), art.ART_ERR_INVALID_ARG),
     ("page 24", dict(shape=good_shape(page_size=24)), art.ART_ERR_INVALID_ARG),
