@@ -32,7 +32,8 @@ Reported (one JSON line on stdout):
                  decode with the scale test, the direction test or
                  patience taken out;
                  importance_first: block-mean keys and the importance
-                 order on the GPU, then ART over that order
+                 order on the GPU, then ART over that order;
+                 multi_row: M = 1, 2, 4 query rows per sequence
 
 Other modes (no timing line):
   --summarize-pmc FETCH_DIR WRITE_DIR   turn two rocprofv3 --pmc runs of
@@ -262,6 +263,33 @@ def importance_report(dec, dev, w, args, head, full_out):
                      "the ART call are per decode step")
 
 
+def multi_row_report(dec, dev, w, args):
+    """Multi-row queries on the same workload (M query rows per sequence,
+    seeded draft-like rows): ART time and query rows per second for M = 1,
+    2, 4; the M * 4 query vectors of a unit share its K/V loads."""
+    import torch
+    from workloads import multi_row_queries
+    rows = {}
+    for M in (1, 2, 4):
+        if M == 1:
+            q = dev.q
+        else:
+            qr = multi_row_queries(w, M)
+            q = torch.from_numpy(qr.view(np.int16) if qr.dtype == np.uint16 else qr).to("cuda")
+        stream = torch.cuda.current_stream()
+        kw = decode_kwargs(dev, w, 1, args.split_blocks, stream)
+        r = dec.decode(q, dev.k, dev.v, dev.context_lens, **kw)
+        ms, _ = time_call(lambda: dec.decode(q, dev.k, dev.v, dev.context_lens, out=r.out, stop_idx=r.stop_idx,
+                                             blocks_issued=r.blocks_issued, **kw), max(3, args.steps // 3),
+                          not args.no_flush)
+        if dec.device_error() != 0:
+            raise RuntimeError(f"device error in multi-row M={M}")
+        stop = r.stop_idx.cpu().numpy()
+        rows[f"M{M}"] = dict(ms=round(ms, 4), query_rows_per_s=round(w.spec.batch * M / (ms * 1e-3), 1),
+                             pct_blocks_skipped=round(float(1 - stop.sum() / w.traversal_lengths().sum()), 4))
+    return rows
+
+
 def copy_leg(mib, steps):
     """Elementwise copy (y = x * 1) of `mib` MiB: reads and writes mib MiB per launch."""
     import torch
@@ -474,6 +502,8 @@ def main():
             print(f"[bench] ablation: {extra['ablation']}", file=sys.stderr, flush=True)
             extra["importance_first"] = importance_report(dec, dev, w, args, head, full_t["out"])
             print(f"[bench] importance-first: {extra['importance_first']}", file=sys.stderr, flush=True)
+            extra["multi_row"] = multi_row_report(dec, dev, w, args)
+            print(f"[bench] multi-row: {extra['multi_row']}", file=sys.stderr, flush=True)
     traffic = traffic_from_summary() if head_mode == 1 else None
     roof = dict(bound="hbm", achieved=round(head["gbs_algorithmic"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(head["gbs_algorithmic"] / HBM_PEAK_GBS, 4),
