@@ -674,53 +674,55 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
   // K: load j of tile nt -> token 16 nt + c, chunk 4j + lg.  The first load
   // of a block waits for `dep` (the score maximum), so it overwrites the K
   // registers only after the MFMAs that read them have completed.
-  auto load_k = [&](const BlockAddr& ba, float dep) {
+  // The four loads of tile nt; tile 0's first load waits for `dep`.
+  auto load_k_tile = [&](const BlockAddr& ba, auto ntc, float dep) {
+    constexpr int nt = decltype(ntc)::value;
     if (PAGED || ba.nvalid == kBlk) {
-      static_for<0, kTiles>([&](auto ntc) {
-        constexpr int nt = decltype(ntc)::value;
-        const char* base = u.k + (size_t)ba.row[nt] * ROW;
-        if constexpr (nt == 0)
-          kr[0] = gload16s_after<0>(koff, base, dep);
-        else
-          kr[4 * nt] = gload16s<0>(koff, base);
-        kr[4 * nt + 1] = gload16s<64>(koff, base);
-        kr[4 * nt + 2] = gload16s<128>(koff, base);
-        kr[4 * nt + 3] = gload16s<192>(koff, base);
-      });
+      const char* base = u.k + (size_t)ba.row[nt] * ROW;
+      if constexpr (nt == 0)
+        kr[0] = gload16s_after<0>(koff, base, dep);
+      else
+        kr[4 * nt] = gload16s<0>(koff, base);
+      kr[4 * nt + 1] = gload16s<64>(koff, base);
+      kr[4 * nt + 2] = gload16s<128>(koff, base);
+      kr[4 * nt + 3] = gload16s<192>(koff, base);
     } else {  // last block of a contiguous sequence: rows clamped to the last token
-      static_for<0, kTiles>([&](auto ntc) {
-        constexpr int nt = decltype(ntc)::value;
-        const int tok = min(ba.j * kBlk + 16 * nt + c, u.n_ctx - 1);
-        const char* p = u.k + (size_t)tok * ROW + lg * 16;
-        if constexpr (nt == 0)
-          kr[0] = gload16_after<0>(p, dep);
-        else
-          kr[4 * nt] = gload16<0>(p);
-        kr[4 * nt + 1] = gload16<64>(p);
-        kr[4 * nt + 2] = gload16<128>(p);
-        kr[4 * nt + 3] = gload16<192>(p);
-      });
+      const int tok = min(ba.j * kBlk + 16 * nt + c, u.n_ctx - 1);
+      const char* p = u.k + (size_t)tok * ROW + lg * 16;
+      if constexpr (nt == 0)
+        kr[0] = gload16_after<0>(p, dep);
+      else
+        kr[4 * nt] = gload16<0>(p);
+      kr[4 * nt + 1] = gload16<64>(p);
+      kr[4 * nt + 2] = gload16<128>(p);
+      kr[4 * nt + 3] = gload16<192>(p);
     }
   };
-  // V: the 16 DMAs of a block into this wave's slab (DMA n -> bytes 1024 n).
-  auto load_v = [&](const BlockAddr& ba) {
-    wait_lgkm0();  // LDS reads of the previous block have landed
+  auto load_k = [&](const BlockAddr& ba, float dep) {
+    static_for<0, kTiles>([&](auto ntc) { load_k_tile(ba, ntc, dep); });
+  };
+  // V: the 16 DMAs of a block into this wave's slab (DMA n -> bytes 1024 n);
+  // group g is DMAs 4g .. 4g + 3 (16-token group g).  The caller has waited
+  // for the LDS reads of the previous block (load_v does).
+  auto load_v_group = [&](const BlockAddr& ba, auto gc) {
+    constexpr int g = decltype(gc)::value;
     if (PAGED || ba.nvalid == kBlk) {
-      static_for<0, kTiles>([&](auto gc) {
-        constexpr int g = decltype(gc)::value;
-        const char* base = u.v + (size_t)ba.row[g] * ROW;
-        static_for<0, 4>([&](auto qc) {
-          constexpr int q = decltype(qc)::value;
-          lds_dma16s(voff[q], base, slab + (4 * g + q) * 1024);
-        });
+      const char* base = u.v + (size_t)ba.row[g] * ROW;
+      static_for<0, 4>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        lds_dma16s(voff[q], base, slab + (4 * g + q) * 1024);
       });
     } else {
-      static_for<0, kLoads>([&](auto nc) {
+      static_for<4 * g, 4 * g + 4>([&](auto nc) {
         constexpr int n = decltype(nc)::value;
         const int tok = min(ba.j * kBlk + 4 * n + lg, u.n_ctx - 1);
         lds_dma16(u.v + (size_t)tok * ROW + ((c ^ (2 * lg) ^ (8 * (n & 1))) * 16), slab + n * 1024);
       });
     }
+  };
+  auto load_v = [&](const BlockAddr& ba) {
+    wait_lgkm0();  // LDS reads of the previous block have landed
+    static_for<0, kTiles>([&](auto gc) { load_v_group(ba, gc); });
     compiler_fence();
   };
   // Transposed V reads (bf16): lane (lg, c) addresses token 4lg + c/4 of a
@@ -1006,21 +1008,22 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
             mx = fmaxf(mx, sv);
           }
         mx = col_max(mx);
-        if (has_next) {
-          load_k(nxt, mx);
-          ++issued;
-        }
         m_new = fmaxf(m_c, mx);
         alpha = __builtin_amdgcn_exp2f(m_c - m_new);
         float ls = 0.f;
-  #pragma unroll
-        for (int nt = 0; nt < kTiles; ++nt)
+        // the next block's K, one tile at a time between the tiles'
+        // exponentials: the wave computes while the address unit drains
+        static_for<0, kTiles>([&](auto ntc) {
+          constexpr int nt = decltype(ntc)::value;
+          if (has_next) load_k_tile(nxt, ntc, mx);
   #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float p = __builtin_amdgcn_exp2f(S[nt][r] - m_new);
             S[nt][r] = p;
             ls += p;
           }
+        });
+        if (has_next) ++issued;
         lblk = col_sum(ls);
         // ---- P V on MFMA ---------------------------------------------------------
   #pragma unroll
@@ -1173,17 +1176,19 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
           for (int i = 0; i < PPC; ++i) pk[k][i] = on ? (double)s2.ps[c * PPC + i][hg] : 0.0;
           M = fmaxf(M, mk[k]);
         }
-        // this wave's next V goes out only now: DMAs landing in LDS would slow
-        // the summary reads above
+        // this wave's next V goes out only now (DMAs landing in LDS would slow
+        // the summary reads above), one 16-token group before each merge
+        // step: the wave merges while the address unit drains
+        static_assert(kMaxWaves == kTiles, "one V group per merge step");
         wait_lgkm0();
-        if (has_next) load_v(nxt);
         const double sP = (double)__builtin_amdgcn_exp2f(mP - M);
         double L = lP * sP, P[PPC];
   #pragma unroll
         for (int i = 0; i < PPC; ++i) P[i] = pP[i] * sP;
         double a_own = 0.0, c_own = 0.0, a_prev = 0.0, L_own = 1.0, L_prev = 0.0;
-  #pragma unroll
-        for (int k = 0; k < kMaxWaves; ++k) {
+        static_for<0, kMaxWaves>([&](auto kc) {
+          constexpr int k = decltype(kc)::value;
+          if (has_next) load_v_group(nxt, kc);
           const double sk = (double)__builtin_amdgcn_exp2f(mk[k] - M);  // 0 past the round's end
           double pa = 0.0, pc = 0.0;
   #pragma unroll
@@ -1201,7 +1206,8 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
           L_own = own ? Ln : L_own;
           a_prev = before ? pa : a_prev;
           L = Ln;
-        }
+        });
+        compiler_fence();
         mP = M;
         lP = L;
   #pragma unroll
