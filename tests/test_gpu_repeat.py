@@ -1,0 +1,61 @@
+"""Repeatability at full size: the kernels have no atomics in their
+arithmetic and a fixed merge order, so the same call on the same inputs must
+give bitwise the same outputs, stops and issued counts.  A load consumed
+before it has landed (a timing-dependent bug) shows up here as a difference
+between runs.  Each launch shape the library has is run twice on the
+large-batch paged workload, with every unit on the GPU.
+"""
+import numpy as np
+import pytest
+
+import oracle as orc
+from tests.parity import log, run_gpu
+from workloads import config, make_workload, multi_row_queries
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+@pytest.fixture(scope="module")
+def big(torch_cuda):
+    from workloads.device import to_device
+    log("[case] repeatability: generating the large-batch paged workload")
+    w = make_workload(config(3, "B"))
+    return w, to_device(w)
+
+
+CASES = [
+    ("ART", dict()),
+    ("full mode", dict(mode=orc.MODE_FULL)),
+    ("full mode, split KV", dict(mode=orc.MODE_FULL, split_blocks=16)),
+    ("ART, two units per workgroup", dict(pairing=2)),
+    ("ART, detect-only", dict(flags=orc.FLAG_DETECT_ONLY)),
+    ("ART, 2 query rows", dict(rows=2)),
+    ("ART, 4 query rows", dict(rows=4)),
+]
+
+
+@pytest.mark.parametrize("name,kw", CASES, ids=[c[0] for c in CASES])
+def test_bitwise_repeatable(big, name, kw):
+    import torch
+    w, dev = big
+    kw = dict(kw)
+    rows = kw.pop("rows", 1)
+    if rows > 1:
+        qr = multi_row_queries(w, rows)
+        kw["q"] = torch.from_numpy(qr.view(np.int16) if qr.dtype == np.uint16 else qr).to("cuda")
+    log(f"[case] repeatability {name}")
+    runs = [run_gpu(w, dev=dev, **kw) for _ in range(2)]
+    for out, stop, issued, err in runs:
+        assert err == 0
+    (o1, s1, i1, _), (o2, s2, i2, _) = runs
+    np.testing.assert_array_equal(s1, s2)
+    np.testing.assert_array_equal(i1, i2)
+    assert np.array_equal(o1, o2, equal_nan=True), f"max diff {np.nanmax(np.abs(o1 - o2))}"
