@@ -50,7 +50,7 @@ __global__ __launch_bounds__(kSelThreads) void block_means_kernel(SelectArgs a) 
   constexpr int D = DT == ART_DT_BF16 ? 128 : 64;
   constexpr int PER = DT == ART_DT_BF16 ? 8 : 4;  // values per 16-byte chunk
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: page ids by scalar loads
   const int item = blockIdx.x;
   const int unit = item / a.groups;
   const int j = (item % a.groups) * 4 + wid;
@@ -60,37 +60,48 @@ __global__ __launch_bounds__(kSelThreads) void block_means_kernel(SelectArgs a) 
   const int T = (n + kSelBlk - 1) / kSelBlk;
   const int c = lane & 15, r0 = lane >> 4;
   if (j < T) {
+    // all 16 row addresses first (rows past the sequence's end re-read its
+    // last row and are masked below), then all 16 loads back to back.  Rows
+    // r0 + 4i (r0 < 4) of one i share a page (pages hold a multiple of 16
+    // tokens), so the page ids are wave-uniform.
+    const int last = n - 1;
+    const int32_t* bt = PAGED ? a.block_table + (size_t)b * a.max_pages : nullptr;
+    const int log2p = PAGED ? 31 - __builtin_clz(a.page_size) : 0;
+    const char* src[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int tok = min(j * kSelBlk + r0 + 4 * i, last);
+      size_t row;
+      if constexpr (PAGED) {
+        int pg = bt[min(j * kSelBlk + 4 * i, last) >> log2p];
+        if ((unsigned)pg >= (unsigned)a.num_pages) {
+          bad = 1;
+          pg = 0;
+        }
+        row = ((size_t)pg * a.hkv + h) * a.page_size + (tok & (a.page_size - 1));
+      } else {
+        row = ((size_t)b * a.hkv + h) * a.max_ctx + tok;
+      }
+      src[i] = (const char*)a.k + row * kRowBytes + c * 16;
+    }
+    u32x4v v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = __builtin_nontemporal_load((const u32x4v*)src[i]);
     float acc[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-    const int32_t* bt = PAGED ? a.block_table + (size_t)b * a.max_pages : nullptr;
-    const int log2p = PAGED ? 31 - __builtin_clz(a.page_size) : 0;
-#pragma unroll 4
+#pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int tok = j * kSelBlk + r0 + 4 * i;
-      if (tok < n) {
-        size_t row;
-        if constexpr (PAGED) {
-          int pg = bt[tok >> log2p];
-          if ((unsigned)pg >= (unsigned)a.num_pages) {
-            bad = 1;
-            pg = 0;
-          }
-          row = ((size_t)pg * a.hkv + h) * a.page_size + (tok & (a.page_size - 1));
-        } else {
-          row = ((size_t)b * a.hkv + h) * a.max_ctx + tok;
-        }
-        const u32x4v v = *(const u32x4v*)((const char*)a.k + row * kRowBytes + c * 16);
-        if constexpr (DT == ART_DT_BF16) {
+      const bool in = j * kSelBlk + r0 + 4 * i <= last;
+      if constexpr (DT == ART_DT_BF16) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[2 * e] += __uint_as_float(v[e] << 16);
-            acc[2 * e + 1] += __uint_as_float(v[e] & 0xffff0000u);
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[e] += __uint_as_float(v[e]);
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += in ? __uint_as_float(v[i][e] << 16) : 0.f;
+          acc[2 * e + 1] += in ? __uint_as_float(v[i][e] & 0xffff0000u) : 0.f;
         }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += in ? __uint_as_float(v[i][e]) : 0.f;
       }
     }
     // the four row groups of each chunk: lanes c, c + 16, c + 32, c + 48
