@@ -433,6 +433,8 @@ struct alignas(16) ReplayLds {
   float l[kSplitMax][4];
   float ps[kSplitMax][4][D / 4];
   double stt[kSplitMax + 1];  // stt[j + 1] = |x|^2 at position j; stt[0] from the carry
+  double cdot[kSplitMax][4];  // w_j (carry numerators . block j's probe sums), per head
+  double plast[4][D / 4];     // numerators after the chunk's last block: Q, then the carry out
   int bits[kSplitMax];
   int stop_local;             // blocks of the chunk up to and including the stop, -1 if none
   int counter;
@@ -746,15 +748,22 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
   }
 
   // ---- split ART: look-back replay of the stop rule over this chunk -----------
-  // After pass 0 the chunk's block summaries are in the workspace.  Wait for
-  // the predecessor chunk's carry (the prefix state on the probe dims after
-  // its last block, its patience counter and |x|^2), then evaluate every
-  // position of the chunk at once: thread (j, g, hh) forms the prefix
-  // numerators of head g at positions j and j-1 on half hh of the probe dims,
-  // all terms on the chunk's common maximum; eight lanes per position give
-  // |x^(t)|^2 and x^(t).x^(t-1).  The patience scan then runs over the
-  // positions in order.  Returns the chunk's blocks up to and including the
-  // stop, or -1; publishes this chunk's carry (or the stop) for its successor.
+  // After pass 0 the chunk's block summaries are in the workspace.  Before
+  // the predecessor's carry is needed, thread (j, g, hh) forms the chunk's
+  // own prefix numerators Q_j and Q_{j-1} of head g on half hh of the probe
+  // dims, on the chunk's own maximum Ml, and their products |Q_j|^2 and
+  // Q_j.Q_{j-1}.  Then it waits for the carry (the prefix state P_c, m_c,
+  // l_c after the predecessor's last block, its patience counter and
+  // |x|^2).  On the common maximum M = max(m_c, Ml) the prefix numerators
+  // are P_j = a P_c + b Q_j with a = 2^(m_c - M), b = 2^(Ml - M), so
+  //   |P_j|^2       = a^2 |P_c|^2 + 2ab P_c.Q_j + b^2 |Q_j|^2,
+  //   P_j.P_{j-1}   = a^2 |P_c|^2 + ab (P_c.Q_j + P_c.Q_{j-1}) + b^2 Q_j.Q_{j-1},
+  // and P_c.Q_j = sum over i <= j of w_i (P_c . ps_i), w_i = 2^(m_i - Ml):
+  // one dot product per block and a prefix sum, the only work left after
+  // the carry arrives.  Eight lanes per position give |x^(t)|^2 and
+  // x^(t).x^(t-1); the patience scan then runs over the positions in order.
+  // Returns the chunk's blocks up to and including the stop, or -1;
+  // publishes this chunk's carry (or the stop) for its successor.
   // The waves' running state (m, l, output) goes to LDS, where the
   // epilogue merges it; pass-0 results of a split chunk wait there during
   // the replay.
@@ -787,6 +796,65 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
     const int Cn = t_end - t_begin;
     wait_vm<0>();     // speculative loads have landed in the V slabs
     __syncthreads();  // this chunk's summaries (written by its own waves) are visible
+    const Summary<D>* gsum = reinterpret_cast<const Summary<D>*>(a.summaries) + ((size_t)unit * a.max_trav + t_begin);
+    {  // stage [j][q][g] -> [j][g][q]; all loads of a thread are issued before its stores
+      constexpr int kPer = kSplitMax * D / (kWave * kMaxWaves);
+      float v[kPer];
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) {
+        const int i = tid + r * kWave * kMaxWaves;
+        v[r] = i < Cn * D ? gsum[i / D].ps[(i % D) >> 2][i & 3] : 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) {
+        const int i = tid + r * kWave * kMaxWaves;
+        if (i < Cn * D) RL.ps[i / D][i & 3][(i % D) >> 2] = v[r];
+      }
+      if (tid < Cn * 4) {
+        const float mv = gsum[tid >> 2].m[tid & 3], lv = gsum[tid >> 2].l[tid & 3];
+        RL.m[tid >> 2][tid & 3] = mv;
+        RL.l[tid >> 2][tid & 3] = lv;
+      }
+    }
+    __syncthreads();
+    // ---- the chunk's own prefix state (needs no carry) ------------------------
+    constexpr int NQ = D / 8;  // probe dims per thread
+    const int j = tid >> 3, g = (tid >> 1) & 3, hh = tid & 1;
+    const bool on = j < Cn && g < G;
+    const int jj = j < Cn ? j : 0, gg = g < G ? g : 0;
+    float Ml = -INFINITY;
+    for (int i = 0; i < Cn; ++i) Ml = fmaxf(Ml, RL.m[i][gg]);
+    double Q[NQ], Qp[NQ];
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq) Q[qq] = Qp[qq] = 0.0;
+    double Lam = 0.0, Lamp = 0.0;
+    for (int i = 0; i < Cn; ++i) {
+      const double si = (double)__builtin_amdgcn_exp2f(RL.m[i][gg] - Ml);
+      const double wi = i <= jj ? si : 0.0, wp = i < jj ? si : 0.0;
+      const double li = (double)RL.l[i][gg];
+      Lam = fma(li, wi, Lam);
+      Lamp = fma(li, wp, Lamp);
+#pragma unroll
+      for (int qq = 0; qq < NQ; ++qq) {
+        const double v = (double)RL.ps[i][gg][hh * NQ + qq];
+        Q[qq] = fma(v, wi, Q[qq]);
+        Qp[qq] = fma(v, wp, Qp[qq]);
+      }
+    }
+    double S1 = 0.0, S2 = 0.0;
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq) {
+      S1 = fma(Q[qq], Q[qq], S1);
+      S2 = fma(Q[qq], Qp[qq], S2);
+    }
+    S1 += dpp<kQx1>(S1);  // the two halves of the probe dims
+    S2 += dpp<kQx1>(S2);
+    if (on && j == Cn - 1) {  // read back by the same thread only
+#pragma unroll
+      for (int qq = 0; qq < NQ; ++qq) RL.plast[g][hh * NQ + qq] = Q[qq];
+    }
+    const double wj = (double)__builtin_amdgcn_exp2f(RL.m[jj][gg] - Ml);
+    // ---- the predecessor's carry -------------------------------------------------
     if (tid == 0) {
       int f = 1;
       if (chunk > 0) {
@@ -814,68 +882,41 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
     if (pflag < 0) dev_status = ART_ERR_TIMEOUT;
     const bool has_carry = chunk > 0 && pflag > 0;
     const CarryRec<D>* cin = &carries[chunk > 0 ? chunk - 1 : 0];
-    const Summary<D>* gsum = reinterpret_cast<const Summary<D>*>(a.summaries) + ((size_t)unit * a.max_trav + t_begin);
-    {  // stage [j][q][g] -> [j][g][q]; all loads of a thread are issued before its stores
-      constexpr int kPer = kSplitMax * D / (kWave * kMaxWaves);
-      float v[kPer];
-#pragma unroll
-      for (int r = 0; r < kPer; ++r) {
-        const int i = tid + r * kWave * kMaxWaves;
-        v[r] = i < Cn * D ? gsum[i / D].ps[(i % D) >> 2][i & 3] : 0.f;
-      }
-#pragma unroll
-      for (int r = 0; r < kPer; ++r) {
-        const int i = tid + r * kWave * kMaxWaves;
-        if (i < Cn * D) RL.ps[i / D][i & 3][(i % D) >> 2] = v[r];
-      }
-      if (tid < Cn * 4) {
-        const float mv = gsum[tid >> 2].m[tid & 3], lv = gsum[tid >> 2].l[tid & 3];
-        RL.m[tid >> 2][tid & 3] = mv;
-        RL.l[tid >> 2][tid & 3] = lv;
-      }
-    }
     if (tid == 0) {
       RL.stt[0] = has_carry ? ld_sys(&cin->stt_last) : 0.0;
       RL.counter = has_carry ? ld_sys(&cin->counter) : 0;
     }
-    __syncthreads();
-    constexpr int NQ = D / 8;  // probe dims per thread
-    const int j = tid >> 3, g = (tid >> 1) & 3, hh = tid & 1;
-    const bool on = j < Cn && g < G;
-    const int jj = j < Cn ? j : 0, gg = g < G ? g : 0;
     const float Mc = has_carry ? ld_sys(&cin->m[gg]) : -INFINITY;
     const double Lc = has_carry ? ld_sys(&cin->l[gg]) : 0.0;
-    float Ms = Mc;
-    for (int i = 0; i < Cn; ++i) Ms = fmaxf(Ms, RL.m[i][gg]);
-    const double sc = has_carry ? (double)__builtin_amdgcn_exp2f(Mc - Ms) : 0.0;
-    double P[NQ], Pp[NQ];
+    double Pc[NQ];
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq) Pc[qq] = has_carry ? ld_sys(&cin->p[hh * NQ + qq][gg]) : 0.0;
+    const float Ms = fmaxf(Mc, Ml);
+    const double ca = has_carry ? (double)__builtin_amdgcn_exp2f(Mc - Ms) : 0.0;
+    const double cb = (double)__builtin_amdgcn_exp2f(Ml - Ms);
+    double cpc = 0.0, cj = 0.0;
 #pragma unroll
     for (int qq = 0; qq < NQ; ++qq) {
-      P[qq] = has_carry ? ld_sys(&cin->p[hh * NQ + qq][gg]) * sc : 0.0;
-      Pp[qq] = P[qq];
+      cpc = fma(Pc[qq], Pc[qq], cpc);
+      cj = fma(Pc[qq], (double)RL.ps[jj][gg][hh * NQ + qq], cj);
     }
-    double L = Lc * sc, Lp = L;
+    cpc += dpp<kQx1>(cpc);
+    cj += dpp<kQx1>(cj);
+    if (on && j == Cn - 1) {  // the carry out: P after the last block, on the common maximum
+#pragma unroll
+      for (int qq = 0; qq < NQ; ++qq) RL.plast[g][hh * NQ + qq] = fma(ca, Pc[qq], cb * RL.plast[g][hh * NQ + qq]);
+    }
+    if (on && hh == 0) RL.cdot[j][g] = wj * cj;
+    __syncthreads();
+    double Dj = 0.0, Dp = 0.0;  // P_c.Q_j and P_c.Q_{j-1}
     for (int i = 0; i < Cn; ++i) {
-      const double si = (double)__builtin_amdgcn_exp2f(RL.m[i][gg] - Ms);
-      const double wi = i <= jj ? si : 0.0, wp = i < jj ? si : 0.0;
-      const double li = (double)RL.l[i][gg];
-      L = fma(li, wi, L);
-      Lp = fma(li, wp, Lp);
-#pragma unroll
-      for (int qq = 0; qq < NQ; ++qq) {
-        const double v = (double)RL.ps[i][gg][hh * NQ + qq];
-        P[qq] = fma(v, wi, P[qq]);
-        Pp[qq] = fma(v, wp, Pp[qq]);
-      }
+      const double ci = RL.cdot[i][gg];
+      Dj += i <= jj ? ci : 0.0;
+      Dp += i < jj ? ci : 0.0;
     }
-    double A = 0.0, X = 0.0;
-#pragma unroll
-    for (int qq = 0; qq < NQ; ++qq) {
-      A = fma(P[qq], P[qq], A);
-      X = fma(P[qq], Pp[qq], X);
-    }
-    A += dpp<kQx1>(A);  // the two halves of the probe dims
-    X += dpp<kQx1>(X);
+    const double A = ca * ca * cpc + 2.0 * ca * cb * Dj + cb * cb * S1;
+    const double X = ca * ca * cpc + ca * cb * (Dj + Dp) + cb * cb * S2;
+    const double L = fma(ca, Lc, cb * Lam), Lp = fma(ca, Lc, cb * Lamp);
     const double iL = recip_d(L), iLp = Lp > 0.0 ? recip_d(Lp) : 0.0;
     double stt = on ? A * (iL * iL) : 0.0, stp = on ? X * (iL * iLp) : 0.0;
     stt += dpp<kQx2>(stt);  // heads g and g ^ 1
@@ -914,7 +955,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
       CarryRec<D>& co = carries[chunk];
       if (on && j == Cn - 1) {
 #pragma unroll
-        for (int qq = 0; qq < NQ; ++qq) st_sys(&co.p[hh * NQ + qq][g], P[qq]);
+        for (int qq = 0; qq < NQ; ++qq) st_sys(&co.p[hh * NQ + qq][g], RL.plast[g][hh * NQ + qq]);
         if (hh == 0) {
           st_sys(&co.m[g], Ms);
           st_sys(&co.l[g], L);

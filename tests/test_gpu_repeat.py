@@ -1,6 +1,7 @@
 """Repeatability at full size: the kernels have no atomics in their
 arithmetic and a fixed merge order, so the same call on the same inputs must
-give bitwise the same outputs, stops and issued counts.  A load consumed
+give bitwise the same outputs, stops and issued counts (ordered split ART:
+outputs and stops; its speculative loads depend on timing).  A load consumed
 before it has landed (a timing-dependent bug) shows up here as a difference
 between runs.  Each launch shape the library has is run twice on the
 large-batch paged workload, with every unit on the GPU.
@@ -35,6 +36,7 @@ CASES = [
     ("ART", dict()),
     ("full mode", dict(mode=orc.MODE_FULL)),
     ("full mode, split KV", dict(mode=orc.MODE_FULL, split_blocks=16)),
+    ("ART, ordered split", dict(split_blocks=32)),
     ("ART, two units per workgroup", dict(pairing=2)),
     ("ART, detect-only", dict(flags=orc.FLAG_DETECT_ONLY)),
     ("ART, 2 query rows", dict(rows=2)),
@@ -57,5 +59,11 @@ def test_bitwise_repeatable(big, name, kw):
         assert err == 0
     (o1, s1, i1, _), (o2, s2, i2, _) = runs
     np.testing.assert_array_equal(s1, s2)
-    np.testing.assert_array_equal(i1, i2)
+    if kw.get("split_blocks") and kw.get("mode", orc.MODE_ART) == orc.MODE_ART:
+        # ordered split ART: how many speculative blocks a later chunk loads
+        # before it sees the unit's stop depends on timing; the stop and the
+        # output do not
+        assert np.all(i1 >= s1) and np.all(i2 >= s2)
+    else:
+        np.testing.assert_array_equal(i1, i2)
     assert np.array_equal(o1, o2, equal_nan=True), f"max diff {np.nanmax(np.abs(o1 - o2))}"
