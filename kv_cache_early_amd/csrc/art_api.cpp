@@ -31,6 +31,10 @@ int64_t max_traversal(const art_shape& s) {
 
 // Query rows per sequence (0 is read as 1).
 int rows_of(const art_shape& s) { return s.q_rows > 0 ? s.q_rows : 1; }
+// Query vectors per unit: G query heads times the query rows.
+int64_t query_vectors(const art_shape& s) {
+  return s.num_kv_heads > 0 ? (int64_t)(s.num_q_heads / s.num_kv_heads) * rows_of(s) : 1;
+}
 
 // Shape rules shared by every entry point.
 art_status validate_shape(const art_shape* sp) {
@@ -90,10 +94,15 @@ art_status validate(const art_shape* sp, const art_params* pp) {
 //     kSplitArtBlocks (the look-back replay handles at most that many).
 constexpr int64_t kTargetItems = 4096;
 constexpr int kWavesPerItem = 4;
-// Fewer units than this: split ART by default.  Zero for now: the split path
-// is correct but its look-back chain is still slower than one work item per
-// unit on the measured configurations; callers can ask for it explicitly.
-constexpr int64_t kSplitArtUnits = 0;
+// Fewer units than this (a quarter of the 256 CUs): split ART by default.
+// With so few units one work item per unit leaves most of the chip idle and
+// every unit walks at the latency of its rounds; the chunks' speculative
+// passes run in parallel and only the look-back replay is sequential.
+// Measured with 32 units of 1024 kept blocks: 0.70 ms against 1.27 ms
+// (criterion never firing) and 0.44 against 0.54 ms (firing).  At 128 units
+// (512 blocks each) the two are about even, so the default stays one work
+// item per unit there.
+constexpr int64_t kSplitArtUnits = 64;
 constexpr int kSplitArtBlocks = 32;
 int chunk_blocks(const art_shape& s, const art_params& p) {
   const int64_t tmax = std::max<int64_t>(1, max_traversal(s));
@@ -102,8 +111,8 @@ int chunk_blocks(const art_shape& s, const art_params& p) {
     int64_t c;
     if (p.split_blocks > 0)
       c = p.split_blocks >= tmax ? tmax : std::min<int64_t>((p.split_blocks + 3) / 4 * 4, kSplitArtBlocks);
-    else
-      c = units >= kSplitArtUnits ? tmax : kSplitArtBlocks;
+    else  // split ART handles at most 4 query vectors per unit
+      c = (units >= kSplitArtUnits || query_vectors(s) > 4) ? tmax : kSplitArtBlocks;
     return (int)std::min<int64_t>(c, tmax);
   }
   if (p.split_blocks > 0) return (int)std::min<int64_t>(p.split_blocks, tmax);

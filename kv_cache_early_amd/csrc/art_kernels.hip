@@ -824,28 +824,25 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
     const int jj = j < Cn ? j : 0, gg = g < G ? g : 0;
     float Ml = -INFINITY;
     for (int i = 0; i < Cn; ++i) Ml = fmaxf(Ml, RL.m[i][gg]);
-    double Q[NQ], Qp[NQ];
+    // Q_{j-1} = Q_j - w_j ps_j (fp64; the rounding is far below the tests' margins)
+    double Q[NQ];
 #pragma unroll
-    for (int qq = 0; qq < NQ; ++qq) Q[qq] = Qp[qq] = 0.0;
-    double Lam = 0.0, Lamp = 0.0;
-    for (int i = 0; i < Cn; ++i) {
-      const double si = (double)__builtin_amdgcn_exp2f(RL.m[i][gg] - Ml);
-      const double wi = i <= jj ? si : 0.0, wp = i < jj ? si : 0.0;
-      const double li = (double)RL.l[i][gg];
-      Lam = fma(li, wi, Lam);
-      Lamp = fma(li, wp, Lamp);
+    for (int qq = 0; qq < NQ; ++qq) Q[qq] = 0.0;
+    double Lam = 0.0;
+    for (int i = 0; i <= jj; ++i) {
+      const double wi = (double)__builtin_amdgcn_exp2f(RL.m[i][gg] - Ml);
+      Lam = fma((double)RL.l[i][gg], wi, Lam);
 #pragma unroll
-      for (int qq = 0; qq < NQ; ++qq) {
-        const double v = (double)RL.ps[i][gg][hh * NQ + qq];
-        Q[qq] = fma(v, wi, Q[qq]);
-        Qp[qq] = fma(v, wp, Qp[qq]);
-      }
+      for (int qq = 0; qq < NQ; ++qq) Q[qq] = fma((double)RL.ps[i][gg][hh * NQ + qq], wi, Q[qq]);
     }
+    const double wj = (double)__builtin_amdgcn_exp2f(RL.m[jj][gg] - Ml);
+    const double Lamp = jj == 0 ? 0.0 : fma(-(double)RL.l[jj][gg], wj, Lam);
     double S1 = 0.0, S2 = 0.0;
 #pragma unroll
     for (int qq = 0; qq < NQ; ++qq) {
+      const double qp = jj == 0 ? 0.0 : fma(-(double)RL.ps[jj][gg][hh * NQ + qq], wj, Q[qq]);
       S1 = fma(Q[qq], Q[qq], S1);
-      S2 = fma(Q[qq], Qp[qq], S2);
+      S2 = fma(Q[qq], qp, S2);
     }
     S1 += dpp<kQx1>(S1);  // the two halves of the probe dims
     S2 += dpp<kQx1>(S2);
@@ -853,7 +850,6 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
 #pragma unroll
       for (int qq = 0; qq < NQ; ++qq) RL.plast[g][hh * NQ + qq] = Q[qq];
     }
-    const double wj = (double)__builtin_amdgcn_exp2f(RL.m[jj][gg] - Ml);
     // ---- the predecessor's carry -------------------------------------------------
     if (tid == 0) {
       int f = 1;
@@ -881,16 +877,25 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
     }
     if (pflag < 0) dev_status = ART_ERR_TIMEOUT;
     const bool has_carry = chunk > 0 && pflag > 0;
+    // The carry is loaded unconditionally (chunk 0 reads its own, still
+    // unwritten record: valid workspace memory) and selected afterwards, so
+    // the loads go out together instead of one branch at a time.
     const CarryRec<D>* cin = &carries[chunk > 0 ? chunk - 1 : 0];
     if (tid == 0) {
-      RL.stt[0] = has_carry ? ld_sys(&cin->stt_last) : 0.0;
-      RL.counter = has_carry ? ld_sys(&cin->counter) : 0;
+      const double sl = ld_sys(&cin->stt_last);
+      const int cn = ld_sys(&cin->counter);
+      RL.stt[0] = has_carry ? sl : 0.0;
+      RL.counter = has_carry ? cn : 0;
     }
-    const float Mc = has_carry ? ld_sys(&cin->m[gg]) : -INFINITY;
-    const double Lc = has_carry ? ld_sys(&cin->l[gg]) : 0.0;
     double Pc[NQ];
 #pragma unroll
-    for (int qq = 0; qq < NQ; ++qq) Pc[qq] = has_carry ? ld_sys(&cin->p[hh * NQ + qq][gg]) : 0.0;
+    for (int qq = 0; qq < NQ; ++qq) Pc[qq] = ld_sys(&cin->p[hh * NQ + qq][gg]);
+    const float Mc_in = ld_sys(&cin->m[gg]);
+    const double Lc_in = ld_sys(&cin->l[gg]);
+    const float Mc = has_carry ? Mc_in : -INFINITY;
+    const double Lc = has_carry ? Lc_in : 0.0;
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq) Pc[qq] = has_carry ? Pc[qq] : 0.0;
     const float Ms = fmaxf(Mc, Ml);
     const double ca = has_carry ? (double)__builtin_amdgcn_exp2f(Mc - Ms) : 0.0;
     const double cb = (double)__builtin_amdgcn_exp2f(Ml - Ms);
@@ -932,19 +937,22 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
       RL.bits[j] = (exists ? 2 : 0) | (stable ? 1 : 0);
     }
     __syncthreads();
-    if (tid == 0) {
-      int cnt = RL.counter, st = -1;
+    if (wid == 0) {  // patience scan in order, on two ballots (Cn <= 32 positions)
+      const int bt = lane < Cn ? RL.bits[lane] : 0;
+      const uint64_t ex = __ballot((bt & 2) != 0), sb = __ballot((bt & 1) != 0);
+      int cnt = __builtin_amdgcn_readfirstlane(RL.counter), st = -1;
       for (int i = 0; i < Cn; ++i) {
-        const int bt = RL.bits[i];
-        if (!(bt & 2)) continue;
-        cnt = (bt & 1) ? cnt + 1 : 0;
+        if (!((ex >> i) & 1)) continue;
+        cnt = ((sb >> i) & 1) ? cnt + 1 : 0;
         if (cnt >= a.patience) {
           st = i + 1;
           break;
         }
       }
-      RL.stop_local = st;
-      RL.counter = cnt;
+      if (lane == 0) {
+        RL.stop_local = st;
+        RL.counter = cnt;
+      }
     }
     __syncthreads();
     const int st = uni(RL.stop_local);

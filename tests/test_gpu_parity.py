@@ -42,10 +42,21 @@ def check(w, mode=1, tag="", **kw):
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("mode", [0, 1])
 def test_scaled_configs(torch_cuda, n, reading, mode):
+    """The library's own choice of work decomposition (few units: ordered
+    split ART in ART mode)."""
     w = make_workload(scaled(n, reading))
     _, stop, _, _ = check(w, mode=mode, tag=f"scaled cfg{n}")
     if mode == 0:
         np.testing.assert_array_equal(stop, w.traversal_lengths())
+
+
+@pytest.mark.parametrize("reading", ["A", "B"])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_scaled_configs_one_item_per_unit(torch_cuda, n, reading):
+    """ART mode with one work item per unit (in-round stopping)."""
+    w = make_workload(scaled(n, reading))
+    _, stop, issued, _ = check(w, tag=f"scaled cfg{n} one item per unit", split_blocks=10 ** 6)
+    assert np.all(issued <= np.minimum(w.traversal_lengths(), stop + 7))
 
 
 @pytest.mark.parametrize("p", [1, 2, 3])
@@ -109,8 +120,8 @@ def test_layout_equivalence_bitwise(torch_cuda):
     wp = make_workload(base, context_lens=lens)
     wc = make_workload(replace(base, page_size=0), context_lens=lens)
     log("[case] layout equivalence")
-    op, sp, _, e1 = run_gpu(wp)
-    oc, sc, _, e2 = run_gpu(wc)
+    op, sp, _, e1 = run_gpu(wp, split_blocks=10 ** 6)
+    oc, sc, _, e2 = run_gpu(wc, split_blocks=10 ** 6)
     assert e1 == e2 == 0
     np.testing.assert_array_equal(sp, sc)
     np.testing.assert_array_equal(op, oc)
@@ -322,6 +333,7 @@ def test_two_units_per_workgroup(torch_cuda, case):
     oracle's within the parity bar."""
     from kv_cache_early_amd import art
     w, kw = _pair_case(case)
+    kw["split_blocks"] = 10 ** 6  # one work item per unit (few units would otherwise split)
     log(f"[case] pairing {case}: one unit per workgroup")
     o1, s1, i1, e1 = run_gpu(w, pairing=1, **kw)
     log(f"[case] pairing {case}: two units per workgroup")
