@@ -142,6 +142,11 @@ def eviction_buffer():
     return torch.ones(1 << 28, dtype=torch.float32, device="cuda")
 
 
+def write_eviction_buffer():
+    import torch
+    return torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+
 def evict(buf):
     """Read all of `buf` (a sum): evicts the MALL (256 MB) and the L2s
     without leaving dirty lines for the next kernel to write back."""
@@ -153,7 +158,7 @@ def time_steps(dec, dev, w, mode, steps, warmup, split_blocks, flush, flags=0, o
     import torch
     stream = torch.cuda.current_stream()
     kw = decode_kwargs(dev, w, mode, split_blocks, stream, flags, order=order)
-    scratch = eviction_buffer() if flush else None
+    scratch = (write_eviction_buffer() if flush == "write" else eviction_buffer()) if flush else None
     r = dec.decode(dev.q, dev.k, dev.v, dev.context_lens, **kw)
     for _ in range(warmup):
         dec.decode(dev.q, dev.k, dev.v, dev.context_lens, out=r.out, stop_idx=r.stop_idx,
@@ -162,8 +167,11 @@ def time_steps(dec, dev, w, mode, steps, warmup, split_blocks, flush, flags=0, o
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
     for a, b in evs:
-        if scratch is not None:
-            evict(scratch)  # untimed: evicts the MALL and the L2s
+        if scratch is not None:  # untimed: evicts the MALL and the L2s
+            if flush == "write":
+                scratch.fill_(1)
+            else:
+                evict(scratch)
         a.record(stream)
         dec.decode(dev.q, dev.k, dev.v, dev.context_lens, out=r.out, stop_idx=r.stop_idx,
                    blocks_issued=r.blocks_issued, **kw)
@@ -495,6 +503,15 @@ def main():
     print(f"[bench] {'full' if head_mode == 0 else 'ART'}: {head['ms']:.3f} ms {head['gbs_loaded']:.0f} GB/s "
           f"skip {head['pct_blocks_skipped']:.3f}", file=sys.stderr, flush=True)
     extra = {}
+    if head_mode == 1 and not args.no_flush and not args.skip_extra:
+        # the headline call once more with the caches evicted by a 1 GiB write
+        # instead: the write's dirty lines are written back during the call
+        tw = time_steps(dec, dev, w, 1, args.steps, args.warmup, args.split_blocks, "write")
+        extra["eviction_check"] = {"ms_after_1GiB_read": round(head["ms"], 4),
+                                   "ms_after_1GiB_write": round(tw["ms_mean"], 4),
+                                   "note": "headline uses the read; a write leaves dirty lines whose write-back "
+                                           "lands in the timed call"}
+        print(f"[bench] ART after a write eviction: {tw['ms_mean']:.3f} ms", file=sys.stderr, flush=True)
     if not args.skip_extra and args.only is None:
         full_res, full_t, _ = measure(dec, w, 0, args, dev=dev)
         extra["full_mode"] = {k: round(full_res[k], 4) for k in ("ms", "gbs_loaded", "pct_of_peak",
