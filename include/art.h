@@ -111,7 +111,16 @@ typedef struct {
                             a speculative pass per chunk, a look-back replay
                             of the stop rule on the predecessor's carry, and
                             a recompute of the chunk holding the stop);
-                            blocks_issued then counts the re-read blocks     */
+                            blocks_issued then counts the speculative and
+                            re-read blocks, which vary from call to call.
+                            The library's choice in ART mode: split ART in
+                            32-block chunks when the call has fewer than 64
+                            units and at most 4 query vectors per unit, one
+                            chunk per unit otherwise.  In full mode: chunks
+                            of at least 32 blocks, sized so that about 4096
+                            work items balance uneven lengths.  Either way
+                            stop_idx and out do not depend on the choice
+                            beyond floating-point rounding.                 */
   int32_t flags;         /* OR of art_flag; must be 0 in full mode           */
   int32_t pairing;       /* ART mode with one work item per unit: 0 =
                             library's choice (one), 1 = one unit per workgroup,
