@@ -138,6 +138,14 @@ __device__ __forceinline__ double col_sum_d(double x) {
          __builtin_bit_cast(double, ((uint64_t)th[1] << 32) | tl[1]);
 }
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+// The lane index, produced by an instruction the compiler cannot move or
+// reuse: LDS addresses derived from it are computed where they are used
+// instead of being kept (and spilled) from the kernel's start.
+__device__ __forceinline__ int fresh_lane() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
 __device__ __forceinline__ float lane_f(float x, int l) { return u2f(__builtin_amdgcn_readlane(f2u(x), l)); }
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
@@ -875,6 +883,12 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
       if (tid == 0) st_sys(&carries[chunk].flag, 2);
       return -1;
     }
+    {  // from here on, indices (and the LDS addresses built on them) are recomputed
+    const int tid = wid * kWave + fresh_lane();
+    const int lane = tid & (kWave - 1);
+    const int j = tid >> 3, g = (tid >> 1) & 3, hh = tid & 1;
+    const bool on = j < Cn && g < G;
+    const int jj = j < Cn ? j : 0, gg = g < G ? g : 0;
     if (pflag < 0) dev_status = ART_ERR_TIMEOUT;
     const bool has_carry = chunk > 0 && pflag > 0;
     // The carry is loaded unconditionally (chunk 0 reads its own, still
@@ -983,6 +997,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
     }
     __syncthreads();  // the V slabs are free again
     return detect_only ? -1 : st;
+    }
   };
 
   if (split && chunk > 0 && !detect_only) {  // an earlier chunk already stopped before this one: nothing to do
