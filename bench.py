@@ -450,7 +450,8 @@ def summarize_trace(args):
                 line = json.loads(l)
     steps = line["steps"] if line else len(tr)
     timed = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in tr[-steps:]]
-    md = ["# rocprofv3 kernel trace: art_decode_kernel (bf16, G=4, paged), " + WORKLOAD + ", generator B, ART mode",
+    mode = line["config"].get("mode", "ART") if line else "ART"
+    md = ["# rocprofv3 kernel trace: art_decode_kernel (bf16, G=4, paged), " + WORKLOAD + f", generator B, {mode} mode",
           "", "Command (repository root):", "", "```", args.command, "```", "",
           "## --stats summary (all dispatches of the run)", "",
           "| kernel | calls | average us | min us | max us | total % |", "|---|---|---|---|---|---|"]

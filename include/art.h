@@ -118,7 +118,10 @@ typedef struct {
                             units and at most 4 query vectors per unit, one
                             chunk per unit otherwise.  In full mode: chunks
                             of at least 32 blocks, sized so that about 4096
-                            work items balance uneven lengths.  Either way
+                            work items balance uneven lengths when the call
+                            has at least 256 units (one per compute unit),
+                            and about 256 work items when it has fewer.
+                            Either way
                             stop_idx and out do not depend on the choice
                             beyond floating-point rounding.                 */
   int32_t flags;         /* OR of art_flag; must be 0 in full mode           */

@@ -84,15 +84,23 @@ art_status validate(const art_shape* sp, const art_params* pp) {
 }
 
 // Traversal blocks per work item.
-//   full mode: chunks sized so that about kTargetItems workgroups balance
-//     uneven context lengths across the compute units (at least 32 blocks,
-//     multiples of the wave count);
+//   full mode, at least one unit per compute unit: chunks sized so that
+//     about kTargetItems workgroups balance uneven context lengths across
+//     the compute units;
+//   full mode, fewer units than compute units: about one work item per
+//     compute unit.  A work item's first round costs more than the steady
+//     state, so many short items lose more than they balance; measured on
+//     MI355X with 128 units of 512 blocks, 0.371 ms at 256 items against
+//     0.409 ms at 2048, and with 32 units of 1024 kept blocks 0.212 ms at
+//     256 items against 0.280 ms at 1024;
+//   either way at least 32 blocks and a multiple of the wave count;
 //   ART mode: one work item per unit (in-round sequential stopping) when
 //     there are enough units to fill the chip; otherwise chunks of
 //     kSplitArtBlocks with look-back (ordered split ART).  A caller's
 //     split_blocks is honoured, rounded up to the wave count and capped at
 //     kSplitArtBlocks (the look-back replay handles at most that many).
 constexpr int64_t kTargetItems = 4096;
+constexpr int64_t kComputeUnits = 256;  // MI355X
 constexpr int kWavesPerItem = 4;
 // Fewer units than this (a quarter of the 256 CUs): split ART by default.
 // With so few units one work item per unit leaves most of the chip idle and
@@ -117,7 +125,8 @@ int chunk_blocks(const art_shape& s, const art_params& p) {
   }
   if (p.split_blocks > 0) return (int)std::min<int64_t>(p.split_blocks, tmax);
   const int64_t units = std::max<int64_t>(1, (int64_t)s.batch * s.num_kv_heads);
-  int64_t c = (tmax * units + kTargetItems - 1) / kTargetItems;
+  const int64_t target = units < kComputeUnits ? kComputeUnits : kTargetItems;
+  int64_t c = (tmax * units + target - 1) / target;
   c = std::max<int64_t>(c, 32);
   c = (c + kWavesPerItem - 1) / kWavesPerItem * kWavesPerItem;
   return (int)std::min<int64_t>(c, tmax);

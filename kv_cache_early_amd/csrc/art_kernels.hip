@@ -1498,8 +1498,12 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
 // ---------------------------------------------------------------------------
 // LSE combine of split partials (full mode)
 // ---------------------------------------------------------------------------
+// One workgroup per unit, one wave per query vector.  Lane k of a wave
+// holds chunk k's reference max and mass (64 chunks per pass), so the
+// common max and the total mass are wave reductions; the output loop then
+// walks the chunks in order with its independent loads unrolled by four.
 template <int D, int G>
-__global__ __launch_bounds__(kWave) void art_combine_kernel(KernelArgs a) {
+__global__ __launch_bounds__(kWave * 16) void art_combine_kernel(KernelArgs a) {
   const int unit = blockIdx.x;
   const int b = unit / a.hkv, h = unit % a.hkv;
   int n_ctx = sload(a.context_lens + b);
@@ -1514,35 +1518,77 @@ __global__ __launch_bounds__(kWave) void art_combine_kernel(KernelArgs a) {
   const int n_chunks = (n_trav + a.chunk_blocks - 1) / a.chunk_blocks;
   if (n_chunks <= 1) return;  // written directly by the decode kernel
   if (a.items[unit].issued == -1) return;  // kept list rejected: already reported
+  const int lane = threadIdx.x & (kWave - 1);
+  const int g = uni((int)(threadIdx.x / kWave));
   const float* part = a.partials + (size_t)unit * a.max_chunks * G * (D + 2);
-  for (int g = 0; g < G; ++g) {
-    float M = -INFINITY;
-    for (int k = 0; k < n_chunks; ++k)
-      if (part[(k * G + g) * (D + 2) + 1] > 0.f) M = fmaxf(M, part[(k * G + g) * (D + 2)]);
-    float L = 0.f, o0 = 0.f, o1 = 0.f;
-    for (int k = 0; k < n_chunks; ++k) {
-      const float* pk = part + (k * G + g) * (D + 2);
-      if (!(pk[1] > 0.f)) continue;
-      const float w = __builtin_amdgcn_exp2f(pk[0] - M);
-      L = fmaf(pk[1], w, L);
-      o0 = fmaf(pk[2 + threadIdx.x], w, o0);
-      if (D > kWave) o1 = fmaf(pk[2 + kWave + threadIdx.x], w, o1);
-    }
-    float* dst = a.out + (((size_t)b * a.rows + g / a.gh) * a.hq + (size_t)h * a.gh + g % a.gh) * D;
-    dst[threadIdx.x] = o0 / L;
-    if (D > kWave) dst[kWave + threadIdx.x] = o1 / L;
+  constexpr int S = G * (D + 2);  // floats between consecutive chunks of one query vector
+  const float* pg = part + g * (D + 2);
+
+  // common reference max over the chunks that hold mass
+  float M = -INFINITY;
+  for (int k = lane; k < n_chunks; k += kWave) {
+    const float l = pg[(size_t)k * S + 1];
+    if (l > 0.f) M = fmaxf(M, pg[(size_t)k * S]);
   }
-  if (threadIdx.x == 0) {
-    int stop = n_trav;
-    if (a.split_art) {
-      const int us = a.unit_stop[unit];
-      if (us > 0) stop = us;
+  for (int o = kWave / 2; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
+  // total mass
+  float L = 0.f;
+  for (int k = lane; k < n_chunks; k += kWave) {
+    const float l = pg[(size_t)k * S + 1];
+    if (l > 0.f) L = fmaf(l, __builtin_amdgcn_exp2f(pg[(size_t)k * S] - M), L);
+  }
+  for (int o = kWave / 2; o > 0; o >>= 1) L += __shfl_xor(L, o, kWave);
+
+  // numerators, chunk by chunk in order; a chunk without mass weighs 0
+  float o0 = 0.f, o1 = 0.f;
+  for (int k0 = 0; k0 < n_chunks; k0 += kWave) {
+    const int k = k0 + lane;
+    float wl = 0.f;
+    if (k < n_chunks) {
+      const float l = pg[(size_t)k * S + 1];
+      wl = l > 0.f ? __builtin_amdgcn_exp2f(pg[(size_t)k * S] - M) : 0.f;
     }
-    a.stop_idx[unit] = stop;
-    if (a.blocks_issued) {
-      int tot = 0;
-      for (int k = 0; k < n_chunks; ++k) tot += a.items[(size_t)k * a.batch * a.hkv + unit].issued;
-      a.blocks_issued[unit] = tot;
+    const int n = min(kWave, n_chunks - k0);
+    int j = 0;
+    for (; j + 4 <= n; j += 4) {
+      float x0[4], x1[4], w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float* pk = pg + (size_t)(k0 + j + i) * S + 2;
+        x0[i] = pk[lane];
+        x1[i] = D > kWave ? pk[kWave + lane] : 0.f;
+        w[i] = __shfl(wl, j + i, kWave);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o0 = fmaf(x0[i], w[i], o0);
+        if (D > kWave) o1 = fmaf(x1[i], w[i], o1);
+      }
+    }
+    for (; j < n; ++j) {
+      const float* pk = pg + (size_t)(k0 + j) * S + 2;
+      const float w = __shfl(wl, j, kWave);
+      o0 = fmaf(pk[lane], w, o0);
+      if (D > kWave) o1 = fmaf(pk[kWave + lane], w, o1);
+    }
+  }
+  float* dst = a.out + (((size_t)b * a.rows + g / a.gh) * a.hq + (size_t)h * a.gh + g % a.gh) * D;
+  dst[lane] = o0 / L;
+  if (D > kWave) dst[kWave + lane] = o1 / L;
+
+  if (g == 0) {
+    int tot = 0;
+    if (a.blocks_issued)
+      for (int k = lane; k < n_chunks; k += kWave) tot += a.items[(size_t)k * a.batch * a.hkv + unit].issued;
+    for (int o = kWave / 2; o > 0; o >>= 1) tot += __shfl_xor(tot, o, kWave);
+    if (lane == 0) {
+      int stop = n_trav;
+      if (a.split_art) {
+        const int us = a.unit_stop[unit];
+        if (us > 0) stop = us;
+      }
+      a.stop_idx[unit] = stop;
+      if (a.blocks_issued) a.blocks_issued[unit] = tot;
     }
   }
 }
@@ -1569,7 +1615,7 @@ static hipError_t launch_t(const KernelArgs& a, int grid, int waves, hipStream_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.max_chunks > 1) {
-    hipLaunchKernelGGL((art_combine_kernel<Geo<DT>::D, G>), dim3(a.batch * a.hkv), dim3(kWave), 0, s, a);
+    hipLaunchKernelGGL((art_combine_kernel<Geo<DT>::D, G>), dim3(a.batch * a.hkv), dim3(kWave * G), 0, s, a);
     e = hipGetLastError();
   }
   return e;
