@@ -86,6 +86,7 @@ struct KernelArgs {
   void* carries;       // split ART: [units][max_chunks] CarryRec<d>
   void* summaries;     // split ART: [units][max_trav] Summary<d>
   uint32_t spin_limit; // look-back polls before ART_ERR_TIMEOUT
+  int32_t spec_depth;  // split ART: chunk k starts once chunk k - spec_depth has published its carry
 };
 
 // Workspace layout for a given shape (bytes, 256-aligned pieces).

@@ -1009,6 +1009,36 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
       if (tid == 0) st_sys(&(reinterpret_cast<CarryRec<D>*>(a.carries) + (size_t)unit * a.max_chunks)[chunk].flag, 2);
     }
   }
+  // Bounded speculation: a chunk walks only once the chunk spec_depth places
+  // before it has published its carry (or the unit's stop).  That chunk holds
+  // a smaller ticket, so it is running or done, and the wait ends.  Without
+  // the bound every chunk handed out walks at once, and with few units
+  // nearly all of them lie past the stop.
+  if (split && !discard && a.spec_depth > 0 && chunk >= a.spec_depth) {
+    CarryRec<D>* const uc = reinterpret_cast<CarryRec<D>*>(a.carries) + (size_t)unit * a.max_chunks;
+    __syncthreads();  // every wave has read R.flag above
+    if (tid == 0) {
+      int f;
+      uint32_t polls = 0;
+      for (;;) {
+        f = ld_sys(&uc[chunk - a.spec_depth].flag);
+        if (f != 0) break;
+        if (++polls >= a.spin_limit) {
+          f = -1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(8);
+      }
+      R.flag = f;
+    }
+    __syncthreads();
+    const int f = uni(R.flag);
+    if (f < 0) dev_status = ART_ERR_TIMEOUT;
+    if (f == 2 && !detect_only) {  // the unit stopped at or before that chunk's end
+      discard = true;
+      if (tid == 0) st_sys(&uc[chunk].flag, 2);
+    }
+  }
   bool stashed = false;
   for (int pass = 0; pass < 2 && !discard; ++pass) {
     if (pass == 1) {

@@ -14,6 +14,7 @@ from workloads import config, make_workload, scaled
 pytestmark = pytest.mark.gpu
 
 SPLIT_MAX = 32  # longest split-ART chunk
+SPEC_DEPTH = 8  # split ART: chunks a unit may walk ahead of its resolved look-back
 
 
 @pytest.fixture(scope="module")
@@ -219,6 +220,23 @@ def test_split_art_firing(torch_cuda, split):
     w = make_workload(config(2, "B", batch=2, num_q_heads=8, num_kv_heads=2, ctx=(20000, 32768)))
     _, stop, _, _ = check(w, tag=f"split ART {split}", split_blocks=split)
     assert np.all(stop < w.traversal_lengths())
+
+
+def test_split_art_bounded_speculation(torch_cuda):
+    """A chunk starts loading only once the chunk SPEC_DEPTH places before it
+    has published its carry, so a unit loads at most the chunks up to
+    SPEC_DEPTH - 1 past its stop chunk, plus the stop chunk's recompute.
+    With 4-block chunks the calls hand out up to 128 chunks per unit, nearly
+    all past the stop."""
+    C = 4
+    w = make_workload(config(2, "B", batch=2, num_q_heads=8, num_kv_heads=2, ctx=(20000, 32768)))
+    _, stop, issued, _ = check(w, tag="split ART bounded speculation", split_blocks=C)
+    Tp = w.traversal_lengths()
+    assert np.all(stop < Tp)
+    stop_chunk = (stop - 1) // C
+    bound = np.minimum(Tp, (stop_chunk + SPEC_DEPTH) * C) + C
+    log(f"   issued {issued.ravel().tolist()} stop {stop.ravel().tolist()} bound {bound.ravel().tolist()}")
+    assert np.all(issued <= bound)
 
 
 @pytest.mark.parametrize("p", [1, 2, 3])
