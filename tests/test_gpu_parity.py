@@ -186,7 +186,7 @@ def test_device_error_is_per_call(torch_cuda):
 # ---------------------------------------------------------------------------
 # full-size configurations: every unit on the GPU, sampled units in the oracle
 # ---------------------------------------------------------------------------
-FULL = [(2, "B"), (3, "A"), (3, "B"), (4, "A"), (4, "B"), (5, "A"), (5, "B")]
+FULL = [(2, "A"), (2, "B"), (3, "A"), (3, "B"), (4, "A"), (4, "B"), (5, "A"), (5, "B")]
 
 
 @pytest.mark.parametrize("n,reading", FULL)
@@ -207,6 +207,15 @@ def test_full_size_sampled(torch_cuda, n, reading):
             log(f"   p={p} split={split} {rep} skipped={1 - stop.sum() / w.traversal_lengths().sum():.3f}")
             assert rep.ok(), (rep.unexcused[:5], rep.bad_outputs[:5])
             assert np.all((stop >= 1) & (stop <= w.traversal_lengths()))
+    # full mode, in the library's own decomposition at this size (split-KV
+    # chunks and the combine kernel), on the same sampled units
+    out, stop, issued, err = run_gpu(w, mode=0, dev=dev)
+    assert err == 0
+    rep, _ = compare(w, out, stop, units=units, mode=0)
+    log(f"   full mode {rep}")
+    assert rep.ok(), (rep.unexcused[:5], rep.bad_outputs[:5])
+    np.testing.assert_array_equal(stop, w.traversal_lengths())
+    np.testing.assert_array_equal(issued, w.traversal_lengths())
     del dev
 
 
