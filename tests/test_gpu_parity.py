@@ -152,6 +152,16 @@ def test_full_mode_split_kv(torch_cuda, split):
     np.testing.assert_array_equal(issued, w.traversal_lengths())
 
 
+def test_full_mode_more_than_64_chunks(torch_cuda):
+    """One block per chunk over 65 blocks: the combine kernel's lanes take
+    the chunks 64 at a time, so this unit needs two passes."""
+    w = make_workload(scaled(2, "B"))
+    assert np.all(w.traversal_lengths() == 65)
+    _, stop, issued, _ = check(w, mode=0, tag="full mode, 65 chunks", split_blocks=1)
+    np.testing.assert_array_equal(stop, w.traversal_lengths())
+    np.testing.assert_array_equal(issued, w.traversal_lengths())
+
+
 def test_kept_list_out_of_range_is_reported(torch_cuda):
     from kv_cache_early_amd import art
     w = make_workload(scaled(5, "B"))
