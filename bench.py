@@ -38,6 +38,10 @@ Reported (one JSON line on stdout):
                  multi_row: M = 1, 2, 4 query rows per sequence
 
 Other modes (no timing line):
+  --table    every configuration (cfg1..cfg5) in the library's default
+        decomposition: full mode, then ART under generator readings A and
+        B (cfg4 at patience 1, 2 and 4); one markdown row per measurement
+        on stderr and a JSON object on stdout
   --summarize-pmc FETCH_DIR WRITE_DIR   turn two rocprofv3 --pmc runs of
         `bench.py --only art --copy-mib N ...` into the counter summary
   --summarize-trace TRACE_DIR BENCH_LOG  turn a rocprofv3 --kernel-trace
@@ -83,6 +87,7 @@ def parse():
     ap.add_argument("--no-flush", action="store_true", help="skip the cache-evicting read between steps")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run an elementwise copy of this many MiB `steps` times (counter calibration)")
+    ap.add_argument("--table", action="store_true", help="measure every configuration (no timing line)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_LOG"))
     ap.add_argument("--command", default="", help="command line recorded in a summary")
@@ -474,8 +479,52 @@ def summarize_trace(args):
     print("\n".join(md))
 
 
+def config_table(args):
+    """Every configuration in the library's default decomposition."""
+    import dataclasses
+
+    import torch
+    from kv_cache_early_amd import ArtDecoder
+    from workloads import config, make_workload
+    from workloads.device import to_device
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    torch.cuda.set_device(0)
+    dec = ArtDecoder()
+    rows = []
+
+    def row(n, reading, mode, r, patience):
+        rec = dict(config=n, reading=reading, mode="full" if mode == 0 else "ART", patience=patience,
+                   **{k: round(float(r[k]), 4) for k in ("ms", "ms_median", "gbs_loaded", "gbs_algorithmic",
+                                                          "pct_blocks_skipped", "wasted_frac")})
+        rows.append(rec)
+        print(f"| cfg{n} | {rec['mode']} | {reading} | {patience} | {rec['ms'] * 1e3:.0f} µs | "
+              f"{rec['gbs_loaded']:.0f} GB/s | {rec['gbs_algorithmic']:.0f} GB/s | "
+              f"{100 * rec['pct_blocks_skipped']:.1f}% | {100 * rec['wasted_frac']:.1f}% |", file=sys.stderr, flush=True)
+
+    print("| config | mode | generator | patience | time | loaded | useful | skipped | wasted |\n"
+          "|---|---|---|---|---|---|---|---|---|", file=sys.stderr, flush=True)
+    for n in (1, 2, 3, 4, 5):
+        for reading in ("A", "B"):
+            w = make_workload(config(n, reading))
+            dev = to_device(w)
+            if reading == "A":  # full mode reads every block whatever the keys
+                r, _, _ = measure(dec, w, 0, args, dev=dev)
+                row(n, "-", 0, r, "-")
+            for p in ((1, 2, 4) if n == 4 else (w.spec.patience,)):
+                w.spec = dataclasses.replace(w.spec, patience=p)
+                r, _, _ = measure(dec, w, 1, args, dev=dev)
+                row(n, reading, 1, r, p)
+            del dev, w
+            torch.cuda.empty_cache()
+    print(json.dumps({"table": rows, "steps": args.steps, "warmup": args.warmup,
+                      "cache_eviction": "untimed 1 GiB read before each timed call"}))
+
+
 def main():
     args = parse()
+    if args.table:
+        return config_table(args)
     if args.summarize_pmc:
         return summarize_pmc(args)
     if args.summarize_trace:
