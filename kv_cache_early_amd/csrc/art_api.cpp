@@ -106,10 +106,12 @@ constexpr int kWavesPerItem = 4;
 // With so few units one work item per unit leaves most of the chip idle and
 // every unit walks at the latency of its rounds; the chunks' speculative
 // passes run in parallel and only the look-back replay is sequential.
-// Measured with 32 units of 1024 kept blocks: 0.70 ms against 1.27 ms
-// (criterion never firing) and 0.44 against 0.54 ms (firing).  At 128 units
-// (512 blocks each) the two are about even, so the default stays one work
-// item per unit there.
+// Measured on MI355X with 32 units of 1024 kept blocks: 0.47 ms against
+// 1.27 ms (criterion never firing) and 0.30 against 0.54 ms (firing).  At
+// 128 units of 512 blocks split ART wins when the criterion fires (0.46 vs
+// 0.59 ms) and loses when it never does (0.64 vs 0.62 ms); at 128 units of
+// 128-512 blocks it loses when it fires (0.36 vs 0.24 ms).  So the default
+// stays one work item per unit from 64 units on.
 constexpr int64_t kSplitArtUnits = 64;
 constexpr int kSplitArtBlocks = 32;
 // Split ART: a chunk starts its speculative pass only once the chunk this
