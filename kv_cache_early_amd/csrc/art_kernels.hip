@@ -1382,10 +1382,12 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
   #pragma unroll
         for (int i = 0; i < PPCQ; ++i) P[i] = pPq[i] * sP;
         double a_own = 0.0, c_own = 0.0, a_prev = 0.0, L_own = 1.0, L_prev = 0.0;
-  #pragma unroll
+        // not unrolled: one summary's values live at a time (register budget)
+  #pragma unroll 1
         for (int k = 0; k < kMaxWaves; ++k) {
           const bool on = k < n_act;
-          const double sk = (double)__builtin_amdgcn_exp2f(mk[k] - M);  // 0 past the round's end
+          const float mkk = on ? R.sum[0][k].m[hq] : -INFINITY;
+          const double sk = (double)__builtin_amdgcn_exp2f(mkk - M);  // 0 past the round's end
           const double lk = on ? (double)R.sum[0][k].l[hq] : 0.0;
           double pa = 0.0, pc = 0.0;
   #pragma unroll
