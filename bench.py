@@ -422,7 +422,8 @@ def summarize_pmc(args):
     fs = copy_bytes / (f_cp * 1024.0)
     ws = copy_bytes / (w_cp * 1024.0)
     traffic = f_art * 1024.0 * fs + w_art * 1024.0 * ws
-    out = dict(kernel="art::art_decode_kernel<bf16, G=4, paged>", workload=WORKLOAD + ", generator B, ART mode",
+    mode = "full mode" if args.only == "full" else "ART mode"
+    out = dict(kernel="art::art_decode_kernel<bf16, G=4, paged>", workload=WORKLOAD + f", generator B, {mode}",
                fetch_kib_per_dispatch=f_art, write_kib_per_dispatch=w_art, dispatches=[n1, n2],
                copy_kernel="elementwise y = x * 1 (torch), fp32", copy_bytes_each_way=copy_bytes,
                copy_fetch_kib=f_cp, copy_write_kib=w_cp, copy_dispatches=[n3, n4],
