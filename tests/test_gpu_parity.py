@@ -152,6 +152,18 @@ def test_full_mode_split_kv(torch_cuda, split):
     np.testing.assert_array_equal(issued, w.traversal_lengths())
 
 
+@pytest.mark.parametrize("mode", [0, 1])
+def test_length_ranked_unit_order(torch_cuda, mode):
+    """One work item per unit pairs long and short sequences on a CU by
+    ranking the lengths in every workgroup: an odd batch with repeated
+    lengths still gives every unit exactly once, in place."""
+    lens = [1500, 900, 1500, 2900, 700]
+    w = make_workload(config(3, "B", batch=5, num_q_heads=8, num_kv_heads=2), context_lens=lens)
+    _, stop, issued, _ = check(w, mode=mode, tag=f"ranked unit order mode {mode}", split_blocks=10 ** 6)
+    if mode == 0:
+        np.testing.assert_array_equal(stop, w.traversal_lengths())
+
+
 def test_full_mode_more_than_64_chunks(torch_cuda):
     """One block per chunk over 65 blocks: the combine kernel's lanes take
     the chunks 64 at a time, so this unit needs two passes."""
