@@ -113,12 +113,12 @@ typedef struct {
                             a recompute of the chunk holding the stop);
                             blocks_issued then counts the speculative and
                             re-read blocks, which vary from call to call.
-                            A chunk starts loading only once the chunk 8
-                            places before it has published its carry, so a
-                            unit loads at most 7 chunks past its stop chunk
-                            plus that chunk's recompute.
+                            A chunk starts loading only once the chunk 12
+                            places before it has resolved the stop rule, so
+                            a unit loads at most 11 chunks past its stop
+                            chunk plus that chunk's recompute.
                             The library's choice in ART mode: split ART in
-                            32-block chunks when the call has fewer than 64
+                            16-block chunks when the call has fewer than 64
                             units and at most 4 query vectors per unit, one
                             chunk per unit otherwise.  In full mode: chunks
                             of at least 32 blocks, sized so that about 4096

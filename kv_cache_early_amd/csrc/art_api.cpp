@@ -113,14 +113,17 @@ constexpr int kWavesPerItem = 4;
 // 128-512 blocks it loses when it fires (0.36 vs 0.24 ms).  So the default
 // stays one work item per unit from 64 units on.
 constexpr int64_t kSplitArtUnits = 64;
-constexpr int kSplitArtBlocks = 32;
+constexpr int kSplitArtBlocks = 32;   // longest chunk the look-back replay handles
+constexpr int kSplitArtDefault = 16;  // the library's chunk length for split ART
 // Split ART: a chunk starts its speculative pass only once the chunk this
-// many places before it (same unit) has published its carry.  Measured on
-// MI355X with 32 units of 1024 kept blocks (32 chunks each), criterion
-// firing: unbounded 0.312 ms with 56% of the kept blocks loaded past the
-// stop; 8 places 0.299 ms, 25%; 4 places 0.364 ms, 12.5%.  With the
-// criterion never firing, 8 places costs nothing (0.468 ms), 4 costs 46%.
-constexpr int kSplitArtDepth = 8;
+// many places before it (same unit) has resolved the stop rule.  Measured
+// on MI355X with 32 units of 1024 kept blocks, criterion firing / never
+// firing: 32-block chunks unbounded 0.312 ms (56% of the kept blocks loaded
+// past the stop), 8 places 0.309 / 0.469 ms (25%); 16-block chunks 8 places
+// 0.284 / 0.517 ms, 12 places 0.254 / 0.428 ms (19%), 16 places 0.269 /
+// 0.415 ms.  With 32 units of 128-512 blocks, 16-block chunks at 12 places:
+// 0.175 / 0.203 ms against 0.217 / 0.229 ms for 32-block chunks at 8.
+constexpr int kSplitArtDepth = 12;
 int chunk_blocks(const art_shape& s, const art_params& p) {
   const int64_t tmax = std::max<int64_t>(1, max_traversal(s));
   if (p.mode == ART_MODE_ART) {
@@ -129,7 +132,7 @@ int chunk_blocks(const art_shape& s, const art_params& p) {
     if (p.split_blocks > 0)
       c = p.split_blocks >= tmax ? tmax : std::min<int64_t>((p.split_blocks + 3) / 4 * 4, kSplitArtBlocks);
     else  // split ART handles at most 4 query vectors per unit
-      c = (units >= kSplitArtUnits || query_vectors(s) > 4) ? tmax : kSplitArtBlocks;
+      c = (units >= kSplitArtUnits || query_vectors(s) > 4) ? tmax : kSplitArtDefault;
     return (int)std::min<int64_t>(c, tmax);
   }
   if (p.split_blocks > 0) return (int)std::min<int64_t>(p.split_blocks, tmax);

@@ -38,10 +38,11 @@ struct alignas(16) Summary {
 // published for the next chunk (look-back).
 template <int D>
 struct alignas(16) CarryRec {
-  int32_t flag;        // 0 not yet; 1 ready (no stop so far); 2 stopped at or before this chunk's end;
-                       // 3 ready, a stop was detected at or before this chunk's end (detect-only)
-  int32_t counter;     // consecutive stable checks at the chunk's end
-  double stt_last;     // |x|^2 at the chunk's last position
+  int32_t flag;        // the stop rule's state at the chunk's end: status | counter << 2, status
+                       // 0 not yet; 1 ready (no stop so far); 2 stopped at or before this chunk's end;
+                       // 3 ready, a stop was detected at or before this chunk's end (detect-only);
+                       // counter = consecutive stable checks at the chunk's end
+  int32_t pflag;       // the prefix below: 0 not yet; 1 ready; 2 the unit stopped at or before this chunk
   float m[4];          // reference max per head (log2 domain)
   double l[4];         // prefix mass per head relative to m
   double p[D / 4][4];  // prefix numerators on the probe dims relative to m

@@ -895,9 +895,121 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
 #pragma unroll
       for (int qq = 0; qq < NQ; ++qq) RL.plast[g][hh * NQ + qq] = Q[qq];
     }
-    // ---- the predecessor's carry -------------------------------------------------
+    // ---- the predecessor's prefix ------------------------------------------------
+    // Two hand-offs per chunk boundary.  The prefix state after the
+    // predecessor's last block (numerators, max, mass on the probe dims)
+    // depends on no stop decision, so each chunk publishes its own as soon
+    // as its predecessor's has arrived (pflag), and only then runs its checks
+    // and waits for the stop rule's state (status and patience counter in
+    // one word, flag).  The prefix thus moves down the chain without waiting
+    // for any chunk's scan.
     if (tid == 0) {
       int f = 1;
+      if (chunk > 0) {
+        uint32_t polls = 0;
+        for (;;) {
+          f = ld_sys(&carries[chunk - 1].pflag);
+          if (f != 0) break;
+          if (++polls >= a.spin_limit) {
+            f = -1;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(8);
+        }
+      }
+      R.flag = f;
+    }
+    __syncthreads();
+    const int pf = uni(R.flag);
+    if (pf == 2) {  // the unit stopped at or before the predecessor's end
+      discard = true;
+      if (tid == 0) {
+        st_sys(&carries[chunk].pflag, 2);
+        st_sys(&carries[chunk].flag, 2);
+      }
+      return -1;
+    }
+    {  // from here on, indices (and the LDS addresses built on them) are recomputed
+    const int tid = wid * kWave + fresh_lane();
+    const int lane = tid & (kWave - 1);
+    const int j = tid >> 3, g = (tid >> 1) & 3, hh = tid & 1;
+    const bool on = j < Cn && g < G;
+    const int jj = j < Cn ? j : 0, gg = g < G ? g : 0;
+    if (pf < 0) dev_status = ART_ERR_TIMEOUT;
+    const bool has_carry = chunk > 0 && pf == 1;
+    // The prefix is loaded unconditionally (chunk 0 reads its own, still
+    // unwritten record: valid workspace memory) and selected afterwards, so
+    // the loads go out together instead of one branch at a time.
+    const CarryRec<D>* cin = &carries[chunk > 0 ? chunk - 1 : 0];
+    double Pc[NQ];
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq) Pc[qq] = ld_sys(&cin->p[hh * NQ + qq][gg]);
+    const float Mc_in = ld_sys(&cin->m[gg]);
+    const double Lc_in = ld_sys(&cin->l[gg]);
+    const float Mc = has_carry ? Mc_in : -INFINITY;
+    const double Lc = has_carry ? Lc_in : 0.0;
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq) Pc[qq] = has_carry ? Pc[qq] : 0.0;
+    const float Ms = fmaxf(Mc, Ml);
+    const double ca = has_carry ? (double)__builtin_amdgcn_exp2f(Mc - Ms) : 0.0;
+    const double cb = (double)__builtin_amdgcn_exp2f(Ml - Ms);
+    const double L = fma(ca, Lc, cb * Lam), Lp = fma(ca, Lc, cb * Lamp);
+    // ---- this chunk's prefix, published at once: P after its last block on
+    // the common maximum, and the mass there
+    CarryRec<D>& co = carries[chunk];
+    if (on && j == Cn - 1) {
+#pragma unroll
+      for (int qq = 0; qq < NQ; ++qq)
+        st_sys(&co.p[hh * NQ + qq][g], fma(ca, Pc[qq], cb * RL.plast[g][hh * NQ + qq]));
+      if (hh == 0) {
+        st_sys(&co.m[g], Ms);
+        st_sys(&co.l[g], L);
+      }
+    }
+    wait_vm<0>();  // the prefix's stores are acknowledged
+    __syncthreads();
+    if (tid == 0) st_sys(&co.pflag, 1);
+    double cpc = 0.0, cj = 0.0;
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq) {
+      cpc = fma(Pc[qq], Pc[qq], cpc);
+      cj = fma(Pc[qq], (double)RL.ps[jj][gg][hh * NQ + qq], cj);
+    }
+    cpc += dpp<kQx1>(cpc);
+    cj += dpp<kQx1>(cj);
+    // |x|^2 at the predecessor's last position, from its prefix
+    const double iLc = Lc > 0.0 ? recip_d(Lc) : 0.0;
+    double s0 = g < G ? cpc * (iLc * iLc) : 0.0;
+    s0 += dpp<kQx2>(s0);  // heads g and g ^ 1
+    s0 += dpp<kHalfMirror>(s0);  // heads {0, 1} and {2, 3}
+    if (tid == 0) RL.stt[0] = has_carry ? s0 : 0.0;
+    if (on && hh == 0) RL.cdot[j][g] = wj * cj;
+    __syncthreads();
+    double Dj = 0.0, Dp = 0.0;  // P_c.Q_j and P_c.Q_{j-1}
+    for (int i = 0; i < Cn; ++i) {
+      const double ci = RL.cdot[i][gg];
+      Dj += i <= jj ? ci : 0.0;
+      Dp += i < jj ? ci : 0.0;
+    }
+    const double A = ca * ca * cpc + 2.0 * ca * cb * Dj + cb * cb * S1;
+    const double X = ca * ca * cpc + ca * cb * (Dj + Dp) + cb * cb * S2;
+    const double iL = recip_d(L), iLp = Lp > 0.0 ? recip_d(Lp) : 0.0;
+    double stt = on ? A * (iL * iL) : 0.0, stp = on ? X * (iL * iLp) : 0.0;
+    stt += dpp<kQx2>(stt);  // heads g and g ^ 1
+    stp += dpp<kQx2>(stp);
+    stt += dpp<kHalfMirror>(stt);  // heads {0, 1} and {2, 3}
+    stp += dpp<kHalfMirror>(stp);
+    if (on && (tid & 7) == 0) RL.stt[j + 1] = stt;
+    __syncthreads();
+    if (on && (tid & 7) == 0) {
+      const double spr = RL.stt[j];
+      const bool exists = t_begin + j + 1 >= 2;  // a check exists from the second block on
+      const bool stable = (spr > 0.0) & (stt > 0.0) & crit.scale_ok(spr, stt) & crit.dir_ok(spr, stt, stp);
+      RL.bits[j] = (exists ? 2 : 0) | (stable ? 1 : 0);
+    }
+    // ---- the predecessor's stop-rule state ----------------------------------------
+    if (tid == 0) {
+      int f = 1;  // chunk 0: no stop so far, counter 0
       if (chunk > 0) {
         uint32_t polls = 0;
         for (;;) {
@@ -913,85 +1025,19 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
       R.flag = f;
     }
     __syncthreads();
-    const int pflag = uni(R.flag);
-    const bool upstream = pflag == 3;  // detect-only: a stop was already detected
-    if (pflag == 2) {  // the unit stopped at or before the predecessor's end
+    const int sf = uni(R.flag);
+    if (sf < 0) dev_status = ART_ERR_TIMEOUT;
+    if (sf > 0 && (sf & 3) == 2) {  // the unit stopped at or before the predecessor's end
       discard = true;
-      if (tid == 0) st_sys(&carries[chunk].flag, 2);
+      if (tid == 0) st_sys(&co.flag, 2);
       return -1;
     }
-    {  // from here on, indices (and the LDS addresses built on them) are recomputed
-    const int tid = wid * kWave + fresh_lane();
-    const int lane = tid & (kWave - 1);
-    const int j = tid >> 3, g = (tid >> 1) & 3, hh = tid & 1;
-    const bool on = j < Cn && g < G;
-    const int jj = j < Cn ? j : 0, gg = g < G ? g : 0;
-    if (pflag < 0) dev_status = ART_ERR_TIMEOUT;
-    const bool has_carry = chunk > 0 && pflag > 0;
-    // The carry is loaded unconditionally (chunk 0 reads its own, still
-    // unwritten record: valid workspace memory) and selected afterwards, so
-    // the loads go out together instead of one branch at a time.
-    const CarryRec<D>* cin = &carries[chunk > 0 ? chunk - 1 : 0];
-    if (tid == 0) {
-      const double sl = ld_sys(&cin->stt_last);
-      const int cn = ld_sys(&cin->counter);
-      RL.stt[0] = has_carry ? sl : 0.0;
-      RL.counter = has_carry ? cn : 0;
-    }
-    double Pc[NQ];
-#pragma unroll
-    for (int qq = 0; qq < NQ; ++qq) Pc[qq] = ld_sys(&cin->p[hh * NQ + qq][gg]);
-    const float Mc_in = ld_sys(&cin->m[gg]);
-    const double Lc_in = ld_sys(&cin->l[gg]);
-    const float Mc = has_carry ? Mc_in : -INFINITY;
-    const double Lc = has_carry ? Lc_in : 0.0;
-#pragma unroll
-    for (int qq = 0; qq < NQ; ++qq) Pc[qq] = has_carry ? Pc[qq] : 0.0;
-    const float Ms = fmaxf(Mc, Ml);
-    const double ca = has_carry ? (double)__builtin_amdgcn_exp2f(Mc - Ms) : 0.0;
-    const double cb = (double)__builtin_amdgcn_exp2f(Ml - Ms);
-    double cpc = 0.0, cj = 0.0;
-#pragma unroll
-    for (int qq = 0; qq < NQ; ++qq) {
-      cpc = fma(Pc[qq], Pc[qq], cpc);
-      cj = fma(Pc[qq], (double)RL.ps[jj][gg][hh * NQ + qq], cj);
-    }
-    cpc += dpp<kQx1>(cpc);
-    cj += dpp<kQx1>(cj);
-    if (on && j == Cn - 1) {  // the carry out: P after the last block, on the common maximum
-#pragma unroll
-      for (int qq = 0; qq < NQ; ++qq) RL.plast[g][hh * NQ + qq] = fma(ca, Pc[qq], cb * RL.plast[g][hh * NQ + qq]);
-    }
-    if (on && hh == 0) RL.cdot[j][g] = wj * cj;
-    __syncthreads();
-    double Dj = 0.0, Dp = 0.0;  // P_c.Q_j and P_c.Q_{j-1}
-    for (int i = 0; i < Cn; ++i) {
-      const double ci = RL.cdot[i][gg];
-      Dj += i <= jj ? ci : 0.0;
-      Dp += i < jj ? ci : 0.0;
-    }
-    const double A = ca * ca * cpc + 2.0 * ca * cb * Dj + cb * cb * S1;
-    const double X = ca * ca * cpc + ca * cb * (Dj + Dp) + cb * cb * S2;
-    const double L = fma(ca, Lc, cb * Lam), Lp = fma(ca, Lc, cb * Lamp);
-    const double iL = recip_d(L), iLp = Lp > 0.0 ? recip_d(Lp) : 0.0;
-    double stt = on ? A * (iL * iL) : 0.0, stp = on ? X * (iL * iLp) : 0.0;
-    stt += dpp<kQx2>(stt);  // heads g and g ^ 1
-    stp += dpp<kQx2>(stp);
-    stt += dpp<kHalfMirror>(stt);  // heads {0, 1} and {2, 3}
-    stp += dpp<kHalfMirror>(stp);
-    if (on && (tid & 7) == 0) RL.stt[j + 1] = stt;
-    __syncthreads();
-    if (on && (tid & 7) == 0) {
-      const double spr = RL.stt[j];
-      const bool exists = t_begin + j + 1 >= 2;  // a check exists from the second block on
-      const bool stable = (spr > 0.0) & (stt > 0.0) & crit.scale_ok(spr, stt) & crit.dir_ok(spr, stt, stp);
-      RL.bits[j] = (exists ? 2 : 0) | (stable ? 1 : 0);
-    }
-    __syncthreads();
+    const bool upstream = sf > 0 && (sf & 3) == 3;  // detect-only: a stop was already detected
+    const int counter_in = sf > 0 ? (sf >> 2) : 0;
     if (wid == 0) {  // patience scan in order, on two ballots (Cn <= 32 positions)
       const int bt = lane < Cn ? RL.bits[lane] : 0;
       const uint64_t ex = __ballot((bt & 2) != 0), sb = __ballot((bt & 1) != 0);
-      int cnt = __builtin_amdgcn_readfirstlane(RL.counter), st = -1;
+      int cnt = counter_in, st = -1;
       for (int i = 0; i < Cn; ++i) {
         if (!((ex >> i) & 1)) continue;
         cnt = ((sb >> i) & 1) ? cnt + 1 : 0;
@@ -1009,28 +1055,15 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
     const int st = uni(RL.stop_local);
     const bool stop_here = st >= 0 && !upstream;
     // With no stop here, or in detect-only mode (which never terminates), the
-    // prefix state after the chunk's last block goes to the successor.
+    // successor goes on from this chunk's counter.
     if (st < 0 || detect_only) {
-      CarryRec<D>& co = carries[chunk];
-      if (on && j == Cn - 1) {
-#pragma unroll
-        for (int qq = 0; qq < NQ; ++qq) st_sys(&co.p[hh * NQ + qq][g], RL.plast[g][hh * NQ + qq]);
-        if (hh == 0) {
-          st_sys(&co.m[g], Ms);
-          st_sys(&co.l[g], L);
-        }
-      }
       if (tid == 0) {
-        st_sys(&co.counter, RL.counter);
-        st_sys(&co.stt_last, RL.stt[Cn]);
         if (stop_here) st_sys(&a.unit_stop[unit], t_begin + st);  // detect-only: the first stop
+        st_sys(&co.flag, ((stop_here || upstream) ? 3 : 1) | (RL.counter << 2));
       }
-      wait_vm<0>();  // the carry's stores are acknowledged
-      __syncthreads();
-      if (tid == 0) st_sys(&co.flag, (stop_here || upstream) ? 3 : 1);
     } else if (tid == 0) {
       st_sys(&a.unit_stop[unit], t_begin + st);
-      st_sys(&carries[chunk].flag, 2);
+      st_sys(&co.flag, 2);
     }
     __syncthreads();  // the V slabs are free again
     return detect_only ? -1 : st;
@@ -1043,7 +1076,11 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
     const int us = uni(R.flag);
     if (us > 0 && us <= t_begin) {
       discard = true;
-      if (tid == 0) st_sys(&(reinterpret_cast<CarryRec<D>*>(a.carries) + (size_t)unit * a.max_chunks)[chunk].flag, 2);
+      if (tid == 0) {
+        CarryRec<D>& own = (reinterpret_cast<CarryRec<D>*>(a.carries) + (size_t)unit * a.max_chunks)[chunk];
+        st_sys(&own.pflag, 2);
+        st_sys(&own.flag, 2);
+      }
     }
   }
   // Bounded speculation: a chunk walks only once the chunk spec_depth places
@@ -1071,9 +1108,12 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
     __syncthreads();
     const int f = uni(R.flag);
     if (f < 0) dev_status = ART_ERR_TIMEOUT;
-    if (f == 2 && !detect_only) {  // the unit stopped at or before that chunk's end
+    if (f > 0 && (f & 3) == 2 && !detect_only) {  // the unit stopped at or before that chunk's end
       discard = true;
-      if (tid == 0) st_sys(&uc[chunk].flag, 2);
+      if (tid == 0) {
+        st_sys(&uc[chunk].pflag, 2);
+        st_sys(&uc[chunk].flag, 2);
+      }
     }
   }
   bool stashed = false;
@@ -1703,7 +1743,10 @@ __global__ void art_split_init_kernel(KernelArgs a) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i == 0) a.ws->ticket = 0;
   if (i < n_units) a.unit_stop[i] = 0;
-  if (i < n_units * a.max_chunks) reinterpret_cast<CarryRec<D>*>(a.carries)[i].flag = 0;
+  if (i < n_units * a.max_chunks) {
+    reinterpret_cast<CarryRec<D>*>(a.carries)[i].flag = 0;
+    reinterpret_cast<CarryRec<D>*>(a.carries)[i].pflag = 0;
+  }
 }
 
 hipError_t launch(const KernelArgs& a, hipStream_t s) {
