@@ -96,9 +96,10 @@ art_status validate(const art_shape* sp, const art_params* pp) {
 //   either way at least 32 blocks and a multiple of the wave count;
 //   ART mode: one work item per unit (in-round sequential stopping) when
 //     there are enough units to fill the chip; otherwise chunks of
-//     kSplitArtBlocks with look-back (ordered split ART).  A caller's
-//     split_blocks is honoured, rounded up to the wave count and capped at
-//     kSplitArtBlocks (the look-back replay handles at most that many).
+//     kSplitArtDefault blocks with look-back (ordered split ART).  A
+//     caller's split_blocks is honoured, rounded up to the wave count and
+//     capped at kSplitArtBlocks (the look-back replay handles at most that
+//     many).
 constexpr int64_t kTargetItems = 4096;
 constexpr int64_t kComputeUnits = 256;  // MI355X
 constexpr int kWavesPerItem = 4;
@@ -106,8 +107,8 @@ constexpr int kWavesPerItem = 4;
 // With so few units one work item per unit leaves most of the chip idle and
 // every unit walks at the latency of its rounds; the chunks' speculative
 // passes run in parallel and only the look-back replay is sequential.
-// Measured on MI355X with 32 units of 1024 kept blocks: 0.47 ms against
-// 1.27 ms (criterion never firing) and 0.30 against 0.54 ms (firing).  At
+// Measured on MI355X with 32 units of 1024 kept blocks: 0.43 ms against
+// 1.27 ms (criterion never firing) and 0.255 against 0.55 ms (firing).  At
 // 128 units of 512 blocks split ART wins when the criterion fires (0.46 vs
 // 0.59 ms) and loses when it never does (0.64 vs 0.62 ms); at 128 units of
 // 128-512 blocks it loses when it fires (0.36 vs 0.24 ms).  So the default
