@@ -84,6 +84,8 @@ def parse():
     ap.add_argument("--cpu-units", type=int, default=0, help="oracle sample size (0 = every unit)")
     ap.add_argument("--skip-extra", action="store_true", help="only the headline measurement")
     ap.add_argument("--split-blocks", type=int, default=0)
+    ap.add_argument("--waves", type=int, default=0, choices=[0, 4, 8],
+                    help="waves per workgroup in ART mode (0 = the library's choice)")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache-evicting read between steps")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run an elementwise copy of this many MiB `steps` times (counter calibration)")
@@ -132,12 +134,16 @@ def accounting(w, stop, issued):
     return kv_bytes(issued) + per_unit + pages, kv_bytes(stop) + per_unit + pages, kv_bytes
 
 
+WAVES = 0  # art_params.waves for ART-mode calls (set from --waves)
+
+
 def decode_kwargs(dev, w, mode, split_blocks, stream, flags=0, patience=None, order=None):
     s = w.spec
     return dict(dtype=dev.dtype_code, page_size=dev.page_size, block_table=dev.block_table,
                 kept_blocks=dev.kept_blocks, kept_count=dev.kept_count, eps_scale=s.eps_scale, eps_dir=s.eps_dir,
                 patience=s.patience if patience is None else patience, order=s.order if order is None else order,
-                mode=mode, split_blocks=split_blocks, flags=flags, stream=stream.cuda_stream)
+                mode=mode, split_blocks=split_blocks, flags=flags, stream=stream.cuda_stream,
+                waves=WAVES if mode == 1 else 0)
 
 
 def eviction_buffer():
@@ -523,7 +529,9 @@ def config_table(args):
 
 
 def main():
+    global WAVES
     args = parse()
+    WAVES = args.waves
     if args.table:
         return config_table(args)
     if args.summarize_pmc:

@@ -63,15 +63,25 @@
 extern "C" {
 #endif
 
+/* Version of this interface: the layout of art_params and art_shape and the
+ * meaning of their fields.  A caller checks art_abi_version() against the
+ * ART_ABI_VERSION it was built with, and sets every struct's struct_size to
+ * sizeof(the struct); a mismatch makes every call return
+ * ART_ERR_INVALID_ARG. */
+#define ART_ABI_VERSION 2
+
 typedef enum {
   ART_OK = 0,
   ART_ERR_INVALID_ARG = 1,   /* null pointer, bad size, bad parameter       */
   ART_ERR_UNSUPPORTED = 2,   /* valid but outside the supported set         */
   ART_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required  */
   ART_ERR_HIP = 4,           /* a HIP runtime call or launch failed         */
-  ART_ERR_TIMEOUT = 5,       /* device: a split look-back wait timed out    */
-  ART_ERR_DEVICE_INPUT = 6   /* device: a kept list was out of range or not
-                                strictly ascending where required           */
+  ART_ERR_TIMEOUT = 5,       /* device: a bounded wait between waves or work
+                                items of a call timed out                   */
+  ART_ERR_DEVICE_INPUT = 6   /* device: a context length, page id or kept list
+                                was out of range, a kept list not strictly
+                                ascending where required, or a GIVEN-order
+                                list held a block twice                     */
 } art_status;
 
 typedef enum { ART_DT_F32 = 0, ART_DT_BF16 = 1 } art_dtype;
@@ -98,6 +108,7 @@ typedef enum { ART_MODE_FULL = 0, ART_MODE_ART = 1 } art_mode;
 typedef enum { ART_FLAG_NO_SCALE = 1, ART_FLAG_NO_DIR = 2, ART_FLAG_DETECT_ONLY = 4 } art_flag;
 
 typedef struct {
+  int32_t struct_size;   /* sizeof(art_params)                               */
   int32_t block_size;    /* tokens per ART block (64)                        */
   float eps_scale;       /* tau: threshold on d_scale, >= 0, finite          */
   float eps_dir;         /* phi: threshold on d_dir (1 - cos), >= 0, finite  */
@@ -129,15 +140,23 @@ typedef struct {
                             stop_idx and out do not depend on the choice
                             beyond floating-point rounding.                 */
   int32_t flags;         /* OR of art_flag; must be 0 in full mode           */
-  int32_t pairing;       /* ART mode with one work item per unit: 0 =
-                            library's choice (one), 1 = one unit per workgroup,
-                            2 = two units per workgroup walked in lockstep
-                            (the two units sharing a CU then advance at the
-                            same pace); ignored otherwise.  Results do not
-                            depend on it.                                    */
+  int32_t waves;         /* ART mode with one work item per unit and at most
+                            4 query vectors per unit: waves per workgroup,
+                            0 = library's choice, 4 or 8.  The library picks
+                            8 (one workgroup per compute unit) for calls of
+                            at most 256 units and 4 (two per compute unit)
+                            above.  With W waves, W consecutive traversal
+                            positions of a unit are in flight at once: a
+                            unit loads at most 2 W - 1 blocks past its stop
+                            (blocks_issued <= stop_idx + 2 W - 1).  Ignored
+                            (4) in every other case; 8 where it does not
+                            apply is ART_ERR_UNSUPPORTED.  out and stop_idx
+                            do not depend on it beyond floating-point
+                            rounding.                                        */
 } art_params;
 
 typedef struct {
+  int32_t struct_size;    /* sizeof(art_shape)                               */
   int32_t batch;          /* B                                               */
   int32_t num_q_heads;    /* Hq                                              */
   int32_t num_kv_heads;   /* Hkv (Hq % Hkv == 0)                             */
@@ -159,7 +178,7 @@ typedef struct {
                              writes Q with any number of rows; per-row or
                              per-block stopping is not fixed by the pages).
                              M * G must be 1, 2, 4, 8 or 16; above 4, split
-                             ART and pairing are not available.              */
+                             ART and 8 waves are not available.              */
 } art_shape;
 
 /* Bytes of device workspace art_decode needs for this shape and params
@@ -176,7 +195,11 @@ size_t art_workspace_size(const art_shape* shape, const art_params* params);
  *                 entries past ceil(len/page_size) are never read
  *   kept_blocks   int32 [B][Hkv][max_kept] candidate block indices, or NULL;
  *                 strictly ascending for NATURAL/RECENT_FIRST, distinct and
- *                 in [0, ceil(len/block_size)) for all orders
+ *                 in [0, ceil(len/block_size)) for all orders; a list that
+ *                 breaks this is reported as ART_ERR_DEVICE_INPUT (its unit
+ *                 gets out = 0, stop_idx = -1).  GIVEN order needs
+ *                 ceil(capacity / 64) <= 524288 blocks (capacity = max_ctx
+ *                 or max_pages * page_size), ART_ERR_UNSUPPORTED otherwise
  *   kept_count    int32 [B][Hkv] entries used per unit (NULL iff kept_blocks)
  *   out           fp32 [B][M][Hq][d]               (written)
  *   stop_idx      int32 [B][Hkv]                   (written)
@@ -267,6 +290,9 @@ const char* art_status_string(art_status status);
 
 /* Probe-stride constant used for x^(t) (4), for callers that report it. */
 int32_t art_probe_stride(void);
+
+/* ART_ABI_VERSION of the built library. */
+int32_t art_abi_version(void);
 
 #ifdef __cplusplus
 }

@@ -35,19 +35,22 @@ ART_FLAG_NO_DIR = 2
 ART_FLAG_DETECT_ONLY = 4
 ART_SELECT_ASCENDING = 0
 ART_SELECT_IMPORTANCE = 1
+ART_ABI_VERSION = 2  # include/art.h
 
 EXPORTS = ("art_workspace_size", "art_decode", "art_last_error", "art_status_string", "art_probe_stride",
-           "art_select_workspace_size", "art_block_means", "art_select_blocks")
+           "art_select_workspace_size", "art_block_means", "art_select_blocks", "art_abi_version")
 
 
 class art_params(ctypes.Structure):
-    _fields_ = [("block_size", ctypes.c_int32), ("eps_scale", ctypes.c_float), ("eps_dir", ctypes.c_float),
-                ("patience", ctypes.c_int32), ("order", ctypes.c_int32), ("mode", ctypes.c_int32),
-                ("split_blocks", ctypes.c_int32), ("flags", ctypes.c_int32), ("pairing", ctypes.c_int32)]
+    _fields_ = [("struct_size", ctypes.c_int32), ("block_size", ctypes.c_int32), ("eps_scale", ctypes.c_float),
+                ("eps_dir", ctypes.c_float), ("patience", ctypes.c_int32), ("order", ctypes.c_int32),
+                ("mode", ctypes.c_int32), ("split_blocks", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("waves", ctypes.c_int32)]
 
 
 class art_shape(ctypes.Structure):
-    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+    _fields_ = [("struct_size", ctypes.c_int32), ("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("max_ctx", ctypes.c_int32), ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int32),
                 ("max_kept", ctypes.c_int32), ("q_rows", ctypes.c_int32)]
@@ -94,6 +97,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.art_select_blocks.argtypes = [ctypes.POINTER(art_shape), ctypes.POINTER(art_select_params), vp, vp,
                                       ctypes.c_int32, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.art_select_blocks.restype = ctypes.c_int
+    lib.art_abi_version.argtypes = []
+    lib.art_abi_version.restype = ctypes.c_int32
+    if lib.art_abi_version() != ART_ABI_VERSION:
+        raise ImportError(f"libart.so reports ABI version {lib.art_abi_version()}, the binding expects "
+                          f"{ART_ABI_VERSION}; rebuild it")
     _lib = lib
     return lib
 
@@ -104,13 +112,14 @@ def status_string(status: int) -> str:
 
 def make_shape(batch, num_q_heads, num_kv_heads, head_dim, dtype, page_size=0, max_ctx=0, max_pages=0,
                num_pages=0, max_kept=0, q_rows=1) -> art_shape:
-    return art_shape(batch, num_q_heads, num_kv_heads, head_dim, dtype, page_size, max_ctx, max_pages,
-                     num_pages, max_kept, q_rows)
+    return art_shape(ctypes.sizeof(art_shape), batch, num_q_heads, num_kv_heads, head_dim, dtype, page_size,
+                     max_ctx, max_pages, num_pages, max_kept, q_rows)
 
 
 def make_params(eps_scale=1e-3, eps_dir=1e-4, patience=2, order=ART_ORDER_RECENT_FIRST, mode=ART_MODE_ART,
-                block_size=64, split_blocks=0, flags=0, pairing=0) -> art_params:
-    return art_params(block_size, eps_scale, eps_dir, patience, order, mode, split_blocks, flags, pairing)
+                block_size=64, split_blocks=0, flags=0, waves=0) -> art_params:
+    return art_params(ctypes.sizeof(art_params), block_size, eps_scale, eps_dir, patience, order, mode,
+                      split_blocks, flags, waves)
 
 
 def workspace_size(shape: art_shape, params: art_params) -> int:
@@ -183,7 +192,7 @@ class ArtDecoder:
 
     def decode(self, q, k, v, context_lens, *, dtype: int, page_size: int = 0, block_table=None,
                kept_blocks=None, kept_count=None, eps_scale=1e-3, eps_dir=1e-4, patience=2,
-               order=ART_ORDER_RECENT_FIRST, mode=ART_MODE_ART, block_size=64, split_blocks=0, flags=0, pairing=0,
+               order=ART_ORDER_RECENT_FIRST, mode=ART_MODE_ART, block_size=64, split_blocks=0, flags=0, waves=0,
                out=None, stop_idx=None, blocks_issued=None, stream=None) -> DecodeResult:
         torch = self.torch
         if q.dim() == 4:  # [B, M, Hq, d]: M query rows per sequence
@@ -199,7 +208,7 @@ class ArtDecoder:
                            max_pages=block_table.shape[1] if block_table is not None else 0,
                            num_pages=k.shape[0] if page_size else 0,
                            max_kept=kept_blocks.shape[2] if kept_blocks is not None else 0, q_rows=M)
-        params = make_params(eps_scale, eps_dir, patience, order, mode, block_size, split_blocks, flags, pairing)
+        params = make_params(eps_scale, eps_dir, patience, order, mode, block_size, split_blocks, flags, waves)
         nbytes = workspace_size(shape, params)
         if nbytes == 0:  # invalid shape or params: art_decode names the reason before using anything
             raise ArtError(decode_raw(shape, params, q, k, v, context_lens, block_table, kept_blocks, kept_count,

@@ -29,6 +29,16 @@ int64_t max_traversal(const art_shape& s) {
   return (tokens + kBlockTokens - 1) / kBlockTokens;
 }
 
+// Blocks a sequence can hold: ceil(capacity / 64), capacity = max_ctx or
+// max_pages * page_size (the kept list does not matter for this bound).
+int64_t capacity_blocks(const art_shape& s) {
+  const int64_t tokens = s.page_size == 0 ? (int64_t)s.max_ctx : (int64_t)s.max_pages * s.page_size;
+  return (tokens + kBlockTokens - 1) / kBlockTokens;
+}
+// Longest sequence (in blocks) whose GIVEN-order kept list the kernel can
+// check for repeats: one bit per block in the 64 KiB of V slabs.
+constexpr int64_t kGivenMaxBlocks = 65536LL * 8;
+
 // Query rows per sequence (0 is read as 1).
 int rows_of(const art_shape& s) { return s.q_rows > 0 ? s.q_rows : 1; }
 // Query vectors per unit: G query heads times the query rows.
@@ -38,7 +48,7 @@ int64_t query_vectors(const art_shape& s) {
 
 // Shape rules shared by every entry point.
 art_status validate_shape(const art_shape* sp) {
-  if (!sp) return ART_ERR_INVALID_ARG;
+  if (!sp || sp->struct_size != (int32_t)sizeof(art_shape)) return ART_ERR_INVALID_ARG;
   const art_shape& s = *sp;
   if (s.batch < 0 || s.num_q_heads <= 0 || s.num_kv_heads <= 0 || s.head_dim <= 0) return ART_ERR_INVALID_ARG;
   if (s.num_q_heads % s.num_kv_heads != 0) return ART_ERR_INVALID_ARG;
@@ -62,7 +72,7 @@ art_status validate_shape(const art_shape* sp) {
 }
 
 art_status validate(const art_shape* sp, const art_params* pp) {
-  if (!sp || !pp) return ART_ERR_INVALID_ARG;
+  if (!sp || !pp || pp->struct_size != (int32_t)sizeof(art_params)) return ART_ERR_INVALID_ARG;
   const art_shape& s = *sp;
   const art_params& p = *pp;
   if (p.block_size <= 0 || p.patience < 1 || p.split_blocks < 0) return ART_ERR_INVALID_ARG;
@@ -71,7 +81,7 @@ art_status validate(const art_shape* sp, const art_params* pp) {
   if (p.mode != ART_MODE_FULL && p.mode != ART_MODE_ART) return ART_ERR_INVALID_ARG;
   constexpr int32_t kAllFlags = ART_FLAG_NO_SCALE | ART_FLAG_NO_DIR | ART_FLAG_DETECT_ONLY;
   if ((p.flags & ~kAllFlags) != 0 || (p.mode == ART_MODE_FULL && p.flags != 0)) return ART_ERR_INVALID_ARG;
-  if (p.pairing < 0 || p.pairing > 2) return ART_ERR_INVALID_ARG;
+  if (p.waves != 0 && p.waves != 4 && p.waves != 8) return ART_ERR_INVALID_ARG;
   if (p.order == ART_ORDER_GIVEN && s.max_kept == 0) return ART_ERR_INVALID_ARG;
   const art_status st = validate_shape(sp);
   if (st != ART_OK) return st;
@@ -80,6 +90,11 @@ art_status validate(const art_shape* sp, const art_params* pp) {
   const int GQ = (s.num_q_heads / s.num_kv_heads) * rows_of(s);
   if (GQ > 4 && p.mode == ART_MODE_ART && p.split_blocks > 0 && p.split_blocks < max_traversal(s))
     return ART_ERR_UNSUPPORTED;
+  // eight waves per workgroup: ART mode, one work item per unit, at most 4 query vectors
+  if (p.waves == 8 && (p.mode != ART_MODE_ART || GQ > 4)) return ART_ERR_UNSUPPORTED;
+  // GIVEN order: the kernel checks the kept list for repeated blocks with one
+  // bit per block of the sequence in a 64 KiB LDS buffer
+  if (p.order == ART_ORDER_GIVEN && capacity_blocks(s) > kGivenMaxBlocks) return ART_ERR_UNSUPPORTED;
   return ART_OK;
 }
 
@@ -145,13 +160,6 @@ int chunk_blocks(const art_shape& s, const art_params& p) {
   return (int)std::min<int64_t>(c, tmax);
 }
 
-// Blocks a sequence can hold: ceil(capacity / 64), capacity = max_ctx or
-// max_pages * page_size (the kept list does not matter for selection).
-int64_t capacity_blocks(const art_shape& s) {
-  const int64_t tokens = s.page_size == 0 ? (int64_t)s.max_ctx : (int64_t)s.max_pages * s.page_size;
-  return (tokens + kBlockTokens - 1) / kBlockTokens;
-}
-
 // Selection workspace: the header and one ItemState per workgroup of the
 // larger of the two launches (block means: four blocks per workgroup).
 size_t select_ws_bytes(const art_shape& s) {
@@ -162,6 +170,20 @@ size_t select_ws_bytes(const art_shape& s) {
 }
 
 constexpr int64_t kSelectSortMax = 4096;  // blocks per unit the selection kernel sorts
+
+// Waves per workgroup.  ART mode with one work item per unit and at most 4
+// query vectors per unit: 8 waves (one workgroup per CU, eight positions in
+// flight per unit) when the call has at most one unit per CU, where each
+// unit's own walk sets the time; 4 waves (two workgroups per CU) otherwise.
+// Everything else runs 4 waves.  A caller's art_params.waves overrides the
+// choice for the single-item ART case.
+constexpr int64_t kEightWaveUnits = kComputeUnits;
+int waves_per_item(const art_shape& s, const art_params& p, int max_chunks) {
+  const int64_t units = (int64_t)s.batch * s.num_kv_heads;
+  if (p.mode != ART_MODE_ART || max_chunks != 1 || query_vectors(s) > 4) return kWavesPerItem;
+  if (p.waves == 4 || p.waves == 8) return p.waves;
+  return units <= kEightWaveUnits ? 8 : kWavesPerItem;
+}
 
 art::WsLayout layout(const art_shape& s, const art_params& p, int chunk, int max_chunks) {
   art::WsLayout L{};
@@ -252,21 +274,15 @@ art_status art_decode(const art_shape* shape, const art_params* params, const vo
     }
   }
   a.detect_only = (p.flags & ART_FLAG_DETECT_ONLY) ? 1 : 0;
-  // Two units per workgroup only on request: it evens out the progress of
-  // the two units sharing a CU, but on the large-batch paged workload (512
-  // units, two per CU) it measured about 4% slower than one unit per
-  // workgroup (the lockstep rounds wait for the slower of eight waves), and
-  // with fewer units than two per CU it would leave CUs idle.
   a.rows = rows_of(s);
   a.gh = s.num_q_heads / s.num_kv_heads;
-  a.pair = (p.mode == ART_MODE_ART && max_chunks == 1 && p.pairing == 2 && a.rows * a.gh <= 4) ? 1 : 0;
   a.order = p.order;
   a.mode = p.mode;
   a.chunk_blocks = chunk;
   a.max_chunks = max_chunks;
   a.split_art = (p.mode == ART_MODE_ART && max_chunks > 1) ? 1 : 0;
   a.max_trav = (int)tmax;
-  a.waves = kWavesPerItem;
+  a.waves = waves_per_item(s, p, max_chunks);
   a.q = q;
   a.k = k;
   a.v = v;
@@ -418,5 +434,7 @@ const char* art_status_string(art_status status) {
 }
 
 int32_t art_probe_stride(void) { return kProbeStride; }
+
+int32_t art_abi_version(void) { return ART_ABI_VERSION; }
 
 }  // extern "C"

@@ -59,14 +59,13 @@ struct KernelArgs {
   double crit_hi, crit_lo, crit_c2;  // (1+eps_scale)^2, (1-eps_scale)^2, (1-eps_dir)^2
   int32_t crit_tau_lt1, crit_phi_le1; // eps_scale < 1, eps_dir <= 1
   int32_t detect_only;   // record the stop, never terminate
-  int32_t pair;          // two units per workgroup (single-chunk ART)
   int32_t rows;          // query rows per sequence (q and out are [B][rows][Hq][d])
   int32_t gh;            // query heads per kv head (Hq / Hkv); a unit has rows * gh query vectors
   int32_t split_art;     // ART mode with several chunks per unit (look-back)
   int32_t max_trav;      // traversal blocks per unit bound (summary row stride)
   int32_t chunk_blocks;  // traversal blocks per work item
   int32_t max_chunks;    // work items per unit
-  int32_t waves;         // waves per workgroup (one work item per workgroup)
+  int32_t waves;         // waves per workgroup, 4 or 8 (one work item per workgroup)
   // inputs
   const void* q;
   const void* k;

@@ -66,7 +66,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kMaxWaves = 4;      // waves per workgroup (launch bound)
+constexpr int kMaxWaves = 8;      // waves per workgroup (4 or 8)
 constexpr int kBlk = 64;          // tokens per ART block
 constexpr int kTiles = kBlk / 16; // 16-token MFMA tiles per block
 constexpr int kRowChunks = 16;    // 16-byte chunks per K/V row
@@ -413,23 +413,36 @@ __device__ __forceinline__ BlockAddr block_addr4(const UnitView& u, int j, int& 
 // ---------------------------------------------------------------------------
 // LDS layout (one workgroup)
 // ---------------------------------------------------------------------------
-struct alignas(16) Check {     // one position's stability test, published by its wave
-  double stt;                  // |x^(t)|^2
-  int stable;                  // the check at this position passed
-  int pad;
+// The stop rule runs as a chain over the traversal positions (ART mode with
+// one work item per unit): the wave holding position t merges its block
+// onto the prefix state after position t - 1, runs the checks of position
+// t and publishes the prefix state after t.  A record holds one lane's
+// share of that state (lane (lg, c): query vectors lg + 4 hh for hh < NH,
+// or lg alone with up to four; probe dims c * PPC .. c * PPC + PPC - 1).
+template <int NPL, int NH>
+struct alignas(16) LaneLink {
+  double p[NPL];  // prefix numerators on the probe dims, relative to m
+  double l[NH];   // prefix mass per query vector, relative to m
+  float m[NH];    // reference max per query vector (log2 domain)
 };
-template <int G, int D>
+struct alignas(16) LinkHead {
+  int seq;        // position + 1 once the record of that position is complete
+  int counter;    // consecutive stable checks after the position
+  int detected;   // detect-only: the first stop the rule reached, 0 if none
+  int pad;
+  double stt;     // |x|^2 after the position
+};
+template <int NPL, int NH>
 struct alignas(16) RoundLds {
-  // by round parity; more than 4 query vectors per unit: one buffer (every
-  // read of a round's summaries happens before its second barrier, every
-  // write of the next round's after it)
-  Summary<D, (G > 4 ? G : 4)> sum[G > 4 ? 1 : 2][kMaxWaves];
-  Check chk[2][kMaxWaves];            // by round parity: per position
+  LaneLink<NPL, NH> link[2][kWave];    // by position parity
+  LinkHead head[2];
+  int stop_at;                         // blocks processed at the stop, 0 while none
+  int detected;                        // detect-only: the first stop, 0 while none
+  int timeout;                         // a wave's wait for its predecessor's record timed out
   int bad;
   int zero_pos;
-  int ticket;                         // split ART: this workgroup's work item
-  int flag;                           // split ART: predecessor's carry flag / early stop
-  int live;                           // two units per workgroup: positions left after the last round
+  int ticket;                          // split ART: this workgroup's work item
+  int flag;                            // split ART: predecessor's carry flag / early stop
 };
 // Split ART look-back replay state (reuses the V slabs): the chunk's block
 // summaries transposed to [block][head][probe dim], |x|^2 per position and
@@ -447,14 +460,14 @@ struct alignas(16) ReplayLds {
   int stop_local;             // blocks of the chunk up to and including the stop, -1 if none
   int counter;
 };
-template <int G, int D>
+template <int G, int D, int W>
 struct alignas(16) EpilogueLds {     // per-wave final state (reuses the V slabs)
   static constexpr int GS = G > 4 ? G : 4;
-  float m[kMaxWaves][GS];
-  float l[kMaxWaves][GS];
-  int issued[kMaxWaves];
-  int bad[kMaxWaves];
-  float acc[kMaxWaves][D][GS];       // [wave][dim][query vector]
+  float m[W][GS];
+  float l[W][GS];
+  int issued[W];
+  int bad[W];
+  float acc[W][D][GS];               // [wave][dim][query vector]
 };
 
 // ---------------------------------------------------------------------------
@@ -462,39 +475,34 @@ struct alignas(16) EpilogueLds {     // per-wave final state (reuses the V slabs
 // ---------------------------------------------------------------------------
 // SPLIT: the ordered split-ART instantiation (ticket order, look-back replay,
 // recompute); the other instantiation serves full mode and single-chunk ART.
-// TEAMS = 2 (single-chunk ART only): a workgroup of two teams of 4 waves
-// walks two units, one per team, in lockstep: both teams meet at every
-// round's barriers, so the two units on a CU advance at the same pace (two
-// separate workgroups on one CU do not: the older one's loads are served
-// first and the younger unit falls far behind).  A team whose unit is done,
-// or that has no unit, stays idle in the loop until both are done.
-template <int DT, int G, bool PAGED, bool SPLIT, int TEAMS>
-__global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_decode_kernel(KernelArgs a) {
-  static_assert(TEAMS == 1 || (TEAMS == 2 && !SPLIT), "two teams only in single-chunk ART");
+// W waves per workgroup: 4 (two workgroups per CU) or 8 (one per CU; single
+// chunk ART with up to 4 query vectors per unit, for calls with at most one
+// unit per CU, where a unit's own walk sets the time).
+template <int DT, int G, bool PAGED, bool SPLIT, int W>
+__global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(KernelArgs a) {
+  static_assert(W == 4 || (W == 8 && !SPLIT && G <= 4), "waves per workgroup");
   // G is the number of query vectors of a unit: rows * (Hq / Hkv).  Up to 4
   // they fill the 16 MFMA columns by repetition; 8 or 16 (multi-row queries)
-  // take the columns and output rows one for one, with the criterion below
-  // laid out per query vector (no split ART, no pairing).
-  static_assert(G == 1 || G == 2 || G == 4 || ((G == 8 || G == 16) && !SPLIT && TEAMS == 1), "query vectors per unit");
+  // take the columns and output rows one for one (no split ART).
+  static_assert(G == 1 || G == 2 || G == 4 || ((G == 8 || G == 16) && !SPLIT), "query vectors per unit");
   using GE = Geo<DT>;
   constexpr int D = GE::D, ES = GE::ES, PPC = GE::PPC;
   constexpr int NDT = D / 16;  // 16-dim output tiles
   constexpr int ROW = D * ES;
+  constexpr int NT = kWave * W;  // threads per workgroup
+  constexpr int NH = G > 4 ? G / 4 : 1;  // query vectors per lane row in the stop rule's layout
+  constexpr int NPL = NH * PPC;          // probe values per lane there
   static_assert(ROW == kRowChunks * 16, "rows must be 16 chunks of 16 bytes");
-  __shared__ RoundLds<G, D> R_all[TEAMS];
-  __shared__ alignas(16) uint8_t vbuf_all[TEAMS][kMaxWaves][kVSlab];
+  __shared__ RoundLds<NPL, NH> R;
+  __shared__ alignas(16) uint8_t vbuf[W][kVSlab];
   // the waves' final state is stashed above the replay state, so a split
   // chunk can keep its pass-0 result in LDS while the replay runs
   constexpr int kEpiOff = SPLIT ? 32768 : 0;
   static_assert(!SPLIT || sizeof(ReplayLds<D>) <= kEpiOff, "replay state must fit below the stash");
-  static_assert(kEpiOff + sizeof(EpilogueLds<G, D>) <= sizeof(vbuf_all[0]), "stash must fit the V slabs");
+  static_assert(kEpiOff + sizeof(EpilogueLds<G, D, W>) <= sizeof(vbuf), "stash must fit the V slabs");
 
-  constexpr int W = kMaxWaves;  // waves per work item
-  const int team = TEAMS == 1 ? 0 : uni((int)(threadIdx.x >> 8));
-  const int tid = threadIdx.x & (kWave * kMaxWaves - 1);  // thread within the team
+  const int tid = threadIdx.x;
   const int wid = uni(tid >> 6);
-  RoundLds<G, D>& R = R_all[team];
-  auto& vbuf = vbuf_all[team];
   const int lane = threadIdx.x & 63;
   const int lg = lane >> 4;
   const int c = lane & 15;
@@ -505,17 +513,13 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
   // Split ART hands out work items in ticket order, chunk-major: an item's
   // predecessor chunk always holds a smaller ticket, so it is running or done
   // when the item waits for its carry.
-  int item = blockIdx.x * TEAMS + team;
-  // two teams: an odd unit count leaves the last team without a unit
-  const bool phantom = TEAMS == 2 && item >= n_items;
-  if (phantom) item = n_items - 1;
-  bool idle = phantom;  // two teams: nothing to walk (outputs already written)
+  int item = blockIdx.x;
   if constexpr (SPLIT) {
     if (tid == 0) R.ticket = (int)atomicAdd(&a.ws->ticket, 1u);
     __syncthreads();
     item = uni(R.ticket);
   }
-  if (item == 0 && tid == 0 && !phantom) {
+  if (item == 0 && tid == 0) {
     a.ws->magic = kWsMagic;
     a.ws->n_items = n_items;
   }
@@ -532,7 +536,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
   // unit 1.011 -> 0.869 ms; criterion firing (work independent of length)
   // 0.92-1.05x over six seeds, about 1.0 on average.  Ranking all lengths in
   // every workgroup costs B^2/64 compares per lane, hence the bound on B.
-  if (!SPLIT && TEAMS == 1 && a.max_chunks == 1 && a.batch >= 2 && a.batch <= 256) {
+  if (!SPLIT && W == 4 && a.max_chunks == 1 && a.batch >= 2 && a.batch <= 256) {
     const int B = a.batch, half = B / 2;
     const int k = unit / a.hkv, hh = unit % a.hkv;
     const int r = k < half ? k : B - 1 - (k - half);
@@ -613,10 +617,24 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
     }
     __syncthreads();
     if (u.n_trav >= 0 && u.n_trav <= a.max_kept) {
-      for (int i = tid; i < u.n_trav; i += kWave * kMaxWaves) {
+      // GIVEN order: the entries must be distinct.  One bit per block of the
+      // sequence, in the V slabs (unused until the first loads), marks the
+      // entries seen; the host bounds the sequences' block count by the bits
+      // the slabs hold.
+      const bool given = a.order == ART_ORDER_GIVEN;
+      uint32_t* seen = reinterpret_cast<uint32_t*>(&vbuf[0][0]);
+      const int nwords = (u.n_blocks + 31) >> 5;
+      const bool fits = nwords <= (int)(sizeof(vbuf) / sizeof(uint32_t));
+      if (given && fits) {
+        for (int i = tid; i < nwords; i += NT) seen[i] = 0u;
+        __syncthreads();
+      }
+      if (given && !fits && tid == 0) R.bad = 1;
+      for (int i = tid; i < u.n_trav; i += NT) {
         const int e = u.kept[i];
         bool lb = e < 0 || e >= u.n_blocks;
-        if (a.order != ART_ORDER_GIVEN && i > 0) lb |= e <= u.kept[i - 1];
+        if (!given && i > 0) lb |= e <= u.kept[i - 1];
+        if (given && fits && !lb) lb = ((atomicOr(&seen[e >> 5], 1u << (e & 31)) >> (e & 31)) & 1u) != 0;
         if (lb) atomicOr(&R.bad, 1);
         if (e == 0) atomicMin(&R.zero_pos, i);
       }
@@ -625,41 +643,34 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
     const int bad = uni(R.bad);
     const int zp = uni(R.zero_pos);
     __syncthreads();
-    if (bad && !phantom) {
+    if (bad) {
       if (tid == 0) a.items[item] = ItemState{ART_ERR_DEVICE_INPUT, -1};
       if (chunk == 0) {
-        for (int i = tid; i < G * D; i += kWave * kMaxWaves) out_at(i) = 0.f;
+        for (int i = tid; i < G * D; i += NT) out_at(i) = 0.f;
         if (tid == 0) {
           a.stop_idx[unit] = -1;
           if (a.blocks_issued) a.blocks_issued[unit] = 0;
         }
       }
-    }
-    if (bad) {
-      if constexpr (TEAMS == 1) return;
-      idle = true;
+      return;
     }
     u.zero_pos = zp == 0x7fffffff ? -1 : zp;
   }
   const int item_status = bad_input ? ART_ERR_DEVICE_INPUT : ART_OK;
-  if (!idle && (u.n_trav <= 0 || t_begin >= u.n_trav)) {  // nothing (left) to attend to
+  if (u.n_trav <= 0 || t_begin >= u.n_trav) {  // nothing (left) to attend to
     if (tid == 0) a.items[item] = ItemState{item_status, 0};
   }
-  if (!idle && u.n_trav <= 0) {  // out = 0, stop = 0
+  if (u.n_trav <= 0) {  // out = 0, stop = 0
     if (chunk == 0) {
-      for (int i = tid; i < G * D; i += kWave * kMaxWaves) out_at(i) = 0.f;
+      for (int i = tid; i < G * D; i += NT) out_at(i) = 0.f;
       if (tid == 0) {
         a.stop_idx[unit] = 0;
         if (a.blocks_issued) a.blocks_issued[unit] = 0;
       }
     }
-    if constexpr (TEAMS == 1) return;
-    idle = true;
+    return;
   }
-  if (t_begin >= t_end) {  // chunk past this unit's traversal
-    if constexpr (TEAMS == 1) return;
-    idle = true;
-  }
+  if (t_begin >= t_end) return;  // chunk past this unit's traversal
 
   // ---- query operand (B of S^T = K q^T): k-step j, lane (lg, c) holds the
   // 16 bytes of chunk 4j + lg of head c % G (heads replicated over columns)
@@ -680,25 +691,6 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const bool art_mode = a.mode == ART_MODE_ART;
   const bool detect_only = art_mode && a.detect_only != 0;  // record the stop, read every block
-  // prefix state on the probe dims (same in every wave): running max, mass and
-  // numerators for head hg = lg (lanes with lg >= G carry head 0 unused),
-  // the previous probe's squared norm, and the patience counter
-  const int hg = lg < G ? lg : 0;
-  float mP = -INFINITY;
-  double lP = 0.0, pP[PPC];
-#pragma unroll
-  for (int k = 0; k < PPC; ++k) pP[k] = 0.0;
-  double stt_last = 0.0;
-  int counter = 0;
-  // more than 4 query vectors per unit: lane = (query vector hq, chunk cq),
-  // LPH lanes per vector, PPCQ of its probe dims per lane
-  constexpr int LPH = G > 4 ? kWave / G : 16;
-  constexpr int PPCQ = G > 4 ? (D / 4) / LPH : 1;
-  const int hq = lane / LPH, cq = lane % LPH;
-  float mPq = -INFINITY;
-  double lPq = 0.0, pPq[PPCQ];
-#pragma unroll
-  for (int k = 0; k < PPCQ; ++k) pPq[k] = 0.0;
   const Criterion crit{a.crit_hi, a.crit_lo, a.crit_c2, a.crit_tau_lt1 != 0, a.crit_phi_le1 != 0};
 
   // ---- loads ---------------------------------------------------------------
@@ -781,15 +773,24 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
   int bad_page = 0;
   int issued = 0;
   int stop = -1;  // traversal blocks processed at the stop (ART mode)
-  int detected = -1;  // detect-only: the first stop the rule reached
   // Split ART: pass 0 walks the whole chunk speculatively, storing block
   // summaries; the look-back replay then decides the stop; if it lies inside
   // the chunk, pass 1 recomputes the chunk's output up to the stop.
   const bool split = SPLIT && art_mode && !single;
   bool discard = false;  // the unit stopped before this chunk
-  int t_stop = idle ? t_begin : t_end;
-  if constexpr (TEAMS == 2) {
-    if (tid == 0) R.live = idle ? 0 : 1;  // read after the first round's first barrier
+  int t_stop = t_end;
+  // ART mode in one work item per unit: the stop rule runs as a chain over
+  // the positions (below)
+  const bool chain = art_mode && !split;
+  if (chain) {
+    if (tid == 0) {
+      R.stop_at = 0;
+      R.detected = 0;
+      R.timeout = 0;
+      R.head[0].seq = 0;
+      R.head[1].seq = 0;
+    }
+    __syncthreads();
   }
 
   // ---- split ART: look-back replay of the stop rule over this chunk -----------
@@ -812,9 +813,12 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
   // The waves' running state (m, l, output) goes to LDS, where the
   // epilogue merges it; pass-0 results of a split chunk wait there during
   // the replay.
-  auto& E = *reinterpret_cast<EpilogueLds<G, D>*>(&vbuf[0][kEpiOff]);
+  auto& E = *reinterpret_cast<EpilogueLds<G, D, W>*>(reinterpret_cast<uint8_t*>(vbuf) + kEpiOff);
   auto stash_waves = [&]() {
-    wait_vm<0>();  // speculative loads may still be landing in the V slabs
+    // speculative loads may still be landing in the V slabs and in the K
+    // registers (a walk that stopped leaves its prefetch in flight): the K
+    // registers are tied to the wait, so none is reused before it
+    wait_v_tied<0>(kr);
     __syncthreads();
     if (lane < 16) {
 #pragma unroll
@@ -843,16 +847,16 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
     __syncthreads();  // this chunk's summaries (written by its own waves) are visible
     const Summary<D>* gsum = reinterpret_cast<const Summary<D>*>(a.summaries) + ((size_t)unit * a.max_trav + t_begin);
     {  // stage [j][q][g] -> [j][g][q]; all loads of a thread are issued before its stores
-      constexpr int kPer = kSplitMax * D / (kWave * kMaxWaves);
+      constexpr int kPer = kSplitMax * D / NT;
       float v[kPer];
 #pragma unroll
       for (int r = 0; r < kPer; ++r) {
-        const int i = tid + r * kWave * kMaxWaves;
+        const int i = tid + r * NT;
         v[r] = i < Cn * D ? gsum[i / D].ps[(i % D) >> 2][i & 3] : 0.f;
       }
 #pragma unroll
       for (int r = 0; r < kPer; ++r) {
-        const int i = tid + r * kWave * kMaxWaves;
+        const int i = tid + r * NT;
         if (i < Cn * D) RL.ps[i / D][i & 3][(i % D) >> 2] = v[r];
       }
       if (tid < Cn * 4) {
@@ -1117,6 +1121,46 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
     }
   }
   bool stashed = false;
+  // The stop rule's chain.  The wave holding position t (t = t_begin + wid,
+  // then every W positions) merges its block's summary onto the prefix state
+  // after position t - 1, read from the record its predecessor wave
+  // published, runs the two stability tests and the patience counter of
+  // position t, and publishes the state after t.  Records alternate by
+  // position parity: the record of t - 1 is read (by the wave of t) before
+  // the record of t + 1 can be written, since that one needs the record of
+  // t.  The wave commits its block once the record of t - 1 shows no stop
+  // before it, so no block after the stop is ever committed, and the
+  // decision is the one a strictly sequential walk makes.  No workgroup
+  // barrier sits in the walk: a wave waits only for its predecessor's record.
+  // A stop, once found, is also published in R.stop_at, which every wave
+  // reads before it computes or prefetches a block.
+  // true once the record of t - 1 is there; false when the unit stopped
+  // after at most t blocks (position t does not count).  The stop word is
+  // read after the sequence number: a record that stops the unit writes
+  // R.stop_at before its sequence number.
+  // The wait is bounded: past a.spin_limit * 4 polls (far beyond any
+  // legitimate wait) the wave records a timeout and publishes a stop after
+  // the first block, which ends every wave's walk.
+  auto chain_wait = [&](int t) -> bool {
+    volatile int* sq = &R.head[(t - 1) & 1].seq;
+    volatile int* sa = &R.stop_at;
+    for (uint32_t polls = 0;; ++polls) {
+      const int q = uni(*sq);
+      const int st = uni(*sa);
+      if (st > 0 && st <= t) return false;
+      if (q == t) break;
+      if (polls >= 4u * a.spin_limit) {
+        if (lane == 0) {
+          *(volatile int*)&R.timeout = 1;
+          *sa = 1;
+        }
+        return false;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    compiler_fence();
+    return true;
+  };
   for (int pass = 0; pass < 2 && !discard; ++pass) {
     if (pass == 1) {
       m_c = -INFINITY;
@@ -1124,171 +1168,166 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    int t = t_begin + wid;
     BlockAddr cur;
-    if (t_begin + wid < t_stop) {
-      cur = block_addr4<ROW, PAGED>(u, uni(block_at(u, a.order, t_begin + wid)), bad_page);
+    if (t < t_stop) {
+      cur = block_addr4<ROW, PAGED>(u, uni(block_at(u, a.order, t)), bad_page);
       load_k(cur, 0.f);
       load_v(cur);
       ++issued;
     }
-    int parity = 0;
-
-    // two teams: the loop ends for both at once, on the liveness flags (below)
-    for (int t0 = t_begin; (TEAMS == 2 && art_mode) || t0 < t_stop; t0 += W) {
-      const int t = t0 + wid;
-      const bool active = t < t_stop;
-      const int n_act = min(W, t_stop - t0);
+    for (; t < t_stop; t += W) {
       const int tn = t + W;
-      const bool has_next = tn < t_stop;
+      bool has_next = tn < t_stop;
+      if (chain) {  // a stop already found: drop this block, or the next one's loads
+        const int sa = uni(*(volatile int*)&R.stop_at);
+        if (sa > 0 && t >= sa) break;
+        if (sa > 0 && tn >= sa) has_next = false;
+      }
       BlockAddr nxt = cur;
       if (has_next) nxt = block_addr4<ROW, PAGED>(u, uni(block_at(u, a.order, tn)), bad_page);
 
-      float m_new = m_c, alpha = 1.f, lblk = 0.f;
-      f32x4 bacc[NDT];
-      if (active) {
-        const int nvalid = cur.nvalid;
-        // ---- scores S^T[token][head] = k_token . q_head --------------------------
-        wait_v_tied<kLoads>(kr);  // this block's K (its 16 V DMAs were issued after it)
-        f32x4 S[kTiles];
-        static_for<0, kTiles>([&](auto ntc) {
-          constexpr int nt = decltype(ntc)::value;
-          f32x4 s = {0.f, 0.f, 0.f, 0.f};
-          if constexpr (DT == ART_DT_BF16) {
-  #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[4 * nt + j]),
-                                                          __builtin_bit_cast(bf16x8, qv[j]), s, 0, 0, 0);
-          } else {
-  #pragma unroll
-            for (int j = 0; j < 4; ++j)
-  #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                s = __builtin_amdgcn_mfma_f32_16x16x4f32(u2f(kr[4 * nt + j][e]), u2f(qv[j][e]), s, 0, 0, 0);
-          }
-          S[nt] = s;
-        });
-        // ---- online softmax of head c % G against its running max ---------------
-        const int tb = 4 * lg;  // token of register 0 within each tile
-        float mx = -INFINITY;
-  #pragma unroll
-        for (int nt = 0; nt < kTiles; ++nt)
-  #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float sv = (16 * nt + tb + r < nvalid) ? S[nt][r] * c2 : -INFINITY;
-            S[nt][r] = sv;
-            mx = fmaxf(mx, sv);
-          }
-        mx = col_max(mx);
-        m_new = fmaxf(m_c, mx);
-        alpha = __builtin_amdgcn_exp2f(m_c - m_new);
-        float ls = 0.f;
-        // the next block's K, one tile at a time between the tiles'
-        // exponentials: the wave computes while the address unit drains
-        static_for<0, kTiles>([&](auto ntc) {
-          constexpr int nt = decltype(ntc)::value;
-          if (has_next) load_k_tile(nxt, ntc, mx);
-  #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float p = __builtin_amdgcn_exp2f(S[nt][r] - m_new);
-            S[nt][r] = p;
-            ls += p;
-          }
-        });
-        if (has_next) ++issued;
-        lblk = col_sum(ls);
-        // ---- P V on MFMA ---------------------------------------------------------
-  #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) bacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // V of this block: the 16 K loads of the next block (if any) were issued after it
-        if (has_next)
-          wait_vm<kLoads>();
-        else
-          wait_vm<0>();
-        const bool partial = nvalid < kBlk;  // weights of the tail tokens are 0; their V may be garbage
+      const int nvalid = cur.nvalid;
+      // ---- scores S^T[token][head] = k_token . q_head --------------------------
+      wait_v_tied<kLoads>(kr);  // this block's K (its 16 V DMAs were issued after it)
+      f32x4 S[kTiles];
+      static_for<0, kTiles>([&](auto ntc) {
+        constexpr int nt = decltype(ntc)::value;
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
         if constexpr (DT == ART_DT_BF16) {
-          // A operand of tile pair jp: element e < 4 is token 16(2jp) + 4lg + e,
-          // element e >= 4 is token 16(2jp+1) + 4lg + e - 4, split as P = hi + lo
-          u32x4 ph[2], pl[2];
-  #pragma unroll
-          for (int jp = 0; jp < 2; ++jp)
-  #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              const int nt = 2 * jp + hh;
-              const uint32_t w0 = pk_bf16(S[nt][0], S[nt][1]);
-              const uint32_t w1 = pk_bf16(S[nt][2], S[nt][3]);
-              ph[jp][2 * hh] = w0;
-              ph[jp][2 * hh + 1] = w1;
-              pl[jp][2 * hh] = pk_bf16(S[nt][0] - bf16_lo(w0), S[nt][1] - bf16_hi(w0));
-              pl[jp][2 * hh + 1] = pk_bf16(S[nt][2] - bf16_lo(w1), S[nt][3] - bf16_hi(w1));
-            }
-          // B operand of (tile pair jp, dim tile dt): two transposed reads,
-          // tokens of tile 2jp then tile 2jp+1, dims 16dt + c
-          auto read_b = [&](int jp, int dt, bool mask) -> bf16x8 {
-            const auto* pv = vb + tr_lane + (((uint32_t)(32 * dt)) ^ tr_x);
-            s16x4 v0 = lds_read_tr(pv + (2 * jp) * 4096);
-            s16x4 v1 = lds_read_tr(pv + (2 * jp + 1) * 4096);
-            if (mask) {
-  #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                if (32 * jp + tb + e >= nvalid) v0[e] = 0;
-                if (32 * jp + 16 + tb + e >= nvalid) v1[e] = 0;
-              }
-            }
-            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-          };
-          // per tile pair and group of four dim tiles: the reads first, then the
-          // hi MFMAs, then the lo MFMAs (four independent accumulator chains)
-          auto pv_pass = [&](int jp, bool mask) {
-  #pragma unroll
-            for (int d0 = 0; d0 < NDT; d0 += 4) {
-              bf16x8 bv[4];
-  #pragma unroll
-              for (int i = 0; i < 4; ++i) bv[i] = read_b(jp, d0 + i, mask);
-  #pragma unroll
-              for (int i = 0; i < 4; ++i)
-                bacc[d0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ph[jp]), bv[i],
-                                                                       bacc[d0 + i], 0, 0, 0);
-  #pragma unroll
-              for (int i = 0; i < 4; ++i)
-                bacc[d0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pl[jp]), bv[i],
-                                                                       bacc[d0 + i], 0, 0, 0);
-            }
-          };
-          if (!partial) {
-            pv_pass(0, false);
-            pv_pass(1, false);
-          } else {  // the last block of a sequence: zero the tail tokens' values
-            pv_pass(0, true);
-            pv_pass(1, true);
-          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[4 * nt + j]),
+                                                           __builtin_bit_cast(bf16x8, qv[j]), sacc, 0, 0, 0);
         } else {
-          // fp32: k = lg of step (nt, r) is token 16nt + 4lg + r; B element
-          // (token, dim 16dt + c) read directly from the slab
-          const auto* vf = (const __attribute__((address_space(3))) float*)vb;
-  #pragma unroll
-          for (int nt = 0; nt < kTiles; ++nt)
-  #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int tok = 16 * nt + tb + r;
-              const int zsw = (2 * r) ^ (8 * (lg & 1));
-  #pragma unroll
-              for (int dt = 0; dt < NDT; ++dt) {
-                const int pos = (4 * dt + (c >> 2)) ^ zsw;
-                float v = vf[((4 * nt + lg) * 1024 + r * 256 + pos * 16 + 4 * (c & 3)) >> 2];
-                if (tok >= nvalid) v = 0.f;
-                bacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(S[nt][r], v, bacc[dt], 0, 0, 0);
-              }
-            }
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(u2f(kr[4 * nt + j][e]), u2f(qv[j][e]), sacc, 0, 0, 0);
         }
-        if (has_next && !(art_mode && !split)) load_v(nxt);  // in-round ART: after the summary reads below
+        S[nt] = sacc;
+      });
+      // ---- online softmax of head c % G against its running max ---------------
+      const int tb = 4 * lg;  // token of register 0 within each tile
+      float mx = -INFINITY;
+#pragma unroll
+      for (int nt = 0; nt < kTiles; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float sv = (16 * nt + tb + r < nvalid) ? S[nt][r] * c2 : -INFINITY;
+          S[nt][r] = sv;
+          mx = fmaxf(mx, sv);
+        }
+      mx = col_max(mx);
+      const float m_new = fmaxf(m_c, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_c - m_new);
+      float ls = 0.f;
+      // the next block's K, one tile at a time between the tiles'
+      // exponentials: the wave computes while the address unit drains
+      static_for<0, kTiles>([&](auto ntc) {
+        constexpr int nt = decltype(ntc)::value;
+        if (has_next) load_k_tile(nxt, ntc, mx);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(S[nt][r] - m_new);
+          S[nt][r] = p;
+          ls += p;
+        }
+      });
+      if (has_next) ++issued;
+      const float lblk = col_sum(ls);
+      // ---- P V on MFMA ---------------------------------------------------------
+      f32x4 bacc[NDT];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) bacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // V of this block: the 16 K loads of the next block (if any) were issued after it
+      if (has_next)
+        wait_vm<kLoads>();
+      else
+        wait_vm<0>();
+      const bool partial = nvalid < kBlk;  // weights of the tail tokens are 0; their V may be garbage
+      if constexpr (DT == ART_DT_BF16) {
+        // A operand of tile pair jp: element e < 4 is token 16(2jp) + 4lg + e,
+        // element e >= 4 is token 16(2jp+1) + 4lg + e - 4, split as P = hi + lo
+        u32x4 ph[2], pl[2];
+#pragma unroll
+        for (int jp = 0; jp < 2; ++jp)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int nt = 2 * jp + hh;
+            const uint32_t w0 = pk_bf16(S[nt][0], S[nt][1]);
+            const uint32_t w1 = pk_bf16(S[nt][2], S[nt][3]);
+            ph[jp][2 * hh] = w0;
+            ph[jp][2 * hh + 1] = w1;
+            pl[jp][2 * hh] = pk_bf16(S[nt][0] - bf16_lo(w0), S[nt][1] - bf16_hi(w0));
+            pl[jp][2 * hh + 1] = pk_bf16(S[nt][2] - bf16_lo(w1), S[nt][3] - bf16_hi(w1));
+          }
+        // B operand of (tile pair jp, dim tile dt): two transposed reads,
+        // tokens of tile 2jp then tile 2jp+1, dims 16dt + c
+        auto read_b = [&](int jp, int dt, bool mask) -> bf16x8 {
+          const auto* pv = vb + tr_lane + (((uint32_t)(32 * dt)) ^ tr_x);
+          s16x4 v0 = lds_read_tr(pv + (2 * jp) * 4096);
+          s16x4 v1 = lds_read_tr(pv + (2 * jp + 1) * 4096);
+          if (mask) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (32 * jp + tb + e >= nvalid) v0[e] = 0;
+              if (32 * jp + 16 + tb + e >= nvalid) v1[e] = 0;
+            }
+          }
+          return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        // per tile pair and group of four dim tiles: the reads first, then the
+        // hi MFMAs, then the lo MFMAs (four independent accumulator chains)
+        auto pv_pass = [&](int jp, bool mask) {
+#pragma unroll
+          for (int d0 = 0; d0 < NDT; d0 += 4) {
+            bf16x8 bv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bv[i] = read_b(jp, d0 + i, mask);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              bacc[d0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ph[jp]), bv[i],
+                                                                     bacc[d0 + i], 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              bacc[d0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pl[jp]), bv[i],
+                                                                     bacc[d0 + i], 0, 0, 0);
+          }
+        };
+        if (!partial) {
+          pv_pass(0, false);
+          pv_pass(1, false);
+        } else {  // the last block of a sequence: zero the tail tokens' values
+          pv_pass(0, true);
+          pv_pass(1, true);
+        }
+      } else {
+        // fp32: k = lg of step (nt, r) is token 16nt + 4lg + r; B element
+        // (token, dim 16dt + c) read directly from the slab
+        const auto* vf = (const __attribute__((address_space(3))) float*)vb;
+#pragma unroll
+        for (int nt = 0; nt < kTiles; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int tok = 16 * nt + tb + r;
+            const int zsw = (2 * r) ^ (8 * (lg & 1));
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+              const int pos = (4 * dt + (c >> 2)) ^ zsw;
+              float v = vf[((4 * nt + lg) * 1024 + r * 256 + pos * 16 + 4 * (c & 3)) >> 2];
+              if (tok >= nvalid) v = 0.f;
+              bacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(S[nt][r], v, bacc[dt], 0, 0, 0);
+            }
+          }
       }
 
-      int stop_round = -1;  // this round's stop, as a traversal count
-      if (split && pass == 0 && active) {
+      if (split && pass == 0) {
         // split ART: the block summary goes to the workspace for the replay
         Summary<D>* gs = reinterpret_cast<Summary<D>*>(a.summaries) + ((size_t)unit * a.max_trav + t);
         if (lane < 16 && (c & 3) == 0) {
-  #pragma unroll
+#pragma unroll
           for (int dt = 0; dt < NDT; ++dt) *(f32x4*)&gs->ps[4 * dt + (c >> 2)][0] = bacc[dt];
         }
         if (lane < G) {
@@ -1296,262 +1335,165 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
           gs->l[lane] = lblk;
         }
       }
-      if (art_mode && !split) {
+      // V of the next block: after this block's LDS reads (load_v waits for
+      // them); in ART mode also after the block summary's round trip
+      // through the slab (below)
+      if (has_next && !chain) load_v(nxt);
+
+      bool commit = true, last = false;
+      if (chain) {
+        // ---- the block's summary, read back in the stop rule's layout --------
+        // It goes through the wave's own V slab, free between this block's
+        // P V reads and the next block's V loads.  Probe dim 4p of query
+        // vector r (G <= 4: rows r % G) is register r of lane c = 4 (p % 4),
+        // tile p / 4, in the O layout's row 0 (more than 4 query vectors:
+        // rows 4 lg .. 4 lg + 3 are vectors of their own).
+        wait_lgkm0();  // this block's transposed V reads have landed
+        auto& sw = *reinterpret_cast<Summary<D, (G > 4 ? G : 4)>*>(&vbuf[wid][0]);
         if constexpr (G <= 4) {
-        // ---- publish the block summary ------------------------------------------
-        // probe dims 4p: lanes c = 0, 4, 8, 12 of row 0 hold dims 16dt + c for
-        // heads r % G in register r
-        Summary<D>& sw = R.sum[parity][wid];
-        if (active) {
           if (lane < 16 && (c & 3) == 0) {
-  #pragma unroll
+#pragma unroll
             for (int dt = 0; dt < NDT; ++dt) *(f32x4*)&sw.ps[4 * dt + (c >> 2)][0] = bacc[dt];
           }
-          if (lane < G) {
-            sw.m[lane] = m_new;
-            sw.l[lane] = lblk;
-          }
-        }
-        lds_barrier();
-        bool team_live = true;
-        if constexpr (TEAMS == 2) {
-          // liveness of both teams after the previous round (written before
-          // its end, read here after a barrier): when neither has positions
-          // left, this round is empty for both and the walk ends
-          if (!uni(R_all[0].live | R_all[1].live)) break;
-          team_live = uni(R.live) != 0;
-        }
-        // ---- the round's positions, in order ------------------------------------
-        // Every wave merges the round's block summaries, in traversal order,
-        // onto the carried prefix state on the probe dims (lane (lg, c): head
-        // lg if lg < G, probe dims of chunk c); all waves keep the same state.
-        // All terms are first put on the round's common maximum M, so the scale
-        // factors are independent of one another.  With P^(t) the prefix
-        // numerators and l^(t) the prefix mass of a head, x^(t) = P^(t) / l^(t)
-        // (the ratio is scale free).  A wave keeps the per-lane parts of
-        // |P|^2 at its own position and the one before, and of P^(t).P^(t-1)
-        // at its own, then forms |x^(t)|^2, |x^(t-1)|^2 and x^(t).x^(t-1)
-        // (per-head row sums, divided by that head's mass, summed over heads)
-        // and runs the two tests for its own position only.
-        if (team_live) {
-        float mk[kMaxWaves];
-        double lk[kMaxWaves], pk[kMaxWaves][PPC];
-        float M = mP;
-  #pragma unroll
-        for (int k = 0; k < kMaxWaves; ++k) {
-          const Summary<D>& s2 = R.sum[parity][k];
-          const bool on = k < n_act;  // slots past the round's end hold stale data
-          mk[k] = on ? s2.m[hg] : -INFINITY;
-          lk[k] = on ? (double)s2.l[hg] : 0.0;
-  #pragma unroll
-          for (int i = 0; i < PPC; ++i) pk[k][i] = on ? (double)s2.ps[c * PPC + i][hg] : 0.0;
-          M = fmaxf(M, mk[k]);
-        }
-        // this wave's next V goes out only now (DMAs landing in LDS would slow
-        // the summary reads above), one 16-token group before each merge
-        // step: the wave merges while the address unit drains
-        static_assert(kMaxWaves == kTiles, "one V group per merge step");
-        wait_lgkm0();
-        const double sP = (double)__builtin_amdgcn_exp2f(mP - M);
-        double L = lP * sP, P[PPC];
-  #pragma unroll
-        for (int i = 0; i < PPC; ++i) P[i] = pP[i] * sP;
-        double a_own = 0.0, c_own = 0.0, a_prev = 0.0, L_own = 1.0, L_prev = 0.0;
-        static_for<0, kMaxWaves>([&](auto kc) {
-          constexpr int k = decltype(kc)::value;
-          if (has_next) load_v_group(nxt, kc);
-          const double sk = (double)__builtin_amdgcn_exp2f(mk[k] - M);  // 0 past the round's end
-          double pa = 0.0, pc = 0.0;
-  #pragma unroll
-          for (int i = 0; i < PPC; ++i) {
-            const double pn = fma(pk[k][i], sk, P[i]);
-            pa = fma(pn, pn, pa);
-            pc = fma(pn, P[i], pc);
-            P[i] = pn;
-          }
-          const double Ln = fma(lk[k], sk, L);
-          const bool own = k == wid, before = k + 1 == wid;
-          a_own = own ? pa : a_own;
-          c_own = own ? pc : c_own;
-          L_prev = own ? L : L_prev;
-          L_own = own ? Ln : L_own;
-          a_prev = before ? pa : a_prev;
-          L = Ln;
-        });
-        compiler_fence();
-        mP = M;
-        lP = L;
-  #pragma unroll
-        for (int i = 0; i < PPC; ++i) pP[i] = P[i];
-        if (active) {
-          const double keep = lg < G ? 1.0 : 0.0;  // rows past G carry head 0 again
-          const double io = recip_d(L_own);
-          const double ip = L_prev > 0.0 ? recip_d(L_prev) : 0.0;
-          const double stt = col_sum_d(row_sum_d(a_own) * (io * io * keep));
-          const double stp = col_sum_d(row_sum_d(c_own) * (io * ip * keep));
-          const double spr = wid == 0 ? stt_last : col_sum_d(row_sum_d(a_prev) * (ip * ip * keep));
-          const bool stable =
-              (spr > 0.0) & (stt > 0.0) & crit.scale_ok(spr, stt) & crit.dir_ok(spr, stt, stp);
-          if (lane == 0) {
-            R.chk[parity][wid].stt = stt;
-            R.chk[parity][wid].stable = stable;
-          }
-        }
-        }  // team_live
-        lds_barrier();
-        // ---- patience counter over the round's checks, in traversal order ---------
-        if (team_live) {
-        int sbits = 0;  // bit w2: the check at position t0 + w2 passed
-  #pragma unroll
-        for (int w2 = 0; w2 < kMaxWaves; ++w2) {
-          const Check ck = R.chk[parity][w2];
-          sbits |= (ck.stable & 1) << w2;
-          if (w2 + 1 == n_act) stt_last = ck.stt;
-        }
-        sbits = uni(sbits);
-        // a check exists from the second traversal block on
-  #pragma unroll
-        for (int w2 = 0; w2 < kMaxWaves; ++w2) {
-          const int cnt = t0 + w2 + 1;
-          if (w2 < n_act && cnt >= 2 && stop_round < 0) {
-            counter = ((sbits >> w2) & 1) ? counter + 1 : 0;
-            if (counter >= a.patience) stop_round = cnt;
-          }
-        }
-        stop_round = uni(stop_round);
-        }  // team_live
-        parity ^= 1;
-        if (detect_only) {  // keep the first stop, terminate nothing
-          if (detected < 0) detected = stop_round;
-          stop_round = -1;
-        }
-        if constexpr (TEAMS == 2) {  // read by both teams after the next round's first barrier
-          if (tid == 0) R.live = (team_live && stop_round < 0 && t0 + W < t_stop) ? 1 : 0;
-        }
-              } else {
-        // ---- more than 4 query vectors (multi-row queries) ------------------------
-        // publish: probe dim 4p of query vector 4 lg + r is register r of
-        // lane (lg, 4 (p % 4)), tile p / 4 (rows 4 lg .. 4 lg + 3 of the O layout)
-        auto& sw = R.sum[0][wid];
-        if (active) {
+        } else {
           if ((c & 3) == 0 && lg < G / 4) {
-  #pragma unroll
+#pragma unroll
             for (int dt = 0; dt < NDT; ++dt) *(f32x4*)&sw.ps[4 * dt + (c >> 2)][4 * lg] = bacc[dt];
           }
-          if (lane < G) {
-            sw.m[lane] = m_new;
-            sw.l[lane] = lblk;
+        }
+        if (lane < G) {
+          sw.m[lane] = m_new;
+          sw.l[lane] = lblk;
+        }
+        // this wave's own writes, read back by this wave (LDS keeps a wave's order)
+        float mt[NH];
+        double lt[NH], ps[NPL];
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh) {
+          const int g = G <= 4 ? (lg < G ? lg : 0) : lg + 4 * hh;
+          mt[hh] = sw.m[g];
+          lt[hh] = (double)sw.l[g];
+#pragma unroll
+          for (int i = 0; i < PPC; ++i) ps[hh * PPC + i] = (double)sw.ps[c * PPC + i][g];
+        }
+        if (has_next) load_v(nxt);  // waits for the summary reads above
+        // ---- the prefix state after position t - 1 ------------------------------
+        float Mp[NH];
+        double Lp[NH], P[NPL];
+        double spr = 0.0;
+        int counter = 0, det = 0;
+        bool go = true;
+        if (t > t_begin) {
+          go = chain_wait(t);
+          if (go) {
+            const LaneLink<NPL, NH>& lk = R.link[(t - 1) & 1][lane];
+#pragma unroll
+            for (int i = 0; i < NPL; ++i) P[i] = lk.p[i];
+#pragma unroll
+            for (int hh = 0; hh < NH; ++hh) {
+              Lp[hh] = lk.l[hh];
+              Mp[hh] = lk.m[hh];
+            }
+            const LinkHead& hd = R.head[(t - 1) & 1];
+            spr = hd.stt;
+            counter = hd.counter;
+            det = hd.detected;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < NPL; ++i) P[i] = 0.0;
+#pragma unroll
+          for (int hh = 0; hh < NH; ++hh) {
+            Lp[hh] = 0.0;
+            Mp[hh] = -INFINITY;
           }
         }
-        lds_barrier();
-        // The round's positions in order, as in the path above, but each lane
-        // carries one query vector's prefix state on its share of the probe
-        // dims, and the summaries are merged one at a time (register budget).
-        float mk[kMaxWaves];
-        float M = mPq;
-  #pragma unroll
-        for (int k = 0; k < kMaxWaves; ++k) {
-          mk[k] = k < n_act ? R.sum[0][k].m[hq] : -INFINITY;  // slots past the round's end hold stale data
-          M = fmaxf(M, mk[k]);
-        }
-        const double sP = (double)__builtin_amdgcn_exp2f(mPq - M);
-        double L = lPq * sP, P[PPCQ];
-  #pragma unroll
-        for (int i = 0; i < PPCQ; ++i) P[i] = pPq[i] * sP;
-        double a_own = 0.0, c_own = 0.0, a_prev = 0.0, L_own = 1.0, L_prev = 0.0;
-        // not unrolled: one summary's values live at a time (register budget)
-  #pragma unroll 1
-        for (int k = 0; k < kMaxWaves; ++k) {
-          const bool on = k < n_act;
-          const float mkk = on ? R.sum[0][k].m[hq] : -INFINITY;
-          const double sk = (double)__builtin_amdgcn_exp2f(mkk - M);  // 0 past the round's end
-          const double lk = on ? (double)R.sum[0][k].l[hq] : 0.0;
-          double pa = 0.0, pc = 0.0;
-  #pragma unroll
-          for (int i = 0; i < PPCQ; ++i) {
-            const double pv = on ? (double)R.sum[0][k].ps[cq * PPCQ + i][hq] : 0.0;
-            const double pn = fma(pv, sk, P[i]);
-            pa = fma(pn, pn, pa);
-            pc = fma(pn, P[i], pc);
-            P[i] = pn;
+        if (!go) {  // the unit stopped before this position: the block does not count
+          commit = false;
+          last = true;
+        } else {
+          // ---- merge, |x^(t)|^2 and x^(t).x^(t-1) -------------------------------
+          // x = P / L per query vector (scale free): both on the common maximum
+          double sa = 0.0, sc = 0.0;
+          float Mn[NH];
+          double Ln[NH], Pn[NPL];
+#pragma unroll
+          for (int hh = 0; hh < NH; ++hh) {
+            Mn[hh] = fmaxf(Mp[hh], mt[hh]);
+            const double fa = (double)__builtin_amdgcn_exp2f(Mp[hh] - Mn[hh]);  // 0 before the first block
+            const double fb = (double)__builtin_amdgcn_exp2f(mt[hh] - Mn[hh]);
+            Ln[hh] = fma(Lp[hh], fa, lt[hh] * fb);
+            double pa = 0.0, pc = 0.0;
+#pragma unroll
+            for (int i = 0; i < PPC; ++i) {
+              const double pn = fma(P[hh * PPC + i], fa, ps[hh * PPC + i] * fb);
+              pa = fma(pn, pn, pa);
+              pc = fma(pn, P[hh * PPC + i], pc);
+              Pn[hh * PPC + i] = pn;
+            }
+            const double in = recip_d(Ln[hh]);
+            const double ip = Lp[hh] > 0.0 ? recip_d(Lp[hh]) : 0.0;
+            sa = fma(pa, in * in, sa);
+            sc = fma(pc, in * ip, sc);
           }
-          const double Ln = fma(lk, sk, L);
-          const bool own = k == wid, before = k + 1 == wid;
-          a_own = own ? pa : a_own;
-          c_own = own ? pc : c_own;
-          L_prev = own ? L : L_prev;
-          L_own = own ? Ln : L_own;
-          a_prev = before ? pa : a_prev;
-          L = Ln;
-        }
-        mPq = M;
-        lPq = L;
-  #pragma unroll
-        for (int i = 0; i < PPCQ; ++i) pPq[i] = P[i];
-        if (has_next) load_v(nxt);  // after the summary reads (it waits for them)
-        if (active) {
-          // each lane scales its own query vector's part; the sums run over all lanes
-          const double io = recip_d(L_own);
-          const double ip = L_prev > 0.0 ? recip_d(L_prev) : 0.0;
-          const double stt = col_sum_d(row_sum_d(a_own * (io * io)));
-          const double stp = col_sum_d(row_sum_d(c_own * (io * ip)));
-          const double spr = wid == 0 ? stt_last : col_sum_d(row_sum_d(a_prev * (ip * ip)));
+          const double keep = (G >= 4 || lg < G) ? 1.0 : 0.0;  // rows past G repeat query vector 0
+          const double stt = col_sum_d(row_sum_d(sa * keep));
+          const double stp = col_sum_d(row_sum_d(sc * keep));
+          // a check exists from the second traversal block on
+          const bool exists = t >= 1;
           const bool stable =
-              (spr > 0.0) & (stt > 0.0) & crit.scale_ok(spr, stt) & crit.dir_ok(spr, stt, stp);
+              exists & (spr > 0.0) & (stt > 0.0) & crit.scale_ok(spr, stt) & crit.dir_ok(spr, stt, stp);
+          counter = exists ? (stable ? counter + 1 : 0) : 0;
+          int st = (exists && counter >= a.patience) ? t + 1 : 0;
+          if (detect_only) {  // keep the first stop, terminate nothing
+            if (st > 0 && det == 0) det = st;
+            st = 0;
+          }
+          st = uni(st);
+          // ---- publish the state after position t ---------------------------------
+          LaneLink<NPL, NH>& lo = R.link[t & 1][lane];
+#pragma unroll
+          for (int i = 0; i < NPL; ++i) lo.p[i] = Pn[i];
+#pragma unroll
+          for (int hh = 0; hh < NH; ++hh) {
+            lo.l[hh] = Ln[hh];
+            lo.m[hh] = Mn[hh];
+          }
           if (lane == 0) {
-            R.chk[parity][wid].stt = stt;
-            R.chk[parity][wid].stable = stable;
+            LinkHead& ho = R.head[t & 1];
+            ho.stt = stt;
+            ho.counter = counter;
+            ho.detected = det;
+            if (st > 0) R.stop_at = st;
+            if (detect_only && det > 0 && det == t + 1) R.detected = det;
           }
-        }
-        lds_barrier();
-        // ---- patience counter over the round's checks, in traversal order ---------
-        int sbits = 0;
-  #pragma unroll
-        for (int w2 = 0; w2 < kMaxWaves; ++w2) {
-          const Check ck = R.chk[parity][w2];
-          sbits |= (ck.stable & 1) << w2;
-          if (w2 + 1 == n_act) stt_last = ck.stt;
-        }
-        sbits = uni(sbits);
-  #pragma unroll
-        for (int w2 = 0; w2 < kMaxWaves; ++w2) {
-          const int cnt = t0 + w2 + 1;
-          if (w2 < n_act && cnt >= 2 && stop_round < 0) {
-            counter = ((sbits >> w2) & 1) ? counter + 1 : 0;
-            if (counter >= a.patience) stop_round = cnt;
+          wait_lgkm0();  // the record is in LDS before its sequence number
+          if (lane == 0) *(volatile int*)&R.head[t & 1].seq = t + 1;
+          if (st > 0) {
+            stop = st;
+            last = true;
           }
-        }
-        stop_round = uni(stop_round);
-        parity ^= 1;
-        if (detect_only) {
-          if (detected < 0) detected = stop_round;
-          stop_round = -1;
-        }
         }
       }
-      // ---- commit this wave's block (unless it lies after the stop) -------------
-      if (active && (stop_round < 0 || t + 1 <= stop_round)) {
+      // ---- commit this wave's block ----------------------------------------------
+      if (commit) {
         // row r of the O layout holds head r % G, whose column values sit in lane r % G
         float al[4];
-  #pragma unroll
+#pragma unroll
         for (int r = 0; r < 4; ++r) {
           if constexpr (G <= 4)
             al[r] = lane_f(alpha, r % G);
           else  // row 4 lg + r is query vector (4 lg + r) % G
             al[r] = __shfl(alpha, (4 * lg + r) % G);
         }
-  #pragma unroll
+#pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
-  #pragma unroll
+#pragma unroll
           for (int r = 0; r < 4; ++r) acc[dt][r] = fmaf(acc[dt][r], al[r], bacc[dt][r]);
         m_c = m_new;
         l_c = fmaf(l_c, alpha, lblk);
       }
-      if (stop_round >= 0) {
-        stop = stop_round;
-        if constexpr (TEAMS == 1) break;
-        t_stop = stop_round;  // two teams: idle until the other team is done
-      }
+      if (last) break;
       cur = nxt;
     }
     if (!split || pass == 1) break;
@@ -1562,11 +1504,16 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
     t_stop = t_begin + stop_local;  // recompute the blocks up to the stop
     stashed = false;
   }
-  if (stop < 0) stop = detected >= 0 ? detected : t_end;
   if (!stashed) stash_waves();
+  if (chain) {  // every wave has left the walk (stash_waves ends on a barrier)
+    const int sa = uni(R.stop_at), dd = uni(R.detected);
+    stop = sa > 0 ? sa : (dd > 0 ? dd : t_end);
+    if (R.timeout) dev_status = ART_ERR_TIMEOUT;
+  }
+  if (stop < 0) stop = t_end;
 
   // ---- epilogue: merge the stashed waves, normalize -----------------------------
-  for (int o = tid; o < G * D && !idle; o += kWave * kMaxWaves) {
+  for (int o = tid; o < G * D; o += NT) {
     const int g = o / D, dim = o % D;
     float M = -INFINITY;
     for (int w2 = 0; w2 < W; ++w2)
@@ -1590,7 +1537,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves * TEAMS, 2 / TEAMS) void art_deco
       }
     }
   }
-  if (tid == 0 && !idle) {
+  if (tid == 0) {
     int tot = 0, bad = 0;
     for (int w2 = 0; w2 < W; ++w2) {
       tot += E.issued[w2];
@@ -1707,19 +1654,19 @@ __global__ __launch_bounds__(kWave * 16) void art_combine_kernel(KernelArgs a) {
 // ---------------------------------------------------------------------------
 template <int DT, int G, bool PAGED>
 static hipError_t launch_t(const KernelArgs& a, int grid, int waves, hipStream_t s) {
-  (void)waves;
   if constexpr (G <= 4) {
     if (a.split_art) {
-      hipLaunchKernelGGL((art_decode_kernel<DT, G, PAGED, true, 1>), dim3(grid), dim3(kWave * kMaxWaves), 0, s, a);
-    } else if (a.pair) {  // one work item per unit, two per workgroup
-      hipLaunchKernelGGL((art_decode_kernel<DT, G, PAGED, false, 2>), dim3((grid + 1) / 2),
-                         dim3(2 * kWave * kMaxWaves), 0, s, a);
+      if (waves != 4) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((art_decode_kernel<DT, G, PAGED, true, 4>), dim3(grid), dim3(kWave * 4), 0, s, a);
+    } else if (waves == 8) {
+      if (a.max_chunks != 1 || a.mode != ART_MODE_ART) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((art_decode_kernel<DT, G, PAGED, false, 8>), dim3(grid), dim3(kWave * 8), 0, s, a);
     } else {
-      hipLaunchKernelGGL((art_decode_kernel<DT, G, PAGED, false, 1>), dim3(grid), dim3(kWave * kMaxWaves), 0, s, a);
+      hipLaunchKernelGGL((art_decode_kernel<DT, G, PAGED, false, 4>), dim3(grid), dim3(kWave * 4), 0, s, a);
     }
-  } else {  // more than 4 query vectors per unit: neither split ART nor pairing
-    if (a.split_art || a.pair) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((art_decode_kernel<DT, G, PAGED, false, 1>), dim3(grid), dim3(kWave * kMaxWaves), 0, s, a);
+  } else {  // more than 4 query vectors per unit: no split ART, 4 waves
+    if (a.split_art || waves != 4) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((art_decode_kernel<DT, G, PAGED, false, 4>), dim3(grid), dim3(kWave * 4), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1751,7 +1698,6 @@ __global__ void art_split_init_kernel(KernelArgs a) {
 
 hipError_t launch(const KernelArgs& a, hipStream_t s) {
   const int n_units = a.batch * a.hkv;
-  if (a.pair && (a.max_chunks != 1 || a.mode != ART_MODE_ART || a.split_art)) return hipErrorInvalidValue;
   if (a.split_art) {
     const int n = n_units * a.max_chunks;
     if (a.dtype == ART_DT_BF16)
@@ -1762,7 +1708,8 @@ hipError_t launch(const KernelArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const int grid = n_units * a.max_chunks;
-  const int waves = a.waves < 1 ? 1 : (a.waves > kMaxWaves ? kMaxWaves : a.waves);
+  const int waves = a.waves;
+  if (waves != 4 && waves != 8) return hipErrorInvalidValue;
   const int G = a.rows * a.gh;  // query vectors per unit
   if (a.dtype == ART_DT_BF16) {
     switch (G) {

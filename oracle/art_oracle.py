@@ -110,11 +110,20 @@ def traversal(num_blocks: int, kept: Optional[Sequence[int]] = None,
               order: int = ORDER_RECENT_FIRST) -> list:
     """Block indices in the order they are processed.
 
-    Candidates are ``kept`` (a kept-block list from a key-based KV manager)
-    or every block 0..num_blocks-1.  Block 0, when a candidate, is first.
+    Candidates are ``kept`` (a kept-block list from a key-based KV manager;
+    distinct blocks of the sequence, else ValueError) or every block
+    0..num_blocks-1.  Block 0, when a candidate, is first.
     NATURAL: ascending.  RECENT_FIRST: descending.  GIVEN: the list order.
     """
     cand = list(range(num_blocks)) if kept is None else [int(c) for c in kept]
+    if kept is not None:
+        # the candidates are a set of the sequence's blocks (the blocks a KV
+        # manager retains, [GIST-2.4]); a list naming a block twice or one
+        # outside the sequence is not such a set and is refused
+        if len(set(cand)) != len(cand):
+            raise ValueError("kept list names a block more than once")
+        if any(c < 0 or c >= num_blocks for c in cand):
+            raise ValueError("kept list names a block outside the sequence")
     head = [0] if 0 in cand else []
     rest = [c for c in cand if c != 0]
     if order == ORDER_NATURAL:

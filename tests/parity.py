@@ -32,7 +32,7 @@ def log(*a):
 
 
 def run_gpu(w, mode=1, patience=None, eps_scale=None, eps_dir=None, order=None, split_blocks=0, dev=None,
-            decoder=None, flags=0, pairing=0, q=None):
+            decoder=None, flags=0, waves=0, q=None):
     """Upload (unless ``dev`` is given) and run art_decode; returns numpy arrays."""
     import torch
     from kv_cache_early_amd import ArtDecoder
@@ -45,7 +45,7 @@ def run_gpu(w, mode=1, patience=None, eps_scale=None, eps_dir=None, order=None, 
                    eps_dir=s.eps_dir if eps_dir is None else eps_dir,
                    patience=s.patience if patience is None else patience,
                    order=s.order if order is None else order, mode=mode, split_blocks=split_blocks, flags=flags,
-                   pairing=pairing)
+                   waves=waves)
     torch.cuda.synchronize()
     err = dec.device_error()
     return (r.out.cpu().numpy().astype(np.float64), r.stop_idx.cpu().numpy().astype(np.int64),
@@ -112,7 +112,9 @@ def compare(w, out_gpu, stop_gpu, units=None, mode=1, patience=None, eps_scale=N
                 rep.excused += 1
             else:
                 rep.unexcused.append(((b, h), sg, so, float(m)))
-        if not (0 <= sg <= r.num_traversal):
+        # a unit with blocks processes at least one; an empty unit none
+        lo = 1 if r.num_traversal > 0 else 0
+        if not (lo <= sg <= r.num_traversal):
             rep.bad_outputs.append(((b, h), "stop out of range", sg))
             continue
         t_out = r.num_traversal if detect_only else sg

@@ -46,7 +46,7 @@ def good_shape(**kw):
 
 def good_params(**kw):
     d = dict(eps_scale=1e-3, eps_dir=1e-4, patience=2, order=art.ART_ORDER_RECENT_FIRST, mode=art.ART_MODE_ART,
-             block_size=64, split_blocks=0, flags=0, pairing=0)
+             block_size=64, split_blocks=0, flags=0, waves=0)
     d.update(kw)
     return art.make_params(**d)
 
@@ -84,7 +84,13 @@ CASES = [
     ("given without kept list", dict(params=good_params(order=art.ART_ORDER_GIVEN)), art.ART_ERR_INVALID_ARG),
     ("negative split", dict(params=good_params(split_blocks=-1)), art.ART_ERR_INVALID_ARG),
     ("unknown flag", dict(params=good_params(flags=8)), art.ART_ERR_INVALID_ARG),
-    ("bad pairing", dict(params=good_params(pairing=3)), art.ART_ERR_INVALID_ARG),
+    ("bad waves", dict(params=good_params(waves=3)), art.ART_ERR_INVALID_ARG),
+    ("8 waves in full mode", dict(params=good_params(waves=8, mode=art.ART_MODE_FULL)), art.ART_ERR_UNSUPPORTED),
+    ("8 waves with 8 query vectors", dict(shape=good_shape(q_rows=2), params=good_params(waves=8)),
+     art.ART_ERR_UNSUPPORTED),
+    ("given order past the repeat check's capacity",
+     dict(shape=good_shape(max_pages=(524288 * 64) // 16 + 16, max_kept=8), kept=FAKE, kc=FAKE,
+          params=good_params(order=art.ART_ORDER_GIVEN)), art.ART_ERR_UNSUPPORTED),
     ("flags in full mode", dict(params=good_params(mode=art.ART_MODE_FULL, flags=art.ART_FLAG_DETECT_ONLY)),
      art.ART_ERR_INVALID_ARG),
     ("kept without count", dict(shape=good_shape(max_kept=8), kept=FAKE), art.ART_ERR_INVALID_ARG),
@@ -108,6 +114,26 @@ def test_host_rejects(name, kw, expect):
     shape = kw.pop("shape", good_shape())
     params = kw.pop("params", good_params())
     assert call(shape, params, **kw) == expect
+
+
+def test_struct_size_mismatch_is_rejected():
+    """A caller built against another layout of the structs is refused, not misread."""
+    sh, pa = good_shape(), good_params()
+    sh.struct_size -= 4
+    assert call(sh, pa) == art.ART_ERR_INVALID_ARG
+    sh, pa = good_shape(), good_params()
+    pa.struct_size = 0
+    assert call(sh, pa) == art.ART_ERR_INVALID_ARG
+    sh = good_shape()
+    sh.struct_size += 4
+    assert art.load().art_workspace_size(ctypes.byref(sh), ctypes.byref(good_params())) == 0
+    assert art.load().art_select_workspace_size(ctypes.byref(sh)) == 0
+
+
+def test_abi_version():
+    assert art.load().art_abi_version() == art.ART_ABI_VERSION == 2
+    text = open(HEADER).read()
+    assert re.search(r"#define ART_ABI_VERSION 2\b", text)
 
 
 def test_empty_batch_is_a_no_op():

@@ -52,16 +52,77 @@ def test_clobber_and_load_reuse():
     assert [h[0] for h in scan_function(body)] == [2]
 
 
-def test_jump_target_starts_clean():
+def test_hazard_reached_only_through_a_branch():
+    """The load is outstanding only on the path that jumps over the wait."""
+    body = _fn([
+        "global_load_dwordx4 v[4:7], v1, s[2:3]",
+        "s_cbranch_scc1 .LBB0_2",
+        "s_waitcnt vmcnt(0)",
+        ".LBB0_2:",
+        "v_mov_b32_e32 v8, v5",          # reached with the load in flight via the branch
+        "s_endpgm",
+    ])
+    assert [h[0] for h in scan_function(body)] == [3]
+
+
+def test_hazard_reached_only_through_a_back_edge():
+    """A load issued at the bottom of a loop for the next iteration, and a
+    copy at the loop head before its wait: in layout order the head comes
+    first, so only the back-edge carries the load there."""
+    body = _fn([
+        "s_mov_b32 s0, 0",
+        ".LBB0_1:",
+        "v_mov_b32_e32 v8, v4",          # loop head: v4 may still be loading
+        "s_waitcnt vmcnt(0)",
+        "v_add_f32_e32 v9, v4, v5",
+        "global_load_dwordx4 v[4:7], v1, s[2:3]",
+        "s_add_i32 s0, s0, 1",
+        "s_cmp_lg_u32 s0, 8",
+        "s_cbranch_scc1 .LBB0_1",
+        "s_waitcnt vmcnt(0)",
+        "s_endpgm",
+    ])
+    assert [h[0] for h in scan_function(body)] == [1]
+
+
+def test_jump_over_the_only_use_is_clean():
     body = _fn([
         "global_load_dwordx4 v[4:7], v1, s[2:3]",
         "s_branch .LBB0_2",
         ".LBB0_1:",
-        "v_mov_b32_e32 v4, 0",          # reached by a jump only
+        "v_mov_b32_e32 v4, 0",          # no path reaches it
         ".LBB0_2:",
         "s_waitcnt vmcnt(0)",
+        "v_mov_b32_e32 v8, v4",
+        "s_endpgm",
     ])
     assert scan_function(body) == []
+
+
+def test_flag_steered_paths_are_kept_apart():
+    """The compiler's flag pattern: one path loads and sets s[4:5] = 0, the
+    other sets it to -1; the join branches on it, so the block that writes
+    v18 is reached only from the path without the load."""
+    body = _fn([
+        "s_cbranch_scc0 .LBB0_2",
+        "global_load_dwordx4 v[18:21], v[30:31], off",
+        "s_mov_b64 s[4:5], 0",
+        "s_branch .LBB0_3",
+        ".LBB0_2:",
+        "s_mov_b64 s[4:5], -1",
+        ".LBB0_3:",
+        "s_andn2_b64 vcc, exec, s[4:5]",
+        "s_cbranch_vccnz .LBB0_4",
+        "v_mov_b32_e32 v18, 0",          # only the s[4:5] = -1 path gets here
+        ".LBB0_4:",
+        "s_waitcnt vmcnt(0)",
+        "s_endpgm",
+    ])
+    assert scan_function(body) == []
+    # the same shape with the flag overwritten before the branch is flagged
+    body2 = body.replace("s_andn2_b64 vcc, exec, s[4:5]", "s_and_b64 s[4:5], s[4:5], s[6:7]\n"
+                         "s_andn2_b64 vcc, exec, s[4:5]")
+    assert [h[1] for h in scan_function(body2)] == ["v_mov_b32_e32 v18, 0"]
 
 
 def test_kernel_bodies_split():

@@ -54,9 +54,9 @@ def test_scaled_configs(torch_cuda, n, reading, mode):
 @pytest.mark.parametrize("reading", ["A", "B"])
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
 def test_scaled_configs_one_item_per_unit(torch_cuda, n, reading):
-    """ART mode with one work item per unit (in-round stopping)."""
+    """ART mode with one work item per unit (the stop rule's chain over 4 waves)."""
     w = make_workload(scaled(n, reading))
-    _, stop, issued, _ = check(w, tag=f"scaled cfg{n} one item per unit", split_blocks=10 ** 6)
+    _, stop, issued, _ = check(w, tag=f"scaled cfg{n} one item per unit", split_blocks=10 ** 6, waves=4)
     assert np.all(issued <= np.minimum(w.traversal_lengths(), stop + 7))
 
 
@@ -65,11 +65,12 @@ def test_forced_stop_after_p_plus_one(torch_cuda, p):
     """eps huge: every check is stable, so the stop is at min(T', p+1)."""
     w = make_workload(scaled(3, "B"))
     # one work item per unit (in-round stopping; split ART is tested below)
-    _, stop, issued, _ = check(w, tag="huge eps", eps_scale=1e30, eps_dir=1e30, patience=p, split_blocks=10 ** 6)
+    _, stop, issued, _ = check(w, tag="huge eps", eps_scale=1e30, eps_dir=1e30, patience=p, split_blocks=10 ** 6,
+                               waves=4)
     Tp = w.traversal_lengths()
     np.testing.assert_array_equal(stop, np.minimum(Tp, p + 1))
-    # loads stop: the round holding the stop and the prefetch of the next round
-    # (W = 4 waves per unit) are the most that can be issued past it
+    # loads stop: the W positions in flight and their prefetches (W = 4
+    # waves per unit) are the most that can be issued past it
     W = 4
     assert np.all(issued <= np.minimum(Tp, stop + 2 * W - 1))
 
@@ -340,73 +341,71 @@ def test_detect_only_never_fires(torch_cuda):
 
 
 # ---------------------------------------------------------------------------
-# two units per workgroup (lockstep teams) against one unit per workgroup
+# the stop rule's chain: 4 or 8 waves per unit, stops at every position
 # ---------------------------------------------------------------------------
-def _pair_case(case):
-    s3 = scaled(3, "B")
-    kw = {}
-    if case == "scaled":
-        w = make_workload(s3)
-    elif case == "odd units":  # 3 units: the second workgroup's second team has none
-        w = make_workload(replace(s3, batch=3, num_q_heads=4, num_kv_heads=1))
-        kw = dict(eps_scale=5e-2, eps_dir=5e-3)
-    elif case == "edge lengths":  # empty and one-block units next to long ones
-        lens = np.array([0, 1, 63, 64, 65, 127, 129, 1000], dtype=np.int32)
-        w = make_workload(replace(s3, batch=8), context_lens=lens)
-        kw = dict(eps_scale=5e-2, eps_dir=5e-3, patience=1)
-    elif case == "bad kept list":  # one team's unit is rejected, its partner runs
-        w = make_workload(scaled(5, "B"))
-        w.kept_blocks = w.kept_blocks.copy()
-        w.kept_blocks[0, 1, 3] = 10 ** 6
-    elif case == "forced stop":  # partners stop at different rounds
-        w = make_workload(s3)
-        kw = dict(eps_scale=1e30, eps_dir=1e30, patience=2)
-    elif case == "detect-only":
-        w = make_workload(s3)
-        kw = dict(eps_scale=5e-2, eps_dir=5e-3, flags=orc.FLAG_DETECT_ONLY)
-    elif case == "natural order":
-        w = make_workload(s3)
-        kw = dict(order=orc.ORDER_NATURAL, eps_scale=5e-2, eps_dir=5e-3)
-    else:
-        raise ValueError(case)
-    return w, kw
+@pytest.mark.parametrize("waves", [4, 8])
+@pytest.mark.parametrize("p", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_chain_forced_stop_at_every_position(torch_cuda, waves, p):
+    """eps huge: every check is stable, so the stop is at min(T', p+1).  p
+    from 1 to 8 puts the stop on every position modulo 4 and 8, so each
+    wave of the chain once holds the stopping position, and the patience
+    runs cross from wave to wave.  Loads past the stop: at most 2W - 1."""
+    w = make_workload(scaled(3, "B"))
+    _, stop, issued, _ = check(w, tag=f"chain W={waves} p={p}", eps_scale=1e30, eps_dir=1e30, patience=p,
+                               split_blocks=10 ** 6, waves=waves)
+    Tp = w.traversal_lengths()
+    np.testing.assert_array_equal(stop, np.minimum(Tp, p + 1))
+    assert np.all(issued <= np.minimum(Tp, stop + 2 * waves - 1))
 
 
-PAIR_CASES = ["scaled", "odd units", "edge lengths", "bad kept list", "forced stop", "detect-only", "natural order"]
+@pytest.mark.parametrize("reading", ["A", "B"])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_eight_waves_per_unit(torch_cuda, n, reading):
+    """8 waves per workgroup on every scaled configuration: parity with the
+    oracle, and loads past the stop bounded by 2 * 8 - 1."""
+    w = make_workload(scaled(n, reading))
+    _, stop, issued, _ = check(w, tag=f"scaled cfg{n} 8 waves", split_blocks=10 ** 6, waves=8)
+    assert np.all(issued <= np.minimum(w.traversal_lengths(), stop + 15))
 
 
-@pytest.mark.parametrize("case", PAIR_CASES)
-def test_two_units_per_workgroup(torch_cuda, case):
-    """Lockstep teams change scheduling only: outputs, stops and issued
-    counts equal the one-unit-per-workgroup kernel's bit for bit, and the
-    oracle's within the parity bar."""
+@pytest.mark.parametrize("waves", [4, 8])
+def test_chain_natural_stops(torch_cuda, waves):
+    """Generator B at its own lengths: the criterion fires at data-dependent
+    positions; 4 and 8 waves agree with the oracle (and so with each other,
+    up to margin-excused units)."""
+    w = make_workload(config(2, "B", batch=2, num_q_heads=8, num_kv_heads=2, ctx=(20000, 32768)))
+    _, stop, issued, _ = check(w, tag=f"chain natural W={waves}", split_blocks=10 ** 6, waves=waves)
+    assert np.all(stop < w.traversal_lengths())
+    assert np.all(issued <= np.minimum(w.traversal_lengths(), stop + 2 * waves - 1))
+
+
+@pytest.mark.parametrize("waves", [4, 8])
+def test_chain_detect_only(torch_cuda, waves):
+    w = make_workload(config(2, "B", batch=2, num_q_heads=8, num_kv_heads=2, ctx=(20000, 32768)))
+    eps = dict(eps_scale=5e-2, eps_dir=5e-3)
+    _, stop_d, issued, _ = check(w, tag=f"chain detect-only W={waves}", flags=orc.FLAG_DETECT_ONLY,
+                                 split_blocks=10 ** 6, waves=waves, **eps)
+    np.testing.assert_array_equal(issued, w.traversal_lengths())
+    _, stop_a, _, _ = check(w, tag=f"chain ART W={waves}", split_blocks=10 ** 6, waves=waves, **eps)
+    np.testing.assert_array_equal(stop_d, stop_a)
+
+
+def test_given_order_repeated_block_is_reported(torch_cuda):
+    """GIVEN order with a block listed twice: the unit is rejected
+    (ART_ERR_DEVICE_INPUT, stop -1, out 0); the other units are unaffected."""
     from kv_cache_early_amd import art
-    w, kw = _pair_case(case)
-    kw["split_blocks"] = 10 ** 6  # one work item per unit (few units would otherwise split)
-    log(f"[case] pairing {case}: one unit per workgroup")
-    o1, s1, i1, e1 = run_gpu(w, pairing=1, **kw)
-    log(f"[case] pairing {case}: two units per workgroup")
-    o2, s2, i2, e2 = run_gpu(w, pairing=2, **kw)
-    assert e1 == e2
-    np.testing.assert_array_equal(s2, s1)
-    np.testing.assert_array_equal(i2, i1)
-    np.testing.assert_array_equal(o2, o1)
-    ckw = {k: v for k, v in kw.items() if k in ("patience", "eps_scale", "eps_dir", "order", "flags")}
-    units = None
-    if case == "bad kept list":
-        assert e2 == art.ART_ERR_DEVICE_INPUT and s2[0, 1] == -1
-        units = [(b, h) for b in range(w.spec.batch) for h in range(w.spec.num_kv_heads) if (b, h) != (0, 1)]
-    else:
-        assert e2 == 0
-    rep, _ = compare(w, o2, s2, units=units, **ckw)
-    log(f"   {rep}")
-    assert rep.ok(), (rep.unexcused[:5], rep.bad_outputs[:5])
-
-
-def test_pairing_is_ignored_in_full_mode(torch_cuda):
-    w = make_workload(scaled(3, "A"))
-    log("[case] pairing 2 in full mode")
-    o1, s1, i1, _ = run_gpu(w, mode=0, pairing=1)
-    o2, s2, i2, _ = run_gpu(w, mode=0, pairing=2)
-    np.testing.assert_array_equal(o2, o1)
-    np.testing.assert_array_equal(s2, s1)
+    s = scaled(5, "B")
+    w = make_workload(s)
+    kb = w.kept_blocks.copy()
+    n = int(w.kept_count[1, 0])
+    kb[1, 0, n - 1] = kb[1, 0, 2]  # a duplicate inside the used part of the list
+    w.kept_blocks = kb
+    log("[case] GIVEN order with a repeated block")
+    for split in (0, 10 ** 6):
+        out, stop, issued, err = run_gpu(w, order=orc.ORDER_GIVEN, split_blocks=split)
+        assert err == art.ART_ERR_DEVICE_INPUT
+        assert stop[1, 0] == -1 and np.all(out[1, 0:s.group] == 0) and issued[1, 0] == 0
+        good = [(b, h) for b in range(s.batch) for h in range(s.num_kv_heads) if (b, h) != (1, 0)]
+        rep, _ = compare(w, out, stop, units=good, order=orc.ORDER_GIVEN)
+        log(f"   split={split} {rep}")
+        assert rep.ok(), str(rep)

@@ -4,7 +4,9 @@ Every mutation below is a plausible slip when writing ART from its
 description: a wrong denominator in the scale metric, a sign slip in the
 direction metric, a non-strict threshold, a contiguous probe slice, block 0
 not forced first, a dropped 1/sqrt(d), a patience off by one, a prefix off by
-one, a dropped ragged tail.  The test patches the oracle module in place,
+one, a dropped ragged tail, an absolute instead of a relative margin band
+(or one taken the wrong way round), a mis-shifted bf16 widening, a kept list
+whose repeats are accepted.  The test patches the oracle module in place,
 runs the pin functions, and requires at least one of them to fail.
 """
 import math
@@ -46,11 +48,14 @@ def _run_pins():
         (pins.test_kept_list_restricts_to_kept_tokens, {}),
         (pins.test_brute_force_tiny, dict(seed=0)),
         (pins.test_hand_derived_worked_example, {}),
+        (pins.test_relative_margin_hand_values, {}),
+        (pins.test_widen_bf16_bit_patterns, {}),
+        (pins.test_kept_lists_must_be_distinct_blocks_of_the_sequence, {}),
     ]
     for fn, kw in cases:
         try:
             fn(**kw)
-        except Exception:  # noqa: BLE001 - any failure counts
+        except (Exception, pytest.fail.Exception):  # noqa: BLE001 - any failure counts
             failed.append(fn.__name__)
     return failed
 
@@ -145,7 +150,47 @@ def _mut_drop_ragged_tail(mp):
     mp.setattr(ao, "block_tokens", bad)
 
 
+def _mut_absolute_margin(mp):
+    def bad(d, eps):
+        with np.errstate(invalid="ignore"):
+            return np.abs(np.asarray(d) - ao.threshold(eps))
+    mp.setattr(ao, "relative_margin", bad)
+
+
+def _mut_margin_inverted(mp):
+    def bad(d, eps):
+        with np.errstate(invalid="ignore", divide="ignore"):
+            return np.abs(ao.threshold(eps) / np.asarray(d) - 1.0)
+    mp.setattr(ao, "relative_margin", bad)
+
+
+def _mut_widen_mantissa_shift(mp):
+    def bad(arr, dtype):
+        if dtype == "bf16":
+            bits = np.asarray(arr, dtype=np.uint16).astype(np.uint32) << 15
+            return bits.view(np.float32).astype(np.float64)
+        return np.asarray(arr, dtype=np.float32).astype(np.float64)
+    mp.setattr(ao, "widen", bad)
+
+
+def _mut_kept_duplicates_accepted(mp):
+    def bad(nb, kept=None, order=ao.ORDER_RECENT_FIRST):
+        cand = list(range(nb)) if kept is None else [int(c) for c in kept]
+        head = [0] if 0 in cand else []
+        rest = [c for c in cand if c != 0]
+        if order == ao.ORDER_NATURAL:
+            rest = sorted(rest)
+        elif order == ao.ORDER_RECENT_FIRST:
+            rest = sorted(rest, reverse=True)
+        return head + rest
+    mp.setattr(ao, "traversal", bad)
+
+
 MUTATIONS = {
+    "absolute margin band": _mut_absolute_margin,
+    "margin inverted (eps / d)": _mut_margin_inverted,
+    "bf16 widened with a 15-bit shift": _mut_widen_mantissa_shift,
+    "kept list repeats accepted": _mut_kept_duplicates_accepted,
     "scale-metric uses current norm": _mut_scale_denominator,
     "direction metric sign slip": _mut_dir_sign,
     "non-strict thresholds": _mut_nonstrict,

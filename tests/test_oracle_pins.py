@@ -480,3 +480,62 @@ def test_rows_full_mode_is_per_row_attention():
                 V = v[b, h, :n].astype(np.float32).astype(np.float64)
                 ref = sdpa64(qq[None], K, V, np.zeros(n))[0]
                 np.testing.assert_allclose(out[b, i, hq], ref, rtol=1e-11, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# the parity rule's margin, the exact widening of stored inputs, kept lists
+# ---------------------------------------------------------------------------
+def test_relative_margin_hand_values():
+    """Pins relative_margin, which excuses a stop mismatch when a metric sits
+    within a relative 1e-4 of its threshold: |d / eps - 1|, eps as the
+    float32 the C ABI carries.  An absolute band |d - eps| would give about
+    1e-8 for d = 1.0001 eps and so excuse nearly every check; a margin on
+    the wrong side (eps / d) or without the absolute value fails the values
+    below."""
+    for eps in (1e-4, 2e-4, 1e-3, 2e-3, 5e-2):
+        e = float(np.float32(eps))
+        m = orc.relative_margin(np.array([1.0001 * e, e, 0.5 * e, 3.0 * e, 0.9999 * e, np.nan]), eps)
+        assert abs(m[0] - 1e-4) < 1e-12
+        assert m[1] == 0.0
+        assert abs(m[2] - 0.5) < 1e-15 and abs(m[3] - 2.0) < 1e-15
+        assert abs(m[4] - 1e-4) < 1e-12
+        assert np.isnan(m[5])
+    # a check 2e-4 above eps_dir = 1e-4 in absolute terms is far (margin 2), not near
+    assert orc.relative_margin(np.array([3e-4]), 1e-4)[0] > 1.9
+
+
+def test_widen_bf16_bit_patterns():
+    """Pins widen: bf16 bit patterns are the upper halves of float32 (sign,
+    8 exponent bits, 7 mantissa bits), widened exactly; float32 inputs are
+    widened exactly."""
+    table = {
+        0x3F80: 1.0, 0xC000: -2.0, 0x4049: 3.140625, 0x3E80: 0.25, 0x0000: 0.0,
+        0x7F80: math.inf, 0xFF80: -math.inf,
+        0x0001: 2.0 ** -133,            # smallest subnormal
+        0x007F: 127 * 2.0 ** -133,      # largest subnormal
+        0x0080: 2.0 ** -126,            # smallest normal
+        0x7F7F: (2 - 2.0 ** -7) * 2.0 ** 127,  # largest finite
+    }
+    bits = np.array(list(table), dtype=np.uint16)
+    got = orc.widen(bits, "bf16")
+    assert got.dtype == np.float64
+    for b, v in zip(table, got):
+        assert v == table[b], hex(b)
+    neg0 = orc.widen(np.array([0x8000], dtype=np.uint16), "bf16")[0]
+    assert neg0 == 0.0 and math.copysign(1.0, neg0) == -1.0
+    assert np.isnan(orc.widen(np.array([0x7FC0, 0xFFC1], dtype=np.uint16), "bf16")).all()
+    f = np.array([0.1, -3.5, 1e-40], dtype=np.float32)
+    assert [float(x) for x in orc.widen(f, "f32")] == [float(x) for x in f]
+
+
+def test_kept_lists_must_be_distinct_blocks_of_the_sequence():
+    """A kept list is a set of the sequence's blocks: repeats and blocks
+    outside the sequence are refused, in every order."""
+    for order in (orc.ORDER_NATURAL, orc.ORDER_RECENT_FIRST, orc.ORDER_GIVEN):
+        with pytest.raises(ValueError):
+            orc.traversal(10, [1, 3, 3], order)
+        with pytest.raises(ValueError):
+            orc.traversal(10, [1, 10], order)
+        with pytest.raises(ValueError):
+            orc.traversal(10, [-1, 2], order)
+        assert sorted(orc.traversal(10, [7, 0, 3], order)) == [0, 3, 7]
