@@ -296,6 +296,16 @@ __device__ __forceinline__ void st_sys(T* p, T v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
+// Single LDS words shared between the waves of a workgroup, read and written
+// as volatile LDS accesses.  The explicit address space matters: a volatile
+// access through a generic pointer (which is what a lambda's captured
+// reference to a __shared__ object is) stays a flat access, and a flat load
+// waits on the vector-memory counter too, i.e. for every K/V load in flight.
+__device__ __forceinline__ int lds_get(const int& x) {
+  return *(const volatile __attribute__((address_space(3))) int*)(&x);
+}
+__device__ __forceinline__ void lds_put(int& x, int v) { *(volatile __attribute__((address_space(3))) int*)(&x) = v; }
+
 // Workgroup barrier that orders LDS only: waits for this wave's LDS traffic
 // and meets the other waves, without waiting for in-flight global loads (a
 // full __syncthreads() would drain the K/V prefetch).
@@ -1142,17 +1152,16 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
   // legitimate wait) the wave records a timeout and publishes a stop after
   // the first block, which ends every wave's walk.
   auto chain_wait = [&](int t) -> bool {
-    volatile int* sq = &R.head[(t - 1) & 1].seq;
-    volatile int* sa = &R.stop_at;
+    int& sq = R.head[(t - 1) & 1].seq;
     for (uint32_t polls = 0;; ++polls) {
-      const int q = uni(*sq);
-      const int st = uni(*sa);
+      const int q = uni(lds_get(sq));
+      const int st = uni(lds_get(R.stop_at));
       if (st > 0 && st <= t) return false;
       if (q == t) break;
       if (polls >= 4u * a.spin_limit) {
         if (lane == 0) {
-          *(volatile int*)&R.timeout = 1;
-          *sa = 1;
+          lds_put(R.timeout, 1);
+          lds_put(R.stop_at, 1);
         }
         return false;
       }
@@ -1180,7 +1189,7 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
       const int tn = t + W;
       bool has_next = tn < t_stop;
       if (chain) {  // a stop already found: drop this block, or the next one's loads
-        const int sa = uni(*(volatile int*)&R.stop_at);
+        const int sa = uni(lds_get(R.stop_at));
         if (sa > 0 && t >= sa) break;
         if (sa > 0 && tn >= sa) has_next = false;
       }
@@ -1468,7 +1477,7 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
             if (detect_only && det > 0 && det == t + 1) R.detected = det;
           }
           wait_lgkm0();  // the record is in LDS before its sequence number
-          if (lane == 0) *(volatile int*)&R.head[t & 1].seq = t + 1;
+          if (lane == 0) lds_put(R.head[t & 1].seq, t + 1);
           if (st > 0) {
             stop = st;
             last = true;

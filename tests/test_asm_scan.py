@@ -7,6 +7,7 @@ assembly and require that no instruction touches a register with an
 outstanding load into it.
 """
 import os
+import re
 import shutil
 import subprocess
 
@@ -151,3 +152,10 @@ def test_generated_kernels_have_no_access_to_outstanding_loads(tmp_path, src):
     assert bodies, "no kernels found in the assembly"
     bad = {name: hits[:3] for name, body in bodies.items() if (hits := scan_function(body))}
     assert not bad, bad
+    # No flat (generic address) memory instruction: a flat load is counted
+    # on the vector-memory counter as well, so waiting for one waits for
+    # every K/V load in flight.  Accesses to LDS words shared between waves
+    # must be LDS instructions.
+    flat = {name: re.findall(r"^\s*(flat_\w+.*)$", body, re.M)[:3] for name, body in bodies.items()}
+    flat = {k: v for k, v in flat.items() if v}
+    assert not flat, flat
