@@ -221,6 +221,29 @@ art_status art_decode(const art_shape* shape, const art_params* params,
                       float* out, int32_t* stop_idx, int32_t* blocks_issued,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* art_decode without a caller-provided workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Arguments and outputs as for
+ * art_decode; the workspace is a device buffer of ART_STATIC_SCRATCH_BYTES
+ * that the library holds on each GPU it runs on until the process ends
+ * (one per device, found on the device current at the call).
+ *   * Returns ART_ERR_WORKSPACE, before anything is enqueued, when
+ *     art_workspace_size(shape, params) exceeds ART_STATIC_SCRATCH_BYTES;
+ *     other argument errors as art_decode.  Allocates nothing.
+ *   * All calls on one GPU share its buffer: calls that overlap in time on
+ *     one GPU (other streams, other host threads) race and give undefined
+ *     results.  Sequential calls need no clearing between them.
+ *   * Device-side errors are recorded in that buffer and cannot be read
+ *     back with art_last_error; a unit whose kept list is rejected still
+ *     shows stop_idx = -1 and out = 0. */
+#define ART_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+art_status art_decode_static(const art_shape* shape, const art_params* params,
+                             const void* q, const void* k, const void* v,
+                             const int32_t* context_lens, const int32_t* block_table,
+                             const int32_t* kept_blocks, const int32_t* kept_count,
+                             float* out, int32_t* stop_idx, int32_t* blocks_issued,
+                             void* stream);
+
 /* Device-side error recorded by the last call (art_decode, art_block_means
  * or art_select_blocks) that enqueued work on `workspace` (ART_OK,
  * ART_ERR_TIMEOUT or ART_ERR_DEVICE_INPUT; the most severe over its work

@@ -38,7 +38,9 @@ ART_SELECT_IMPORTANCE = 1
 ART_ABI_VERSION = 2  # include/art.h
 
 EXPORTS = ("art_workspace_size", "art_decode", "art_last_error", "art_status_string", "art_probe_stride",
-           "art_select_workspace_size", "art_block_means", "art_select_blocks", "art_abi_version")
+           "art_select_workspace_size", "art_block_means", "art_select_blocks", "art_abi_version",
+           "art_decode_static")
+ART_STATIC_SCRATCH_BYTES = 32 << 20  # include/art.h
 
 
 class art_params(ctypes.Structure):
@@ -97,6 +99,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.art_select_blocks.argtypes = [ctypes.POINTER(art_shape), ctypes.POINTER(art_select_params), vp, vp,
                                       ctypes.c_int32, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.art_select_blocks.restype = ctypes.c_int
+    lib.art_decode_static.argtypes = [ctypes.POINTER(art_shape), ctypes.POINTER(art_params), vp, vp, vp, vp, vp,
+                                      vp, vp, vp, vp, vp, vp]
+    lib.art_decode_static.restype = ctypes.c_int
     lib.art_abi_version.argtypes = []
     lib.art_abi_version.restype = ctypes.c_int32
     if lib.art_abi_version() != ART_ABI_VERSION:
@@ -137,6 +142,15 @@ def decode_raw(shape: art_shape, params: art_params, q, k, v, context_lens, bloc
                                  _ptr(context_lens), _ptr(block_table), _ptr(kept_blocks), _ptr(kept_count),
                                  _ptr(out), _ptr(stop_idx), _ptr(blocks_issued), _ptr(workspace),
                                  workspace_bytes, stream))
+
+
+def decode_static_raw(shape: art_shape, params: art_params, q, k, v, context_lens, block_table, kept_blocks,
+                      kept_count, out, stop_idx, blocks_issued, stream: Optional[int]) -> int:
+    """Call art_decode_static (the library's own per-device workspace); returns the status."""
+    return int(load().art_decode_static(ctypes.byref(shape), ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v),
+                                        _ptr(context_lens), _ptr(block_table), _ptr(kept_blocks),
+                                        _ptr(kept_count), _ptr(out), _ptr(stop_idx), _ptr(blocks_issued),
+                                        stream))
 
 
 def select_workspace_size(shape: art_shape) -> int:

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libart.so")
 
-SOURCES = ["art_kernels.hip", "select_kernels.hip", "art_api.cpp"]
+SOURCES = ["art_kernels.hip", "select_kernels.hip", "art_static.hip", "art_api.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # packed fp32 VALU forms are kept out of the generated code on purpose

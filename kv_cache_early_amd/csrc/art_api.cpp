@@ -207,20 +207,14 @@ art::WsLayout layout(const art_shape& s, const art_params& p, int chunk, int max
 
 }  // namespace
 
-extern "C" {
+namespace art {
 
-size_t art_workspace_size(const art_shape* shape, const art_params* params) {
-  if (validate(shape, params) != ART_OK) return 0;
-  const int chunk = chunk_blocks(*shape, *params);
-  const int64_t tmax = std::max<int64_t>(1, max_traversal(*shape));
-  const int max_chunks = (int)((tmax + chunk - 1) / chunk);
-  return layout(*shape, *params, chunk, max_chunks).total;
-}
-
-art_status art_decode(const art_shape* shape, const art_params* params, const void* q, const void* k,
-                      const void* v, const int32_t* context_lens, const int32_t* block_table,
-                      const int32_t* kept_blocks, const int32_t* kept_count, float* out, int32_t* stop_idx,
-                      int32_t* blocks_issued, void* workspace, size_t workspace_bytes, void* stream) {
+// art_decode's work on a given workspace (also the body of the entry point
+// that uses the library's own device buffer).
+art_status decode_impl(const art_shape* shape, const art_params* params, const void* q, const void* k,
+                       const void* v, const int32_t* context_lens, const int32_t* block_table,
+                       const int32_t* kept_blocks, const int32_t* kept_count, float* out, int32_t* stop_idx,
+                       int32_t* blocks_issued, void* workspace, size_t workspace_bytes, void* stream) {
   art_status st = validate(shape, params);
   if (st != ART_OK) return st;
   const art_shape& s = *shape;
@@ -310,6 +304,26 @@ art_status art_decode(const art_shape* shape, const art_params* params, const vo
 
   hipError_t e = art::launch(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ART_OK : ART_ERR_HIP;
+}
+
+}  // namespace art
+
+extern "C" {
+
+size_t art_workspace_size(const art_shape* shape, const art_params* params) {
+  if (validate(shape, params) != ART_OK) return 0;
+  const int chunk = chunk_blocks(*shape, *params);
+  const int64_t tmax = std::max<int64_t>(1, max_traversal(*shape));
+  const int max_chunks = (int)((tmax + chunk - 1) / chunk);
+  return layout(*shape, *params, chunk, max_chunks).total;
+}
+
+art_status art_decode(const art_shape* shape, const art_params* params, const void* q, const void* k,
+                      const void* v, const int32_t* context_lens, const int32_t* block_table,
+                      const int32_t* kept_blocks, const int32_t* kept_count, float* out, int32_t* stop_idx,
+                      int32_t* blocks_issued, void* workspace, size_t workspace_bytes, void* stream) {
+  return art::decode_impl(shape, params, q, k, v, context_lens, block_table, kept_blocks, kept_count, out,
+                          stop_idx, blocks_issued, workspace, workspace_bytes, stream);
 }
 
 size_t art_select_workspace_size(const art_shape* shape) {

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "art.h"
+
 namespace art {
 
 // Workspace header, written by work item 0 of every decode launch.  Every
@@ -95,6 +97,13 @@ struct WsLayout {
 };
 
 hipError_t launch(const KernelArgs& a, hipStream_t stream);
+
+// art_decode's work on a caller-chosen workspace (art_api.cpp): shared by
+// art_decode and art_decode_static.
+art_status decode_impl(const art_shape* shape, const art_params* params, const void* q, const void* k,
+                       const void* v, const int32_t* context_lens, const int32_t* block_table,
+                       const int32_t* kept_blocks, const int32_t* kept_count, float* out, int32_t* stop_idx,
+                       int32_t* blocks_issued, void* workspace, size_t workspace_bytes, void* stream);
 
 // Key-based block selection (block-mean keys, kept lists).
 struct SelectArgs {

@@ -248,3 +248,19 @@ def test_select_workspace_size():
     assert art.select_workspace_size(good_shape(dtype=7)) == 0
     assert call_means(shape=good_shape(batch=0)) == art.ART_OK  # empty batch: nothing enqueued
     assert call_select(shape=good_shape(batch=0, max_kept=512)) == art.ART_OK
+
+
+def test_static_workspace_entry_point_rejects_large_calls_before_launching():
+    """art_decode_static refuses, on the host, a call whose workspace would
+    not fit the library's per-device buffer (fake pointers: nothing may be
+    touched), and validates arguments as art_decode does."""
+    lib = art.load()
+    sh = good_shape(batch=4096, num_kv_heads=8, num_q_heads=32, max_pages=2048)
+    pa = good_params(mode=art.ART_MODE_FULL, split_blocks=1)
+    need = art.workspace_size(sh, pa)
+    assert need > art.ART_STATIC_SCRATCH_BYTES
+    assert lib.art_decode_static(ctypes.byref(sh), ctypes.byref(pa), FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                                 FAKE, FAKE, None, None) == art.ART_ERR_WORKSPACE
+    bad = good_params(patience=0)
+    assert lib.art_decode_static(ctypes.byref(good_shape()), ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                 None, FAKE, FAKE, None, None) == art.ART_ERR_INVALID_ARG
