@@ -137,6 +137,48 @@ __device__ __forceinline__ double col_sum_d(double x) {
   return __builtin_bit_cast(double, ((uint64_t)th[0] << 32) | tl[0]) +
          __builtin_bit_cast(double, ((uint64_t)th[1] << 32) | tl[1]);
 }
+// All-reduce of two fp64 values over the 64 lanes, in lockstep: two
+// independent chains, so each stage's latency is paid once.  The row stages
+// are DPP moves with bound_ctrl (every lane reads a lane of its own row, so
+// no old value is needed), the column stages the row and half swaps.
+template <int CTRL>
+__device__ __forceinline__ double dpp_b(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)u, CTRL, 0xF, 0xF, true);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, true);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+template <bool H32>
+__device__ __forceinline__ double swap_add(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+  if constexpr (H32) {
+    const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    return __builtin_bit_cast(double, ((uint64_t)h[0] << 32) | l[0]) +
+           __builtin_bit_cast(double, ((uint64_t)h[1] << 32) | l[1]);
+  } else {
+    const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    return __builtin_bit_cast(double, ((uint64_t)h[0] << 32) | l[0]) +
+           __builtin_bit_cast(double, ((uint64_t)h[1] << 32) | l[1]);
+  }
+}
+__device__ __forceinline__ void allsum2_d(double& x, double& y) {
+  x += dpp_b<kQx1>(x);
+  y += dpp_b<kQx1>(y);
+  x += dpp_b<kQx2>(x);
+  y += dpp_b<kQx2>(y);
+  x += dpp_b<kHalfMirror>(x);
+  y += dpp_b<kHalfMirror>(y);
+  x += dpp_b<kMirror>(x);
+  y += dpp_b<kMirror>(y);
+  x = swap_add<false>(x);
+  y = swap_add<false>(y);
+  x = swap_add<true>(x);
+  y = swap_add<true>(y);
+}
+
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 // The lane index, produced by an instruction the compiler cannot move or
 // reuse: LDS addresses derived from it are computed where they are used
@@ -305,6 +347,12 @@ __device__ __forceinline__ int lds_get(const int& x) {
   return *(const volatile __attribute__((address_space(3))) int*)(&x);
 }
 __device__ __forceinline__ void lds_put(int& x, int v) { *(volatile __attribute__((address_space(3))) int*)(&x) = v; }
+__device__ __forceinline__ double lds_get(const double& x) {
+  return *(const volatile __attribute__((address_space(3))) double*)(&x);
+}
+__device__ __forceinline__ float lds_get(const float& x) {
+  return *(const volatile __attribute__((address_space(3))) float*)(&x);
+}
 
 // Workgroup barrier that orders LDS only: waits for this wave's LDS traffic
 // and meets the other waves, without waiting for in-flight global loads (a
@@ -724,11 +772,14 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
   // of a block waits for `dep` (the score maximum), so it overwrites the K
   // registers only after the MFMAs that read them have completed.
   // The four loads of tile nt; tile 0's first load waits for `dep`.
-  auto load_k_tile = [&](const BlockAddr& ba, auto ntc, float dep) {
+  // Before a walk (no MFMA reads the K registers) the first load needs no
+  // dependency: `first` drops it.
+  auto load_k_tile = [&](const BlockAddr& ba, auto ntc, float dep, auto first) {
     constexpr int nt = decltype(ntc)::value;
+    constexpr bool kDep = nt == 0 && !decltype(first)::value;
     if (PAGED || ba.nvalid == kBlk) {
       const char* base = u.k + (size_t)ba.row[nt] * ROW;
-      if constexpr (nt == 0)
+      if constexpr (kDep)
         kr[0] = gload16s_after<0>(koff, base, dep);
       else
         kr[4 * nt] = gload16s<0>(koff, base);
@@ -736,19 +787,19 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
       kr[4 * nt + 2] = gload16s<128>(koff, base);
       kr[4 * nt + 3] = gload16s<192>(koff, base);
     } else {  // last block of a contiguous sequence: rows clamped to the last token
-      const int tok = min(ba.j * kBlk + 16 * nt + c, u.n_ctx - 1);
-      const char* p = u.k + (size_t)tok * ROW + lg * 16;
-      if constexpr (nt == 0)
-        kr[0] = gload16_after<0>(p, dep);
+      const char* base = u.k + (size_t)ba.row[0] * ROW;
+      const uint32_t off = (uint32_t)(min(16 * nt + c, ba.nvalid - 1) * ROW + lg * 16);
+      if constexpr (kDep)
+        kr[0] = gload16s_after<0>(off, base, dep);
       else
-        kr[4 * nt] = gload16<0>(p);
-      kr[4 * nt + 1] = gload16<64>(p);
-      kr[4 * nt + 2] = gload16<128>(p);
-      kr[4 * nt + 3] = gload16<192>(p);
+        kr[4 * nt] = gload16s<0>(off, base);
+      kr[4 * nt + 1] = gload16s<64>(off, base);
+      kr[4 * nt + 2] = gload16s<128>(off, base);
+      kr[4 * nt + 3] = gload16s<192>(off, base);
     }
   };
-  auto load_k = [&](const BlockAddr& ba, float dep) {
-    static_for<0, kTiles>([&](auto ntc) { load_k_tile(ba, ntc, dep); });
+  auto load_k_first = [&](const BlockAddr& ba) {
+    static_for<0, kTiles>([&](auto ntc) { load_k_tile(ba, ntc, 0.f, std::true_type{}); });
   };
   // V: the 16 DMAs of a block into this wave's slab (DMA n -> bytes 1024 n);
   // group g is DMAs 4g .. 4g + 3 (16-token group g).  The caller has waited
@@ -761,11 +812,12 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
         constexpr int q = decltype(qc)::value;
         lds_dma16s(voff[q], base, slab + (4 * g + q) * 1024);
       });
-    } else {
+    } else {  // last block of a contiguous sequence: rows clamped to the last token
+      const char* base = u.v + (size_t)ba.row[0] * ROW;
       static_for<4 * g, 4 * g + 4>([&](auto nc) {
         constexpr int n = decltype(nc)::value;
-        const int tok = min(ba.j * kBlk + 4 * n + lg, u.n_ctx - 1);
-        lds_dma16(u.v + (size_t)tok * ROW + ((c ^ (2 * lg) ^ (8 * (n & 1))) * 16), slab + n * 1024);
+        const uint32_t off = (uint32_t)(min(4 * n + lg, ba.nvalid - 1) * ROW + ((c ^ (2 * lg) ^ (8 * (n & 1))) * 16));
+        lds_dma16s(off, base, slab + n * 1024);
       });
     }
   };
@@ -1144,17 +1196,29 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
   // barrier sits in the walk: a wave waits only for its predecessor's record.
   // A stop, once found, is also published in R.stop_at, which every wave
   // reads before it computes or prefetches a block.
-  // true once the record of t - 1 is there; false when the unit stopped
-  // after at most t blocks (position t does not count).  The stop word is
-  // read after the sequence number: a record that stops the unit writes
-  // R.stop_at before its sequence number.
-  // The wait is bounded: past a.spin_limit * 4 polls (far beyond any
-  // legitimate wait) the wave records a timeout and publishes a stop after
-  // the first block, which ends every wave's walk.
-  auto chain_wait = [&](int t) -> bool {
-    int& sq = R.head[(t - 1) & 1].seq;
+  // Waits until the record of position t - 1 is there and returns true with
+  // its contents in `in`; false when the unit stopped after at most t blocks
+  // (position t does not count).  A poll reads the sequence number, then the
+  // stop word; once the sequence number matches, the record is read.  These
+  // are ordered LDS reads (LDS serves a wave's accesses in order), and a
+  // writer completes the record (and, on a stop, the stop word) before its
+  // sequence number, so a matching sequence number vouches for what is read
+  // after it.  The poll does not sleep between reads: measured on MI355X,
+  // s_sleep 1 there slowed a lone unit's walk by a quarter.  The wait is
+  // bounded: past a.spin_limit * 4 polls (far beyond any legitimate wait)
+  // the wave records a timeout and publishes a stop after the first block,
+  // which ends every wave's walk.
+  struct LinkIn {
+    double p[NPL];
+    double l[NH];
+    float m[NH];
+    double stt;
+    int counter, detected;
+  };
+  auto chain_wait = [&](int t, LinkIn& in) -> bool {
+    const int par = (t - 1) & 1;
     for (uint32_t polls = 0;; ++polls) {
-      const int q = uni(lds_get(sq));
+      const int q = uni(lds_get(R.head[par].seq));
       const int st = uni(lds_get(R.stop_at));
       if (st > 0 && st <= t) return false;
       if (q == t) break;
@@ -1165,9 +1229,18 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
         }
         return false;
       }
-      __builtin_amdgcn_s_sleep(1);
     }
-    compiler_fence();
+    const LaneLink<NPL, NH>& lk = R.link[par][lane];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) in.p[i] = lds_get(lk.p[i]);
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      in.l[hh] = lds_get(lk.l[hh]);
+      in.m[hh] = lds_get(lk.m[hh]);
+    }
+    in.stt = lds_get(R.head[par].stt);
+    in.counter = lds_get(R.head[par].counter);
+    in.detected = lds_get(R.head[par].detected);
     return true;
   };
   for (int pass = 0; pass < 2 && !discard; ++pass) {
@@ -1181,7 +1254,7 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
     BlockAddr cur;
     if (t < t_stop) {
       cur = block_addr4<ROW, PAGED>(u, uni(block_at(u, a.order, t)), bad_page);
-      load_k(cur, 0.f);
+      load_k_first(cur);
       load_v(cur);
       ++issued;
     }
@@ -1233,10 +1306,14 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
       const float alpha = __builtin_amdgcn_exp2f(m_c - m_new);
       float ls = 0.f;
       // the next block's K, one tile at a time between the tiles'
-      // exponentials: the wave computes while the address unit drains
+      // exponentials: the wave computes while the address unit drains.  With
+      // no next block the loads still go out, to this block's own addresses
+      // (read a moment ago, so mostly from L2): every iteration then issues
+      // the same 16 K loads and 16 V loads whatever the path, which keeps
+      // the explicit vmcnt waits path independent.
       static_for<0, kTiles>([&](auto ntc) {
         constexpr int nt = decltype(ntc)::value;
-        if (has_next) load_k_tile(nxt, ntc, mx);
+        load_k_tile(nxt, ntc, mx, std::false_type{});
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float p = __builtin_amdgcn_exp2f(S[nt][r] - m_new);
@@ -1250,11 +1327,8 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
       f32x4 bacc[NDT];
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) bacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // V of this block: the 16 K loads of the next block (if any) were issued after it
-      if (has_next)
-        wait_vm<kLoads>();
-      else
-        wait_vm<0>();
+      // V of this block: the 16 K loads of the next block were issued after it
+      wait_vm<kLoads>();
       const bool partial = nvalid < kBlk;  // weights of the tail tokens are 0; their V may be garbage
       if constexpr (DT == ART_DT_BF16) {
         // A operand of tile pair jp: element e < 4 is token 16(2jp) + 4lg + e,
@@ -1344,19 +1418,15 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
           gs->l[lane] = lblk;
         }
       }
-      // V of the next block: after this block's LDS reads (load_v waits for
-      // them); in ART mode also after the block summary's round trip
-      // through the slab (below)
-      if (has_next && !chain) load_v(nxt);
-
-      bool commit = true, last = false;
+      // ---- (ART mode) the block's summary, read back in the stop rule's layout ----
+      // It goes through the wave's own V slab, free between this block's P V
+      // reads and the next block's V loads.  Probe dim 4p of query vector r
+      // (G <= 4: rows r % G) is register r of lane c = 4 (p % 4), tile p / 4,
+      // in the O layout's row 0 (more than 4 query vectors: rows 4 lg .. 4 lg
+      // + 3 are vectors of their own).
+      float mt[NH];
+      double lt[NH], ps[NPL];
       if (chain) {
-        // ---- the block's summary, read back in the stop rule's layout --------
-        // It goes through the wave's own V slab, free between this block's
-        // P V reads and the next block's V loads.  Probe dim 4p of query
-        // vector r (G <= 4: rows r % G) is register r of lane c = 4 (p % 4),
-        // tile p / 4, in the O layout's row 0 (more than 4 query vectors:
-        // rows 4 lg .. 4 lg + 3 are vectors of their own).
         wait_lgkm0();  // this block's transposed V reads have landed
         auto& sw = *reinterpret_cast<Summary<D, (G > 4 ? G : 4)>*>(&vbuf[wid][0]);
         if constexpr (G <= 4) {
@@ -1375,8 +1445,6 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
           sw.l[lane] = lblk;
         }
         // this wave's own writes, read back by this wave (LDS keeps a wave's order)
-        float mt[NH];
-        double lt[NH], ps[NPL];
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh) {
           const int g = G <= 4 ? (lg < G ? lg : 0) : lg + 4 * hh;
@@ -1385,7 +1453,13 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
 #pragma unroll
           for (int i = 0; i < PPC; ++i) ps[hh * PPC + i] = (double)sw.ps[c * PPC + i][g];
         }
-        if (has_next) load_v(nxt);  // waits for the summary reads above
+      }
+      // V of the next block: after this block's LDS reads (load_v waits for
+      // them, and in ART mode for the summary's round trip)
+      load_v(nxt);
+
+      bool commit = true, last = false;
+      if (chain) {
         // ---- the prefix state after position t - 1 ------------------------------
         float Mp[NH];
         double Lp[NH], P[NPL];
@@ -1393,21 +1467,18 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
         int counter = 0, det = 0;
         bool go = true;
         if (t > t_begin) {
-          go = chain_wait(t);
-          if (go) {
-            const LaneLink<NPL, NH>& lk = R.link[(t - 1) & 1][lane];
+          LinkIn in;
+          go = uni(chain_wait(t, in) ? 1 : 0) != 0;
 #pragma unroll
-            for (int i = 0; i < NPL; ++i) P[i] = lk.p[i];
+          for (int i = 0; i < NPL; ++i) P[i] = in.p[i];
 #pragma unroll
-            for (int hh = 0; hh < NH; ++hh) {
-              Lp[hh] = lk.l[hh];
-              Mp[hh] = lk.m[hh];
-            }
-            const LinkHead& hd = R.head[(t - 1) & 1];
-            spr = hd.stt;
-            counter = hd.counter;
-            det = hd.detected;
+          for (int hh = 0; hh < NH; ++hh) {
+            Lp[hh] = in.l[hh];
+            Mp[hh] = in.m[hh];
           }
+          spr = in.stt;
+          counter = uni(in.counter);
+          det = uni(in.detected);
         } else {
 #pragma unroll
           for (int i = 0; i < NPL; ++i) P[i] = 0.0;
@@ -1446,8 +1517,8 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
             sc = fma(pc, in * ip, sc);
           }
           const double keep = (G >= 4 || lg < G) ? 1.0 : 0.0;  // rows past G repeat query vector 0
-          const double stt = col_sum_d(row_sum_d(sa * keep));
-          const double stp = col_sum_d(row_sum_d(sc * keep));
+          double stt = sa * keep, stp = sc * keep;
+          allsum2_d(stt, stp);
           // a check exists from the second traversal block on
           const bool exists = t >= 1;
           const bool stable =

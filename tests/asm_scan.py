@@ -68,6 +68,49 @@ def _sregs_of(text: str) -> set:
     return out
 
 
+def _scalar_effect(op: str, text: str, ops: list) -> tuple:
+    """What an instruction does to the scalar facts tracked on a path:
+    ("cmp",) a comparison (a new SCC symbol); ("csel", lo, a, b); ("mov64",
+    lo, src_lo or None, const); ("mov32", dst, src or None, const); ("xor1",
+    dst_lo, src_lo); ("vcc", lo, negate); ("wlane", vgpr, sreg, lane);
+    ("rlane", sreg, vgpr, lane); else ("other", clobbers_scc, clobbers_vcc,
+    vgpr written or -1)."""
+    if re.match(r"^s_(?:cmp|bitcmp)", op):
+        return ("cmp",)
+    m = re.match(r"^s_cselect_b64 s\[(\d+):\d+\], (-1|0), (-1|0)$", text)
+    if m:
+        return ("csel", int(m.group(1)), int(m.group(2)), int(m.group(3)))
+    m = re.match(r"^s_mov_b64 s\[(\d+):\d+\], (?:s\[(\d+):\d+\]|(-1|0))$", text)
+    if m:
+        return ("mov64", int(m.group(1)), None if m.group(2) is None else int(m.group(2)),
+                None if m.group(3) is None else int(m.group(3)))
+    m = re.match(r"^s_mov_b32 s(\d+), (?:s(\d+)|(-1|0))$", text)
+    if m:
+        return ("mov32", int(m.group(1)), None if m.group(2) is None else int(m.group(2)),
+                None if m.group(3) is None else int(m.group(3)))
+    m = re.match(r"^s_xor_b64 s\[(\d+):\d+\], s\[(\d+):\d+\], -1$", text)
+    if m:
+        return ("xor1", int(m.group(1)), int(m.group(2)))
+    m = re.match(r"^s_(and|andn2)_b64 vcc, exec, s\[(\d+):\d+\]$", text)
+    if m:
+        return ("vcc", int(m.group(2)), m.group(1) == "andn2")
+    m = re.match(r"^v_writelane_b32 v(\d+), s(\d+), (\d+)$", text)
+    if m:
+        return ("wlane", int(m.group(1)), int(m.group(2)), int(m.group(3)))
+    m = re.match(r"^v_readlane_b32 s(\d+), v(\d+), (\d+)$", text)
+    if m:
+        return ("rlane", int(m.group(1)), int(m.group(2)), int(m.group(3)))
+    clob_scc = op.startswith("s_") and not op.startswith(("s_cbranch", "s_branch", "s_waitcnt", "s_nop", "s_sleep",
+                                                           "s_barrier", "s_setprio", "s_load", "s_store",
+                                                           "s_mov", "s_cselect"))
+    clob_vcc = "vcc" in text and not op.startswith("s_cbranch")
+    vdef = -1
+    if op.startswith("v_") and not op.startswith(("v_readlane", "v_readfirstlane", "v_cmp")) and ops:
+        regs = [r for k, r in regs_of(ops[0]) if k == "v"]
+        vdef = regs[0] if len(regs) == 1 else (-2 if regs else -1)
+    return ("other", clob_scc, clob_vcc, vdef)
+
+
 @dataclass
 class Insn:
     index: int
@@ -79,8 +122,7 @@ class Insn:
     dest: frozenset = frozenset()  # registers a load writes
     used: frozenset = frozenset()  # registers otherwise accessed
     sdef: frozenset = frozenset()  # scalar registers possibly written
-    flag_set: tuple = ()           # (lo, value) for s_mov_b64 s[lo:lo+1], 0 / -1
-    vcc_from: tuple = ()           # (lo, negate) for s_and(n2)_b64 vcc, exec, s[lo:lo+1]
+    sc: tuple = ()                 # its effect on the scalar facts (see _scalar_effect)
 
     def __post_init__(self):
         op, text = self.op, self.text
@@ -102,12 +144,7 @@ class Insn:
             if op.startswith("s_") or op.startswith("v_"):
                 self.sdef = frozenset(_sregs_of(ops[0]) | (_sregs_of(ops[1]) if op.startswith("v_") and len(ops) > 1
                                                            else set()))
-        m = re.match(r"s_mov_b64 s\[(\d+):\d+\], (0|-1)$", text)
-        if m:
-            self.flag_set = (int(m.group(1)), int(m.group(2)))
-        m = re.match(r"s_(and|andn2)_b64 vcc, exec, s\[(\d+):\d+\]$", text)
-        if m:
-            self.vcc_from = (int(m.group(2)), m.group(1) == "andn2")
+        self.sc = _scalar_effect(op, text, ops)
 
 
 def _split_operands(text: str, op: str) -> list:
@@ -217,45 +254,118 @@ def parse_blocks(body: str) -> list:
     return blocks
 
 
-def _run_block(b: Block, state: tuple, flags: frozenset, hits):
-    """Load state and flags at the block's end, and the successors the path
-    can take."""
-    fl = dict(flags)
-    vcc = None  # None unknown; True non-zero; False zero
+# Scalar facts on a path.  A value is ("k", 0 or -1), a known 64-bit flag
+# (one half of it for a 32-bit register), or ("s", id, negated), the
+# boolean a comparison produced (id: the comparison's instruction index).
+# `env` maps scalar registers and VGPR-lane spill slots ("l", vgpr, lane) to
+# values, and "scc"/"vcc" to the condition bits; `known` maps comparison
+# ids to the outcome a branch on this path has fixed.
+def _neg(v):
+    if v is None:
+        return None
+    if v[0] == "k":
+        return ("k", -1 if v[1] == 0 else 0)
+    return ("s", v[1], not v[2])
+
+
+def _truth(v, known):
+    """True/False if the flag's value is fixed on this path, else None."""
+    if v is None:
+        return None
+    if v[0] == "k":
+        return v[1] == -1
+    t = known.get(v[1])
+    return None if t is None else (t != v[2])
+
+
+def _pair(env, lo):
+    a, b = env.get(lo), env.get(lo + 1)
+    return a if a == b else None
+
+
+def _run_block(b: Block, state: tuple, flags, hits):
+    """Load state and scalar facts at the block's end, and the successors
+    the path can take (with the facts each branch adds)."""
+    env = dict(flags[0]) if flags else {}
+    known = dict(flags[1]) if flags else {}
     for ins in b.insns:
         state = _step(state, ins, hits)
-        if ins.vcc_from:
-            lo, neg = ins.vcc_from
-            v = fl.get(lo)
-            vcc = None if v is None else ((v == 0) if neg else (v == -1))
-        elif "vcc" in ins.text and not ins.op.startswith("s_cbranch"):
-            vcc = None
-        if ins.flag_set:
-            fl[ins.flag_set[0]] = ins.flag_set[1]
-        elif ins.sdef:
-            for lo in list(fl):
-                if lo in ins.sdef or lo + 1 in ins.sdef:
-                    del fl[lo]
-    succ = b.succ
+        e = ins.sc
+        k = e[0] if e else "other"
+        if k == "cmp":
+            env["scc"] = ("s", ins.index, False)
+            known.pop(ins.index, None)  # a new outcome each time it runs
+        elif k == "csel":
+            lo, a, bb = e[1], e[2], e[3]
+            sc = env.get("scc")
+            v = ("k", a) if a == bb else (None if sc is None else (sc if a == -1 else _neg(sc)))
+            env[lo] = env[lo + 1] = v
+        elif k == "mov64":
+            v = ("k", e[3]) if e[3] is not None else _pair(env, e[2])
+            env[e[1]] = env[e[1] + 1] = v
+        elif k == "mov32":
+            env[e[1]] = ("k", e[3]) if e[3] is not None else env.get(e[2])
+        elif k == "xor1":
+            v = _neg(_pair(env, e[2]))
+            env[e[1]] = env[e[1] + 1] = v
+            env["scc"] = None
+        elif k == "vcc":
+            v = _pair(env, e[1])
+            env["vcc"] = _neg(v) if e[2] else v
+            env["scc"] = None
+        elif k == "wlane":
+            env[("l", e[1], e[3])] = env.get(e[2])
+        elif k == "rlane":
+            env[e[1]] = env.get(("l", e[2], e[3]))
+        else:
+            if e and e[1]:
+                env["scc"] = None
+            if e and e[2]:
+                env["vcc"] = None
+            for r in ins.sdef:
+                env.pop(r, None)
+            if e and e[3] != -1:
+                dead = [key for key in env if type(key) is tuple and (e[3] == -2 or key[1] == e[3])]
+                for key in dead:
+                    del env[key]
+    out = []
     last = b.insns[-1] if b.insns else None
-    if last is not None and last.op in ("s_cbranch_vccz", "s_cbranch_vccnz") and vcc is not None:
-        take = (not vcc) if last.op == "s_cbranch_vccz" else vcc
-        nxt = b.taken if take else b.fall
-        succ = [nxt] if nxt is not None else []
-    return state, frozenset(fl.items()), succ
+    cond = None
+    if last is not None and last.op in ("s_cbranch_vccz", "s_cbranch_vccnz"):
+        cond, nz = env.get("vcc"), last.op == "s_cbranch_vccnz"
+    elif last is not None and last.op in ("s_cbranch_scc0", "s_cbranch_scc1"):
+        cond, nz = env.get("scc"), last.op == "s_cbranch_scc1"
+    envf = frozenset((kk, vv) for kk, vv in env.items() if vv is not None)
+    if cond is not None and b.taken is not None:
+        tv = _truth(cond, known)
+        for succ, take in ((b.taken, True), (b.fall, False)):
+            if succ is None:
+                continue
+            want = take if nz else not take  # the value of cond on this edge
+            if tv is not None and tv != want:
+                continue
+            k2 = dict(known)
+            if cond[0] == "s":
+                k2[cond[1]] = want != cond[2]
+            out.append((succ, (envf, frozenset(k2.items()))))
+    else:
+        kf = frozenset(known.items())
+        out = [(s2, (envf, kf)) for s2 in b.succ]
+    return state, out
 
 
-def _meet(f1: frozenset, f2: frozenset) -> frozenset:
-    """Flags known on both paths (same value)."""
-    return f1 & f2
+def _meet(f1, f2):
+    """Facts both paths share."""
+    if not f1 or not f2:
+        return (frozenset(), frozenset())
+    return (f1[0] & f2[0], f1[1] & f2[1])
 
 
-def _add(states: dict, i: int, st: tuple, fl: frozenset) -> bool:
+def _add(states: dict, i: int, st: tuple, fl) -> bool:
     """Add a path state to block i; returns whether the block's set grew.
-
-    The set is kept to _MAX_STATES entries: first states with equal load
-    states are merged (keeping the flags both know), then states with equal
-    flags (joining their load states), then all of them."""
+    Past _MAX_STATES distinct facts the block keeps one state: the facts
+    all paths share and the join of their load states (monotone, so the
+    iteration ends)."""
     cur = states.setdefault(i, {})
     if fl in cur:
         new = join(cur[fl], st)
@@ -263,24 +373,21 @@ def _add(states: dict, i: int, st: tuple, fl: frozenset) -> bool:
             return False
         cur[fl] = new
         return True
-    before = dict(cur)
-    cur[fl] = st
-    if len(cur) > _MAX_STATES:
-        by_loads = {}
+    # covered by a state that knows less and may be loading at least as much
+    for f2, s2 in cur.items():
+        if f2[0] <= fl[0] and f2[1] <= fl[1] and join(s2, st) == s2:
+            return False
+    if len(cur) + 1 > _MAX_STATES:
+        allf, alls = fl, st
         for f, s2 in cur.items():
-            by_loads[s2] = _meet(by_loads[s2], f) if s2 in by_loads else f
-        merged = {}
-        for s2, f in by_loads.items():
-            merged[f] = join(merged[f], s2) if f in merged else s2
-        if len(merged) > _MAX_STATES:
-            allf, alls = None, ()
-            for f, s2 in merged.items():
-                allf = f if allf is None else _meet(allf, f)
-                alls = join(alls, s2)
-            merged = {allf: alls}
-        states[i] = merged
-        cur = merged
-    return cur != before
+            allf = _meet(allf, f)
+            alls = join(alls, s2)
+        if len(cur) == 1 and allf in cur and cur[allf] == alls:
+            return False
+        states[i] = {allf: alls}
+        return True
+    cur[fl] = st
+    return True
 
 
 def scan_function(body: str) -> list:
@@ -291,14 +398,14 @@ def scan_function(body: str) -> list:
     if not blocks:
         return []
     states = {}
-    _add(states, 0, (), frozenset())
+    _add(states, 0, (), ())
     work, queued = [0], {0}
     while work:
         i = work.pop()
         queued.discard(i)
         for fl, st in list(states[i].items()):
-            out, fl2, succ = _run_block(blocks[i], st, fl, None)
-            for s in succ:
+            out, succ = _run_block(blocks[i], st, fl, None)
+            for s, fl2 in succ:
                 if _add(states, s, out, fl2) and s not in queued:
                     work.append(s)
                     queued.add(s)

@@ -150,7 +150,11 @@ def test_generated_kernels_have_no_access_to_outstanding_loads(tmp_path, src):
     assert r.returncode == 0, r.stderr[-2000:]
     bodies = kernel_bodies(out.read_text(), "_ZN3art")
     assert bodies, "no kernels found in the assembly"
-    bad = {name: hits[:3] for name, body in bodies.items() if (hits := scan_function(body))}
+    from concurrent.futures import ProcessPoolExecutor
+    names = sorted(bodies)
+    with ProcessPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as pool:
+        results = list(pool.map(scan_function, [bodies[n] for n in names]))
+    bad = {n: hits[:3] for n, hits in zip(names, results) if hits}
     assert not bad, bad
     # No flat (generic address) memory instruction: a flat load is counted
     # on the vector-memory counter as well, so waiting for one waits for
