@@ -142,10 +142,9 @@ typedef struct {
   int32_t flags;         /* OR of art_flag; must be 0 in full mode           */
   int32_t waves;         /* ART mode with one work item per unit and at most
                             4 query vectors per unit: waves per workgroup,
-                            0 = library's choice, 4 or 8.  The library picks
-                            8 (one workgroup per compute unit) for calls of
-                            at most 256 units and 4 (two per compute unit)
-                            above.  With W waves, W consecutive traversal
+                            0 = library's choice (4: two workgroups per
+                            compute unit), 4 or 8 (one workgroup per compute
+                            unit).  With W waves, W consecutive traversal
                             positions of a unit are in flight at once: a
                             unit loads at most 2 W - 1 blocks past its stop
                             (blocks_issued <= stop_idx + 2 W - 1).  Ignored

@@ -171,18 +171,16 @@ size_t select_ws_bytes(const art_shape& s) {
 
 constexpr int64_t kSelectSortMax = 4096;  // blocks per unit the selection kernel sorts
 
-// Waves per workgroup.  ART mode with one work item per unit and at most 4
-// query vectors per unit: 8 waves (one workgroup per CU, eight positions in
-// flight per unit) when the call has at most one unit per CU, where each
-// unit's own walk sets the time; 4 waves (two workgroups per CU) otherwise.
-// Everything else runs 4 waves.  A caller's art_params.waves overrides the
-// choice for the single-item ART case.
-constexpr int64_t kEightWaveUnits = kComputeUnits;
+// Waves per workgroup: 4 (two workgroups per CU) unless the caller asks
+// for 8 (ART mode, one work item per unit, at most 4 query vectors per
+// unit; one workgroup per CU, eight positions of a unit in flight).  Eight
+// measured slower on MI355X wherever tried: 128 units of 512 blocks 0.447 vs
+// 0.421 ms, 32 units of 1024 kept blocks 0.38 vs 0.34 ms, 512 units of
+// 128-512 blocks 0.42 vs 0.40 ms (the stop rule's chain, not the waves'
+// compute, sets a lone unit's pace).
 int waves_per_item(const art_shape& s, const art_params& p, int max_chunks) {
-  const int64_t units = (int64_t)s.batch * s.num_kv_heads;
   if (p.mode != ART_MODE_ART || max_chunks != 1 || query_vectors(s) > 4) return kWavesPerItem;
-  if (p.waves == 4 || p.waves == 8) return p.waves;
-  return units <= kEightWaveUnits ? 8 : kWavesPerItem;
+  return p.waves == 8 ? 8 : kWavesPerItem;
 }
 
 art::WsLayout layout(const art_shape& s, const art_params& p, int chunk, int max_chunks) {
