@@ -1,6 +1,6 @@
 """Parity helpers: run libart on a workload and compare with the fp64 oracle.
 
-The acceptance rule (per unit = (batch, kv head)):
+The acceptance rule per unit (batch, kv head) is oracle.acceptance's:
   * stop_idx equal to the oracle's, unless the unit is margin-excused: some
     check t <= max(stop_gpu, stop_oracle) has a metric within a relative
     margin of 1e-4 of its threshold (|d / eps - 1| <= 1e-4);
@@ -21,9 +21,7 @@ import numpy as np
 import oracle as orc
 from workloads.device import to_device
 
-REL_L2 = 1e-3
-MAX_ABS = 4e-3
-MARGIN = 1e-4
+from oracle.acceptance import MARGIN, MAX_ABS, REL_L2, unit_agreement  # noqa: F401
 
 
 def log(*a):
@@ -91,45 +89,24 @@ def compare(w, out_gpu, stop_gpu, units=None, mode=1, patience=None, eps_scale=N
         M = q_rows.shape[1]
         out_gpu = out_gpu.reshape(s.batch, M, s.num_kv_heads, s.group, -1).transpose(0, 2, 1, 3, 4).reshape(
             s.batch, s.num_kv_heads * M * s.group, -1)
-    detect_only = bool(flags & orc.FLAG_DETECT_ONLY)
     G = s.group * (1 if q_rows is None else q_rows.shape[1])  # query vectors per unit
     rep = Report()
     for (b, h), r in res.items():
         rep.units += 1
-        sg, so = int(stop_gpu[b, h]), int(r.stop)
-        if sg == so:
-            rep.stop_equal += 1
-        else:
-            hi = max(sg, so)
-            rs = orc.relative_margin(r.d_scale[1:hi], es)
-            rd = orc.relative_margin(r.d_dir[1:hi], ed)
-            if flags & orc.FLAG_NO_SCALE:
-                rs = np.full_like(rs, np.inf)
-            if flags & orc.FLAG_NO_DIR:
-                rd = np.full_like(rd, np.inf)
-            m = np.nanmin(np.minimum(rs, rd)) if hi > 1 else np.inf
-            if m <= MARGIN:
-                rep.excused += 1
-            else:
-                rep.unexcused.append(((b, h), sg, so, float(m)))
-        # a unit with blocks processes at least one; an empty unit none
-        lo = 1 if r.num_traversal > 0 else 0
-        if not (lo <= sg <= r.num_traversal):
+        sg = int(stop_gpu[b, h])
+        a = unit_agreement(r, out_gpu[b, h * G:(h + 1) * G], sg, es, ed, flags)
+        rep.stop_equal += int(a.stop_equal)
+        if a.excused:
+            rep.excused += 1
+        elif not a.stop_equal:
+            rep.unexcused.append(((b, h), sg, int(r.stop), a.margin))
+        if not a.stop_in_range:
             rep.bad_outputs.append(((b, h), "stop out of range", sg))
             continue
-        t_out = r.num_traversal if detect_only else sg
-        ref = r.O[t_out - 1] if t_out > 0 else np.zeros_like(r.out)
-        got = out_gpu[b, h * G:(h + 1) * G]
-        diff = got - ref
-        nrm = np.linalg.norm(ref)
-        rel = np.linalg.norm(diff) / nrm if nrm > 0 else np.linalg.norm(diff)
-        mab = float(np.abs(diff).max()) if diff.size else 0.0
-        if not np.isfinite(rel):
-            rel = np.inf
-        rep.worst_rel_l2 = max(rep.worst_rel_l2, rel)
-        rep.worst_abs = max(rep.worst_abs, mab)
-        if not (rel <= REL_L2 and mab <= MAX_ABS):
-            rep.bad_outputs.append(((b, h), rel, mab))
+        rep.worst_rel_l2 = max(rep.worst_rel_l2, a.rel_l2)
+        rep.worst_abs = max(rep.worst_abs, a.max_abs)
+        if not a.output_ok:
+            rep.bad_outputs.append(((b, h), a.rel_l2, a.max_abs))
     return rep, res
 
 
