@@ -118,18 +118,20 @@ typedef struct {
   int32_t split_blocks;  /* blocks per split-KV chunk; 0 = library's choice,
                             a value >= T' means one chunk per unit.  In ART
                             mode, a value below T' selects ordered split ART
-                            (chunks of min(round4(split_blocks), 32) blocks:
-                            a speculative pass per chunk, a look-back replay
-                            of the stop rule on the predecessor's carry, and
+                            (chunks of min(round4(split_blocks), 16) blocks:
+                            a speculative pass per chunk, the stop rule
+                            resolved by a look-back over the earlier chunks'
+                            published prefixes and patience descriptors, and
                             a recompute of the chunk holding the stop);
                             blocks_issued then counts the speculative and
                             re-read blocks, which vary from call to call.
                             A chunk starts loading only once the chunk 12
-                            places before it has resolved the stop rule, so
-                            a unit loads at most 11 chunks past its stop
+                            places before it has resolved the stop rule, and
+                            stops loading once the unit's stop is published,
+                            so a unit loads at most 11 chunks past its stop
                             chunk plus that chunk's recompute.
                             The library's choice in ART mode: split ART in
-                            16-block chunks when the call has fewer than 64
+                            16-block chunks when the call has fewer than 256
                             units and at most 4 query vectors per unit, one
                             chunk per unit otherwise.  In full mode: chunks
                             of at least 32 blocks, sized so that about 4096

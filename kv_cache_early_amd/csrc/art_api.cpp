@@ -109,27 +109,27 @@ art_status validate(const art_shape* sp, const art_params* pp) {
 //     0.409 ms at 2048, and with 32 units of 1024 kept blocks 0.212 ms at
 //     256 items against 0.280 ms at 1024;
 //   either way at least 32 blocks and a multiple of the wave count;
-//   ART mode: one work item per unit (in-round sequential stopping) when
-//     there are enough units to fill the chip; otherwise chunks of
-//     kSplitArtDefault blocks with look-back (ordered split ART).  A
-//     caller's split_blocks is honoured, rounded up to the wave count and
-//     capped at kSplitArtBlocks (the look-back replay handles at most that
-//     many).
+//   ART mode: one work item per unit (the stop rule's chain over the
+//     positions) when there are enough units to fill the chip; otherwise
+//     chunks of kSplitArtDefault blocks with look-back (ordered split ART).
+//     A caller's split_blocks is honoured, rounded up to the wave count and
+//     capped at kSplitArtBlocks (the look-back handles at most that many).
 constexpr int64_t kTargetItems = 4096;
 constexpr int64_t kComputeUnits = 256;  // MI355X
 constexpr int kWavesPerItem = 4;
-// Fewer units than this (a quarter of the 256 CUs): split ART by default.
-// With so few units one work item per unit leaves most of the chip idle and
-// every unit walks at the latency of its rounds; the chunks' speculative
-// passes run in parallel and only the look-back replay is sequential.
-// Measured on MI355X with 32 units of 1024 kept blocks: 0.43 ms against
-// 1.27 ms (criterion never firing) and 0.255 against 0.55 ms (firing).  At
-// 128 units of 512 blocks split ART wins when the criterion fires (0.46 vs
-// 0.59 ms) and loses when it never does (0.64 vs 0.62 ms); at 128 units of
-// 128-512 blocks it loses when it fires (0.36 vs 0.24 ms).  So the default
-// stays one work item per unit from 64 units on.
-constexpr int64_t kSplitArtUnits = 64;
-constexpr int kSplitArtBlocks = 32;   // longest chunk the look-back replay handles
+// Fewer units than this (the 256 CUs): split ART by default.  With fewer
+// units than compute units, one work item per unit leaves CUs idle and a
+// unit's walk is held to what one CU can stream (about 64 GB/s measured on
+// MI355X); split ART spreads a unit over several CUs, its chunks' passes
+// run in parallel and the stop rule is resolved by a decoupled look-back.
+// Measured on MI355X (one work item per unit / split ART in 16-block
+// chunks): 128 units of 512 blocks 0.394 / 0.249 ms where the criterion
+// fires and 0.448 / 0.441 ms where it never does; 32 units of 1024 kept
+// blocks 0.145 ms split (full mode 0.19 ms); one unit of 512 blocks 0.151
+// / 0.067 ms.  At 512 units of 128-512 blocks one item per unit wins (0.40
+// against 0.57 ms): every CU is busy and the chunks' look-backs only add.
+constexpr int64_t kSplitArtUnits = 256;
+constexpr int kSplitArtBlocks = 16;   // longest chunk the look-back handles
 constexpr int kSplitArtDefault = 16;  // the library's chunk length for split ART
 // Split ART: a chunk starts its speculative pass only once the chunk this
 // many places before it (same unit) has resolved the stop rule.  Measured
@@ -192,14 +192,11 @@ art::WsLayout layout(const art_shape& s, const art_params& p, int chunk, int max
   L.items = round256(sizeof(art::ItemState) * (size_t)std::max<int64_t>(units * max_chunks, 1));
   L.partials = max_chunks > 1 ? round256((size_t)units * max_chunks * G * (d + 2) * sizeof(float)) : 0;
   const bool split_art = max_chunks > 1 && p.mode == ART_MODE_ART;
-  const size_t carry_bytes = d == 128 ? sizeof(art::CarryRec<128>) : sizeof(art::CarryRec<64>);
-  const size_t summary_bytes = d == 128 ? sizeof(art::Summary<128>) : sizeof(art::Summary<64>);
-  const int64_t tmax = std::max<int64_t>(1, max_traversal(s));
+  const size_t carry_bytes = d == 128 ? sizeof(art::ChunkRec<128>) : sizeof(art::ChunkRec<64>);
   L.unit_stop = split_art ? round256((size_t)units * sizeof(int32_t)) : 0;
   L.carries = split_art ? round256((size_t)units * max_chunks * carry_bytes) : 0;
-  L.summaries = split_art ? round256((size_t)units * tmax * summary_bytes) : 0;
   (void)chunk;
-  L.total = L.header + L.items + L.partials + L.unit_stop + L.carries + L.summaries;
+  L.total = L.header + L.items + L.partials + L.unit_stop + L.carries;
   return L;
 }
 
@@ -295,8 +292,6 @@ art_status decode_impl(const art_shape* shape, const art_params* params, const v
   a.unit_stop = L.unit_stop ? reinterpret_cast<int32_t*>(w + off) : nullptr;
   off += L.unit_stop;
   a.carries = L.carries ? static_cast<void*>(w + off) : nullptr;
-  off += L.carries;
-  a.summaries = L.summaries ? static_cast<void*>(w + off) : nullptr;
   a.spin_limit = 1u << 20;  // about a second of polling before ART_ERR_TIMEOUT
   a.spec_depth = kSplitArtDepth;
 

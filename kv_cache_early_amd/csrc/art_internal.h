@@ -36,18 +36,38 @@ struct alignas(16) Summary {
   float ps[D / 4][GS];  // sums on the probe dims relative to m
 };
 
-// Split ART: prefix state of a unit after the last block of one chunk,
-// published for the next chunk (look-back).
+// Split ART: what one chunk of a unit publishes for the chunks after it.
+// Each part is written once and none waits for a later chunk, so a chunk
+// finds its carry and its patience state by looking back over its
+// predecessors' parts instead of waiting for a chain of hand-offs
+// (decoupled look-back).  One state word, written whole by the chunk's
+// thread 0 after the part it announces, says what is there:
+//   bits 0-1   prefix: 0 nothing yet; 1 the aggregate is written; 2 the
+//              inclusive prefix is written too; 3 the unit stopped before
+//              this chunk (nothing else is written)
+//   bit 2      the patience descriptor below is written
+//   bits 3-7   descriptor: checks in the chunk (its positions but the unit's first)
+//   bits 8-12  descriptor: leading stable checks
+//   bits 13-17 descriptor: trailing stable checks
+//   bits 18-22 descriptor: 1 + the blocks of the chunk up to the stop that a
+//              run of `patience` stable checks after its first unstable one
+//              makes (0: none)
+//   bits 32-63 the stop rule's state at the chunk's end: 0 not yet; 1 |
+//              counter << 2 no stop so far; 2 the unit stopped at or before
+//              this chunk's end; 3 | counter << 2 detect-only, a stop
+//              detected at or before this chunk's end
 template <int D>
-struct alignas(16) CarryRec {
-  int32_t flag;        // the stop rule's state at the chunk's end: status | counter << 2, status
-                       // 0 not yet; 1 ready (no stop so far); 2 stopped at or before this chunk's end;
-                       // 3 ready, a stop was detected at or before this chunk's end (detect-only);
-                       // counter = consecutive stable checks at the chunk's end
-  int32_t pflag;       // the prefix below: 0 not yet; 1 ready; 2 the unit stopped at or before this chunk
-  float m[4];          // reference max per head (log2 domain)
-  double l[4];         // prefix mass per head relative to m
-  double p[D / 4][4];  // prefix numerators on the probe dims relative to m
+struct alignas(16) ChunkRec {
+  uint64_t state;
+  uint64_t pad;
+  // aggregate: the chunk's own blocks, relative to their max (log2 domain)
+  float am[4];
+  double al[4];        // mass per query vector
+  double ap[D / 4][4]; // numerators on the probe dims
+  // inclusive prefix: every block of the unit up to the chunk's last
+  float im[4];
+  double il[4];
+  double ip[D / 4][4];
 };
 
 
@@ -85,15 +105,14 @@ struct KernelArgs {
   ItemState* items;    // [max_chunks][units], grid order
   int32_t* unit_stop;  // split ART: [units] traversal count at the stop, 0 while none
   float* partials;     // [units][max_chunks][G][d + 2]  (m, l, acc[d])
-  void* carries;       // split ART: [units][max_chunks] CarryRec<d>
-  void* summaries;     // split ART: [units][max_trav] Summary<d>
+  void* carries;       // split ART: [units][max_chunks] ChunkRec<d>
   uint32_t spin_limit; // look-back polls before ART_ERR_TIMEOUT
-  int32_t spec_depth;  // split ART: chunk k starts once chunk k - spec_depth has published its carry
+  int32_t spec_depth;  // split ART: chunk k starts once chunk k - spec_depth has resolved the stop rule
 };
 
 // Workspace layout for a given shape (bytes, 256-aligned pieces).
 struct WsLayout {
-  size_t header, items, partials, unit_stop, carries, summaries, total;
+  size_t header, items, partials, unit_stop, carries, total;
 };
 
 hipError_t launch(const KernelArgs& a, hipStream_t stream);

@@ -319,6 +319,24 @@ __device__ __forceinline__ void wait_v_tied(u32x4 (&v)[16]) {
                : "memory");
 }
 
+// The same wait, also tying one more register (a dword loaded by gload_sys).
+template <int N>
+__device__ __forceinline__ void wait_v_tied_s(u32x4 (&v)[16], int& w) {
+  asm volatile("s_waitcnt vmcnt(%17)"
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]),
+                 "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]),
+                 "+v"(v[15]), "+v"(w)
+               : "n"(N)
+               : "memory");
+}
+// A dword read at the point of coherence (like ld_sys), issued as inline
+// assembly so that it joins the hand-counted vector-memory waits.
+__device__ __forceinline__ int gload_sys(const int* p) {
+  int r;
+  asm volatile("global_load_dword %0, %1, off sc0 sc1" : "=v"(r) : "v"(p) : "memory");
+  return r;
+}
+
 // Transposing 8-byte LDS read (gfx950): within each 16-lane row, element e of
 // lane i is element i % 4 of what lane 4e + i / 4 of that row addresses.
 __device__ __forceinline__ s16x4 lds_read_tr(const __attribute__((address_space(3))) uint8_t* p) {
@@ -502,21 +520,31 @@ struct alignas(16) RoundLds {
   int ticket;                          // split ART: this workgroup's work item
   int flag;                            // split ART: predecessor's carry flag / early stop
 };
-// Split ART look-back replay state (reuses the V slabs): the chunk's block
-// summaries transposed to [block][head][probe dim], |x|^2 per position and
-// the per-position stability bits.
-constexpr int kSplitMax = 32;  // chunk length the replay handles
+// Split ART: the block summaries of the chunk being walked (pass 0), in
+// the look-back's layout [block][query vector][probe dim]; LDS of their own,
+// written during the walk.
+constexpr int kSplitMax = 16;  // chunk length the look-back handles
+template <int D, int N>
+struct alignas(16) SplitSum {
+  float m[N][4];        // reference max per query vector
+  float l[N][4];        // softmax mass per query vector relative to m
+  float ps[N][4][D / 4];  // sums on the probe dims relative to m
+};
+// Split ART look-back state (reuses the V slabs, below the waves' stash).
 template <int D>
 struct alignas(16) ReplayLds {
-  float m[kSplitMax][4];
-  float l[kSplitMax][4];
-  float ps[kSplitMax][4][D / 4];
-  double stt[kSplitMax + 1];  // stt[j + 1] = |x|^2 at position j; stt[0] from the carry
-  double cdot[kSplitMax][4];  // w_j (carry numerators . block j's probe sums), per head
-  double plast[4][D / 4];     // numerators after the chunk's last block: Q, then the carry out
+  double Q[kSplitMax][4][D / 4];  // the chunk's prefix numerators after each block, on its own maximum
+  double lam[kSplitMax][4];       // the chunk's prefix mass after each block, on the same maximum
+  double pc[4][D / 4];            // the carry's numerators
+  double lc[4];                   // the carry's mass
+  float mc[4];                    // the carry's maximum
+  float ml[4];                    // the chunk's own maximum
+  double stt[kSplitMax + 1];      // stt[j + 1] = |x|^2 at position j; stt[0] from the carry
   int bits[kSplitMax];
-  int stop_local;             // blocks of the chunk up to and including the stop, -1 if none
-  int counter;
+  int stop_local;                 // blocks of the chunk up to and including the stop, -1 if none
+  int lb;                         // look-back: the chunk whose inclusive prefix the carry starts from
+  int found;                      // the stop (or detect-only: the first stop) this chunk found, -1 if none
+  int outcome;                    // 0 the chunk counts; 1 a wait timed out; 2 the unit stopped before it
 };
 template <int G, int D, int W>
 struct alignas(16) EpilogueLds {     // per-wave final state (reuses the V slabs)
@@ -551,12 +579,15 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
   constexpr int NH = G > 4 ? G / 4 : 1;  // query vectors per lane row in the stop rule's layout
   constexpr int NPL = NH * PPC;          // probe values per lane there
   static_assert(ROW == kRowChunks * 16, "rows must be 16 chunks of 16 bytes");
-  __shared__ RoundLds<NPL, NH> R;
+  // the chain's records are not used by split ART, whose block summaries
+  // take LDS of their own instead
+  __shared__ RoundLds<SPLIT ? 1 : NPL, SPLIT ? 1 : NH> R;
+  __shared__ SplitSum<D, SPLIT ? kSplitMax : 1> SS;
   __shared__ alignas(16) uint8_t vbuf[W][kVSlab];
   // the waves' final state is stashed above the replay state, so a split
   // chunk can keep its pass-0 result in LDS while the replay runs
   constexpr int kEpiOff = SPLIT ? 32768 : 0;
-  static_assert(!SPLIT || sizeof(ReplayLds<D>) <= kEpiOff, "replay state must fit below the stash");
+  static_assert(!SPLIT || sizeof(ReplayLds<D>) <= kEpiOff, "look-back state must fit below the stash");
   static_assert(kEpiOff + sizeof(EpilogueLds<G, D, W>) <= sizeof(vbuf), "stash must fit the V slabs");
 
   const int tid = threadIdx.x;
@@ -756,47 +787,36 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
   const __attribute__((address_space(3))) uint8_t* vb =
       (const __attribute__((address_space(3))) uint8_t*)&vbuf[wid][0];
   const uint32_t slab = (uint32_t)(uintptr_t)vb;
-  // V DMA n = 4g + q (tile g, quad q of its 16 tokens): lane (lg, c) carries
-  // token 4n + lg, global chunk c ^ 2lg ^ 8(q & 1) (byte offsets within the
-  // 16-token group of rows, one per q)
-  uint32_t voff[4];
-  {
-    const uint32_t e = (uint32_t)(lg * ROW + ((c ^ (2 * lg)) * 16));
-    voff[0] = e;
-    voff[1] = (e ^ 128u) + 4 * ROW;
-    voff[2] = e + 8 * ROW;
-    voff[3] = (e ^ 128u) + 12 * ROW;
-  }
-  const uint32_t koff = (uint32_t)(c * ROW + lg * 16);  // K: token c of the tile, chunk lg (+4j)
   // K: load j of tile nt -> token 16 nt + c, chunk 4j + lg.  The first load
   // of a block waits for `dep` (the score maximum), so it overwrites the K
   // registers only after the MFMAs that read them have completed.
   // The four loads of tile nt; tile 0's first load waits for `dep`.
   // Before a walk (no MFMA reads the K registers) the first load needs no
   // dependency: `first` drops it.
+  // The lane's offsets are formed at each call from a fresh lane index, so
+  // they are not held in registers across the walk.  Contiguous KV takes one
+  // path for every block: rows clamped to the sequence's last token, which
+  // changes nothing for a full block.
   auto load_k_tile = [&](const BlockAddr& ba, auto ntc, float dep, auto first) {
     constexpr int nt = decltype(ntc)::value;
     constexpr bool kDep = nt == 0 && !decltype(first)::value;
-    if (PAGED || ba.nvalid == kBlk) {
-      const char* base = u.k + (size_t)ba.row[nt] * ROW;
-      if constexpr (kDep)
-        kr[0] = gload16s_after<0>(koff, base, dep);
-      else
-        kr[4 * nt] = gload16s<0>(koff, base);
-      kr[4 * nt + 1] = gload16s<64>(koff, base);
-      kr[4 * nt + 2] = gload16s<128>(koff, base);
-      kr[4 * nt + 3] = gload16s<192>(koff, base);
-    } else {  // last block of a contiguous sequence: rows clamped to the last token
-      const char* base = u.k + (size_t)ba.row[0] * ROW;
-      const uint32_t off = (uint32_t)(min(16 * nt + c, ba.nvalid - 1) * ROW + lg * 16);
-      if constexpr (kDep)
-        kr[0] = gload16s_after<0>(off, base, dep);
-      else
-        kr[4 * nt] = gload16s<0>(off, base);
-      kr[4 * nt + 1] = gload16s<64>(off, base);
-      kr[4 * nt + 2] = gload16s<128>(off, base);
-      kr[4 * nt + 3] = gload16s<192>(off, base);
+    const int fl = fresh_lane(), flg = fl >> 4, fc = fl & 15;
+    const char* base;
+    uint32_t off;
+    if constexpr (PAGED) {
+      base = u.k + (size_t)ba.row[nt] * ROW;
+      off = (uint32_t)(fc * ROW + flg * 16);
+    } else {
+      base = u.k + (size_t)ba.row[0] * ROW;
+      off = (uint32_t)(min(16 * nt + fc, uni(ba.nvalid) - 1) * ROW + flg * 16);
     }
+    if constexpr (kDep)
+      kr[0] = gload16s_after<0>(off, base, dep);
+    else
+      kr[4 * nt] = gload16s<0>(off, base);
+    kr[4 * nt + 1] = gload16s<64>(off, base);
+    kr[4 * nt + 2] = gload16s<128>(off, base);
+    kr[4 * nt + 3] = gload16s<192>(off, base);
   };
   auto load_k_first = [&](const BlockAddr& ba) {
     static_for<0, kTiles>([&](auto ntc) { load_k_tile(ba, ntc, 0.f, std::true_type{}); });
@@ -804,46 +824,54 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
   // V: the 16 DMAs of a block into this wave's slab (DMA n -> bytes 1024 n);
   // group g is DMAs 4g .. 4g + 3 (16-token group g).  The caller has waited
   // for the LDS reads of the previous block (load_v does).
-  auto load_v_group = [&](const BlockAddr& ba, auto gc) {
-    constexpr int g = decltype(gc)::value;
-    if (PAGED || ba.nvalid == kBlk) {
-      const char* base = u.v + (size_t)ba.row[g] * ROW;
-      static_for<0, 4>([&](auto qc) {
-        constexpr int q = decltype(qc)::value;
-        lds_dma16s(voff[q], base, slab + (4 * g + q) * 1024);
+  // V DMA n = 4g + q (tile g, quad q of its 16 tokens): lane (lg, c) carries
+  // token 4n + lg, global chunk c ^ 2lg ^ 8(q & 1).  Paged: byte offsets
+  // within the 16-token group of rows, one per q; contiguous: rows clamped
+  // to the sequence's last token, from the block's first row.
+  auto load_v = [&](const BlockAddr& ba) {
+    wait_lgkm0();  // LDS reads of the previous block have landed
+    const int fl = fresh_lane(), flg = fl >> 4, fc = fl & 15;
+    if constexpr (PAGED) {
+      const uint32_t e = (uint32_t)(flg * ROW + ((fc ^ (2 * flg)) * 16));
+      const uint32_t voff[4] = {e, (e ^ 128u) + 4 * ROW, e + 8 * ROW, (e ^ 128u) + 12 * ROW};
+      static_for<0, kTiles>([&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        const char* base = u.v + (size_t)ba.row[g] * ROW;
+        static_for<0, 4>([&](auto qc) {
+          constexpr int q = decltype(qc)::value;
+          lds_dma16s(voff[q], base, slab + (4 * g + q) * 1024);
+        });
       });
-    } else {  // last block of a contiguous sequence: rows clamped to the last token
+    } else {
       const char* base = u.v + (size_t)ba.row[0] * ROW;
-      static_for<4 * g, 4 * g + 4>([&](auto nc) {
+      const int last = uni(ba.nvalid) - 1;
+      static_for<0, 4 * kTiles>([&](auto nc) {
         constexpr int n = decltype(nc)::value;
-        const uint32_t off = (uint32_t)(min(4 * n + lg, ba.nvalid - 1) * ROW + ((c ^ (2 * lg) ^ (8 * (n & 1))) * 16));
+        const uint32_t off = (uint32_t)(min(4 * n + flg, last) * ROW + ((fc ^ (2 * flg) ^ (8 * (n & 1))) * 16));
         lds_dma16s(off, base, slab + n * 1024);
       });
     }
-  };
-  auto load_v = [&](const BlockAddr& ba) {
-    wait_lgkm0();  // LDS reads of the previous block have landed
-    static_for<0, kTiles>([&](auto gc) { load_v_group(ba, gc); });
     compiler_fence();
   };
   // Transposed V reads (bf16): lane (lg, c) addresses token 4lg + c/4 of a
   // tile, dims 16dt + 4(c%4)..+3, i.e. chunk 2dt + (c%4)/2, half c%2, stored
   // at position (2dt + (c%4)/2) ^ 2(c/4) ^ 8(lg&1) of row c/4 of DMA 4tt + lg.
-  const uint32_t tr_lane = (uint32_t)(lg * 1024 + (c >> 2) * 256 + 8 * (c & 1));
-  const uint32_t tr_x = (uint32_t)(16 * (((c & 3) >> 1) | (2 * (c >> 2)) | (8 * (lg & 1))));
 
   int bad_page = 0;
   int issued = 0;
   int stop = -1;  // traversal blocks processed at the stop (ART mode)
   // Split ART: pass 0 walks the whole chunk speculatively, storing block
-  // summaries; the look-back replay then decides the stop; if it lies inside
-  // the chunk, pass 1 recomputes the chunk's output up to the stop.
-  const bool split = SPLIT && art_mode && !single;
+  // summaries; the look-back then decides the stop; if it lies inside the
+  // chunk, pass 1 recomputes the chunk's output up to the stop.  In a split
+  // launch a unit whose traversal fits one chunk takes the same path (its
+  // look-back finds nothing before it), so the split instantiation carries
+  // no code of the chain below.
+  const bool split = SPLIT && art_mode;
   bool discard = false;  // the unit stopped before this chunk
   int t_stop = t_end;
   // ART mode in one work item per unit: the stop rule runs as a chain over
   // the positions (below)
-  const bool chain = art_mode && !split;
+  const bool chain = !SPLIT && art_mode;
   if (chain) {
     if (tid == 0) {
       R.stop_at = 0;
@@ -855,26 +883,34 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
     __syncthreads();
   }
 
-  // ---- split ART: look-back replay of the stop rule over this chunk -----------
-  // After pass 0 the chunk's block summaries are in the workspace.  Before
-  // the predecessor's carry is needed, thread (j, g, hh) forms the chunk's
-  // own prefix numerators Q_j and Q_{j-1} of head g on half hh of the probe
-  // dims, on the chunk's own maximum Ml, and their products |Q_j|^2 and
-  // Q_j.Q_{j-1}.  Then it waits for the carry (the prefix state P_c, m_c,
-  // l_c after the predecessor's last block, its patience counter and
-  // |x|^2).  On the common maximum M = max(m_c, Ml) the prefix numerators
-  // are P_j = a P_c + b Q_j with a = 2^(m_c - M), b = 2^(Ml - M), so
+  // ---- split ART: the stop rule over this chunk, by decoupled look-back -------
+  // After pass 0 the chunk's block summaries are in the workspace.  Thread
+  // (j, g, hh) forms the chunk's own prefix numerators Q_j and Q_{j-1} of
+  // head g on half hh of the probe dims, on the chunk's own maximum Ml, and
+  // their products |Q_j|^2 and Q_j.Q_{j-1}; the chunk's aggregate (Ml, its
+  // mass, Q after its last block) is published at once.  The carry (the
+  // prefix state P_c, m_c, l_c after the predecessor's last block) is then
+  // the inclusive prefix of the nearest predecessor that has published one,
+  // merged with the aggregates of the chunks after it, so no chunk waits for
+  // its predecessor's own look-back.  On the common maximum M = max(m_c, Ml)
+  // the prefix numerators are P_j = a P_c + b Q_j with a = 2^(m_c - M),
+  // b = 2^(Ml - M), so
   //   |P_j|^2       = a^2 |P_c|^2 + 2ab P_c.Q_j + b^2 |Q_j|^2,
   //   P_j.P_{j-1}   = a^2 |P_c|^2 + ab (P_c.Q_j + P_c.Q_{j-1}) + b^2 Q_j.Q_{j-1},
   // and P_c.Q_j = sum over i <= j of w_i (P_c . ps_i), w_i = 2^(m_i - Ml):
-  // one dot product per block and a prefix sum, the only work left after
-  // the carry arrives.  Eight lanes per position give |x^(t)|^2 and
-  // x^(t).x^(t-1); the patience scan then runs over the positions in order.
-  // Returns the chunk's blocks up to and including the stop, or -1;
-  // publishes this chunk's carry (or the stop) for its successor.
+  // one dot product per block and a prefix sum.  Eight lanes per position
+  // give |x^(t)|^2 and x^(t).x^(t-1), hence every check of the chunk at once.
+  // The patience counter's passage through a chunk depends on the counter
+  // it enters with only through the chunk's leading and trailing stable
+  // checks and the first run of `patience` stable checks after its first
+  // unstable one; the chunk publishes that descriptor, and the counter
+  // entering it is the state of the nearest resolved predecessor carried
+  // through the descriptors of the chunks after it.
+  // Returns the chunk's blocks up to and including the stop, or -1; sets
+  // `discard` when the unit stopped before the chunk.
   // The waves' running state (m, l, output) goes to LDS, where the
   // epilogue merges it; pass-0 results of a split chunk wait there during
-  // the replay.
+  // the look-back.
   auto& E = *reinterpret_cast<EpilogueLds<G, D, W>*>(reinterpret_cast<uint8_t*>(vbuf) + kEpiOff);
   auto stash_waves = [&]() {
     // speculative loads may still be landing in the V slabs and in the K
@@ -901,162 +937,171 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
     __syncthreads();
   };
   int dev_status = item_status;
+  ChunkRec<D>* const recs = SPLIT ? reinterpret_cast<ChunkRec<D>*>(a.carries) + (size_t)unit * a.max_chunks : nullptr;
+  // A chunk that will not count (the unit stopped before it) says so in its
+  // state word, so that chunks looking back past it stop there too.
+  constexpr uint64_t kDiscardWord = 3ull | 4ull | (2ull << 32);
+  auto publish_discard = [&]() {
+    if (tid == 0) st_sys(&recs[chunk].state, kDiscardWord);
+  };
+  // The stop (blocks of a chunk up to and including it) that a chunk starting
+  // at traversal position tb makes when the patience counter enters it at c,
+  // from its descriptor; -1 if none.  A counter that reaches `patience` within
+  // the leading stable checks stops at the (patience - c)-th check (the
+  // unit's first position has no check).
+  auto chunk_stop = [&](int tb, int lead, int run_stop, int cin) -> int {
+    if (cin < a.patience && cin + lead >= a.patience) return (tb == 0 ? 1 : 0) + (a.patience - cin);
+    return run_stop;
+  };
   auto split_replay = [&]() -> int {
     ReplayLds<D>& RL = *reinterpret_cast<ReplayLds<D>*>(&vbuf[0][0]);
-    CarryRec<D>* carries = reinterpret_cast<CarryRec<D>*>(a.carries) + (size_t)unit * a.max_chunks;
+    ChunkRec<D>& co = recs[chunk];
     const int Cn = t_end - t_begin;
-    wait_vm<0>();     // speculative loads have landed in the V slabs
-    __syncthreads();  // this chunk's summaries (written by its own waves) are visible
-    const Summary<D>* gsum = reinterpret_cast<const Summary<D>*>(a.summaries) + ((size_t)unit * a.max_trav + t_begin);
-    {  // stage [j][q][g] -> [j][g][q]; all loads of a thread are issued before its stores
-      constexpr int kPer = kSplitMax * D / NT;
-      float v[kPer];
-#pragma unroll
-      for (int r = 0; r < kPer; ++r) {
-        const int i = tid + r * NT;
-        v[r] = i < Cn * D ? gsum[i / D].ps[(i % D) >> 2][i & 3] : 0.f;
-      }
-#pragma unroll
-      for (int r = 0; r < kPer; ++r) {
-        const int i = tid + r * NT;
-        if (i < Cn * D) RL.ps[i / D][i & 3][(i % D) >> 2] = v[r];
-      }
-      if (tid < Cn * 4) {
-        const float mv = gsum[tid >> 2].m[tid & 3], lv = gsum[tid >> 2].l[tid & 3];
-        RL.m[tid >> 2][tid & 3] = mv;
-        RL.l[tid >> 2][tid & 3] = lv;
-      }
-    }
-    __syncthreads();
-    // ---- the chunk's own prefix state (needs no carry) ------------------------
-    constexpr int NQ = D / 8;  // probe dims per thread
-    const int j = tid >> 3, g = (tid >> 1) & 3, hh = tid & 1;
-    const bool on = j < Cn && g < G;
-    const int jj = j < Cn ? j : 0, gg = g < G ? g : 0;
-    float Ml = -INFINITY;
-    for (int i = 0; i < Cn; ++i) Ml = fmaxf(Ml, RL.m[i][gg]);
-    // Q_{j-1} = Q_j - w_j ps_j (fp64; the rounding is far below the tests' margins)
-    double Q[NQ];
-#pragma unroll
-    for (int qq = 0; qq < NQ; ++qq) Q[qq] = 0.0;
-    double Lam = 0.0;
-    for (int i = 0; i <= jj; ++i) {
-      const double wi = (double)__builtin_amdgcn_exp2f(RL.m[i][gg] - Ml);
-      Lam = fma((double)RL.l[i][gg], wi, Lam);
-#pragma unroll
-      for (int qq = 0; qq < NQ; ++qq) Q[qq] = fma((double)RL.ps[i][gg][hh * NQ + qq], wi, Q[qq]);
-    }
-    const double wj = (double)__builtin_amdgcn_exp2f(RL.m[jj][gg] - Ml);
-    const double Lamp = jj == 0 ? 0.0 : fma(-(double)RL.l[jj][gg], wj, Lam);
-    double S1 = 0.0, S2 = 0.0;
-#pragma unroll
-    for (int qq = 0; qq < NQ; ++qq) {
-      const double qp = jj == 0 ? 0.0 : fma(-(double)RL.ps[jj][gg][hh * NQ + qq], wj, Q[qq]);
-      S1 = fma(Q[qq], Q[qq], S1);
-      S2 = fma(Q[qq], qp, S2);
-    }
-    S1 += dpp<kQx1>(S1);  // the two halves of the probe dims
-    S2 += dpp<kQx1>(S2);
-    if (on && j == Cn - 1) {  // read back by the same thread only
-#pragma unroll
-      for (int qq = 0; qq < NQ; ++qq) RL.plast[g][hh * NQ + qq] = Q[qq];
-    }
-    // ---- the predecessor's prefix ------------------------------------------------
-    // Two hand-offs per chunk boundary.  The prefix state after the
-    // predecessor's last block (numerators, max, mass on the probe dims)
-    // depends on no stop decision, so each chunk publishes its own as soon
-    // as its predecessor's has arrived (pflag), and only then runs its checks
-    // and waits for the stop rule's state (status and patience counter in
-    // one word, flag).  The prefix thus moves down the chain without waiting
-    // for any chunk's scan.
-    if (tid == 0) {
-      int f = 1;
-      if (chunk > 0) {
-        uint32_t polls = 0;
-        for (;;) {
-          f = ld_sys(&carries[chunk - 1].pflag);
-          if (f != 0) break;
-          if (++polls >= a.spin_limit) {
-            f = -1;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(8);
+    constexpr int NP = D / 4;  // probe dims
+    constexpr int NQ = D / 8;  // probe dims per thread in the per-position layout (half of them)
+    uint64_t word = 0;         // this chunk's state word (thread 0 writes it)
+    wait_vm<0>();     // speculative loads have landed (the V slabs are reused below)
+    __syncthreads();  // the block summaries (LDS, written by every wave) are complete
+    // ---- the chunk's own prefix: a scan over its blocks per (query vector,
+    // probe dim), on the chunk's own maximum; published as its aggregate at
+    // once (it needs no other chunk)
+    if (tid < 4 * NP + 4) {
+      const int g = tid < 4 * NP ? tid / NP : tid - 4 * NP;
+      const int gg = g < G ? g : 0;
+      float Ml = -INFINITY;
+      for (int i = 0; i < Cn; ++i) Ml = fmaxf(Ml, SS.m[i][gg]);
+      double acc = 0.0;
+      if (tid < 4 * NP) {
+        const int q = tid % NP;
+        for (int i = 0; i < Cn; ++i) {
+          acc = fma((double)SS.ps[i][g][q], (double)__builtin_amdgcn_exp2f(SS.m[i][gg] - Ml), acc);
+          RL.Q[i][g][q] = acc;
         }
+        st_sys(&co.ap[q][g], acc);
+        if (q == 0) {
+          st_sys(&co.am[g], Ml);
+          RL.ml[g] = Ml;
+        }
+      } else {
+        for (int i = 0; i < Cn; ++i) {
+          acc = fma((double)SS.l[i][gg], (double)__builtin_amdgcn_exp2f(SS.m[i][gg] - Ml), acc);
+          RL.lam[i][g] = acc;
+        }
+        st_sys(&co.al[g], acc);
       }
-      R.flag = f;
+    }
+    wait_vm<0>();  // the aggregate's stores are acknowledged
+    __syncthreads();
+    if (tid == 0) {
+      word = 1;
+      st_sys(&co.state, word);
+    }
+    // ---- the carry: look back to the nearest inclusive prefix ---------------------
+    // Lane i of wave 0 watches chunk - 1 - i; before chunk 0 is the unit's
+    // start (an empty prefix).  The wait ends once some predecessor has its
+    // inclusive prefix written and every chunk after it its aggregate; a
+    // predecessor that knows the unit stopped before it ends it at once.
+    if (wid == 0) {
+      int lo;
+      for (uint32_t polls = 0;; ++polls) {
+        const int jc = chunk - 1 - lane;
+        const int s = jc >= 0 ? (int)(ld_sys(&recs[jc].state) & 3ull) : 2;
+        const uint64_t inc = __ballot(s == 2), agg = __ballot(s >= 1), gone = __ballot(s == 3);
+        if (gone) {
+          lo = -3;
+          break;
+        }
+        const int i0 = inc ? __builtin_ctzll(inc) : 64;
+        const uint64_t below = i0 >= 64 ? ~0ull : ((1ull << i0) - 1);
+        if (i0 < 64 && (agg & below) == below) {
+          lo = chunk - 1 - i0;
+          break;
+        }
+        if (polls >= a.spin_limit) {
+          lo = -4;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(4);
+      }
+      if (lane == 0) RL.lb = lo;
     }
     __syncthreads();
-    const int pf = uni(R.flag);
-    if (pf == 2) {  // the unit stopped at or before the predecessor's end
+    const int lb = uni(RL.lb);
+    if (lb < -1) {  // the unit stopped before this chunk (or the wait timed out)
+      if (lb == -4) dev_status = ART_ERR_TIMEOUT;
       discard = true;
-      if (tid == 0) {
-        st_sys(&carries[chunk].pflag, 2);
-        st_sys(&carries[chunk].flag, 2);
-      }
+      publish_discard();
       return -1;
     }
     {  // from here on, indices (and the LDS addresses built on them) are recomputed
     const int tid = wid * kWave + fresh_lane();
     const int lane = tid & (kWave - 1);
+    // The records to merge, in order: the inclusive prefix of chunk lb (none
+    // for lb = -1), then the aggregates of chunks lb + 1 .. chunk - 1.
+    // Thread (query vector, probe dim) folds its element of every record
+    // into a running (maximum, sum), and four threads do the same for the
+    // mass; the loads of successive records do not wait for one another.
+    {
+      const int n_rec = (lb >= 0 ? 1 : 0) + (chunk - 1 - lb);
+      if (tid < 4 * NP + 4) {
+        const bool mass = tid >= 4 * NP;
+        const int g = mass ? tid - 4 * NP : tid / NP, q = mass ? 0 : tid % NP, gg = g < G ? g : 0;
+        float Mr = -INFINITY;
+        double Sr = 0.0;
+#pragma unroll 4
+        for (int r = 0; r < n_rec; ++r) {
+          const bool inc = lb >= 0 && r == 0;
+          const ChunkRec<D>& rc = recs[inc ? lb : lb + r + (lb >= 0 ? 0 : 1)];
+          const float m2 = ld_sys(inc ? &rc.im[gg] : &rc.am[gg]);
+          const double v2 = mass ? ld_sys(inc ? &rc.il[gg] : &rc.al[gg]) : ld_sys(inc ? &rc.ip[q][gg] : &rc.ap[q][gg]);
+          const float Mn = fmaxf(Mr, m2);
+          Sr = fma((double)__builtin_amdgcn_exp2f(Mr - Mn), Sr, (double)__builtin_amdgcn_exp2f(m2 - Mn) * v2);
+          Mr = Mn;
+        }
+        if (mass) {
+          RL.mc[g] = Mr;
+          RL.lc[g] = Sr;
+        } else {
+          RL.pc[g][q] = Sr;
+        }
+      }
+      __syncthreads();
+    }
+    // ---- every check of the chunk at once ------------------------------------------
+    const bool has_carry = chunk > 0;
     const int j = tid >> 3, g = (tid >> 1) & 3, hh = tid & 1;
     const bool on = j < Cn && g < G;
     const int jj = j < Cn ? j : 0, gg = g < G ? g : 0;
-    if (pf < 0) dev_status = ART_ERR_TIMEOUT;
-    const bool has_carry = chunk > 0 && pf == 1;
-    // The prefix is loaded unconditionally (chunk 0 reads its own, still
-    // unwritten record: valid workspace memory) and selected afterwards, so
-    // the loads go out together instead of one branch at a time.
-    const CarryRec<D>* cin = &carries[chunk > 0 ? chunk - 1 : 0];
-    double Pc[NQ];
-#pragma unroll
-    for (int qq = 0; qq < NQ; ++qq) Pc[qq] = ld_sys(&cin->p[hh * NQ + qq][gg]);
-    const float Mc_in = ld_sys(&cin->m[gg]);
-    const double Lc_in = ld_sys(&cin->l[gg]);
-    const float Mc = has_carry ? Mc_in : -INFINITY;
-    const double Lc = has_carry ? Lc_in : 0.0;
-#pragma unroll
-    for (int qq = 0; qq < NQ; ++qq) Pc[qq] = has_carry ? Pc[qq] : 0.0;
+    const float Mc = RL.mc[gg], Ml = RL.ml[gg];
+    const double Lc = RL.lc[gg];
     const float Ms = fmaxf(Mc, Ml);
     const double ca = has_carry ? (double)__builtin_amdgcn_exp2f(Mc - Ms) : 0.0;
     const double cb = (double)__builtin_amdgcn_exp2f(Ml - Ms);
+    const double Lam = RL.lam[jj][gg], Lamp = jj == 0 ? 0.0 : RL.lam[jj - 1][gg];
     const double L = fma(ca, Lc, cb * Lam), Lp = fma(ca, Lc, cb * Lamp);
-    // ---- this chunk's prefix, published at once: P after its last block on
-    // the common maximum, and the mass there
-    CarryRec<D>& co = carries[chunk];
-    if (on && j == Cn - 1) {
-#pragma unroll
-      for (int qq = 0; qq < NQ; ++qq)
-        st_sys(&co.p[hh * NQ + qq][g], fma(ca, Pc[qq], cb * RL.plast[g][hh * NQ + qq]));
-      if (hh == 0) {
-        st_sys(&co.m[g], Ms);
-        st_sys(&co.l[g], L);
-      }
-    }
-    wait_vm<0>();  // the prefix's stores are acknowledged
-    __syncthreads();
-    if (tid == 0) st_sys(&co.pflag, 1);
-    double cpc = 0.0, cj = 0.0;
+    double S1 = 0.0, S2 = 0.0, cpc = 0.0, Dj = 0.0, Dp = 0.0;
 #pragma unroll
     for (int qq = 0; qq < NQ; ++qq) {
-      cpc = fma(Pc[qq], Pc[qq], cpc);
-      cj = fma(Pc[qq], (double)RL.ps[jj][gg][hh * NQ + qq], cj);
+      const double qj = RL.Q[jj][gg][hh * NQ + qq];
+      const double qp = jj == 0 ? 0.0 : RL.Q[jj - 1][gg][hh * NQ + qq];
+      const double pc = RL.pc[gg][hh * NQ + qq];
+      S1 = fma(qj, qj, S1);
+      S2 = fma(qj, qp, S2);
+      cpc = fma(pc, pc, cpc);
+      Dj = fma(pc, qj, Dj);
+      Dp = fma(pc, qp, Dp);
     }
+    S1 += dpp<kQx1>(S1);  // the two halves of the probe dims
+    S2 += dpp<kQx1>(S2);
     cpc += dpp<kQx1>(cpc);
-    cj += dpp<kQx1>(cj);
-    // |x|^2 at the predecessor's last position, from its prefix
+    Dj += dpp<kQx1>(Dj);
+    Dp += dpp<kQx1>(Dp);
+    // |x|^2 at the predecessor's last position, from the carry
     const double iLc = Lc > 0.0 ? recip_d(Lc) : 0.0;
     double s0 = g < G ? cpc * (iLc * iLc) : 0.0;
     s0 += dpp<kQx2>(s0);  // heads g and g ^ 1
     s0 += dpp<kHalfMirror>(s0);  // heads {0, 1} and {2, 3}
     if (tid == 0) RL.stt[0] = has_carry ? s0 : 0.0;
-    if (on && hh == 0) RL.cdot[j][g] = wj * cj;
-    __syncthreads();
-    double Dj = 0.0, Dp = 0.0;  // P_c.Q_j and P_c.Q_{j-1}
-    for (int i = 0; i < Cn; ++i) {
-      const double ci = RL.cdot[i][gg];
-      Dj += i <= jj ? ci : 0.0;
-      Dp += i < jj ? ci : 0.0;
-    }
     const double A = ca * ca * cpc + 2.0 * ca * cb * Dj + cb * cb * S1;
     const double X = ca * ca * cpc + ca * cb * (Dj + Dp) + cb * cb * S2;
     const double iL = recip_d(L), iLp = Lp > 0.0 ? recip_d(Lp) : 0.0;
@@ -1069,70 +1114,132 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
     __syncthreads();
     if (on && (tid & 7) == 0) {
       const double spr = RL.stt[j];
-      const bool exists = t_begin + j + 1 >= 2;  // a check exists from the second block on
+      const bool exists = t_begin + j >= 1;  // a check exists from the second traversal block on
       const bool stable = (spr > 0.0) & (stt > 0.0) & crit.scale_ok(spr, stt) & crit.dir_ok(spr, stt, stp);
       RL.bits[j] = (exists ? 2 : 0) | (stable ? 1 : 0);
     }
-    // ---- the predecessor's stop-rule state ----------------------------------------
-    if (tid == 0) {
-      int f = 1;  // chunk 0: no stop so far, counter 0
-      if (chunk > 0) {
-        uint32_t polls = 0;
-        for (;;) {
-          f = ld_sys(&carries[chunk - 1].flag);
-          if (f != 0) break;
-          if (++polls >= a.spin_limit) {
-            f = -1;
+    // ---- this chunk's inclusive prefix: P after its last block on the common
+    // maximum, and the mass there
+    if (tid < 4 * NP) {
+      const int g2 = tid / NP, q = tid % NP, g3 = g2 < G ? g2 : 0;
+      const float Mc2 = RL.mc[g3], Ml2 = RL.ml[g3], Ms2 = fmaxf(Mc2, Ml2);
+      const double ca2 = has_carry ? (double)__builtin_amdgcn_exp2f(Mc2 - Ms2) : 0.0;
+      const double cb2 = (double)__builtin_amdgcn_exp2f(Ml2 - Ms2);
+      st_sys(&co.ip[q][g2], fma(ca2, RL.pc[g3][q], cb2 * RL.Q[Cn - 1][g3][q]));
+      if (q == 0) {
+        st_sys(&co.im[g2], Ms2);
+        st_sys(&co.il[g2], fma(ca2, RL.lc[g3], cb2 * RL.lam[Cn - 1][g3]));
+      }
+    }
+    wait_vm<0>();  // every wave's share of the inclusive prefix is acknowledged before the flag
+    __syncthreads();
+    if (wid == 0) {
+      // ---- the chunk's patience descriptor (needs no other chunk's stop rule) ------
+      const int bt = lane < Cn ? RL.bits[lane] : 0;
+      const uint64_t ex = __ballot((bt & 2) != 0), sb = __ballot(bt == 3);
+      const uint64_t fail = ex & ~sb;
+      const int n_chk = __popcll(ex);
+      int lead = n_chk, trail = n_chk, run_stop = -1;
+      if (fail) {
+        const int f0 = __builtin_ctzll(fail), f1 = 63 - __builtin_clzll(fail);
+        lead = __popcll(ex & ((1ull << f0) - 1));
+        trail = __popcll(ex & ~((2ull << f1) - 1));
+        int cnt = 0;  // a run after the first unstable check
+        for (int i = f0 + 1; i < Cn; ++i) {
+          if (!((ex >> i) & 1)) continue;
+          cnt = ((sb >> i) & 1) ? cnt + 1 : 0;
+          if (cnt >= a.patience) {
+            run_stop = i + 1;
             break;
           }
-          __builtin_amdgcn_s_sleep(8);
         }
       }
-      R.flag = f;
-    }
-    __syncthreads();
-    const int sf = uni(R.flag);
-    if (sf < 0) dev_status = ART_ERR_TIMEOUT;
-    if (sf > 0 && (sf & 3) == 2) {  // the unit stopped at or before the predecessor's end
-      discard = true;
-      if (tid == 0) st_sys(&co.flag, 2);
-      return -1;
-    }
-    const bool upstream = sf > 0 && (sf & 3) == 3;  // detect-only: a stop was already detected
-    const int counter_in = sf > 0 ? (sf >> 2) : 0;
-    if (wid == 0) {  // patience scan in order, on two ballots (Cn <= 32 positions)
-      const int bt = lane < Cn ? RL.bits[lane] : 0;
-      const uint64_t ex = __ballot((bt & 2) != 0), sb = __ballot((bt & 1) != 0);
-      int cnt = counter_in, st = -1;
-      for (int i = 0; i < Cn; ++i) {
-        if (!((ex >> i) & 1)) continue;
-        cnt = ((sb >> i) & 1) ? cnt + 1 : 0;
-        if (cnt >= a.patience) {
-          st = i + 1;
+      word = 2ull | 4ull | ((uint64_t)n_chk << 3) | ((uint64_t)lead << 8) | ((uint64_t)trail << 13) |
+             ((uint64_t)(run_stop + 1) << 18);
+      if (lane == 0) st_sys(&co.state, word);
+      // ---- the stop rule's state entering the chunk ------------------------------------
+      // The nearest predecessor whose state is resolved, carried through the
+      // descriptors of the chunks after it (each of them must be written).
+      // One word per chunk holds both.
+      if (lane == 0) RL.found = -1;
+      int lo = -1;
+      uint64_t wv = 0;
+      for (uint32_t polls = 0;; ++polls) {
+        const int jc = chunk - 1 - lane;
+        wv = jc >= 0 ? ld_sys(&recs[jc].state) : ((1ull << 32) | 4ull);  // before chunk 0: no stop, counter 0
+        const uint64_t rb = __ballot((wv >> 32) != 0), db = __ballot(((wv >> 2) & 1) != 0);
+        const int i0 = rb ? __builtin_ctzll(rb) : 64;
+        const uint64_t below = i0 >= 64 ? ~0ull : ((1ull << i0) - 1);
+        if (i0 < 64 && (db & below) == below) {
+          lo = i0;
           break;
+        }
+        if (polls >= a.spin_limit) {
+          lo = -4;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(4);
+      }
+      int state;  // as the state word's high half, for this chunk's end
+      int own = -1;
+      int outcome = 0;  // 0 this chunk counts; 1 the wait timed out; 2 the unit stopped before this chunk
+      if (lo < 0) {
+        state = 2;  // timed out: end here, and every chunk after
+        outcome = 1;
+      } else {
+        const int base = __builtin_amdgcn_readlane((int)(wv >> 32), lo);
+        const int dw = (int)(wv & 0xffffffffu);
+        bool stopped = (base & 3) == 2, det = (base & 3) == 3;
+        int cnt = base >> 2;
+        for (int i = lo - 1; i >= 0 && !stopped; --i) {  // oldest first
+          const int d = __builtin_amdgcn_readlane(dw, i);
+          const int n = (d >> 3) & 31, ld = (d >> 8) & 31, tr = (d >> 13) & 31, rs = ((d >> 18) & 31) - 1;
+          if (!det && chunk_stop((chunk - 1 - i) * a.chunk_blocks, ld, rs, cnt) >= 0) {
+            if (detect_only)
+              det = true;
+            else
+              stopped = true;
+          }
+          cnt = ld == n ? cnt + n : tr;
+        }
+        if (stopped) {
+          state = 2;
+          outcome = 2;
+        } else {
+          own = det ? -1 : chunk_stop(t_begin, lead, run_stop, cnt);
+          const int cout = lead == n_chk ? cnt + n_chk : trail;
+          if (own >= 0 && !detect_only) {
+            state = 2;
+          } else {
+            state = ((det || own >= 0) ? 3 : 1) | (cout << 2);
+          }
+          if (own >= 0 && lane == 0) {
+            st_sys(&a.unit_stop[unit], t_begin + own);
+            RL.found = t_begin + own;  // a unit in one chunk reports it itself
+          }
+          if (detect_only) own = -1;
         }
       }
       if (lane == 0) {
-        RL.stop_local = st;
-        RL.counter = cnt;
+        RL.stop_local = own;
+        RL.outcome = outcome;
       }
+      wait_vm<0>();  // the stop's store is acknowledged before the state
+      word = outcome != 0 ? kDiscardWord : ((word & 0xffffffffull) | ((uint64_t)(uint32_t)state << 32));
+      if (lane == 0) st_sys(&co.state, word);
     }
     __syncthreads();
     const int st = uni(RL.stop_local);
-    const bool stop_here = st >= 0 && !upstream;
-    // With no stop here, or in detect-only mode (which never terminates), the
-    // successor goes on from this chunk's counter.
-    if (st < 0 || detect_only) {
-      if (tid == 0) {
-        if (stop_here) st_sys(&a.unit_stop[unit], t_begin + st);  // detect-only: the first stop
-        st_sys(&co.flag, ((stop_here || upstream) ? 3 : 1) | (RL.counter << 2));
-      }
-    } else if (tid == 0) {
-      st_sys(&a.unit_stop[unit], t_begin + st);
-      st_sys(&co.flag, 2);
-    }
+    const int outcome = uni(RL.outcome);
+    const int found = uni(RL.found);
+    if (found >= 0) stop = found;
     __syncthreads();  // the V slabs are free again
-    return detect_only ? -1 : st;
+    if (outcome == 1) dev_status = ART_ERR_TIMEOUT;
+    if (outcome != 0) {  // the unit stopped before this chunk
+      discard = true;
+      return -1;
+    }
+    return st;
     }
   };
 
@@ -1142,26 +1249,21 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
     const int us = uni(R.flag);
     if (us > 0 && us <= t_begin) {
       discard = true;
-      if (tid == 0) {
-        CarryRec<D>& own = (reinterpret_cast<CarryRec<D>*>(a.carries) + (size_t)unit * a.max_chunks)[chunk];
-        st_sys(&own.pflag, 2);
-        st_sys(&own.flag, 2);
-      }
+      publish_discard();
     }
   }
   // Bounded speculation: a chunk walks only once the chunk spec_depth places
-  // before it has published its carry (or the unit's stop).  That chunk holds
-  // a smaller ticket, so it is running or done, and the wait ends.  Without
-  // the bound every chunk handed out walks at once, and with few units
-  // nearly all of them lie past the stop.
+  // before it has resolved the stop rule (or the unit's stop).  That chunk
+  // holds a smaller ticket, so it is running or done, and the wait ends.
+  // Without the bound every chunk handed out walks at once, and with few
+  // units nearly all of them lie past the stop.
   if (split && !discard && a.spec_depth > 0 && chunk >= a.spec_depth) {
-    CarryRec<D>* const uc = reinterpret_cast<CarryRec<D>*>(a.carries) + (size_t)unit * a.max_chunks;
     __syncthreads();  // every wave has read R.flag above
     if (tid == 0) {
       int f;
       uint32_t polls = 0;
       for (;;) {
-        f = ld_sys(&uc[chunk - a.spec_depth].flag);
+        f = (int)(ld_sys(&recs[chunk - a.spec_depth].state) >> 32);
         if (f != 0) break;
         if (++polls >= a.spin_limit) {
           f = -1;
@@ -1174,12 +1276,9 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
     __syncthreads();
     const int f = uni(R.flag);
     if (f < 0) dev_status = ART_ERR_TIMEOUT;
-    if (f > 0 && (f & 3) == 2 && !detect_only) {  // the unit stopped at or before that chunk's end
+    if ((f < 0 || (f & 3) == 2) && !detect_only) {  // the unit stopped at or before that chunk's end
       discard = true;
-      if (tid == 0) {
-        st_sys(&uc[chunk].pflag, 2);
-        st_sys(&uc[chunk].flag, 2);
-      }
+      publish_discard();
     }
   }
   bool stashed = false;
@@ -1216,6 +1315,9 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
     int counter, detected;
   };
   auto chain_wait = [&](int t, LinkIn& in) -> bool {
+    if constexpr (SPLIT) {
+      return false;
+    } else {
     const int par = (t - 1) & 1;
     for (uint32_t polls = 0;; ++polls) {
       const int q = uni(lds_get(R.head[par].seq));
@@ -1242,15 +1344,17 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
     in.counter = lds_get(R.head[par].counter);
     in.detected = lds_get(R.head[par].detected);
     return true;
-  };
-  for (int pass = 0; pass < 2 && !discard; ++pass) {
-    if (pass == 1) {
-      m_c = -INFINITY;
-      l_c = 0.f;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+  };
+  // The walk over positions t_begin + wid, then every W, up to t_stop.
+  // Split ART walks a chunk twice when its stop lies inside it: pass 0
+  // speculatively over the whole chunk (publishing block summaries), pass 1
+  // up to the stop.  The two passes are separate inlined copies.
+  auto walk = [&](auto passc) __attribute__((always_inline)) {
+    constexpr int pass = decltype(passc)::value;
     int t = t_begin + wid;
+    // split ART, pass 0: the unit's stop as read one block before (see below)
+    int us_seen = 0;
     BlockAddr cur;
     if (t < t_stop) {
       cur = block_addr4<ROW, PAGED>(u, uni(block_at(u, a.order, t)), bad_page);
@@ -1271,7 +1375,17 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
 
       const int nvalid = cur.nvalid;
       // ---- scores S^T[token][head] = k_token . q_head --------------------------
-      wait_v_tied<kLoads>(kr);  // this block's K (its 16 V DMAs were issued after it)
+      if constexpr (SPLIT && pass == 0) {
+        // this block's K, and the unit's stop read with the previous block
+        // (issued before that block's V DMAs, so it has landed with this K)
+        wait_v_tied_s<kLoads>(kr, us_seen);
+        // a chunk that found the unit's stop lies in an earlier chunk (only
+        // the chunk holding the stop writes it): the rest of this chunk is
+        // past the stop
+        if (!detect_only && uni(us_seen) > 0) break;
+      } else {
+        wait_v_tied<kLoads>(kr);  // this block's K (its 16 V DMAs were issued after it)
+      }
       f32x4 S[kTiles];
       static_for<0, kTiles>([&](auto ntc) {
         constexpr int nt = decltype(ntc)::value;
@@ -1347,9 +1461,14 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
             pl[jp][2 * hh + 1] = pk_bf16(S[nt][2] - bf16_lo(w1), S[nt][3] - bf16_hi(w1));
           }
         // B operand of (tile pair jp, dim tile dt): two transposed reads,
-        // tokens of tile 2jp then tile 2jp+1, dims 16dt + c
+        // tokens of tile 2jp then tile 2jp+1, dims 16dt + c.  The lane's
+        // offsets are formed here from a fresh lane index, so their eight
+        // variants are not held in registers across the walk.
+        const int fl = fresh_lane(), flg = fl >> 4, fc = fl & 15;
+        const uint32_t trl = (uint32_t)(flg * 1024 + (fc >> 2) * 256 + 8 * (fc & 1));
+        const uint32_t trx = (uint32_t)(16 * (((fc & 3) >> 1) | (2 * (fc >> 2)) | (8 * (flg & 1))));
         auto read_b = [&](int jp, int dt, bool mask) -> bf16x8 {
-          const auto* pv = vb + tr_lane + (((uint32_t)(32 * dt)) ^ tr_x);
+          const auto* pv = vb + trl + (((uint32_t)(32 * dt)) ^ trx);
           s16x4 v0 = lds_read_tr(pv + (2 * jp) * 4096);
           s16x4 v1 = lds_read_tr(pv + (2 * jp + 1) * 4096);
           if (mask) {
@@ -1406,16 +1525,23 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
           }
       }
 
-      if (split && pass == 0) {
-        // split ART: the block summary goes to the workspace for the replay
-        Summary<D>* gs = reinterpret_cast<Summary<D>*>(a.summaries) + ((size_t)unit * a.max_trav + t);
-        if (lane < 16 && (c & 3) == 0) {
+      if constexpr (SPLIT) {
+        if (split && pass == 0) {
+          // split ART: the block summary goes to LDS for the look-back; probe
+          // dim 4 dt + c / 4 of query vector r is register r of bacc[dt] in
+          // lane c (c % 4 == 0, c < 16)
+          const int jl = t - t_begin;
+          if (lane < 16 && (c & 3) == 0) {
+            float* sp = &SS.ps[jl][0][c >> 2];  // fixed offsets from here on
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) *(f32x4*)&gs->ps[4 * dt + (c >> 2)][0] = bacc[dt];
-        }
-        if (lane < G) {
-          gs->m[lane] = m_new;
-          gs->l[lane] = lblk;
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) sp[r * (D / 4) + 4 * dt] = bacc[dt][r];
+          }
+          if (lane < G) {
+            SS.m[jl][lane] = m_new;
+            SS.l[jl][lane] = lblk;
+          }
         }
       }
       // ---- (ART mode) the block's summary, read back in the stop rule's layout ----
@@ -1456,10 +1582,12 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
       }
       // V of the next block: after this block's LDS reads (load_v waits for
       // them, and in ART mode for the summary's round trip)
+      if constexpr (SPLIT && pass == 0)  // every iteration, whatever the path: the waits count it
+        us_seen = gload_sys(split ? a.unit_stop + unit : a.context_lens);
       load_v(nxt);
 
       bool commit = true, last = false;
-      if (chain) {
+      if constexpr (!SPLIT) if (chain) {  // (split ART has no chain)
         // ---- the prefix state after position t - 1 ------------------------------
         float Mp[NH];
         double Lp[NH], P[NPL];
@@ -1576,14 +1704,28 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
       if (last) break;
       cur = nxt;
     }
-    if (!split || pass == 1) break;
-    stash_waves();
-    stashed = true;
-    const int stop_local = split_replay();
-    if (discard || stop_local < 0 || stop_local == t_end - t_begin) break;
-    t_stop = t_begin + stop_local;  // recompute the blocks up to the stop
-    stashed = false;
+  };
+  if (!discard) {
+    walk(std::integral_constant<int, 0>{});
+    if (split) {
+      stash_waves();
+      stashed = true;
+      const int stop_local = split_replay();
+      if (!discard && stop_local >= 0 && stop_local < t_end - t_begin) {
+        t_stop = t_begin + stop_local;  // recompute the blocks up to the stop
+        stashed = false;
+        m_c = -INFINITY;
+        l_c = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        walk(std::integral_constant<int, 1>{});
+      }
+    }
   }
+  // Every load of the walk has landed before anything below reuses its
+  // registers, on every path out of the loop (stash_waves waits as well, but
+  // only where it runs).
+  wait_v_tied<0>(kr);
   if (!stashed) stash_waves();
   if (chain) {  // every wave has left the walk (stash_waves ends on a barrier)
     const int sa = uni(R.stop_at), dd = uni(R.detected);
@@ -1771,8 +1913,7 @@ __global__ void art_split_init_kernel(KernelArgs a) {
   if (i == 0) a.ws->ticket = 0;
   if (i < n_units) a.unit_stop[i] = 0;
   if (i < n_units * a.max_chunks) {
-    reinterpret_cast<CarryRec<D>*>(a.carries)[i].flag = 0;
-    reinterpret_cast<CarryRec<D>*>(a.carries)[i].pflag = 0;
+    reinterpret_cast<ChunkRec<D>*>(a.carries)[i].state = 0;
   }
 }
 

@@ -73,7 +73,7 @@ def _scalar_effect(op: str, text: str, ops: list) -> tuple:
     ("cmp",) a comparison (a new SCC symbol); ("csel", lo, a, b); ("mov64",
     lo, src_lo or None, const); ("mov32", dst, src or None, const); ("xor1",
     dst_lo, src_lo); ("vcc", lo, negate); ("wlane", vgpr, sreg, lane);
-    ("rlane", sreg, vgpr, lane); else ("other", clobbers_scc, clobbers_vcc,
+    ("rlane", sreg, vgpr, lane); ("vccmov", src_lo or None, const); ("vccself", negate); else ("other", clobbers_scc, clobbers_vcc,
     vgpr written or -1)."""
     if re.match(r"^s_(?:cmp|bitcmp)", op):
         return ("cmp",)
@@ -84,6 +84,10 @@ def _scalar_effect(op: str, text: str, ops: list) -> tuple:
     if m:
         return ("mov64", int(m.group(1)), None if m.group(2) is None else int(m.group(2)),
                 None if m.group(3) is None else int(m.group(3)))
+    m = re.match(r"^s_mov_b64 vcc, (?:s\[(\d+):\d+\]|(-1|0))$", text)
+    if m:
+        return ("vccmov", None if m.group(1) is None else int(m.group(1)),
+                None if m.group(2) is None else int(m.group(2)))
     m = re.match(r"^s_mov_b32 s(\d+), (?:s(\d+)|(-1|0))$", text)
     if m:
         return ("mov32", int(m.group(1)), None if m.group(2) is None else int(m.group(2)),
@@ -94,6 +98,11 @@ def _scalar_effect(op: str, text: str, ops: list) -> tuple:
     m = re.match(r"^s_(and|andn2)_b64 vcc, exec, s\[(\d+):\d+\]$", text)
     if m:
         return ("vcc", int(m.group(2)), m.group(1) == "andn2")
+    # the same on vcc itself (a branch on a flag the compiler already folded
+    # into vcc); exec is taken as non-zero, as on any path where a lane runs
+    m = re.match(r"^s_(and|andn2)_b64 vcc, exec, vcc$", text)
+    if m:
+        return ("vccself", m.group(1) == "andn2")
     m = re.match(r"^v_writelane_b32 v(\d+), s(\d+), (\d+)$", text)
     if m:
         return ("wlane", int(m.group(1)), int(m.group(2)), int(m.group(3)))
@@ -312,6 +321,12 @@ def _run_block(b: Block, state: tuple, flags, hits):
         elif k == "vcc":
             v = _pair(env, e[1])
             env["vcc"] = _neg(v) if e[2] else v
+            env["scc"] = None
+        elif k == "vccmov":
+            env["vcc"] = ("k", e[2]) if e[2] is not None else _pair(env, e[1])
+        elif k == "vccself":
+            v = env.get("vcc")
+            env["vcc"] = _neg(v) if e[1] else v
             env["scc"] = None
         elif k == "wlane":
             env[("l", e[1], e[3])] = env.get(e[2])

@@ -181,6 +181,19 @@ def test_full_mode_default_decomposition(batch, expect):
             assert full(0) != full(other)
 
 
+@pytest.mark.parametrize("batch,split", [(16, True), (31, True), (32, False), (64, False)])
+def test_art_mode_default_decomposition(batch, split):
+    """ART mode: split ART in 16-block chunks below 256 units (fewer units
+    than compute units), one work item per unit from 256 on.  The workspace
+    size shows the choice: it equals the size for that decomposition given
+    explicitly."""
+    s = good_shape(batch=batch, num_q_heads=32, num_kv_heads=8, max_pages=2048, num_pages=8192)  # 512 blocks
+    ws = lambda sb: art.workspace_size(s, good_params(split_blocks=sb))
+    assert ws(16) != ws(10 ** 6)
+    assert ws(0) == (ws(16) if split else ws(10 ** 6))
+    assert ws(32) == ws(16)  # chunks are capped at 16 blocks
+
+
 # ---------------------------------------------------------------------------
 # block selection entry points: host-side rejections (nothing is enqueued)
 # ---------------------------------------------------------------------------

@@ -13,7 +13,7 @@ from workloads import config, make_workload, scaled
 
 pytestmark = pytest.mark.gpu
 
-SPLIT_MAX = 32  # longest split-ART chunk
+SPLIT_MAX = 16  # longest split-ART chunk
 SPEC_DEPTH = 12  # split ART: chunks a unit may walk ahead of its resolved stop rule
 
 
@@ -40,7 +40,7 @@ def check(w, mode=1, tag="", **kw):
     assert rep.ok(), (rep.unexcused[:5], rep.bad_outputs[:5])
     assert rep.excused <= EXCUSED_MAX(rep.units), str(rep)
     Tp = w.traversal_lengths()
-    # split ART may re-read up to one chunk (32 blocks) to recompute the stop chunk
+    # split ART may re-read up to one chunk (16 blocks) to recompute the stop chunk
     assert np.all(issued >= stop) and np.all(issued <= Tp + SPLIT_MAX), "blocks_issued out of range"
     return out, stop, issued, rep
 
