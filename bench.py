@@ -45,8 +45,13 @@ Other modes (no timing line):
         decomposition: full mode, then ART under generator readings A and
         B (cfg4 at patience 1, 2 and 4); one markdown row per measurement
         on stderr and a JSON object on stdout
-  --summarize-pmc FETCH_DIR WRITE_DIR   turn two rocprofv3 --pmc runs of
-        `bench.py --only art --copy-mib N ...` into the counter summary
+  --profile-set   every profile case (cfg1..cfg5 in full and ART mode, the
+        patience sweep, importance-first selection, a lone unit, a copy
+        kernel) in one process, a marker kernel before each case, for
+        rocprofv3 runs; prints a manifest line
+  --summarize-set LOG TRACE_DIR [PMC_DIR ...]   per-case kernel times,
+        algorithmic GB/s, copy-calibrated HBM traffic and other counters of
+        such runs, into OUT.md and OUT.json
   --summarize-trace TRACE_DIR BENCH_LOG  turn a rocprofv3 --kernel-trace
         --stats run into a markdown summary next to the events timing
 """
@@ -70,7 +75,7 @@ HBM_PEAK_GBS = 8000.0
 BLOCK = 64
 KERNEL_SOURCES = ("kv_cache_early_amd/csrc/art_kernels.hip", "kv_cache_early_amd/csrc/art_internal.h",
                   "kv_cache_early_amd/csrc/art_api.cpp")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "art_decode_kernel_cfg3B_art_pmc.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "art_kernels_all_configs.json")
 WORKLOAD = ("cfg3 large-batch paged decode: B=64, Hq=32, Hkv=8, d=128, ctx U[8192,32768], page 16 shuffled, "
             "block 64, eps (2e-3, 2e-4), patience 3, recent-first")
 
@@ -93,8 +98,12 @@ def parse():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run an elementwise copy of this many MiB `steps` times (counter calibration)")
     ap.add_argument("--table", action="store_true", help="measure every configuration (no timing line)")
-    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_LOG"))
+    ap.add_argument("--profile-set", action="store_true",
+                    help="run every profile case in one process, a marker kernel before each (no timing line)")
+    ap.add_argument("--cases", default="", help="comma-separated profile cases (default: all)")
+    ap.add_argument("--summarize-set", nargs="+", metavar="PATH",
+                    help="LOG TRACE_DIR [PMC_DIR ...] of a --profile-set run; writes OUT.md and OUT.json")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
     ap.add_argument("--out", default="", help="summary output path")
     return ap.parse_args()
@@ -483,8 +492,9 @@ def cpu_baseline(w, n_units, stop_gpu, out_gpu, kv_bytes, mode=1):
                                  "rel-L2 <= 1e-3, max-abs <= 4e-3"))
 
 
-def traffic_from_summary():
-    """HBM bytes per launch from the committed counter summary, if it still matches the sources."""
+def traffic_from_summary(tag):
+    """HBM bytes per launch of profile case `tag` from the committed counter
+    summary, if it was taken on the current kernel sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -492,7 +502,10 @@ def traffic_from_summary():
         return None
     if t.get("source_sha256") != source_hash():
         return None
-    return t.get("traffic_bytes_per_launch")
+    for c in t.get("cases", []):
+        if c.get("tag") == tag:
+            return c.get("traffic_bytes_per_launch")
+    return None
 
 
 # ---------------------------------------------------------------------------
@@ -520,32 +533,6 @@ def _per_dispatch(rows, counter, name_pred):
     if not per:
         raise SystemExit(f"no {counter} rows for the kernel")
     return float(np.mean(list(per.values()))), len(per)
-
-
-def summarize_pmc(args):
-    fetch_rows = _counter_rows(args.summarize_pmc[0])
-    write_rows = _counter_rows(args.summarize_pmc[1])
-    is_art = lambda n: "art_decode_kernel" in n
-    is_copy = lambda n: "elementwise" in n.lower() and "mul" in n.lower() or "MulFunctor" in n
-    f_art, n1 = _per_dispatch(fetch_rows, "FETCH_SIZE", is_art)
-    w_art, n2 = _per_dispatch(write_rows, "WRITE_SIZE", is_art)
-    f_cp, n3 = _per_dispatch(fetch_rows, "FETCH_SIZE", is_copy)
-    w_cp, n4 = _per_dispatch(write_rows, "WRITE_SIZE", is_copy)
-    copy_bytes = args.copy_mib * (1 << 20)
-    fs = copy_bytes / (f_cp * 1024.0)
-    ws = copy_bytes / (w_cp * 1024.0)
-    traffic = f_art * 1024.0 * fs + w_art * 1024.0 * ws
-    mode = "full mode" if args.only == "full" else "ART mode"
-    out = dict(kernel="art::art_decode_kernel<bf16, G=4, paged>", workload=WORKLOAD + f", generator B, {mode}",
-               fetch_kib_per_dispatch=f_art, write_kib_per_dispatch=w_art, dispatches=[n1, n2],
-               copy_kernel="elementwise y = x * 1 (torch), fp32", copy_bytes_each_way=copy_bytes,
-               copy_fetch_kib=f_cp, copy_write_kib=w_cp, copy_dispatches=[n3, n4],
-               fetch_scale=fs, write_scale=ws, traffic_bytes_per_launch=traffic,
-               source_sha256=source_hash(), commands=args.command)
-    path = args.out or TRAFFIC_FILE
-    with open(path, "w") as f:
-        json.dump(out, f, indent=1)
-    print(json.dumps(out))
 
 
 def summarize_trace(args):
@@ -590,6 +577,274 @@ def summarize_trace(args):
            "sum's 4-byte output; __amd_rocclr_copyBuffer entries are host-device copies of inputs and results."]
     with open(args.out, "w") as f:
         f.write("\n".join(md) + "\n")
+    print("\n".join(md))
+
+
+# ---------------------------------------------------------------------------
+# profile set: every configuration in one process, cases split by markers
+# ---------------------------------------------------------------------------
+# (tag, config, generator reading, mode 0 full / 1 ART, patience or None, spec overrides, kind)
+PROFILE_CASES = (
+    ("cfg1-full", 1, "A", 0, None, {}, "decode"),
+    ("cfg1-A", 1, "A", 1, None, {}, "decode"),
+    ("cfg1-B", 1, "B", 1, None, {}, "decode"),
+    ("cfg2-full", 2, "A", 0, None, {}, "decode"),
+    ("cfg2-A", 2, "A", 1, None, {}, "decode"),
+    ("cfg2-B", 2, "B", 1, None, {}, "decode"),
+    ("cfg3-full", 3, "A", 0, None, {}, "decode"),
+    ("cfg3-A", 3, "A", 1, None, {}, "decode"),
+    ("cfg3-B", 3, "B", 1, None, {}, "decode"),
+    ("cfg3-B-importance", 3, "B", 1, None, {}, "select"),
+    ("cfg4-full", 4, "A", 0, None, {}, "decode"),
+    ("cfg4-A-p2", 4, "A", 1, 2, {}, "decode"),
+    ("cfg4-B-p1", 4, "B", 1, 1, {}, "decode"),
+    ("cfg4-B-p2", 4, "B", 1, 2, {}, "decode"),
+    ("cfg4-B-p4", 4, "B", 1, 4, {}, "decode"),
+    ("cfg5-full", 5, "A", 0, None, {}, "decode"),
+    ("cfg5-A", 5, "A", 1, None, {}, "decode"),
+    ("cfg5-B", 5, "B", 1, None, {}, "decode"),
+    ("lone-B", 2, "B", 1, None, dict(batch=1, num_q_heads=4, num_kv_heads=1), "decode"),
+)
+MARKER_KERNEL = "spin_kernel"  # torch.cuda._sleep's kernel: one before each case
+
+
+def _marker():
+    import torch
+    torch.cuda._sleep(1000)
+    torch.cuda.synchronize()
+
+
+def profile_set(args):
+    """Run the profile cases in one process (for rocprofv3 runs): a marker
+    kernel, then the case's calls (1 + warmup + steps, the last `steps` timed
+    with the caches evicted before each); prints one JSON manifest line."""
+    import dataclasses
+
+    import torch
+    from kv_cache_early_amd import ART_ORDER_GIVEN, ART_SELECT_IMPORTANCE, ArtDecoder
+    from workloads import config, make_workload
+    from workloads.device import to_device
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    torch.cuda.set_device(0)
+    dec = ArtDecoder()
+    want = set(args.cases.split(",")) if args.cases else None
+    cases = [c for c in PROFILE_CASES if want is None or c[0] in want]
+    if want is not None and len(cases) != len(want):
+        raise SystemExit(f"unknown cases: {sorted(want - {c[0] for c in cases})}")
+    manifest, key, w, dev = [], None, None, None
+    for tag, n, reading, mode, patience, over, kind in cases:
+        k = (n, reading, tuple(sorted(over.items())))
+        if k != key:
+            del w, dev
+            torch.cuda.empty_cache()
+            w = make_workload(config(n, reading, **over))
+            dev = to_device(w)
+            key = k
+        base = w.spec
+        if patience is not None:
+            w.spec = dataclasses.replace(base, patience=patience)
+        print(f"[profile] {tag}", file=sys.stderr, flush=True)
+        _marker()
+        rec = dict(tag=tag, workload=w.spec.name, reading=reading, mode="full" if mode == 0 else "ART",
+                   patience=w.spec.patience, kind=kind, calls=1 + args.warmup + args.steps, steps=args.steps)
+        if kind == "select":
+            s = w.spec
+            mp = int(dev.block_table.shape[1])
+            rec["calls_block_means"] = rec["calls_select"] = 1 + args.steps
+            mms, means = time_call(lambda: dec.block_means(dev.k, dev.context_lens, num_q_heads=s.num_q_heads,
+                                                           dtype=dev.dtype_code, page_size=dev.page_size,
+                                                           block_table=dev.block_table), args.steps,
+                                   not args.no_flush)
+            sms, (kb, kc) = time_call(lambda: dec.select_blocks(dev.q, means, dev.context_lens,
+                                                                dtype=dev.dtype_code, keep_frac=1.0, sink=0,
+                                                                recent=0, order=ART_SELECT_IMPORTANCE,
+                                                                page_size=dev.page_size, max_pages=mp),
+                                      args.steps, not args.no_flush)
+            k_bytes = int(w.context_lens.astype(np.int64).sum()) * s.num_kv_heads * s.head_dim * 2
+            rec.update(block_means_ms=mms, select_ms=sms, block_means_bytes=k_bytes
+                       + s.batch * s.num_kv_heads * int(w.num_blocks.max()) * s.head_dim * 4)
+            dv = dataclasses.replace(dev, kept_blocks=kb, kept_count=kc)
+            r, t, _ = measure(dec, w, mode, args, dev=dv, order=ART_ORDER_GIVEN)
+            del dv, means, kb, kc
+        else:
+            r, t, _ = measure(dec, w, mode, args, dev=dev)
+        if dec.device_error() != 0:
+            raise RuntimeError(f"device error in {tag}")
+        rec.update(ms=r["ms"], bytes_algorithmic=int(r["bytes_algorithmic"]), bytes_loaded=int(r["bytes_loaded"]),
+                   pct_blocks_skipped=r["pct_blocks_skipped"], wasted_frac=r["wasted_frac"],
+                   units=int(w.spec.batch * w.spec.num_kv_heads), blocks_traversal=int(w.traversal_lengths().sum()),
+                   blocks_stop=int(t["stop"].sum()), blocks_issued=int(t["issued"].sum()))
+        manifest.append(rec)
+        w.spec = base
+        print(f"[profile] {tag}: {r['ms'] * 1e3:.1f} us, skipped {r['pct_blocks_skipped']:.3f}", file=sys.stderr,
+              flush=True)
+    if args.copy_mib:
+        _marker()
+        cp = copy_leg(args.copy_mib, args.steps)
+        manifest.append(dict(tag="copy", kind="copy", calls=1 + args.steps, steps=args.steps, ms=cp["ms"],
+                             copy_bytes_each_way=args.copy_mib * (1 << 20)))
+    print(json.dumps({"profile_set": manifest, "steps": args.steps, "warmup": args.warmup,
+                      "source_sha256": source_hash()}), flush=True)
+
+
+def _dispatches(rows, time_key):
+    """Group per-dispatch rows into cases, split at the marker kernel."""
+    by = {}
+    for r in rows:
+        key = int(r.get("Dispatch_Id") or r.get("Correlation_Id"))
+        by.setdefault(key, dict(name=r["Kernel_Name"], order=int(r[time_key]) if time_key else key, rows=[]))
+        by[key]["rows"].append(r)
+    seq = sorted(by.values(), key=lambda x: x["order"])
+    cases, cur = [], None
+    for d in seq:
+        if MARKER_KERNEL in d["name"]:
+            cur = []
+            cases.append(cur)
+        elif cur is not None:
+            cur.append(d)
+    return cases
+
+
+_FAMILIES = (("art_decode_kernel", "decode"), ("art_combine_kernel", "combine"),
+             ("block_means_kernel", "block_means"), ("select_kernel", "select"))
+
+
+def _family(name):
+    for pat, fam in _FAMILIES:
+        if pat in name:
+            return fam
+    if "MulFunctor" in name or ("elementwise" in name.lower() and "mul" in name.lower()):
+        return "copy"
+    return None
+
+
+def _timed(case_disp, rec, fam):
+    """The timed dispatches of one kernel family in a case: its last `steps`."""
+    ds = [d for d in case_disp if _family(d["name"]) == fam]
+    return ds[-rec["steps"]:] if ds else []
+
+
+def summarize_set(args):
+    """Markdown + JSON summary of `bench.py --profile-set` under rocprofv3:
+    argument 1 the run's log (its last JSON line is the manifest), argument 2
+    a --kernel-trace directory, then any --pmc directories."""
+    man_log, trace_dir, *pmc_dirs = args.summarize_set
+    man = None
+    with open(man_log) as f:
+        for l in f:
+            if l.startswith("{") and '"profile_set"' in l:
+                man = json.loads(l)
+    if man is None:
+        raise SystemExit(f"no manifest line in {man_log}")
+    recs = man["profile_set"]
+    trace = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not trace:
+        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
+    with open(trace[0]) as f:
+        tcases = _dispatches(list(csv.DictReader(f)), "Start_Timestamp")
+    if len(tcases) != len(recs):
+        raise SystemExit(f"{len(tcases)} marked cases in the trace, {len(recs)} in the manifest")
+    counters = {}  # (case index, family, counter) -> mean per dispatch
+    for d in pmc_dirs:
+        pcases = _dispatches(_counter_rows(d), None)
+        if len(pcases) != len(recs):
+            raise SystemExit(f"{len(pcases)} marked cases in {d}, {len(recs)} in the manifest")
+        for i, (rec, cd) in enumerate(zip(recs, pcases)):
+            for fam in ("decode", "combine", "block_means", "select", "copy"):
+                ds = _timed(cd, rec, fam)
+                if not ds:
+                    continue
+                names = {r["Counter_Name"] for dd in ds for r in dd["rows"]}
+                for c in names:
+                    vals = [sum(float(r["Counter_Value"]) for r in dd["rows"] if r["Counter_Name"] == c) for dd in ds]
+                    counters[(i, fam, c)] = float(np.mean(vals))
+    copy_i = next((i for i, r in enumerate(recs) if r["kind"] == "copy"), None)
+    fs = ws = None
+    if copy_i is not None and (copy_i, "copy", "FETCH_SIZE") in counters and (copy_i, "copy", "WRITE_SIZE") in counters:
+        cb = recs[copy_i]["copy_bytes_each_way"]
+        fs = cb / (counters[(copy_i, "copy", "FETCH_SIZE")] * 1024.0)
+        ws = cb / (counters[(copy_i, "copy", "WRITE_SIZE")] * 1024.0)
+    out = dict(source_sha256=man["source_sha256"], commands=args.command, steps=man["steps"],
+               warmup=man["warmup"], fetch_scale=fs, write_scale=ws, cases=[])
+    md = ["# rocprofv3: ART decode kernels over every configuration", "",
+          "Each case: one untimed call, the warmup calls, then the timed calls, each after an untimed 1 GiB "
+          "cache-evicting read. Kernel durations are the kernel-trace averages of the timed calls. "
+          "`alg GB/s` is the algorithmic bytes (stop_idx x block bytes + per-unit q, out, stop and page-table "
+          "bytes) per launch over that duration; `traffic` is FETCH_SIZE + WRITE_SIZE per launch scaled by what "
+          "the same counters read for a copy kernel of known size.", "",
+          "Commands (repository root):", "", "```", args.command, "```", ""]
+    if fs is not None:
+        md += [f"Copy calibration: FETCH_SIZE x {fs:.4f}, WRITE_SIZE x {ws:.4f} (bytes per KiB counted / 1024).", ""]
+    md += ["| case | workload | mode | p | decode us (trace) | events us | alg GB/s | frac of 8 TB/s | "
+           "traffic MB | alg MB | skipped | wasted | other kernels us |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    extra_counter_rows = []
+    for i, (rec, cd) in enumerate(zip(recs, tcases)):
+        if rec["kind"] == "copy":
+            ds = _timed(cd, rec, "copy")
+            dur = float(np.mean([(int(d["rows"][0]["End_Timestamp"]) - int(d["rows"][0]["Start_Timestamp"])) / 1e3
+                                 for d in ds]))
+            out["cases"].append(dict(tag="copy", kernel_us=dur, bytes_each_way=rec["copy_bytes_each_way"]))
+            md.append(f"| copy | y = x * 1, {rec['copy_bytes_each_way'] >> 20} MiB | - | - | {dur:.1f} | "
+                      f"{rec['ms'] * 1e3:.1f} | {2 * rec['copy_bytes_each_way'] / dur / 1e3:.0f} | "
+                      f"{2 * rec['copy_bytes_each_way'] / dur / 1e3 / HBM_PEAK_GBS:.3f} | - | - | - | - | - |")
+            continue
+        fam_us = {}
+        for fam in ("decode", "combine", "block_means", "select"):
+            ds = _timed(cd, rec, fam)
+            if ds:
+                fam_us[fam] = float(np.mean([(int(d["rows"][0]["End_Timestamp"])
+                                              - int(d["rows"][0]["Start_Timestamp"])) / 1e3 for d in ds]))
+        dec_us = fam_us["decode"]
+        alg = rec["bytes_algorithmic"]
+        traffic = None
+        if fs is not None and (i, "decode", "FETCH_SIZE") in counters and (i, "decode", "WRITE_SIZE") in counters:
+            traffic = counters[(i, "decode", "FETCH_SIZE")] * 1024.0 * fs + counters[(i, "decode", "WRITE_SIZE")] * 1024.0 * ws
+        kern_name = next(d["name"] for d in cd if _family(d["name"]) == "decode")
+        c = dict(tag=rec["tag"], workload=rec["workload"], mode=rec["mode"], patience=rec["patience"],
+                 kernel=kern_name, decode_kernel_us=dec_us, events_us=rec["ms"] * 1e3, bytes_algorithmic=alg,
+                 bytes_loaded=rec["bytes_loaded"], gbs_algorithmic=alg / dec_us / 1e3,
+                 frac_of_peak=alg / dec_us / 1e3 / HBM_PEAK_GBS, traffic_bytes_per_launch=traffic,
+                 pct_blocks_skipped=rec["pct_blocks_skipped"], wasted_frac=rec["wasted_frac"],
+                 other_kernels_us={k: v for k, v in fam_us.items() if k != "decode"})
+        if rec["kind"] == "select":
+            c.update(block_means_bytes=rec["block_means_bytes"],
+                     block_means_gbs=rec["block_means_bytes"] / fam_us["block_means"] / 1e3)
+            for fam in ("block_means", "select"):
+                if fs is not None and (i, fam, "FETCH_SIZE") in counters and (i, fam, "WRITE_SIZE") in counters:
+                    c[f"{fam}_traffic_bytes"] = (counters[(i, fam, "FETCH_SIZE")] * 1024.0 * fs
+                                                 + counters[(i, fam, "WRITE_SIZE")] * 1024.0 * ws)
+        sq = {cn: v for (j, fam, cn), v in counters.items() if j == i and fam == "decode"
+              and cn not in ("FETCH_SIZE", "WRITE_SIZE")}
+        if sq:
+            c["counters_per_dispatch"] = sq
+            extra_counter_rows.append((rec["tag"], sq))
+        out["cases"].append(c)
+        others = ", ".join(f"{k} {v:.1f}" for k, v in c["other_kernels_us"].items()) or "-"
+        md.append(f"| {rec['tag']} | {rec['workload']} | {rec['mode']} | {rec['patience']} | {dec_us:.1f} | "
+                  f"{rec['ms'] * 1e3:.1f} | {c['gbs_algorithmic']:.0f} | {c['frac_of_peak']:.3f} | "
+                  f"{'-' if traffic is None else f'{traffic / 1e6:.1f}'} | {alg / 1e6:.1f} | "
+                  f"{100 * rec['pct_blocks_skipped']:.1f}% | {100 * rec['wasted_frac']:.1f}% | {others} |")
+    md += ["", "Decode kernel instance per case:", ""]
+    md += [f"- {c['tag']}: `{c['kernel']}`" for c in out["cases"] if "kernel" in c]
+    sel = [c for c in out["cases"] if "block_means_gbs" in c]
+    for c in sel:
+        md += ["", f"Block means ({c['tag']}): {c['other_kernels_us']['block_means']:.1f} us, "
+                   f"{c['block_means_bytes'] / 1e6:.1f} MB algorithmic (every key once + the means), "
+                   f"{c['block_means_gbs']:.0f} GB/s; select: {c['other_kernels_us']['select']:.1f} us"
+               + (f"; traffic block means {c['block_means_traffic_bytes'] / 1e6:.1f} MB, select "
+                  f"{c['select_traffic_bytes'] / 1e6:.1f} MB" if "select_traffic_bytes" in c else "")]
+    if extra_counter_rows:
+        names = sorted({k for _, sq in extra_counter_rows for k in sq})
+        md += ["", "## Other counters, decode kernel, mean per dispatch", "",
+               "| case | " + " | ".join(names) + " |", "|---" * (len(names) + 1) + "|"]
+        for tag, sq in extra_counter_rows:
+            md.append(f"| {tag} | " + " | ".join(f"{sq[n]:.4g}" if n in sq else "-" for n in names) + " |")
+    with open(args.out + ".md", "w") as f:
+        f.write("\n".join(md) + "\n")
+    with open(args.out + ".json", "w") as f:
+        json.dump(out, f, indent=1)
     print("\n".join(md))
 
 
@@ -641,10 +896,12 @@ def main():
     WAVES = args.waves
     if args.table:
         return config_table(args)
-    if args.summarize_pmc:
-        return summarize_pmc(args)
     if args.summarize_trace:
         return summarize_trace(args)
+    if args.summarize_set:
+        return summarize_set(args)
+    if args.profile_set:
+        return profile_set(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this build runs on one GPU; ART units are independent, so --gpus > 1 "
                                    "would shard (batch, kv head) units across devices with no exchange "
@@ -704,7 +961,7 @@ def main():
             print(f"[bench] importance-first: {extra['importance_first']}", file=sys.stderr, flush=True)
             extra["multi_row"] = multi_row_report(dec, dev, w, args)
             print(f"[bench] multi-row: {extra['multi_row']}", file=sys.stderr, flush=True)
-    traffic = traffic_from_summary() if head_mode == 1 else None
+    traffic = traffic_from_summary(f"cfg3-{args.reading}" if head_mode == 1 else "cfg3-full")
     roof = dict(bound="hbm", achieved=round(head["gbs_algorithmic"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(head["gbs_algorithmic"] / HBM_PEAK_GBS, 4),
                 traffic=None if traffic is None else round(traffic),
