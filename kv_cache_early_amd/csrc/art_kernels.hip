@@ -977,36 +977,42 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
           acc = fma((double)SS.ps[i][g][q], (double)__builtin_amdgcn_exp2f(SS.m[i][gg] - Ml), acc);
           RL.Q[i][g][q] = acc;
         }
-        st_sys(&co.ap[q][g], acc);
-        if (q == 0) {
-          st_sys(&co.am[g], Ml);
-          RL.ml[g] = Ml;
-        }
+        if (q == 0) RL.ml[g] = Ml;
       } else {
         for (int i = 0; i < Cn; ++i) {
           acc = fma((double)SS.l[i][gg], (double)__builtin_amdgcn_exp2f(SS.m[i][gg] - Ml), acc);
           RL.lam[i][g] = acc;
         }
-        st_sys(&co.al[g], acc);
       }
     }
-    wait_vm<0>();  // the aggregate's stores are acknowledged
     __syncthreads();
-    if (tid == 0) {
-      word = 1;
-      st_sys(&co.state, word);
-    }
     // ---- the carry: look back to the nearest inclusive prefix ---------------------
-    // Lane i of wave 0 watches chunk - 1 - i; before chunk 0 is the unit's
-    // start (an empty prefix).  The wait ends once some predecessor has its
-    // inclusive prefix written and every chunk after it its aggregate; a
-    // predecessor that knows the unit stopped before it ends it at once.
+    // Wave 0 publishes the aggregate (its stores alone, so that its own
+    // wait covers them) and raises its flag once the first poll has
+    // returned, without holding the other waves.  Lane i of wave 0 watches
+    // chunk - 1 - i; before chunk 0 is the unit's start (an empty prefix).
+    // The wait ends once some predecessor has its inclusive prefix written
+    // and every chunk after it its aggregate; a predecessor that knows the
+    // unit stopped before it ends it at once.
     if (wid == 0) {
+      for (int e = lane; e < 4 * NP; e += kWave) st_sys(&co.ap[e % NP][e / NP], RL.Q[Cn - 1][e / NP][e % NP]);
+      if (lane < 4) {
+        st_sys(&co.am[lane], RL.ml[lane]);
+        st_sys(&co.al[lane], RL.lam[Cn - 1][lane]);
+      }
       int lo;
       for (uint32_t polls = 0;; ++polls) {
         const int jc = chunk - 1 - lane;
         const int s = jc >= 0 ? (int)(ld_sys(&recs[jc].state) & 3ull) : 2;
-        const uint64_t inc = __ballot(s == 2), agg = __ballot(s >= 1), gone = __ballot(s == 3);
+        if (polls == 0) {
+          wait_vm<0>();  // the aggregate's stores are acknowledged
+          word = 1;
+          if (lane == 0) st_sys(&co.state, word);
+        }
+        // the unit's stop, once some chunk has published it, lies before this
+        // chunk (only the chunk holding it writes it)
+        const int us = (lane == 0 && !detect_only) ? ld_sys(&a.unit_stop[unit]) : 0;
+        const uint64_t inc = __ballot(s == 2), agg = __ballot(s >= 1), gone = __ballot(s == 3 || us > 0);
         if (gone) {
           lo = -3;
           break;
@@ -1118,22 +1124,26 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
       const bool stable = (spr > 0.0) & (stt > 0.0) & crit.scale_ok(spr, stt) & crit.dir_ok(spr, stt, stp);
       RL.bits[j] = (exists ? 2 : 0) | (stable ? 1 : 0);
     }
-    // ---- this chunk's inclusive prefix: P after its last block on the common
-    // maximum, and the mass there
-    if (tid < 4 * NP) {
-      const int g2 = tid / NP, q = tid % NP, g3 = g2 < G ? g2 : 0;
-      const float Mc2 = RL.mc[g3], Ml2 = RL.ml[g3], Ms2 = fmaxf(Mc2, Ml2);
-      const double ca2 = has_carry ? (double)__builtin_amdgcn_exp2f(Mc2 - Ms2) : 0.0;
-      const double cb2 = (double)__builtin_amdgcn_exp2f(Ml2 - Ms2);
-      st_sys(&co.ip[q][g2], fma(ca2, RL.pc[g3][q], cb2 * RL.Q[Cn - 1][g3][q]));
-      if (q == 0) {
-        st_sys(&co.im[g2], Ms2);
-        st_sys(&co.il[g2], fma(ca2, RL.lc[g3], cb2 * RL.lam[Cn - 1][g3]));
-      }
-    }
-    wait_vm<0>();  // every wave's share of the inclusive prefix is acknowledged before the flag
     __syncthreads();
     if (wid == 0) {
+      // ---- this chunk's inclusive prefix: P after its last block on the
+      // common maximum, and the mass there; stored by this wave alone, and
+      // announced with the stop rule's state below (after the wait there)
+      for (int e = lane; e < 4 * NP; e += kWave) {
+        const int g2 = e / NP, q = e % NP, g3 = g2 < G ? g2 : 0;
+        const float Mc2 = RL.mc[g3], Ml2 = RL.ml[g3], Ms2 = fmaxf(Mc2, Ml2);
+        const double ca2 = has_carry ? (double)__builtin_amdgcn_exp2f(Mc2 - Ms2) : 0.0;
+        const double cb2 = (double)__builtin_amdgcn_exp2f(Ml2 - Ms2);
+        st_sys(&co.ip[q][g2], fma(ca2, RL.pc[g3][q], cb2 * RL.Q[Cn - 1][g3][q]));
+      }
+      if (lane < 4) {
+        const int g3 = lane < G ? lane : 0;
+        const float Mc2 = RL.mc[g3], Ml2 = RL.ml[g3], Ms2 = fmaxf(Mc2, Ml2);
+        const double ca2 = has_carry ? (double)__builtin_amdgcn_exp2f(Mc2 - Ms2) : 0.0;
+        const double cb2 = (double)__builtin_amdgcn_exp2f(Ml2 - Ms2);
+        st_sys(&co.im[lane], Ms2);
+        st_sys(&co.il[lane], fma(ca2, RL.lc[g3], cb2 * RL.lam[Cn - 1][g3]));
+      }
       // ---- the chunk's patience descriptor (needs no other chunk's stop rule) ------
       const int bt = lane < Cn ? RL.bits[lane] : 0;
       const uint64_t ex = __ballot((bt & 2) != 0), sb = __ballot(bt == 3);
@@ -1154,9 +1164,9 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
           }
         }
       }
-      word = 2ull | 4ull | ((uint64_t)n_chk << 3) | ((uint64_t)lead << 8) | ((uint64_t)trail << 13) |
+      word = 1ull | 4ull | ((uint64_t)n_chk << 3) | ((uint64_t)lead << 8) | ((uint64_t)trail << 13) |
              ((uint64_t)(run_stop + 1) << 18);
-      if (lane == 0) st_sys(&co.state, word);
+      if (lane == 0) st_sys(&co.state, word);  // the descriptor lives in the word itself
       // ---- the stop rule's state entering the chunk ------------------------------------
       // The nearest predecessor whose state is resolved, carried through the
       // descriptors of the chunks after it (each of them must be written).
@@ -1224,8 +1234,8 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
         RL.stop_local = own;
         RL.outcome = outcome;
       }
-      wait_vm<0>();  // the stop's store is acknowledged before the state
-      word = outcome != 0 ? kDiscardWord : ((word & 0xffffffffull) | ((uint64_t)(uint32_t)state << 32));
+      wait_vm<0>();  // the inclusive prefix's and the stop's stores are acknowledged before the state
+      word = outcome != 0 ? kDiscardWord : (((word & 0xffffffffull) & ~3ull) | 2ull | ((uint64_t)(uint32_t)state << 32));
       if (lane == 0) st_sys(&co.state, word);
     }
     __syncthreads();
