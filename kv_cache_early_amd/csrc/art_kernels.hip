@@ -1,15 +1,15 @@
 // ART decode attention kernels for gfx950 (MI355X).
 //
 // Work decomposition.  One workgroup of W waves (W = blockDim.x / 64) owns
-// one work item = (unit, chunk): unit = (batch b, kv head h) with its G
-// query heads, chunk = a range of positions of the unit's traversal order
-// (the whole traversal in ART mode).  The work item is walked in rounds of W
-// consecutive traversal positions; wave w takes position t0 + w of round t0.
+// one work item = (unit, chunk): unit = (batch b, kv head h) with its query
+// vectors (G query heads times the query rows), chunk = a range of
+// positions of the unit's traversal order.  Wave w walks positions
+// t0 + w, t0 + w + W, ... of the item.
 //
 // Per 64-token ART block a wave
 //   1. has K in MFMA A-operand registers (16-byte loads straight from HBM)
 //      and V in a private 16 KB LDS slab (direct global->LDS loads), both
-//      issued one round ahead;
+//      issued one block ahead;
 //   2. computes the transposed scores S^T = K q^T, 64 tokens x G heads, with
 //      v_mfma_f32_16x16x32_bf16 (v_mfma_f32_16x16x4_f32 for fp32 inputs); the
 //      B operand holds the G query rows replicated over the 16 MFMA columns;
@@ -20,16 +20,21 @@
 //      transposing LDS read ds_read_b64_tr_b16 (fp32: plain LDS reads), and
 //      bf16 P is split into a high and a low bf16 part (two MFMAs), which
 //      keeps P to about 16 significant bits;
-//   5. (ART mode) publishes a block summary: per head its reference max,
-//      its softmax mass and its sums on the probe dims.
-// (ART mode) After a barrier every wave merges the round's summaries in
-// order onto the carried prefix state (fp64 on the probe dims); at its own
-// position a wave forms the probe dot products and publishes them.  After a
-// second barrier every wave runs the two stability tests and the patience
-// counter over the round's positions in order: the first position where
-// `patience` consecutive checks were stable is the stop, blocks after it are
-// discarded and no further loads are issued.  The decision is the one a
-// strictly sequential walk makes.
+//   5. (ART mode) folds the block into the stop rule, in one of two ways:
+//      - one work item per unit: a chain over the positions through LDS.
+//        The wave of position t merges its block's summary (per query
+//        vector its max, mass and sums on the probe dims) onto the prefix
+//        state the wave of t - 1 left, runs the two stability tests and the
+//        patience counter of position t, and hands the state on.  A wave
+//        commits its block only once the state of t - 1 shows no stop
+//        before it, so the stop is the one a strictly sequential walk finds.
+//      - split ART (a unit cut into chunks, one workgroup each): a chunk
+//        walks all its blocks speculatively, keeping their summaries in
+//        LDS, then resolves the stop rule by a decoupled look-back over the
+//        earlier chunks' published prefixes and patience descriptors, and
+//        recomputes its output up to the stop if the stop falls inside it.
+// The waves' states are merged in LDS at the end (log-sum-exp); with several
+// chunks per unit a combine kernel merges the chunks' partial outputs.
 //
 // Method sources: ART paper section 3.1 Eq. (1) (blockwise attention and the
 // partial outputs O^(t)), section 3.2 (probe of scattered head dims);
@@ -137,7 +142,7 @@ __device__ __forceinline__ double col_sum_d(double x) {
   return __builtin_bit_cast(double, ((uint64_t)th[0] << 32) | tl[0]) +
          __builtin_bit_cast(double, ((uint64_t)th[1] << 32) | tl[1]);
 }
-// All-reduce of two fp64 values over the 64 lanes, in lockstep: two
+// All-reduce of three fp64 values over the 64 lanes, in lockstep: three
 // independent chains, so each stage's latency is paid once.  The row stages
 // are DPP moves with bound_ctrl (every lane reads a lane of its own row, so
 // no old value is needed), the column stages the row and half swaps.
@@ -164,19 +169,25 @@ __device__ __forceinline__ double swap_add(double x) {
            __builtin_bit_cast(double, ((uint64_t)h[1] << 32) | l[1]);
   }
 }
-__device__ __forceinline__ void allsum2_d(double& x, double& y) {
+__device__ __forceinline__ void allsum3_d(double& x, double& y, double& z) {
   x += dpp_b<kQx1>(x);
   y += dpp_b<kQx1>(y);
+  z += dpp_b<kQx1>(z);
   x += dpp_b<kQx2>(x);
   y += dpp_b<kQx2>(y);
+  z += dpp_b<kQx2>(z);
   x += dpp_b<kHalfMirror>(x);
   y += dpp_b<kHalfMirror>(y);
+  z += dpp_b<kHalfMirror>(z);
   x += dpp_b<kMirror>(x);
   y += dpp_b<kMirror>(y);
+  z += dpp_b<kMirror>(z);
   x = swap_add<false>(x);
   y = swap_add<false>(y);
+  z = swap_add<false>(z);
   x = swap_add<true>(x);
   y = swap_add<true>(y);
+  z = swap_add<true>(z);
 }
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -489,12 +500,14 @@ __device__ __forceinline__ BlockAddr block_addr4(const UnitView& u, int j, int& 
 // ---------------------------------------------------------------------------
 // LDS layout (one workgroup)
 // ---------------------------------------------------------------------------
-// The stop rule runs as a chain over the traversal positions (ART mode with
-// one work item per unit): the wave holding position t merges its block
-// onto the prefix state after position t - 1, runs the checks of position
-// t and publishes the prefix state after t.  A record holds one lane's
-// share of that state (lane (lg, c): query vectors lg + 4 hh for hh < NH,
-// or lg alone with up to four; probe dims c * PPC .. c * PPC + PPC - 1).
+// The stop rule runs as two chains over the traversal positions (ART mode
+// with one work item per unit): the wave holding position t merges its
+// block onto the prefix state after position t - 1 and publishes the
+// prefix state after t (first chain), then runs the checks of position t
+// and hands the patience counter on (second chain).  A prefix record holds
+// one lane's share of that state (lane (lg, c): query vectors lg + 4 hh for
+// hh < NH, or lg alone with up to four; probe dims c * PPC .. c * PPC +
+// PPC - 1).
 template <int NPL, int NH>
 struct alignas(16) LaneLink {
   double p[NPL];  // prefix numerators on the probe dims, relative to m
@@ -502,11 +515,10 @@ struct alignas(16) LaneLink {
   float m[NH];    // reference max per query vector (log2 domain)
 };
 struct alignas(16) LinkHead {
-  int seq;        // position + 1 once the record of that position is complete
+  int seq;        // position + 1 once the prefix record of that position is complete
+  int seqc;       // position + 1 once counter and detected of that position are written
   int counter;    // consecutive stable checks after the position
   int detected;   // detect-only: the first stop the rule reached, 0 if none
-  int pad;
-  double stt;     // |x|^2 after the position
 };
 template <int NPL, int NH>
 struct alignas(16) RoundLds {
@@ -518,7 +530,7 @@ struct alignas(16) RoundLds {
   int bad;
   int zero_pos;
   int ticket;                          // split ART: this workgroup's work item
-  int flag;                            // split ART: predecessor's carry flag / early stop
+  int flag;                            // split ART: the unit's stop, then the bounding chunk's outcome
 };
 // Split ART: the block summaries of the chunk being walked (pass 0), in
 // the look-back's layout [block][query vector][probe dim]; LDS of their own,
@@ -533,7 +545,10 @@ struct alignas(16) SplitSum {
 // Split ART look-back state (reuses the V slabs, below the waves' stash).
 template <int D>
 struct alignas(16) ReplayLds {
-  double Q[kSplitMax][4][D / 4];  // the chunk's prefix numerators after each block, on its own maximum
+  // the chunk's prefix numerators after each block, on its own maximum; rows
+  // padded by one element, so that the 64 lanes of the per-position reads
+  // (eight positions x four query vectors x two halves) spread over the banks
+  double Q[kSplitMax][4][D / 4 + 1];
   double lam[kSplitMax][4];       // the chunk's prefix mass after each block, on the same maximum
   double pc[4][D / 4];            // the carry's numerators
   double lc[4];                   // the carry's mass
@@ -561,9 +576,9 @@ struct alignas(16) EpilogueLds {     // per-wave final state (reuses the V slabs
 // ---------------------------------------------------------------------------
 // SPLIT: the ordered split-ART instantiation (ticket order, look-back replay,
 // recompute); the other instantiation serves full mode and single-chunk ART.
-// W waves per workgroup: 4 (two workgroups per CU) or 8 (one per CU; single
-// chunk ART with up to 4 query vectors per unit, for calls with at most one
-// unit per CU, where a unit's own walk sets the time).
+// W waves per workgroup: 4 (two workgroups per CU), or 8 on request (one
+// per CU; single-chunk ART with up to 4 query vectors per unit: eight
+// positions of a unit in flight).
 template <int DT, int G, bool PAGED, bool SPLIT, int W>
 __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(KernelArgs a) {
   static_assert(W == 4 || (W == 8 && !SPLIT && G <= 4), "waves per workgroup");
@@ -879,12 +894,14 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
       R.timeout = 0;
       R.head[0].seq = 0;
       R.head[1].seq = 0;
+      R.head[0].seqc = 0;
+      R.head[1].seqc = 0;
     }
     __syncthreads();
   }
 
   // ---- split ART: the stop rule over this chunk, by decoupled look-back -------
-  // After pass 0 the chunk's block summaries are in the workspace.  Thread
+  // After pass 0 the chunk's block summaries are in LDS.  Thread
   // (j, g, hh) forms the chunk's own prefix numerators Q_j and Q_{j-1} of
   // head g on half hh of the probe dims, on the chunk's own maximum Ml, and
   // their products |Q_j|^2 and Q_j.Q_{j-1}; the chunk's aggregate (Ml, its
@@ -1292,21 +1309,30 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
     }
   }
   bool stashed = false;
-  // The stop rule's chain.  The wave holding position t (t = t_begin + wid,
-  // then every W positions) merges its block's summary onto the prefix state
-  // after position t - 1, read from the record its predecessor wave
-  // published, runs the two stability tests and the patience counter of
-  // position t, and publishes the state after t.  Records alternate by
-  // position parity: the record of t - 1 is read (by the wave of t) before
-  // the record of t + 1 can be written, since that one needs the record of
-  // t.  The wave commits its block once the record of t - 1 shows no stop
-  // before it, so no block after the stop is ever committed, and the
-  // decision is the one a strictly sequential walk makes.  No workgroup
-  // barrier sits in the walk: a wave waits only for its predecessor's record.
-  // A stop, once found, is also published in R.stop_at, which every wave
-  // reads before it computes or prefetches a block.
-  // Waits until the record of position t - 1 is there and returns true with
-  // its contents in `in`; false when the unit stopped after at most t blocks
+  // The stop rule as two chains over the positions.  The wave holding
+  // position t (t = t_begin + wid, then every W positions)
+  //   1. reads the prefix record of position t - 1 (the prefix state on the
+  //      probe dims after t - 1), merges its block's summary onto it and
+  //      publishes the prefix record of t at once: elementwise work per
+  //      lane, no reduction on this chain;
+  //   2. forms |x^(t)|^2, x^(t).x^(t-1) and |x^(t-1)|^2 from the two prefix
+  //      states (64-lane reductions, off both chains) and the stability of
+  //      check t;
+  //   3. reads the patience counter after t - 1 (second chain), applies
+  //      check t and publishes the counter after t, and the stop if the
+  //      counter reaches `patience`.
+  // Records alternate by position parity: the record of t - 1 is read (by
+  // the wave of t) before the record of t + 1 can be written, since that
+  // one needs the record of t; the same holds for each chain on its own.
+  // The wave commits its block once the counter after t - 1 is there and
+  // shows no stop before t, so no block after the stop is ever committed,
+  // and the decision is the one a strictly sequential walk makes.  No
+  // workgroup barrier sits in the walk: a wave waits only for its
+  // predecessor's records.  A stop, once found, is also published in
+  // R.stop_at, which every wave reads before it computes or prefetches a
+  // block.
+  // Waits until sequence word `seq` (the head's seq or seqc) of position
+  // t - 1 reads t; false when the unit stopped after at most t blocks
   // (position t does not count).  A poll reads the sequence number, then the
   // stop word; once the sequence number matches, the record is read.  These
   // are ordered LDS reads (LDS serves a wave's accesses in order), and a
@@ -1317,23 +1343,12 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
   // bounded: past a.spin_limit * 4 polls (far beyond any legitimate wait)
   // the wave records a timeout and publishes a stop after the first block,
   // which ends every wave's walk.
-  struct LinkIn {
-    double p[NPL];
-    double l[NH];
-    float m[NH];
-    double stt;
-    int counter, detected;
-  };
-  auto chain_wait = [&](int t, LinkIn& in) -> bool {
-    if constexpr (SPLIT) {
-      return false;
-    } else {
-    const int par = (t - 1) & 1;
+  auto link_wait = [&](int t, const int& seq) -> bool {
     for (uint32_t polls = 0;; ++polls) {
-      const int q = uni(lds_get(R.head[par].seq));
+      const int q = uni(lds_get(seq));
       const int st = uni(lds_get(R.stop_at));
       if (st > 0 && st <= t) return false;
-      if (q == t) break;
+      if (q == t) return true;
       if (polls >= 4u * a.spin_limit) {
         if (lane == 0) {
           lds_put(R.timeout, 1);
@@ -1341,19 +1356,6 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
         }
         return false;
       }
-    }
-    const LaneLink<NPL, NH>& lk = R.link[par][lane];
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) in.p[i] = lds_get(lk.p[i]);
-#pragma unroll
-    for (int hh = 0; hh < NH; ++hh) {
-      in.l[hh] = lds_get(lk.l[hh]);
-      in.m[hh] = lds_get(lk.m[hh]);
-    }
-    in.stt = lds_get(R.head[par].stt);
-    in.counter = lds_get(R.head[par].counter);
-    in.detected = lds_get(R.head[par].detected);
-    return true;
     }
   };
   // The walk over positions t_begin + wid, then every W, up to t_stop.
@@ -1363,12 +1365,13 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
   auto walk = [&](auto passc) __attribute__((always_inline)) {
     constexpr int pass = decltype(passc)::value;
     int t = t_begin + wid;
-    // split ART, pass 0: the unit's stop as read one block before (see below)
+    // split ART, pass 0: the unit's stop as read with the block's K (see below)
     int us_seen = 0;
     BlockAddr cur;
     if (t < t_stop) {
       cur = block_addr4<ROW, PAGED>(u, uni(block_at(u, a.order, t)), bad_page);
       load_k_first(cur);
+      if constexpr (SPLIT && pass == 0) us_seen = gload_sys(split ? a.unit_stop + unit : a.context_lens);
       load_v(cur);
       ++issued;
     }
@@ -1386,12 +1389,14 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
       const int nvalid = cur.nvalid;
       // ---- scores S^T[token][head] = k_token . q_head --------------------------
       if constexpr (SPLIT && pass == 0) {
-        // this block's K, and the unit's stop read with the previous block
-        // (issued before that block's V DMAs, so it has landed with this K)
+        // this block's K, and the unit's stop read with it (issued between
+        // the block's K loads and its V DMAs, so it has landed with this K)
         wait_v_tied_s<kLoads>(kr, us_seen);
-        // a chunk that found the unit's stop lies in an earlier chunk (only
-        // the chunk holding the stop writes it): the rest of this chunk is
-        // past the stop
+        // a published stop lies in an earlier chunk (only the chunk holding
+        // the stop writes it, once every chunk before it has walked): the
+        // rest of this chunk is past the stop.  The waves may leave at
+        // different blocks; the look-back then finds the stop published and
+        // discards the chunk for all of them alike.
         if (!detect_only && uni(us_seen) > 0) break;
       } else {
         wait_v_tied<kLoads>(kr);  // this block's K (its 16 V DMAs were issued after it)
@@ -1598,25 +1603,21 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
 
       bool commit = true, last = false;
       if constexpr (!SPLIT) if (chain) {  // (split ART has no chain)
-        // ---- the prefix state after position t - 1 ------------------------------
+        // ---- first chain: the prefix state after position t - 1 ---------------
         float Mp[NH];
         double Lp[NH], P[NPL];
-        double spr = 0.0;
-        int counter = 0, det = 0;
         bool go = true;
         if (t > t_begin) {
-          LinkIn in;
-          go = uni(chain_wait(t, in) ? 1 : 0) != 0;
+          const int par = (t - 1) & 1;
+          go = uni(link_wait(t, R.head[par].seq) ? 1 : 0) != 0;
+          const LaneLink<NPL, NH>& lk = R.link[par][lane];
 #pragma unroll
-          for (int i = 0; i < NPL; ++i) P[i] = in.p[i];
+          for (int i = 0; i < NPL; ++i) P[i] = lds_get(lk.p[i]);
 #pragma unroll
           for (int hh = 0; hh < NH; ++hh) {
-            Lp[hh] = in.l[hh];
-            Mp[hh] = in.m[hh];
+            Lp[hh] = lds_get(lk.l[hh]);
+            Mp[hh] = lds_get(lk.m[hh]);
           }
-          spr = in.stt;
-          counter = uni(in.counter);
-          det = uni(in.detected);
         } else {
 #pragma unroll
           for (int i = 0; i < NPL; ++i) P[i] = 0.0;
@@ -1630,9 +1631,8 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
           commit = false;
           last = true;
         } else {
-          // ---- merge, |x^(t)|^2 and x^(t).x^(t-1) -------------------------------
+          // ---- merge, and publish the state after position t ------------------
           // x = P / L per query vector (scale free): both on the common maximum
-          double sa = 0.0, sc = 0.0;
           float Mn[NH];
           double Ln[NH], Pn[NPL];
 #pragma unroll
@@ -1641,34 +1641,9 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
             const double fa = (double)__builtin_amdgcn_exp2f(Mp[hh] - Mn[hh]);  // 0 before the first block
             const double fb = (double)__builtin_amdgcn_exp2f(mt[hh] - Mn[hh]);
             Ln[hh] = fma(Lp[hh], fa, lt[hh] * fb);
-            double pa = 0.0, pc = 0.0;
 #pragma unroll
-            for (int i = 0; i < PPC; ++i) {
-              const double pn = fma(P[hh * PPC + i], fa, ps[hh * PPC + i] * fb);
-              pa = fma(pn, pn, pa);
-              pc = fma(pn, P[hh * PPC + i], pc);
-              Pn[hh * PPC + i] = pn;
-            }
-            const double in = recip_d(Ln[hh]);
-            const double ip = Lp[hh] > 0.0 ? recip_d(Lp[hh]) : 0.0;
-            sa = fma(pa, in * in, sa);
-            sc = fma(pc, in * ip, sc);
+            for (int i = 0; i < PPC; ++i) Pn[hh * PPC + i] = fma(P[hh * PPC + i], fa, ps[hh * PPC + i] * fb);
           }
-          const double keep = (G >= 4 || lg < G) ? 1.0 : 0.0;  // rows past G repeat query vector 0
-          double stt = sa * keep, stp = sc * keep;
-          allsum2_d(stt, stp);
-          // a check exists from the second traversal block on
-          const bool exists = t >= 1;
-          const bool stable =
-              exists & (spr > 0.0) & (stt > 0.0) & crit.scale_ok(spr, stt) & crit.dir_ok(spr, stt, stp);
-          counter = exists ? (stable ? counter + 1 : 0) : 0;
-          int st = (exists && counter >= a.patience) ? t + 1 : 0;
-          if (detect_only) {  // keep the first stop, terminate nothing
-            if (st > 0 && det == 0) det = st;
-            st = 0;
-          }
-          st = uni(st);
-          // ---- publish the state after position t ---------------------------------
           LaneLink<NPL, NH>& lo = R.link[t & 1][lane];
 #pragma unroll
           for (int i = 0; i < NPL; ++i) lo.p[i] = Pn[i];
@@ -1677,19 +1652,65 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
             lo.l[hh] = Ln[hh];
             lo.m[hh] = Mn[hh];
           }
-          if (lane == 0) {
-            LinkHead& ho = R.head[t & 1];
-            ho.stt = stt;
-            ho.counter = counter;
-            ho.detected = det;
-            if (st > 0) R.stop_at = st;
-            if (detect_only && det > 0 && det == t + 1) R.detected = det;
-          }
           wait_lgkm0();  // the record is in LDS before its sequence number
           if (lane == 0) lds_put(R.head[t & 1].seq, t + 1);
-          if (st > 0) {
-            stop = st;
+          // ---- |x^(t)|^2, x^(t).x^(t-1), |x^(t-1)|^2 ------------------------------
+          double sa = 0.0, sc = 0.0, sb = 0.0;
+#pragma unroll
+          for (int hh = 0; hh < NH; ++hh) {
+            double pa = 0.0, pc = 0.0, pb = 0.0;
+#pragma unroll
+            for (int i = 0; i < PPC; ++i) {
+              const double pn = Pn[hh * PPC + i], pp = P[hh * PPC + i];
+              pa = fma(pn, pn, pa);
+              pc = fma(pn, pp, pc);
+              pb = fma(pp, pp, pb);
+            }
+            const double in = recip_d(Ln[hh]);
+            const double ip = Lp[hh] > 0.0 ? recip_d(Lp[hh]) : 0.0;
+            sa = fma(pa, in * in, sa);
+            sc = fma(pc, in * ip, sc);
+            sb = fma(pb, ip * ip, sb);
+          }
+          const double keep = (G >= 4 || lg < G) ? 1.0 : 0.0;  // rows past G repeat query vector 0
+          double stt = sa * keep, stp = sc * keep, spr = sb * keep;
+          allsum3_d(stt, stp, spr);
+          // a check exists from the second traversal block on
+          const bool exists = t >= 1;
+          const bool stable =
+              exists & (spr > 0.0) & (stt > 0.0) & crit.scale_ok(spr, stt) & crit.dir_ok(spr, stt, stp);
+          // ---- second chain: the patience counter after position t - 1 ----------
+          int counter = 0, det = 0;
+          if (t > t_begin) {
+            const int par = (t - 1) & 1;
+            go = uni(link_wait(t, R.head[par].seqc) ? 1 : 0) != 0;
+            counter = uni(lds_get(R.head[par].counter));
+            det = uni(lds_get(R.head[par].detected));
+          }
+          if (!go) {
+            commit = false;
             last = true;
+          } else {
+            counter = exists ? (stable ? counter + 1 : 0) : 0;
+            int st = (exists && counter >= a.patience) ? t + 1 : 0;
+            if (detect_only) {  // keep the first stop, terminate nothing
+              if (st > 0 && det == 0) det = st;
+              st = 0;
+            }
+            st = uni(st);
+            if (lane == 0) {
+              LinkHead& ho = R.head[t & 1];
+              ho.counter = counter;
+              ho.detected = det;
+              if (st > 0) R.stop_at = st;
+              if (detect_only && det > 0 && det == t + 1) R.detected = det;
+            }
+            wait_lgkm0();  // counter and stop are in LDS before the sequence number
+            if (lane == 0) lds_put(R.head[t & 1].seqc, t + 1);
+            if (st > 0) {
+              stop = st;
+              last = true;
+            }
           }
         }
       }
