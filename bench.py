@@ -604,6 +604,8 @@ PROFILE_CASES = (
     ("cfg5-A", 5, "A", 1, None, {}, "decode"),
     ("cfg5-B", 5, "B", 1, None, {}, "decode"),
     ("lone-B", 2, "B", 1, None, dict(batch=1, num_q_heads=4, num_kv_heads=1), "decode"),
+    # the same unit walked by one workgroup (split_blocks >= its traversal)
+    ("lone-B-1item", 2, "B", 1, None, dict(batch=1, num_q_heads=4, num_kv_heads=1), "decode", 1 << 20),
 )
 MARKER_KERNEL = "spin_kernel"  # torch.cuda._sleep's kernel: one before each case
 
@@ -633,7 +635,7 @@ def profile_set(args):
     if want is not None and len(cases) != len(want):
         raise SystemExit(f"unknown cases: {sorted(want - {c[0] for c in cases})}")
     manifest, key, w, dev = [], None, None, None
-    for tag, n, reading, mode, patience, over, kind in cases:
+    for tag, n, reading, mode, patience, over, kind, *split in cases:
         k = (n, reading, tuple(sorted(over.items())))
         if k != key:
             del w, dev
@@ -647,7 +649,8 @@ def profile_set(args):
         print(f"[profile] {tag}", file=sys.stderr, flush=True)
         _marker()
         rec = dict(tag=tag, workload=w.spec.name, reading=reading, mode="full" if mode == 0 else "ART",
-                   patience=w.spec.patience, kind=kind, calls=1 + args.warmup + args.steps, steps=args.steps)
+                   patience=w.spec.patience, kind=kind, calls=1 + args.warmup + args.steps, steps=args.steps,
+                   split_blocks=split[0] if split else 0)
         if kind == "select":
             s = w.spec
             mp = int(dev.block_table.shape[1])
@@ -668,7 +671,7 @@ def profile_set(args):
             r, t, _ = measure(dec, w, mode, args, dev=dv, order=ART_ORDER_GIVEN)
             del dv, means, kb, kc
         else:
-            r, t, _ = measure(dec, w, mode, args, dev=dev)
+            r, t, _ = measure(dec, w, mode, args, dev=dev, split_blocks=split[0] if split else None)
         if dec.device_error() != 0:
             raise RuntimeError(f"device error in {tag}")
         rec.update(ms=r["ms"], bytes_algorithmic=int(r["bytes_algorithmic"]), bytes_loaded=int(r["bytes_loaded"]),
@@ -767,7 +770,9 @@ def summarize_set(args):
         ws = cb / (counters[(copy_i, "copy", "WRITE_SIZE")] * 1024.0)
     out = dict(source_sha256=man["source_sha256"], commands=args.command, steps=man["steps"],
                warmup=man["warmup"], fetch_scale=fs, write_scale=ws, cases=[])
-    md = ["# rocprofv3: ART decode kernels over every configuration", "",
+    title = ("over every configuration" if len(recs) >= len(PROFILE_CASES)
+             else "on " + ", ".join(r["tag"] for r in recs if r["kind"] != "copy"))
+    md = [f"# rocprofv3: ART decode kernels {title}", "",
           "Each case: one untimed call, the warmup calls, then the timed calls, each after an untimed 1 GiB "
           "cache-evicting read. Kernel durations are the kernel-trace averages of the timed calls. "
           "`alg GB/s` is the algorithmic bytes (stop_idx x block bytes + per-unit q, out, stop and page-table "
