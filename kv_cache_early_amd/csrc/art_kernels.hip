@@ -1270,27 +1270,28 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
     }
   };
 
-  if (split && chunk > 0 && !detect_only) {  // an earlier chunk already stopped before this one: nothing to do
-    if (tid == 0) R.flag = ld_sys(&a.unit_stop[unit]);
-    __syncthreads();
-    const int us = uni(R.flag);
-    if (us > 0 && us <= t_begin) {
-      discard = true;
-      publish_discard();
-    }
-  }
-  // Bounded speculation: a chunk walks only once the chunk spec_depth places
-  // before it has resolved the stop rule (or the unit's stop).  That chunk
-  // holds a smaller ticket, so it is running or done, and the wait ends.
-  // Without the bound every chunk handed out walks at once, and with few
-  // units nearly all of them lie past the stop.
-  if (split && !discard && a.spec_depth > 0 && chunk >= a.spec_depth) {
-    __syncthreads();  // every wave has read R.flag above
+  // Before its walk a chunk k > 0 learns, in one round trip, whether the
+  // unit has stopped before it (a published stop at or before its first
+  // block), and, for k >= spec_depth, whether the chunk spec_depth places
+  // before it has resolved the stop rule.  The second is the bound on
+  // speculation: a chunk walks only once that chunk has resolved (or the
+  // unit's stop is seen).  That chunk holds a smaller ticket, so it is
+  // running or done, and the wait ends.  Without the bound every chunk
+  // handed out walks at once, and with few units nearly all of them lie past
+  // the stop.  f takes the resolved state's low bits (2: the unit stopped at
+  // or before that chunk's end), 2 for a stop seen published, -1 on timeout.
+  if (split && chunk > 0) {
+    const bool bound = a.spec_depth > 0 && chunk >= a.spec_depth;
     if (tid == 0) {
       int f;
       uint32_t polls = 0;
       for (;;) {
-        f = (int)(ld_sys(&recs[chunk - a.spec_depth].state) >> 32);
+        const int us = detect_only ? 0 : ld_sys(&a.unit_stop[unit]);
+        f = bound ? (int)(ld_sys(&recs[chunk - a.spec_depth].state) >> 32) : 1;
+        if (us > 0 && us <= t_begin) {
+          f = 2;
+          break;
+        }
         if (f != 0) break;
         if (++polls >= a.spin_limit) {
           f = -1;
@@ -1303,7 +1304,7 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
     __syncthreads();
     const int f = uni(R.flag);
     if (f < 0) dev_status = ART_ERR_TIMEOUT;
-    if ((f < 0 || (f & 3) == 2) && !detect_only) {  // the unit stopped at or before that chunk's end
+    if ((f < 0 || (f & 3) == 2) && !detect_only) {  // the unit stopped before this chunk or at the bound
       discard = true;
       publish_discard();
     }
