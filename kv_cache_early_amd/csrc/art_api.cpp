@@ -103,7 +103,7 @@ art_status validate(const art_shape* sp, const art_params* pp) {
 //     about kTargetItems workgroups balance uneven context lengths across
 //     the compute units;
 //   full mode, fewer units than compute units: about one work item per
-//     compute unit.  A work item's first round costs more than the steady
+//     compute unit.  A work item's first block costs more than the steady
 //     state, so many short items lose more than they balance; measured on
 //     MI355X with 128 units of 512 blocks, 0.371 ms at 256 items against
 //     0.409 ms at 2048, and with 32 units of 1024 kept blocks 0.212 ms at
@@ -270,7 +270,6 @@ art_status decode_impl(const art_shape* shape, const art_params* params, const v
   a.chunk_blocks = chunk;
   a.max_chunks = max_chunks;
   a.split_art = (p.mode == ART_MODE_ART && max_chunks > 1) ? 1 : 0;
-  a.max_trav = (int)tmax;
   a.waves = waves_per_item(s, p, max_chunks);
   a.q = q;
   a.k = k;

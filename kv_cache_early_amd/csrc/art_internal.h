@@ -41,7 +41,7 @@ struct alignas(16) Summary {
 // finds its carry and its patience state by looking back over its
 // predecessors' parts instead of waiting for a chain of hand-offs
 // (decoupled look-back).  One state word, written whole by the chunk's
-// thread 0 after the part it announces, says what is there:
+// thread 0 once the part it announces is acknowledged, says what is there:
 //   bits 0-1   prefix: 0 nothing yet; 1 the aggregate is written; 2 the
 //              inclusive prefix is written too; 3 the unit stopped before
 //              this chunk (nothing else is written)
@@ -84,7 +84,6 @@ struct KernelArgs {
   int32_t rows;          // query rows per sequence (q and out are [B][rows][Hq][d])
   int32_t gh;            // query heads per kv head (Hq / Hkv); a unit has rows * gh query vectors
   int32_t split_art;     // ART mode with several chunks per unit (look-back)
-  int32_t max_trav;      // traversal blocks per unit bound (summary row stride)
   int32_t chunk_blocks;  // traversal blocks per work item
   int32_t max_chunks;    // work items per unit
   int32_t waves;         // waves per workgroup, 4 or 8 (one work item per workgroup)

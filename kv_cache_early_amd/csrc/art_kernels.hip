@@ -224,12 +224,12 @@ __device__ __forceinline__ double recip_d(double x) {
 //                            p^2 > (1-phi)^2 a^2 b^2; for phi > 1: p >= 0 or
 //                            p^2 < (phi-1)^2 a^2 b^2.
 // Squaring keeps the comparisons strict and avoids fp64 square roots and
-// divisions on the round's critical path.
+// divisions on the stop rule's critical path.
 struct Criterion {
   double hi, lo, c2;   // (1+tau)^2, (1-tau)^2, (1-phi)^2, computed on the host
   bool tau_lt1, phi_le1;
   // Non-short-circuit forms (bitwise on the comparison results): no
-  // branches on the round's critical path.
+  // branches on the stop rule's critical path.
   __device__ bool scale_ok(double a2, double b2) const {
     return (b2 < hi * a2) & ((!tau_lt1) | (b2 > lo * a2));
   }
@@ -544,7 +544,7 @@ struct alignas(16) SplitSum {
 };
 // Split ART look-back state (reuses the V slabs, below the waves' stash).
 template <int D>
-struct alignas(16) ReplayLds {
+struct alignas(16) LookbackLds {
   // the chunk's prefix numerators after each block, on its own maximum; rows
   // padded by one element, so that the 64 lanes of the per-position reads
   // (eight positions x four query vectors x two halves) spread over the banks
@@ -574,7 +574,7 @@ struct alignas(16) EpilogueLds {     // per-wave final state (reuses the V slabs
 // ---------------------------------------------------------------------------
 // the decode kernel
 // ---------------------------------------------------------------------------
-// SPLIT: the ordered split-ART instantiation (ticket order, look-back replay,
+// SPLIT: the ordered split-ART instantiation (ticket order, look-back,
 // recompute); the other instantiation serves full mode and single-chunk ART.
 // W waves per workgroup: 4 (two workgroups per CU), or 8 on request (one
 // per CU; single-chunk ART with up to 4 query vectors per unit: eight
@@ -599,10 +599,10 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
   __shared__ RoundLds<SPLIT ? 1 : NPL, SPLIT ? 1 : NH> R;
   __shared__ SplitSum<D, SPLIT ? kSplitMax : 1> SS;
   __shared__ alignas(16) uint8_t vbuf[W][kVSlab];
-  // the waves' final state is stashed above the replay state, so a split
-  // chunk can keep its pass-0 result in LDS while the replay runs
+  // the waves' final state is stashed above the look-back state, so a split
+  // chunk can keep its pass-0 result in LDS while the look-back runs
   constexpr int kEpiOff = SPLIT ? 32768 : 0;
-  static_assert(!SPLIT || sizeof(ReplayLds<D>) <= kEpiOff, "look-back state must fit below the stash");
+  static_assert(!SPLIT || sizeof(LookbackLds<D>) <= kEpiOff, "look-back state must fit below the stash");
   static_assert(kEpiOff + sizeof(EpilogueLds<G, D, W>) <= sizeof(vbuf), "stash must fit the V slabs");
 
   const int tid = threadIdx.x;
@@ -901,22 +901,21 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
   }
 
   // ---- split ART: the stop rule over this chunk, by decoupled look-back -------
-  // After pass 0 the chunk's block summaries are in LDS.  Thread
-  // (j, g, hh) forms the chunk's own prefix numerators Q_j and Q_{j-1} of
-  // head g on half hh of the probe dims, on the chunk's own maximum Ml, and
-  // their products |Q_j|^2 and Q_j.Q_{j-1}; the chunk's aggregate (Ml, its
-  // mass, Q after its last block) is published at once.  The carry (the
-  // prefix state P_c, m_c, l_c after the predecessor's last block) is then
-  // the inclusive prefix of the nearest predecessor that has published one,
-  // merged with the aggregates of the chunks after it, so no chunk waits for
-  // its predecessor's own look-back.  On the common maximum M = max(m_c, Ml)
-  // the prefix numerators are P_j = a P_c + b Q_j with a = 2^(m_c - M),
-  // b = 2^(Ml - M), so
+  // After pass 0 the chunk's block summaries are in LDS.  A scan (one thread
+  // per query vector and probe dim) forms the chunk's own prefix numerators
+  // Q_j after each of its blocks j, on the chunk's own maximum Ml, and the
+  // masses; the chunk's aggregate (Ml, its mass, Q after its last block) is
+  // published at once.  The carry (the prefix state P_c, m_c, l_c after the
+  // predecessor's last block) is then the inclusive prefix of the nearest
+  // predecessor that has published one, merged with the aggregates of the
+  // chunks after it, so no chunk waits for its predecessor's own look-back.
+  // On the common maximum M = max(m_c, Ml) the prefix numerators are
+  // P_j = a P_c + b Q_j with a = 2^(m_c - M), b = 2^(Ml - M), so
   //   |P_j|^2       = a^2 |P_c|^2 + 2ab P_c.Q_j + b^2 |Q_j|^2,
-  //   P_j.P_{j-1}   = a^2 |P_c|^2 + ab (P_c.Q_j + P_c.Q_{j-1}) + b^2 Q_j.Q_{j-1},
-  // and P_c.Q_j = sum over i <= j of w_i (P_c . ps_i), w_i = 2^(m_i - Ml):
-  // one dot product per block and a prefix sum.  Eight lanes per position
-  // give |x^(t)|^2 and x^(t).x^(t-1), hence every check of the chunk at once.
+  //   P_j.P_{j-1}   = a^2 |P_c|^2 + ab (P_c.Q_j + P_c.Q_{j-1}) + b^2 Q_j.Q_{j-1}.
+  // Eight lanes per position (four query vectors, two halves of the probe
+  // dims) form these dot products, hence |x^(t)|^2 and x^(t).x^(t-1) and
+  // every check of the chunk at once.
   // The patience counter's passage through a chunk depends on the counter
   // it enters with only through the chunk's leading and trailing stable
   // checks and the first run of `patience` stable checks after its first
@@ -970,8 +969,8 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
     if (cin < a.patience && cin + lead >= a.patience) return (tb == 0 ? 1 : 0) + (a.patience - cin);
     return run_stop;
   };
-  auto split_replay = [&]() -> int {
-    ReplayLds<D>& RL = *reinterpret_cast<ReplayLds<D>*>(&vbuf[0][0]);
+  auto split_lookback = [&]() -> int {
+    LookbackLds<D>& RL = *reinterpret_cast<LookbackLds<D>*>(&vbuf[0][0]);
     ChunkRec<D>& co = recs[chunk];
     const int Cn = t_end - t_begin;
     constexpr int NP = D / 4;  // probe dims
@@ -1742,7 +1741,7 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
     if (split) {
       stash_waves();
       stashed = true;
-      const int stop_local = split_replay();
+      const int stop_local = split_lookback();
       if (!discard && stop_local >= 0 && stop_local < t_end - t_begin) {
         t_stop = t_begin + stop_local;  // recompute the blocks up to the stop
         stashed = false;
@@ -1936,7 +1935,7 @@ static hipError_t launch_g(const KernelArgs& a, int grid, int waves, hipStream_t
   return a.page_size ? launch_t<DT, G, true>(a, grid, waves, s) : launch_t<DT, G, false>(a, grid, waves, s);
 }
 
-// Split ART: zero the ticket, the per-unit stops and the carry flags (a
+// Split ART: zero the ticket, the per-unit stops and the chunks' state words (a
 // kernel rather than a memset, so the call stays safe to capture in a graph).
 template <int D>
 __global__ void art_split_init_kernel(KernelArgs a) {

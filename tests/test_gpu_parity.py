@@ -70,7 +70,7 @@ def test_scaled_configs_one_item_per_unit(torch_cuda, n, reading):
 def test_forced_stop_after_p_plus_one(torch_cuda, p):
     """eps huge: every check is stable, so the stop is at min(T', p+1)."""
     w = make_workload(scaled(3, "B"))
-    # one work item per unit (in-round stopping; split ART is tested below)
+    # one work item per unit (the chain's stop; split ART is tested below)
     _, stop, issued, _ = check(w, tag="huge eps", eps_scale=1e30, eps_dir=1e30, patience=p, split_blocks=10 ** 6,
                                waves=4)
     Tp = w.traversal_lengths()
