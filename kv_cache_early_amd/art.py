@@ -79,6 +79,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise ImportError(f"libart.so not built at {path}; run `python -m kv_cache_early_amd.build`")
+    # torch carries its own HIP runtime: loading it first makes libart bind to
+    # that one, so the process has a single runtime whatever the import order
+    # (a second one, loaded first, does not see the device)
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     vp, i32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
     lib.art_workspace_size.argtypes = [ctypes.POINTER(art_shape), ctypes.POINTER(art_params)]
