@@ -1810,7 +1810,7 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
 // One workgroup per unit, one wave per query vector.  Lane k of a wave
 // holds chunk k's reference max and mass (64 chunks per pass), so the
 // common max and the total mass are wave reductions; the output loop then
-// walks the chunks in order with its independent loads unrolled by four.
+// walks the chunks in order with the loads of sixteen chunks in flight.
 template <int D, int G>
 __global__ __launch_bounds__(kWave * 16) void art_combine_kernel(KernelArgs a) {
   const int unit = blockIdx.x;
@@ -1859,6 +1859,23 @@ __global__ __launch_bounds__(kWave * 16) void art_combine_kernel(KernelArgs a) {
     }
     const int n = min(kWave, n_chunks - k0);
     int j = 0;
+    // sixteen chunks' loads in flight at a time, then four, then one; the
+    // sums still run over the chunks in order
+    for (; j + 16 <= n; j += 16) {
+      float x0[16], x1[16], w[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float* pk = pg + (size_t)(k0 + j + i) * S + 2;
+        x0[i] = pk[lane];
+        x1[i] = D > kWave ? pk[kWave + lane] : 0.f;
+        w[i] = __shfl(wl, j + i, kWave);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        o0 = fmaf(x0[i], w[i], o0);
+        if (D > kWave) o1 = fmaf(x1[i], w[i], o1);
+      }
+    }
     for (; j + 4 <= n; j += 4) {
       float x0[4], x1[4], w[4];
 #pragma unroll
