@@ -227,7 +227,8 @@ def test_full_size_sampled(torch_cuda, n, reading):
     patiences = (1, 2, 4) if n == 4 else (w.spec.patience,)
     from workloads.device import to_device
     dev = to_device(w)
-    splits = (0, 32) if n in (2, 5) else (0,)  # few units: also ordered split ART
+    # few units: the library's choice is split ART; also one work item per unit
+    splits = (0, 1 << 20) if n in (2, 5) else (0,)
     for p in patiences:
         for split in splits:
             out, stop, issued, err = run_gpu(w, patience=p, dev=dev, split_blocks=split)
