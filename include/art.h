@@ -125,10 +125,10 @@ typedef struct {
                             a recompute of the chunk holding the stop);
                             blocks_issued then counts the speculative and
                             re-read blocks, which vary from call to call.
-                            A chunk starts loading only once the chunk 12
+                            A chunk starts loading only once the chunk 16
                             places before it has resolved the stop rule, and
                             stops loading once the unit's stop is published,
-                            so a unit loads at most 11 chunks past its stop
+                            so a unit loads at most 15 chunks past its stop
                             chunk plus that chunk's recompute.
                             The library's choice in ART mode: split ART in
                             16-block chunks when the call has fewer than 256

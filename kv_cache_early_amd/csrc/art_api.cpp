@@ -133,13 +133,15 @@ constexpr int kSplitArtBlocks = 16;   // longest chunk the look-back handles
 constexpr int kSplitArtDefault = 16;  // the library's chunk length for split ART
 // Split ART: a chunk starts its speculative pass only once the chunk this
 // many places before it (same unit) has resolved the stop rule.  Measured
-// on MI355X with 32 units of 1024 kept blocks, criterion firing / never
-// firing: 32-block chunks unbounded 0.312 ms (56% of the kept blocks loaded
-// past the stop), 8 places 0.309 / 0.469 ms (25%); 16-block chunks 8 places
-// 0.284 / 0.517 ms, 12 places 0.254 / 0.428 ms (19%), 16 places 0.269 /
-// 0.415 ms.  With 32 units of 128-512 blocks, 16-block chunks at 12 places:
-// 0.175 / 0.203 ms against 0.217 / 0.229 ms for 32-block chunks at 8.
-constexpr int kSplitArtDepth = 12;
+// on MI355X with 16-block chunks, criterion firing / never firing (share of
+// the kept blocks loaded past the stop): 32 units of 1024 kept blocks, 12
+// places 0.136 / 0.275 ms (13.0%), 16 places 0.130 / 0.265 ms (12.1%), 24
+// places 0.131 / 0.264 ms (13.2%); one unit of 512 blocks 0.063 / 0.085 ms
+// (37.5%), 0.048 / 0.065 ms (24.2%), 0.049 / 0.063 ms (46.1%); 128 units of
+// 512 blocks 0.245 / 0.439 ms at 12 and 0.241 / 0.440 ms at 16.  Fewer
+// places serialize the chunks: 8 places 0.167 ms at 32 units, 4 places
+// 0.245 ms (5.1%).
+constexpr int kSplitArtDepth = 16;
 int chunk_blocks(const art_shape& s, const art_params& p) {
   const int64_t tmax = std::max<int64_t>(1, max_traversal(s));
   if (p.mode == ART_MODE_ART) {

@@ -14,7 +14,7 @@ from workloads import config, make_workload, scaled
 pytestmark = pytest.mark.gpu
 
 SPLIT_MAX = 16  # longest split-ART chunk
-SPEC_DEPTH = 12  # split ART: chunks a unit may walk ahead of its resolved stop rule
+SPEC_DEPTH = 16  # split ART: chunks a unit may walk ahead of its resolved stop rule
 
 
 def EXCUSED_MAX(units):
