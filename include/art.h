@@ -118,7 +118,7 @@ typedef struct {
   int32_t split_blocks;  /* blocks per split-KV chunk; 0 = library's choice,
                             a value >= T' means one chunk per unit.  In ART
                             mode, a value below T' selects ordered split ART
-                            (chunks of min(round4(split_blocks), 16) blocks:
+                            (chunks of min(round4(split_blocks), 24) blocks:
                             a speculative pass per chunk, the stop rule
                             resolved by a look-back over the earlier chunks'
                             published prefixes and patience descriptors, and

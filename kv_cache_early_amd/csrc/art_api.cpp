@@ -123,13 +123,22 @@ constexpr int kWavesPerItem = 4;
 // MI355X); split ART spreads a unit over several CUs, its chunks' passes
 // run in parallel and the stop rule is resolved by a decoupled look-back.
 // Measured on MI355X (one work item per unit / split ART in 16-block
-// chunks): 128 units of 512 blocks 0.394 / 0.249 ms where the criterion
-// fires and 0.448 / 0.441 ms where it never does; 32 units of 1024 kept
-// blocks 0.145 ms split (full mode 0.19 ms); one unit of 512 blocks 0.151
-// / 0.067 ms.  At 512 units of 128-512 blocks one item per unit wins (0.40
+// chunks): 128 units of 512 blocks 0.394 / 0.242 ms where the criterion
+// fires and 0.448 / 0.438 ms where it never does; 32 units of 1024 kept
+// blocks 0.129 ms split (full mode 0.20 ms); one unit of 512 blocks 0.147
+// / 0.048 ms.  At 512 units of 128-512 blocks one item per unit wins (0.40
 // against 0.57 ms): every CU is busy and the chunks' look-backs only add.
 constexpr int64_t kSplitArtUnits = 256;
-constexpr int kSplitArtBlocks = 16;   // longest chunk the look-back handles
+// Chunk length: a chunk's look-back costs about the same whatever its
+// length, so longer chunks spend less of the time in it where nothing
+// stops, and load more blocks past the stop where the criterion fires.
+// Measured on MI355X, 16 / 20 / 24-block chunks, criterion firing (share of
+// the kept blocks loaded past the stop) and never firing: 32 units of 1024
+// kept blocks 0.129 / 0.137 / 0.146 ms (12 / 18 / 23%) and 0.263 / 0.253 /
+// 0.256 ms; 128 units of 512 blocks 0.242 / 0.244 / 0.248 ms (14 / 16 / 18%)
+// and 0.438 / 0.423 / 0.416 ms; one unit of 512 blocks 0.048 / 0.055 /
+// 0.054 ms.  The default favours the calls where the criterion fires.
+constexpr int kSplitArtBlocks = 24;   // longest chunk the look-back handles
 constexpr int kSplitArtDefault = 16;  // the library's chunk length for split ART
 // Split ART: a chunk starts its speculative pass only once the chunk this
 // many places before it (same unit) has resolved the stop rule.  Measured

@@ -520,9 +520,9 @@ struct alignas(16) LinkHead {
   int counter;    // consecutive stable checks after the position
   int detected;   // detect-only: the first stop the rule reached, 0 if none
 };
-template <int NPL, int NH>
+template <int NPL, int NH, int NL>
 struct alignas(16) RoundLds {
-  LaneLink<NPL, NH> link[2][kWave];    // by position parity
+  LaneLink<NPL, NH> link[2][NL];       // by position parity (NL lanes; 1 where no chain runs)
   LinkHead head[2];
   int stop_at;                         // blocks processed at the stop, 0 while none
   int detected;                        // detect-only: the first stop, 0 while none
@@ -535,7 +535,7 @@ struct alignas(16) RoundLds {
 // Split ART: the block summaries of the chunk being walked (pass 0), in
 // the look-back's layout [block][query vector][probe dim]; LDS of their own,
 // written during the walk.
-constexpr int kSplitMax = 16;  // chunk length the look-back handles
+constexpr int kSplitMax = 24;  // chunk length the look-back handles
 template <int D, int N>
 struct alignas(16) SplitSum {
   float m[N][4];        // reference max per query vector
@@ -596,7 +596,7 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
   static_assert(ROW == kRowChunks * 16, "rows must be 16 chunks of 16 bytes");
   // the chain's records are not used by split ART, whose block summaries
   // take LDS of their own instead
-  __shared__ RoundLds<SPLIT ? 1 : NPL, SPLIT ? 1 : NH> R;
+  __shared__ RoundLds<SPLIT ? 1 : NPL, SPLIT ? 1 : NH, SPLIT ? 1 : kWave> R;
   __shared__ SplitSum<D, SPLIT ? kSplitMax : 1> SS;
   __shared__ alignas(16) uint8_t vbuf[W][kVSlab];
   // the waves' final state is stashed above the look-back state, so a split

@@ -191,7 +191,7 @@ def test_art_mode_default_decomposition(batch, split):
     ws = lambda sb: art.workspace_size(s, good_params(split_blocks=sb))
     assert ws(16) != ws(10 ** 6)
     assert ws(0) == (ws(16) if split else ws(10 ** 6))
-    assert ws(32) == ws(16)  # chunks are capped at 16 blocks
+    assert ws(32) == ws(24) != ws(16)  # chunks are capped at 24 blocks
 
 
 # ---------------------------------------------------------------------------

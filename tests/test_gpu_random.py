@@ -39,7 +39,7 @@ def draw_case(seed):
                    order=int(rng.choice([orc.ORDER_NATURAL, orc.ORDER_RECENT_FIRST])),
                    kept_frac=0.5 if kept else 0.0, kept_recent=int(rng.integers(2, 9)), seed=seed + 100)
     mode = 0 if rng.random() < 0.2 else 1
-    split = int(rng.choice([0, 4, 8, 12, 16, 1 << 20]))
+    split = int(rng.choice([0, 4, 8, 12, 16, 20, 24, 1 << 20]))
     flags = 0
     if mode == 1 and rng.random() < 0.3:
         flags = int(rng.choice([orc.FLAG_NO_SCALE, orc.FLAG_NO_DIR, orc.FLAG_DETECT_ONLY]))
