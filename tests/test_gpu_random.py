@@ -2,8 +2,9 @@
 
 The other GPU tests take one option at a time; here every case draws the
 element type, head geometry, ragged lengths, layout and page size, kept
-lists, traversal order, generator, thresholds, patience, mode, chunking,
-stop-rule switches and wave count together, and checks every unit against
+lists (the generator's, or a caller-given traversal), traversal order,
+generator, thresholds, patience, mode, chunking, stop-rule switches, wave
+count and query rows per unit together, and checks every unit against
 the fp64 oracle with the same acceptance rule (stop equal or margin-excused;
 output against the oracle's O^(stop)).  Sizes are small so that the oracle
 finishes in a second or two per case.
@@ -15,11 +16,11 @@ import pytest
 
 import oracle as orc
 from tests.parity import compare, log, run_gpu
-from workloads import config, make_workload
+from workloads import config, make_workload, multi_row_queries
 
 pytestmark = pytest.mark.gpu
 
-CASES = 32
+CASES = 96
 
 
 def draw_case(seed):
@@ -45,7 +46,33 @@ def draw_case(seed):
         flags = int(rng.choice([orc.FLAG_NO_SCALE, orc.FLAG_NO_DIR, orc.FLAG_DETECT_ONLY]))
     # eight waves apply to ART mode with one work item per unit
     waves = 8 if (mode == 1 and split == 1 << 20 and rng.random() < 0.5) else 0
-    return spec, mode, split, flags, waves
+    # query rows per unit, and a caller-given traversal (a kept list in the
+    # caller's order) where the generator made no kept list
+    rows = 1 if rng.random() < 0.7 else int(rng.choice([2, 4]))
+    given = (not kept) and rng.random() < 0.15
+    if g * rows > 4:  # split ART and eight waves take at most 4 query vectors per unit
+        waves = 0
+        if mode == 1 and split not in (0, 1 << 20):
+            split = 1 << 20
+    return spec, mode, split, flags, waves, rows, given
+
+
+def given_lists(w, seed):
+    """A distinct random subset of each unit's blocks in random order (block 0
+    may be absent, or anywhere in the list)."""
+    rng = np.random.default_rng([20251203, seed, 1])
+    s = w.spec
+    T = w.num_blocks
+    kb = np.full((s.batch, s.num_kv_heads, max(1, int(T.max()))), -1, dtype=np.int32)
+    kc = np.zeros((s.batch, s.num_kv_heads), dtype=np.int32)
+    for b in range(s.batch):
+        for h in range(s.num_kv_heads):
+            if T[b] == 0:
+                continue
+            n = int(rng.integers(1, T[b] + 1))
+            kb[b, h, :n] = rng.choice(T[b], size=n, replace=False)
+            kc[b, h] = n
+    w.kept_blocks, w.kept_count = kb, kc
 
 
 @pytest.fixture(scope="module")
@@ -58,12 +85,21 @@ def torch_cuda():
 
 @pytest.mark.parametrize("seed", range(CASES))
 def test_random_combination(torch_cuda, seed):
-    spec, mode, split, flags, waves = draw_case(seed)
+    spec, mode, split, flags, waves, rows, given = draw_case(seed)
     w = make_workload(spec)
-    log(f"[case] seed={seed} {spec} mode={mode} split={split} flags={flags} waves={waves}")
-    out, stop, issued, err = run_gpu(w, mode=mode, split_blocks=split, flags=flags, waves=waves)
+    order = spec.order
+    if given:
+        given_lists(w, seed)
+        order = orc.ORDER_GIVEN
+    qr = qd = None
+    if rows > 1:
+        qr = multi_row_queries(w, rows)
+        qd = torch_cuda.from_numpy(qr.view(np.int16) if qr.dtype == np.uint16 else qr).to("cuda")
+    log(f"[case] seed={seed} {spec} mode={mode} split={split} flags={flags} waves={waves} rows={rows} "
+        f"given={given}")
+    out, stop, issued, err = run_gpu(w, mode=mode, split_blocks=split, flags=flags, waves=waves, order=order, q=qd)
     assert err == 0, f"device error {err}"
-    rep, _ = compare(w, out, stop, mode=mode, flags=flags)
+    rep, _ = compare(w, out, stop, mode=mode, flags=flags, order=order, q_rows=qr)
     log(f"   {rep}")
     assert rep.ok(), (rep.unexcused[:5], rep.bad_outputs[:5])
     assert rep.excused <= -(-rep.units // 100), str(rep)
