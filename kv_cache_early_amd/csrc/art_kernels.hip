@@ -200,6 +200,14 @@ __device__ __forceinline__ int fresh_lane() {
   return l;
 }
 __device__ __forceinline__ float lane_f(float x, int l) { return u2f(__builtin_amdgcn_readlane(f2u(x), l)); }
+// A uniform value the compiler must treat as new at each use: the LDS
+// addresses derived from it are then formed where they are used (one scalar
+// add each) instead of being hoisted out of the walk and kept in spilled
+// scalar registers (a lane read back for every DMA).
+__device__ __forceinline__ uint32_t fresh_s(uint32_t x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
 template <int B, int E, typename F>
@@ -846,6 +854,7 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
   auto load_v = [&](const BlockAddr& ba) {
     wait_lgkm0();  // LDS reads of the previous block have landed
     const int fl = fresh_lane(), flg = fl >> 4, fc = fl & 15;
+    const uint32_t sl = fresh_s(slab);
     if constexpr (PAGED) {
       const uint32_t e = (uint32_t)(flg * ROW + ((fc ^ (2 * flg)) * 16));
       const uint32_t voff[4] = {e, (e ^ 128u) + 4 * ROW, e + 8 * ROW, (e ^ 128u) + 12 * ROW};
@@ -854,7 +863,7 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
         const char* base = u.v + (size_t)ba.row[g] * ROW;
         static_for<0, 4>([&](auto qc) {
           constexpr int q = decltype(qc)::value;
-          lds_dma16s(voff[q], base, slab + (4 * g + q) * 1024);
+          lds_dma16s(voff[q], base, sl + (4 * g + q) * 1024);
         });
       });
     } else {
@@ -863,7 +872,7 @@ __global__ __launch_bounds__(kWave * W, W == 4 ? 2 : 1) void art_decode_kernel(K
       static_for<0, 4 * kTiles>([&](auto nc) {
         constexpr int n = decltype(nc)::value;
         const uint32_t off = (uint32_t)(min(4 * n + flg, last) * ROW + ((fc ^ (2 * flg) ^ (8 * (n & 1))) * 16));
-        lds_dma16s(off, base, slab + n * 1024);
+        lds_dma16s(off, base, sl + n * 1024);
       });
     }
     compiler_fence();
