@@ -133,11 +133,14 @@ typedef struct {
                             The library's choice in ART mode: split ART in
                             16-block chunks when the call has fewer than 256
                             units and at most 4 query vectors per unit, one
-                            chunk per unit otherwise.  In full mode: chunks
-                            of at least 32 blocks, sized so that about 4096
-                            work items balance uneven lengths when the call
-                            has at least 256 units (one per compute unit),
-                            and about 256 work items when it has fewer.
+                            chunk per unit otherwise.  In full mode, with
+                            at least 256 units (one per compute unit):
+                            chunks of at least 32 blocks, sized so that about
+                            4096 work items balance uneven lengths; with
+                            fewer: about 512 work items (two per compute
+                            unit), at least 32 blocks each unless that
+                            leaves compute units without one, never fewer
+                            than 8.
                             Either way
                             stop_idx and out do not depend on the choice
                             beyond floating-point rounding.                 */

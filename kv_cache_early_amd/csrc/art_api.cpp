@@ -102,13 +102,21 @@ art_status validate(const art_shape* sp, const art_params* pp) {
 //   full mode, at least one unit per compute unit: chunks sized so that
 //     about kTargetItems workgroups balance uneven context lengths across
 //     the compute units;
-//   full mode, fewer units than compute units: about one work item per
-//     compute unit.  A work item's first block costs more than the steady
-//     state, so many short items lose more than they balance; measured on
-//     MI355X with 128 units of 512 blocks, 0.371 ms at 256 items against
-//     0.409 ms at 2048, and with 32 units of 1024 kept blocks 0.212 ms at
-//     256 items against 0.280 ms at 1024;
-//   either way at least 32 blocks and a multiple of the wave count;
+//   full mode, fewer units than compute units: about two work items per
+//     compute unit (two workgroups fit on one), but no shorter than 32
+//     blocks unless that leaves compute units without an item, and never
+//     shorter than 8.  A work item's first block costs more than the steady
+//     state, so short items lose more than they balance, while a call that
+//     occupies few compute units is held to what each streams alone.
+//     Measured on MI355X (full mode, chunk length: time): 128 units of 512
+//     blocks 256: 0.368, 128: 0.360, 64: 0.365 ms; 32 units of 1024 kept
+//     blocks 128: 0.198, 64: 0.198, 32: 0.205 ms; 16 units of 512 blocks
+//     32: 0.059, 16: 0.063 ms; 4 units of 512 blocks 32: 0.041, 16: 0.030,
+//     8: 0.028 ms; one unit of 512 blocks 32: 0.039, 16: 0.027, 8: 0.023 ms;
+//   from kComputeUnits units on, at least 32 blocks (measured: 512 units of
+//     128-512 blocks 64: 0.900, 32: 0.912 ms; 1024 units of 256 blocks 64:
+//     1.448, 32: 1.481 ms);
+//   either way a multiple of the wave count;
 //   ART mode: one work item per unit (the stop rule's chain over the
 //     positions) when there are enough units to fill the chip; otherwise
 //     chunks of kSplitArtDefault blocks with look-back (ordered split ART).
@@ -164,9 +172,15 @@ int chunk_blocks(const art_shape& s, const art_params& p) {
   }
   if (p.split_blocks > 0) return (int)std::min<int64_t>(p.split_blocks, tmax);
   const int64_t units = std::max<int64_t>(1, (int64_t)s.batch * s.num_kv_heads);
-  const int64_t target = units < kComputeUnits ? kComputeUnits : kTargetItems;
-  int64_t c = (tmax * units + target - 1) / target;
-  c = std::max<int64_t>(c, 32);
+  const int64_t total = tmax * units;
+  int64_t c;
+  if (units < kComputeUnits) {
+    const int64_t two_per_cu = (total + 2 * kComputeUnits - 1) / (2 * kComputeUnits);
+    const int64_t one_per_cu = (total + kComputeUnits - 1) / kComputeUnits;
+    c = std::max<int64_t>(std::max<int64_t>(two_per_cu, std::min<int64_t>(32, one_per_cu)), 8);
+  } else {
+    c = std::max<int64_t>((total + kTargetItems - 1) / kTargetItems, 32);
+  }
   c = (c + kWavesPerItem - 1) / kWavesPerItem * kWavesPerItem;
   return (int)std::min<int64_t>(c, tmax);
 }

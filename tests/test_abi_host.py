@@ -156,23 +156,27 @@ def test_workspace_size():
     assert full_split > n  # room for the split partials
 
 
-@pytest.mark.parametrize("batch,expect", [
-    (16, 256),  # 128 units x 512 blocks, fewer units than CUs: about 256 work items
-    (4, 64),    # 32 units: about 256 work items
-    (64, 64),   # 512 units: about 4096 work items
-    (32, 32),   # 256 units: about 4096 work items, 32 blocks each
-    (8, 128),   # 64 units: about 256 work items
-    (2, 32),    # 16 units: at least 32 blocks per item
+@pytest.mark.parametrize("batch,hkv,expect", [
+    (16, 8, 128),  # 128 units x 512 blocks, fewer units than CUs: about 512 work items
+    (4, 8, 32),    # 32 units: about 512 work items
+    (64, 8, 64),   # 512 units: about 4096 work items
+    (32, 8, 32),   # 256 units: about 4096 work items, 32 blocks each
+    (8, 8, 64),    # 64 units: about 512 work items
+    (2, 8, 32),    # 16 units: 32 blocks still give every CU an item
+    (1, 4, 8),     # 4 units: shorter items, so that every CU gets one
+    (1, 1, 8),     # one unit: at least 8 blocks per item
 ])
-def test_full_mode_default_decomposition(batch, expect):
+def test_full_mode_default_decomposition(batch, hkv, expect):
     """The workspace holds one partial per work item, so its size shows the
     library's default chunk length: it must equal the size for that chunk
     length given explicitly, and differ from the neighbouring lengths."""
-    s = good_shape(batch=batch, num_q_heads=32, num_kv_heads=8, max_pages=2048, num_pages=4096)  # 512 blocks
+    s = good_shape(batch=batch, num_q_heads=4 * hkv, num_kv_heads=hkv, max_pages=2048, num_pages=4096)  # 512 blocks
     full = lambda sb: art.workspace_size(s, good_params(mode=art.ART_MODE_FULL, split_blocks=sb))
-    units, tmax = batch * 8, 512
-    target = 256 if units < 256 else 4096
-    c = max(32, -(-tmax * units // target))
+    units, tmax = batch * hkv, 512
+    if units < 256:  # two items per CU, not below 32 blocks unless CUs would idle, never below 8
+        c = max(-(-tmax * units // 512), min(32, -(-tmax * units // 256)), 8)
+    else:
+        c = max(32, -(-tmax * units // 4096))
     c = min(-(-c // 4) * 4, tmax)
     assert c == expect
     assert full(0) == full(expect)
