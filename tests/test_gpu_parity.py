@@ -159,6 +159,17 @@ def test_full_mode_split_kv(torch_cuda, split):
     np.testing.assert_array_equal(issued, w.traversal_lengths())
 
 
+@pytest.mark.parametrize("batch,hkv", [(1, 1), (1, 4), (2, 8)])
+def test_full_mode_few_units_default_decomposition(torch_cuda, batch, hkv):
+    """Full mode with fewer units than CUs, library default: about two work
+    items per CU, down to 8-block items for one unit (here 1, 4 and 16
+    units of up to 16k tokens, ragged), merged by the combine kernel."""
+    w = make_workload(config(3, "A", batch=batch, num_q_heads=4 * hkv, num_kv_heads=hkv, ctx=(9000, 16384)))
+    _, stop, issued, _ = check(w, mode=0, tag=f"full default {batch}x{hkv}")
+    np.testing.assert_array_equal(stop, w.traversal_lengths())
+    np.testing.assert_array_equal(issued, w.traversal_lengths())
+
+
 @pytest.mark.parametrize("mode", [0, 1])
 def test_length_ranked_unit_order(torch_cuda, mode):
     """One work item per unit pairs long and short sequences on a CU by
